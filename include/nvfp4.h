@@ -1,0 +1,165 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 quantizer library libnvfp4.so.
+ *
+ * The library implements the hot path of Quartet II, the MS-EDEN unbiased NVFP4 quantizer,
+ * with the plain stochastic-rounding (SR) baseline, round-to-nearest (RTN), the forward-pass
+ * "4/6" grid choice, a producer that emits both packed layouts in one pass, and a
+ * dequantizer.  Definitions follow the pages summarising "Quartet II: Accurate LLM
+ * Pre-Training in NVFP4 by Improved Unbiased Gradient Estimation":
+ *   - Telegram digest quant_prune_distill post 640, section "Method": SR; EDEN (random
+ *     Hadamard rotation, then multiplication by <x,x> / <Q(Rx), Rx>); stochastic rounding of
+ *     the scales to FP8; the 4/6 choice between the (-6,6) and (-4,4) grids; 1x16 groups.
+ *   - itsolotime.com summary, Q1 "theory vs hardware compromises": fixed 128-dim rotation
+ *     groups, one rotation per tensor, no SR for scales below about 1/32000 of the max.
+ *   - rit.work note on "Format-Aware Fusion for Fast FP4 Pretraining": the global NVFP4 max
+ *     is a synchronisation point; one producer writes both layouts a GEMM pair needs.
+ * The arithmetic is fixed in binary32 (one rounding per operation, no FMA contraction) so
+ * that results are reproducible bit for bit; the exact order of every step is written out in
+ * the repository's design notes and in the CPU oracle used by the tests.
+ *
+ * Conventions shared by every entry point
+ *   Pointers.   Every data pointer is a DEVICE pointer allocated by the caller (e.g. a torch
+ *               CUDA/HIP tensor).  The library never allocates and keeps no global state,
+ *               so calls are thread-safe; calls on one stream are ordered.
+ *   Stream.     `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *               work is enqueued asynchronously on it; results are valid once it is
+ *               synchronised.  Nothing is copied to the host: the tensor scale stays on the
+ *               device.
+ *   Errors.     Return 0 on success, a negative NVFP4_ERR_* code otherwise.  Argument
+ *               errors are detected synchronously, before anything is enqueued, and leave
+ *               every output untouched.  NVFP4_ERR_HIP reports a failed launch or no device.
+ *   Input.      x is a row-major BF16 matrix [rows][cols], 16-byte aligned, cols % 8 == 0.
+ *               Values must be finite with |x| < 2^56; other values give unspecified
+ *               codes but no fault.  rows, cols < 2^31 and rows * cols < 2^40.
+ *   Layouts.    The row layout quantizes the rows of X (vectors = rows, n = cols); the
+ *               column layout quantizes the columns (vectors = cols, n = rows), i.e. it is
+ *               the row layout of X^T, with its own tensor scale and random stream.
+ *               Pass NULL for a layout that is not wanted; at least one is required.
+ *               Each layout's n must be a multiple of 128 when the rotation is on (always
+ *               for MS-EDEN) and of 16 otherwise.
+ *   Output.     nvfp4_tensor for a layout with vecs vectors of length n:
+ *                 codes  [vecs][n/2] bytes, byte j = code(2j) | code(2j+1) << 4, where a
+ *                        code is sign << 3 | magnitude index into {0,.5,1,1.5,2,3,4,6};
+ *                        16-byte aligned;
+ *                 scales [vecs][n/16] OCP E4M3FN bytes (one per 1x16 block), 8-byte aligned;
+ *                 tensor_scale: one float g, 4-byte aligned.
+ *               A value decodes as sign * (E4M3(scale) * g) * magnitude; with the rotation
+ *               on, the decoded vector is in the rotated domain (see dequantize).
+ *   group/block Must be 128 and 16 (NVFP4 1x16 blocks; 128-element rotation groups).
+ *   Workspace.  Device scratch of at least nvfp4_workspace_bytes() bytes, 256-byte aligned,
+ *               owned by the caller.  The library clears what it uses on the stream; its
+ *               contents between calls do not matter.  Concurrent calls need distinct
+ *               workspaces.
+ *   Seeds.      rht_seed selects the rotation's random signs, shared by every group and both
+ *               layouts; both operands of one GEMM must use the same rht_seed.  seed drives
+ *               stochastic rounding (Philox4x32-10 counter streams).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_OK 0
+#define NVFP4_ERR_NULL (-1)      /* a required pointer is NULL */
+#define NVFP4_ERR_SHAPE (-2)     /* negative size, or n not a multiple of 128 / 16, cols % 8 */
+#define NVFP4_ERR_GROUP (-3)     /* group != 128 or block != 16 */
+#define NVFP4_ERR_ALIGN (-4)     /* a pointer violates the alignment stated above */
+#define NVFP4_ERR_WORKSPACE (-5) /* workspace NULL or smaller than nvfp4_workspace_bytes() */
+#define NVFP4_ERR_HIP (-6)       /* HIP launch failure or no usable device */
+#define NVFP4_ERR_ARG (-7)       /* other invalid argument (flag value, size too large) */
+
+/* Quantizer selector of the two-phase entry points. */
+#define NVFP4_MODE_RTN 0
+#define NVFP4_MODE_SR 1
+#define NVFP4_MODE_EDEN 2
+#define NVFP4_MODE_FP46 3
+
+typedef struct nvfp4_tensor {
+    uint8_t *codes;      /* [vecs][n/2]  packed E2M1 codes, low nibble first */
+    uint8_t *scales;     /* [vecs][n/16] E4M3FN block scales */
+    float *tensor_scale; /* [1]          FP32 tensor scale g */
+} nvfp4_tensor;
+
+/* Bytes of workspace the quantizers need for a rows x cols input and the layouts in
+ * layouts_mask (bit 0 = row, bit 1 = column).  Never fails; 0 means none needed. */
+size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int layouts_mask);
+
+/* Human-readable text for a status code (static storage). */
+const char *nvfp4_strerror(int status);
+
+/* MS-EDEN (Telegram digest "Method"; itsolotime Q1): per 128-group random-sign Hadamard
+ * rotation r = H(sigma * x); FP32 tensor scale g = amax|r| / 2688; 1x16 E4M3 scales by
+ * round-to-nearest of max|r| / (6g); elements rounded to nearest on the E2M1 grid; EDEN ratio
+ * S = <r,r>/<r,q> per group; each scale replaced by a stochastic rounding of S * scale to
+ * E4M3 (no SR below 2^-6; saturating at 448).  Codes stay the RTN codes.  Decoding gives an
+ * unbiased estimate of r in the rotated domain.  Both layouts in one pass when both given. */
+int eden_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
+                  uint64_t seed, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                  const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* Plain stochastic rounding (itsolotime opening paragraph; Telegram "Method"): tensor scale
+ * amax / 2688, block scale rounded UP to E4M3 (no element clips), each element rounded to
+ * one of its two E2M1 neighbours with probability given by its distance to them.
+ * rht != 0 rotates first (random-sign Hadamard, as MS-EDEN), rht == 0 quantizes x as is. */
+int sr_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
+                uint64_t seed, int rht, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Round-to-nearest NVFP4 (no randomness): tensor scale amax / 2688, block scale and
+ * elements rounded to nearest (ties to even), optional rotation as above. */
+int rtn_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
+                 int rht, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                 const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* Forward-pass 4/6 (Telegram "Method"): tensor scale amax / 1792; per 1x16 block, RTN on
+ * the full +-6 grid (scale max/(6g)) and on the clipped +-4 grid (scale max/(4g)); the block
+ * keeps whichever has the lower sum of squared errors (ties keep +-6).  Optional rotation. */
+int fp46_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
+                  int rht, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                  const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* The two phases of every quantizer above, for callers that must act on the tensor-wide
+ * maximum between them.  The rit.work note on "Format-Aware Fusion for Fast FP4 Pretraining"
+ * ("speedup is lost between matmuls") names the global NVFP4 maximum as the one
+ * synchronisation point of the producer: no scale can be rounded before the partial maxima
+ * of the whole tensor are collected.  A tensor sharded over several GPUs runs phase 1 on
+ * each shard, combines the two floats with an all-reduce(MAX), then runs phase 2.
+ *
+ * Phase 1: amax[0] = max |r| over the row layout, amax[1] = over the column layout, where
+ * r is x rotated per 128-group when rht != 0 (always rotate for MS-EDEN) and x itself
+ * otherwise.  amax is a device float[2] (4-byte aligned) written on `stream`; the slot of a
+ * layout not in layouts_mask (bit 0 row, bit 1 column) is set to 0.  Shape rules as for the
+ * quantizers.  The tensor scale phase 2 derives is amax / 2688 (amax / 1792 for 4/6). */
+int nvfp4_amax(const void *x_bf16, int64_t rows, int64_t cols, int group, int block, int rht,
+               uint64_t rht_seed, int layouts_mask, float *amax, void *stream);
+
+/* Phase 2: quantizer `mode` (NVFP4_MODE_*) of x given the phase-1 maxima in amax (device
+ * float[2], read on `stream`).  Same arguments, outputs and rules as the one-call entry
+ * points (rht is ignored and taken as 1 for MS-EDEN; seed is unused by RTN and 4/6).  With
+ * amax from nvfp4_amax on the same inputs, the result is bit-identical to the one-call
+ * quantizer's. */
+int nvfp4_quantize_amax(int mode, const void *x_bf16, int64_t rows, int64_t cols, int group,
+                        int block, uint64_t seed, int rht, uint64_t rht_seed, const float *amax,
+                        const nvfp4_tensor *row_out, const nvfp4_tensor *col_out, void *stream);
+
+/* Decode vecs vectors of length n from `in` into out [vecs][n] FP32 (device, 16-byte
+ * aligned; codes 8-byte aligned): sign * (E4M3(scale) * g) * magnitude.  With rht != 0 the rotation is undone,
+ * x_j = sigma_j * (H q)_j * 2^-7 (H H = 128 I), using the signs of rht_seed, so the output
+ * is in the original domain; n must then be a multiple of 128 (else of 16). */
+int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int block,
+               int rht, uint64_t rht_seed, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,99 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every entry
+point include/nvfp4.h declares, and rejects bad arguments with the documented status codes
+before touching any device memory."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import unbiased_nvfp4_gradient_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000000  # a well-aligned non-null address; validation never dereferences it
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.LIB_PATH):
+        from unbiased_nvfp4_gradient_amd import build
+
+        build.build()
+    return nv.lib()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert declared == set(nv.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_strerror_and_workspace(L):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert nv.strerror(s)
+    assert nv.strerror(-99) == "unknown status"
+    assert nv.workspace_bytes(16384, 8192, 3) >= 8
+
+
+def _layout(codes=FAKE, scales=FAKE + 4096, g=FAKE + 8192):
+    return ctypes.byref(nv._CTensor(codes, scales, g))
+
+
+def _eden(L, x=FAKE, rows=256, cols=256, group=128, block=16, row=True, col=True, ws=FAKE,
+          wsb=256, row_t=None, col_t=None):
+    r = row_t if row_t is not None else (_layout() if row else None)
+    c = col_t if col_t is not None else (_layout(FAKE + 65536, FAKE + 69632, FAKE + 73728)
+                                         if col else None)
+    return L.eden_quantize(x, rows, cols, group, block, 1, 1, r, c, ws, wsb, None)
+
+
+def test_validation_errors(L):
+    assert _eden(L, x=0) == nv.ERR_NULL
+    assert _eden(L, x=0, rows=0) != nv.ERR_NULL          # an empty input may be NULL
+    assert _eden(L, row=False, col=False) == nv.ERR_NULL
+    assert _eden(L, row_t=_layout(codes=0)) == nv.ERR_NULL
+    assert _eden(L, group=64) == nv.ERR_GROUP
+    assert _eden(L, block=32) == nv.ERR_GROUP
+    assert _eden(L, rows=-1) == nv.ERR_SHAPE
+    assert _eden(L, cols=200) == nv.ERR_SHAPE           # row layout needs cols % 128
+    assert _eden(L, rows=200, row=True, col=True) == nv.ERR_SHAPE
+    assert _eden(L, cols=252) == nv.ERR_SHAPE           # cols % 8
+    assert _eden(L, x=FAKE + 8) == nv.ERR_ALIGN
+    assert _eden(L, row_t=_layout(codes=FAKE + 8)) == nv.ERR_ALIGN
+    assert _eden(L, row_t=_layout(scales=FAKE + 4)) == nv.ERR_ALIGN
+    assert _eden(L, ws=0) == nv.ERR_WORKSPACE
+    assert _eden(L, wsb=8) == nv.ERR_WORKSPACE
+    assert _eden(L, rows=1 << 32) == nv.ERR_ARG
+    # sr / rtn / fp46 without rotation accept n % 16
+    assert L.sr_quantize(FAKE, 256, 200, 128, 16, 1, 0, 1, _layout(), None, FAKE, 256,
+                         None) in (nv.ERR_SHAPE,)           # cols % 8 ok, 200 % 16 != 0
+    assert L.rtn_quantize(FAKE, 256, 256, 128, 16, 2, 1, _layout(), None, FAKE, 256,
+                          None) == nv.ERR_ARG               # rht flag must be 0/1
+    assert L.fp46_quantize(FAKE, 256, 144, 128, 16, 1, 1, _layout(), None, FAKE, 256,
+                           None) == nv.ERR_SHAPE           # rotation needs n % 128
+    t = _layout()
+    assert L.dequantize(None, 4, 128, 128, 16, 0, 0, FAKE, None) == nv.ERR_NULL
+    assert L.dequantize(t, 4, 100, 128, 16, 0, 0, FAKE, None) == nv.ERR_SHAPE
+    assert L.dequantize(t, 4, 144, 128, 16, 1, 0, FAKE, None) == nv.ERR_SHAPE
+    assert L.dequantize(t, 4, 128, 128, 16, 0, 0, FAKE + 4, None) == nv.ERR_ALIGN
+
+
+def _has_gpu():
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="only meaningful on a host without a GPU")
+def test_no_device_is_a_hip_error(L):
+    assert _eden(L) == nv.ERR_HIP

@@ -1,0 +1,158 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle, element by element,
+on the same seeded inputs.  Codes and scales bit-exact outside the 2-ulp boundary band
+(tests/parity.py), tensor scales exact, dequantized values within 1e-6 relative."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import unbiased_nvfp4_gradient_amd as nv
+import workloads
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run_gpu(mode, x, layouts, seed=1, rht=False, rht_seed=1):
+    xd = x.to(DEV)
+    if mode == "eden":
+        q = nv.eden_quantize(xd, seed, rht_seed, layouts=layouts)
+    elif mode == "sr":
+        q = nv.sr_quantize(xd, seed, rht=rht, rht_seed=rht_seed, layouts=layouts)
+    elif mode == "rtn":
+        q = nv.rtn_quantize(xd, rht=rht, rht_seed=rht_seed, layouts=layouts)
+    else:
+        q = nv.fp46_quantize(xd, rht=rht, rht_seed=rht_seed, layouts=layouts)
+    torch.cuda.synchronize()
+    out = {}
+    for axis, t in ((0, q.row), (1, q.col)):
+        if t is not None:
+            out[axis] = (t.codes.cpu().numpy(), t.scales.cpu().numpy(),
+                         float(t.tensor_scale.cpu()[0]), t)
+    return out
+
+
+def check_full(mode, x, layouts, seed=1, rht=False, rht_seed=1, what=""):
+    got = run_gpu(mode, x, layouts, seed, rht, rht_seed)
+    xb = workloads.bf16_bits(x)
+    reps = []
+    for axis, (codes, scales, g, _) in got.items():
+        ref = oracle.quantize(mode, xb, axis=axis, seed=seed, rht=rht, rht_seed=rht_seed)
+        reps.append(assert_parity(mode, codes, scales, g, ref, f"{what} axis={axis}"))
+    return got, reps
+
+
+# ----------------------------------------------------------------------------- small / config 1
+
+@pytest.mark.parametrize("mode,rht", [("rtn", False), ("sr", False), ("eden", True),
+                                      ("fp46", False), ("rtn", True), ("sr", True),
+                                      ("fp46", True)])
+@pytest.mark.parametrize("layouts", [("row",), ("col",), ("row", "col")])
+def test_config1_all_modes(mode, rht, layouts):
+    print(f"case: c1 256x1024 mode={mode} rht={rht} layouts={layouts}", flush=True)
+    check_full(mode, workloads.c1(), layouts, seed=1, rht=rht, rht_seed=1,
+               what=f"c1 {mode} rht={rht}")
+
+
+@pytest.mark.parametrize("shape,mode,rht,layouts", [
+    ((200, 256), "eden", True, ("row",)),          # ragged row count (partial tile)
+    ((256, 200), "eden", True, ("col",)),          # ragged column count
+    ((130, 144), "rtn", False, ("row",)),          # n % 128 != 0 without rotation
+    ((48, 40), "sr", False, ("col",)),             # tiny, n = 48
+    ((144, 48), "fp46", False, ("row", "col")),    # both layouts, ragged, no rotation
+    ((384, 640), "eden", True, ("row", "col")),    # several tiles both ways
+    ((128, 128), "sr", True, ("row", "col")),      # exactly one tile
+])
+def test_ragged_and_multi_tile(shape, mode, rht, layouts):
+    print(f"case: shape={shape} mode={mode} rht={rht} layouts={layouts}", flush=True)
+    x = workloads.normal(shape, seed=sum(shape))
+    check_full(mode, x, layouts, seed=7, rht=rht, rht_seed=3, what=f"{shape} {mode}")
+
+
+def test_zero_and_empty():
+    print("case: zeros 256x256 and empty 0x256 / 256x0", flush=True)
+    z = torch.zeros(256, 256, dtype=torch.bfloat16)
+    got, _ = check_full("eden", z, ("row", "col"), what="zeros")
+    for codes, scales, g, _ in got.values():
+        assert g == 0.0 and not codes.any() and not scales.any()
+    for shape, lay in (((0, 256), ("row",)), ((256, 0), ("col",))):
+        x = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+        q = nv.eden_quantize(x, 1, 1, layouts=lay)
+        torch.cuda.synchronize()
+        t = q.row if q.row is not None else q.col
+        assert t.codes.numel() == 0 and float(t.tensor_scale.cpu()[0]) == 0.0
+
+
+def test_extreme_magnitudes():
+    """Tiny values (subnormal products, scales below 2^-6 and zero scales) and large ones."""
+    rng = np.random.default_rng(0)
+    base = rng.standard_normal((256, 256))
+    mags = 10.0 ** rng.uniform(-30, 30, (256, 1))
+    x = workloads.to_bf16(base * mags)
+    print("case: magnitudes 1e-30..1e30 per row", flush=True)
+    for mode, rht in (("eden", True), ("rtn", False), ("sr", False), ("fp46", True)):
+        check_full(mode, x, ("row", "col"), rht=rht, what=f"extreme {mode}")
+
+
+def test_determinism():
+    print("case: determinism eden c1 both layouts", flush=True)
+    x = workloads.c1()
+    a = run_gpu("eden", x, ("row", "col"))
+    b = run_gpu("eden", x, ("row", "col"))
+    for axis in a:
+        assert np.array_equal(a[axis][0], b[axis][0]) and np.array_equal(a[axis][1], b[axis][1])
+
+
+# ----------------------------------------------------------------------------- configs 2 and 3
+
+def test_config2_fp46_both_layouts():
+    print("case: c2 4096x4096 fp46 rht both layouts", flush=True)
+    check_full("fp46", workloads.c2(), ("row", "col"), rht=True, rht_seed=1, what="c2")
+
+
+def test_config3_eden_both_layouts():
+    print("case: c3 16384x2048 eden both layouts", flush=True)
+    check_full("eden", workloads.c3(), ("row", "col"), seed=1, rht_seed=1, what="c3")
+
+
+# ----------------------------------------------------------------------------- config 4 (sampled)
+
+def test_config4_eden_sampled():
+    """Full 16384 x 8192 in the benchmark's launch configuration; the oracle computes the
+    exact amax over the whole tensor, then quantizes sampled rows and columns."""
+    print("case: c4 16384x8192 eden both layouts, sampled vectors", flush=True)
+    x = workloads.c4()
+    xb = workloads.bf16_bits(x)
+    got = run_gpu("eden", x, ("row", "col"), seed=1, rht_seed=1)
+    rng = np.random.default_rng(0)
+    for axis in (0, 1):
+        codes, scales, g, _ = got[axis]
+        amax = oracle.amax(xb, axis, True, 1)
+        ref_g = oracle.tensor_scale("eden", amax)
+        assert np.float32(g) == np.float32(ref_g)
+        nvec = codes.shape[0]
+        ids = np.unique(np.concatenate([[0, nvec - 1], rng.choice(nvec, 48, replace=False)]))
+        ref = oracle.quantize_vectors("eden", xb, axis, ids, ref_g, seed=1, rht_seed=1)
+        assert_parity("eden", codes[ids], scales[ids], g, ref, f"c4 axis={axis}")
+
+
+# ----------------------------------------------------------------------------- dequantize
+
+@pytest.mark.parametrize("mode,rht", [("eden", True), ("rtn", False), ("fp46", True)])
+def test_dequantize_parity(mode, rht):
+    print(f"case: dequantize {mode} rht={rht}", flush=True)
+    x = workloads.c1()
+    got = run_gpu(mode, x, ("row", "col"), rht=rht)
+    rot = rht or mode == "eden"
+    for axis, (codes, scales, g, t) in got.items():
+        out = nv.dequantize(t, rht=rot, rht_seed=1)
+        torch.cuda.synchronize()
+        ref = oracle.dequantize(codes, scales, g, rht=rot, rht_seed=1)
+        o = out.cpu().numpy()
+        # the codes matched the oracle (checked above), so the decode must match too
+        scale = np.maximum(np.abs(ref), np.sqrt((ref.reshape(ref.shape[0], -1, 16) ** 2)
+                                                 .mean(-1)).repeat(16, -1))
+        assert np.all(np.abs(o - ref) <= 1e-6 * scale), (mode, axis)
+        assert np.array_equal(o, ref)   # same operations in the same order: bit-exact

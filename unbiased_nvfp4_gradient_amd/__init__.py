@@ -1,0 +1,224 @@
+"""MI355X-native NVFP4 quantizers of Quartet II (MS-EDEN, SR, RTN, 4/6) -- Python binding.
+
+This module only marshals arguments to the C ABI of ``libnvfp4.so`` (declared in
+``include/nvfp4.h``); every step of the quantizers runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no CPU fallback: if the
+library is missing, or a call fails, a RuntimeError is raised.
+
+Layouts: ``"row"`` quantizes the rows of X (groups along the columns), ``"col"`` the
+columns (groups along the rows, i.e. the row layout of X^T); each layout has its own tensor
+scale and random stream.  Results are ``NVFP4`` triples of device tensors:
+codes uint8 [vecs, n/2] (low nibble = even position), scales uint8 [vecs, n/16] (E4M3FN
+bits; ``.view(torch.float8_e4m3fn)`` works), tensor_scale float32 [1].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+GROUP = 128
+BLOCK = 16
+
+# status codes (include/nvfp4.h)
+OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_ARG = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+
+EXPORTED = ("nvfp4_workspace_bytes", "nvfp4_strerror", "eden_quantize", "sr_quantize",
+            "rtn_quantize", "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize")
+
+MODE_RTN, MODE_SR, MODE_EDEN, MODE_FP46 = 0, 1, 2, 3
+MODES = {"rtn": MODE_RTN, "sr": MODE_SR, "eden": MODE_EDEN, "fp46": MODE_FP46}
+
+
+class _CTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p)]
+
+
+class NVFP4(NamedTuple):
+    codes: torch.Tensor         # uint8 [vecs, n/2]
+    scales: torch.Tensor        # uint8 [vecs, n/16], E4M3FN bits
+    tensor_scale: torch.Tensor  # float32 [1]
+
+
+class Quantized(NamedTuple):
+    row: Optional[NVFP4]
+    col: Optional[NVFP4]
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {strerror(status)}")
+        self.status = status
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libnvfp4.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m unbiased_nvfp4_gradient_amd.build`")
+    h = ctypes.CDLL(LIB_PATH)
+    P, i64, u64, i32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int,
+                            ctypes.c_size_t)
+    TP = ctypes.POINTER(_CTensor)
+    h.nvfp4_workspace_bytes.argtypes = [i64, i64, i32]
+    h.nvfp4_workspace_bytes.restype = sz
+    h.nvfp4_strerror.argtypes = [i32]
+    h.nvfp4_strerror.restype = ctypes.c_char_p
+    h.eden_quantize.argtypes = [P, i64, i64, i32, i32, u64, u64, TP, TP, P, sz, P]
+    h.sr_quantize.argtypes = [P, i64, i64, i32, i32, u64, i32, u64, TP, TP, P, sz, P]
+    h.rtn_quantize.argtypes = [P, i64, i64, i32, i32, i32, u64, TP, TP, P, sz, P]
+    h.fp46_quantize.argtypes = [P, i64, i64, i32, i32, i32, u64, TP, TP, P, sz, P]
+    h.dequantize.argtypes = [TP, i64, i64, i32, i32, i32, u64, P, P]
+    h.nvfp4_amax.argtypes = [P, i64, i64, i32, i32, i32, u64, i32, P, P]
+    h.nvfp4_quantize_amax.argtypes = [i32, P, i64, i64, i32, i32, u64, i32, u64, P, TP, TP, P]
+    for name in ("eden_quantize", "sr_quantize", "rtn_quantize", "fp46_quantize", "dequantize",
+                 "nvfp4_amax", "nvfp4_quantize_amax"):
+        getattr(h, name).restype = i32
+    _lib_handle = h
+    return h
+
+
+def strerror(status: int) -> str:
+    return lib().nvfp4_strerror(int(status)).decode()
+
+
+def workspace_bytes(rows: int, cols: int, layouts_mask: int = 3) -> int:
+    return int(lib().nvfp4_workspace_bytes(rows, cols, layouts_mask))
+
+
+def _stream_ptr(stream, device) -> Optional[int]:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def empty_layout(vecs: int, n: int, device) -> NVFP4:
+    """Caller-side allocation of one layout's outputs."""
+    return NVFP4(torch.empty((vecs, n // 2), dtype=torch.uint8, device=device),
+                 torch.empty((vecs, n // BLOCK), dtype=torch.uint8, device=device),
+                 torch.empty((1,), dtype=torch.float32, device=device))
+
+
+def _ct(t: Optional[NVFP4]):
+    if t is None:
+        return None
+    return ctypes.byref(_CTensor(t.codes.data_ptr(), t.scales.data_ptr(),
+                                 t.tensor_scale.data_ptr()))
+
+
+def _prepare(x: torch.Tensor, layouts: Sequence[str], out: Optional[Quantized], workspace):
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
+    rows, cols = x.shape
+    want_row, want_col = "row" in layouts, "col" in layouts
+    if out is None:
+        out = Quantized(empty_layout(rows, cols, x.device) if want_row else None,
+                        empty_layout(cols, rows, x.device) if want_col else None)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(rows, cols, (1 if want_row else 0) |
+                                                (2 if want_col else 0)),
+                                dtype=torch.uint8, device=x.device)
+    return rows, cols, out, workspace
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise NVFP4Error(fn, status)
+
+
+def eden_quantize(x: torch.Tensor, seed: int, rht_seed: int, layouts=("row", "col"),
+                  out: Optional[Quantized] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> Quantized:
+    """MS-EDEN NVFP4 quantization (see include/nvfp4.h)."""
+    rows, cols, out, ws = _prepare(x, layouts, out, workspace)
+    _check("eden_quantize", lib().eden_quantize(
+        x.data_ptr(), rows, cols, GROUP, BLOCK, seed, rht_seed, _ct(out.row), _ct(out.col),
+        ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
+    return out
+
+
+def sr_quantize(x: torch.Tensor, seed: int, rht: bool = False, rht_seed: int = 0,
+                layouts=("row",), out: Optional[Quantized] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> Quantized:
+    """Plain stochastic-rounding NVFP4 quantization (optionally rotated first)."""
+    rows, cols, out, ws = _prepare(x, layouts, out, workspace)
+    _check("sr_quantize", lib().sr_quantize(
+        x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed, _ct(out.row),
+        _ct(out.col), ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
+    return out
+
+
+def rtn_quantize(x: torch.Tensor, rht: bool = False, rht_seed: int = 0, layouts=("row",),
+                 out: Optional[Quantized] = None, workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> Quantized:
+    """Round-to-nearest NVFP4 quantization (optionally rotated first)."""
+    rows, cols, out, ws = _prepare(x, layouts, out, workspace)
+    _check("rtn_quantize", lib().rtn_quantize(
+        x.data_ptr(), rows, cols, GROUP, BLOCK, int(bool(rht)), rht_seed, _ct(out.row),
+        _ct(out.col), ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
+    return out
+
+
+def fp46_quantize(x: torch.Tensor, rht: bool = False, rht_seed: int = 0,
+                  layouts=("row", "col"), out: Optional[Quantized] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> Quantized:
+    """Forward-pass 4/6 NVFP4 quantization (optionally rotated first)."""
+    rows, cols, out, ws = _prepare(x, layouts, out, workspace)
+    _check("fp46_quantize", lib().fp46_quantize(
+        x.data_ptr(), rows, cols, GROUP, BLOCK, int(bool(rht)), rht_seed, _ct(out.row),
+        _ct(out.col), ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
+    return out
+
+
+def nvfp4_amax(x: torch.Tensor, rht: bool, rht_seed: int = 0, layouts=("row", "col"),
+               amax: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Phase 1: float32 [2] device tensor (row, column) of max |r| (rotated when rht)."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
+    if amax is None:
+        amax = torch.empty((2,), dtype=torch.float32, device=x.device)
+    mask = (1 if "row" in layouts else 0) | (2 if "col" in layouts else 0)
+    _check("nvfp4_amax", lib().nvfp4_amax(
+        x.data_ptr(), x.shape[0], x.shape[1], GROUP, BLOCK, int(bool(rht)), rht_seed, mask,
+        amax.data_ptr(), _stream_ptr(stream, x.device)))
+    return amax
+
+
+def nvfp4_quantize_amax(mode: str, x: torch.Tensor, amax: torch.Tensor, seed: int = 0,
+                        rht: bool = False, rht_seed: int = 0, layouts=("row", "col"),
+                        out: Optional[Quantized] = None, stream=None) -> Quantized:
+    """Phase 2: quantizer `mode` ("rtn", "sr", "eden", "fp46") given phase-1 maxima."""
+    rows, cols, out, _ = _prepare(x, layouts, out, amax)
+    _check("nvfp4_quantize_amax", lib().nvfp4_quantize_amax(
+        MODES[mode], x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
+        amax.data_ptr(), _ct(out.row), _ct(out.col), _stream_ptr(stream, x.device)))
+    return out
+
+
+def dequantize(t: NVFP4, rht: bool = False, rht_seed: int = 0,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode one layout to float32 [vecs, n]; undoes the rotation when rht is set."""
+    vecs, n = t.codes.shape[0], t.codes.shape[1] * 2
+    if out is None:
+        out = torch.empty((vecs, n), dtype=torch.float32, device=t.codes.device)
+    _check("dequantize", lib().dequantize(
+        _ct(t), vecs, n, GROUP, BLOCK, int(bool(rht)), rht_seed, out.data_ptr(),
+        _stream_ptr(stream, t.codes.device)))
+    return out
+
+
+__all__ = ["NVFP4", "Quantized", "NVFP4Error", "eden_quantize", "sr_quantize", "rtn_quantize",
+           "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize", "workspace_bytes", "strerror", "empty_layout", "lib",
+           "LIB_PATH", "EXPORTED"]

@@ -1,0 +1,231 @@
+// nvfp4_api.cpp -- C ABI of libnvfp4.so: argument validation and dispatch to the gfx950
+// kernels in nvfp4_kernels.hip.  The declarations, with the meaning, layout, ownership and
+// error behaviour of every argument, are in include/nvfp4.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+extern "C" hipError_t nvfp4k_amax(int rht, int layouts, const void *x, int64_t R, int64_t C,
+                                  float *amax, uint64_t rht_seed, hipStream_t st);
+extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x, int64_t R,
+                                   int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
+                                   uint8_t *codes1, uint8_t *scales1, float *g1,
+                                   const float *amax, uint64_t seed, uint64_t rht_seed,
+                                   hipStream_t st);
+extern "C" hipError_t nvfp4k_dequantize(const uint8_t *codes, const uint8_t *scales,
+                                        const float *g, int64_t vecs, int64_t n, int rht,
+                                        uint64_t rht_seed, float *out, hipStream_t st);
+
+namespace {
+
+enum { MODE_RTN = 0, MODE_SR = 1, MODE_EDEN = 2, MODE_FP46 = 3 };
+
+constexpr size_t WORKSPACE_BYTES = 256;       // two u32 amax slots, padded
+constexpr int64_t MAX_DIM = (int64_t)1 << 31; // each dimension
+constexpr int64_t MAX_ELEMS = (int64_t)1 << 40;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_device()
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return NVFP4_ERR_HIP;
+    }
+    return NVFP4_OK;
+}
+
+// A layout with no elements may pass NULL codes and scales (its tensor scale is still set).
+int check_layout(const nvfp4_tensor *t, bool empty)
+{
+    if (!t) return NVFP4_OK;
+    if (!t->tensor_scale || (!empty && (!t->codes || !t->scales))) return NVFP4_ERR_NULL;
+    if (!aligned(t->codes, 16) || !aligned(t->scales, 8) || !aligned(t->tensor_scale, 4))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+// Checks shared by every quantizer entry point (everything but the workspace and amax).
+int check_input(int mode, const void *x, int64_t rows, int64_t cols, int group, int block, int rht,
+                bool want_row, bool want_col)
+{
+    if (!x && rows > 0 && cols > 0) return NVFP4_ERR_NULL;
+    if (group != 128 || block != 16) return NVFP4_ERR_GROUP;
+    if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
+    if (mode < MODE_RTN || mode > MODE_FP46) return NVFP4_ERR_ARG;
+    if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+    if (rows > MAX_DIM || cols > MAX_DIM || (rows > 0 && cols > MAX_ELEMS / rows))
+        return NVFP4_ERR_ARG;
+    const bool rotated = rht || mode == MODE_EDEN;
+    const int64_t unit = rotated ? 128 : 16;
+    if (cols % 8) return NVFP4_ERR_SHAPE;
+    if (want_row && cols % unit) return NVFP4_ERR_SHAPE;
+    if (want_col && rows % unit) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+int check_outputs(const nvfp4_tensor *row_out, const nvfp4_tensor *col_out, int64_t rows,
+                  int64_t cols)
+{
+    if (!row_out && !col_out) return NVFP4_ERR_NULL;
+    const bool empty = rows == 0 || cols == 0;
+    int rc = check_layout(row_out, empty);
+    return rc ? rc : check_layout(col_out, empty);
+}
+
+int launch_quant(int mode, const void *x, int64_t rows, int64_t cols, uint64_t seed, int rht,
+                 uint64_t rht_seed, const float *amax, const nvfp4_tensor *row_out,
+                 const nvfp4_tensor *col_out, void *stream)
+{
+    const int layouts = (row_out ? 1 : 0) | (col_out ? 2 : 0);
+    const bool rotated = rht || mode == MODE_EDEN;
+    hipError_t e = nvfp4k_quant(
+        mode, rotated ? 1 : 0, layouts, x, rows, cols, row_out ? row_out->codes : nullptr,
+        row_out ? row_out->scales : nullptr, row_out ? row_out->tensor_scale : nullptr,
+        col_out ? col_out->codes : nullptr, col_out ? col_out->scales : nullptr,
+        col_out ? col_out->tensor_scale : nullptr, amax, seed, rht_seed,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+int quantize_common(int mode, const void *x, int64_t rows, int64_t cols, int group, int block,
+                    uint64_t seed, int rht, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                    const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
+                    void *stream)
+{
+    int rc = check_outputs(row_out, col_out, rows, cols);
+    if (rc) return rc;
+    rc = check_input(mode, x, rows, cols, group, block, rht, row_out != nullptr,
+                     col_out != nullptr);
+    if (rc) return rc;
+    if (!workspace || workspace_bytes < WORKSPACE_BYTES) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+    rc = check_device();
+    if (rc) return rc;
+    const int layouts = (row_out ? 1 : 0) | (col_out ? 2 : 0);
+    const bool rotated = rht || mode == MODE_EDEN;
+    float *amax = static_cast<float *>(workspace);
+    hipError_t e = nvfp4k_amax(rotated ? 1 : 0, layouts, x, rows, cols, amax, rht_seed,
+                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return NVFP4_ERR_HIP;
+    return launch_quant(mode, x, rows, cols, seed, rht, rht_seed, amax, row_out, col_out, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int layouts_mask)
+{
+    (void)rows;
+    (void)cols;
+    (void)layouts_mask;
+    return WORKSPACE_BYTES;
+}
+
+const char *nvfp4_strerror(int status)
+{
+    switch (status) {
+    case NVFP4_OK: return "success";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "unsupported shape (negative size, cols % 8, or n not a multiple of 128/16)";
+    case NVFP4_ERR_GROUP: return "group must be 128 and block must be 16";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_HIP: return "HIP error (launch failure or no device)";
+    case NVFP4_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+    }
+}
+
+int eden_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
+                  uint64_t seed, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                  const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
+                  void *stream)
+{
+    return quantize_common(MODE_EDEN, x_bf16, rows, cols, group, block, seed, 1, rht_seed,
+                           row_out, col_out, workspace, workspace_bytes, stream);
+}
+
+int sr_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
+                uint64_t seed, int rht, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
+                void *stream)
+{
+    return quantize_common(MODE_SR, x_bf16, rows, cols, group, block, seed, rht, rht_seed,
+                           row_out, col_out, workspace, workspace_bytes, stream);
+}
+
+int rtn_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block, int rht,
+                 uint64_t rht_seed, const nvfp4_tensor *row_out, const nvfp4_tensor *col_out,
+                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    return quantize_common(MODE_RTN, x_bf16, rows, cols, group, block, 0, rht, rht_seed,
+                           row_out, col_out, workspace, workspace_bytes, stream);
+}
+
+int fp46_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block, int rht,
+                  uint64_t rht_seed, const nvfp4_tensor *row_out, const nvfp4_tensor *col_out,
+                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    return quantize_common(MODE_FP46, x_bf16, rows, cols, group, block, 0, rht, rht_seed,
+                           row_out, col_out, workspace, workspace_bytes, stream);
+}
+
+int nvfp4_amax(const void *x_bf16, int64_t rows, int64_t cols, int group, int block, int rht,
+               uint64_t rht_seed, int layouts_mask, float *amax, void *stream)
+{
+    if (!amax) return NVFP4_ERR_NULL;
+    if (layouts_mask < 1 || layouts_mask > 3) return NVFP4_ERR_ARG;
+    int rc = check_input(MODE_RTN, x_bf16, rows, cols, group, block, rht, layouts_mask & 1,
+                         layouts_mask & 2);
+    if (rc) return rc;
+    if (!aligned(amax, 4)) return NVFP4_ERR_ALIGN;
+    rc = check_device();
+    if (rc) return rc;
+    hipError_t e = nvfp4k_amax(rht, layouts_mask, x_bf16, rows, cols, amax, rht_seed,
+                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+int nvfp4_quantize_amax(int mode, const void *x_bf16, int64_t rows, int64_t cols, int group,
+                        int block, uint64_t seed, int rht, uint64_t rht_seed, const float *amax,
+                        const nvfp4_tensor *row_out, const nvfp4_tensor *col_out, void *stream)
+{
+    if (!amax) return NVFP4_ERR_NULL;
+    int rc = check_outputs(row_out, col_out, rows, cols);
+    if (rc) return rc;
+    rc = check_input(mode, x_bf16, rows, cols, group, block, rht, row_out != nullptr,
+                     col_out != nullptr);
+    if (rc) return rc;
+    if (!aligned(amax, 4)) return NVFP4_ERR_ALIGN;
+    rc = check_device();
+    if (rc) return rc;
+    return launch_quant(mode, x_bf16, rows, cols, seed, rht, rht_seed, amax, row_out, col_out,
+                        stream);
+}
+
+int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int block, int rht,
+               uint64_t rht_seed, float *out, void *stream)
+{
+    if (!in || !in->tensor_scale) return NVFP4_ERR_NULL;
+    if ((vecs > 0 && n > 0) && (!out || !in->codes || !in->scales)) return NVFP4_ERR_NULL;
+    if (group != 128 || block != 16) return NVFP4_ERR_GROUP;
+    if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
+    if (vecs < 0 || n < 0) return NVFP4_ERR_SHAPE;
+    if (vecs > MAX_DIM || n > MAX_DIM || (vecs > 0 && n > MAX_ELEMS / vecs)) return NVFP4_ERR_ARG;
+    if (n % (rht ? 128 : 16)) return NVFP4_ERR_SHAPE;
+    if (!aligned(in->codes, 8) || !aligned(in->scales, 1) || !aligned(in->tensor_scale, 4) ||
+        !aligned(out, 16))
+        return NVFP4_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = nvfp4k_dequantize(in->codes, in->scales, in->tensor_scale, vecs, n, rht,
+                                     rht_seed, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+}  // extern "C"

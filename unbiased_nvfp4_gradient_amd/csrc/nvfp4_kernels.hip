@@ -1,0 +1,696 @@
+// nvfp4_kernels.hip -- gfx950 kernels of the NVFP4 quantizers (MS-EDEN, SR, RTN, 4/6) and
+// the dequantizer.
+//
+// Method sources (pages summarising "Quartet II: Accurate LLM Pre-Training in NVFP4 by
+// Improved Unbiased Gradient Estimation"):
+//   - Telegram digest quant_prune_distill post 640, "Method": SR; EDEN = random Hadamard
+//     rotation + correction by <x,x>/<Q(Rx),Rx>; FP8 scales rounded stochastically; 4/6
+//     choice between the +-6 and +-4 grids; 1x16 groups.
+//   - itsolotime.com summary, Q1 "theory vs hardware compromises": 128-dim rotation groups,
+//     one rotation per tensor, no SR for scales below about 1/32000 of the max.
+//   - rit.work note on "Format-Aware Fusion for Fast FP4 Pretraining": the global max is a
+//     synchronisation point; one producer writes both layouts.
+//
+// Arithmetic is binary32 with one rounding per operation: the library is built with
+// -ffp-contract=off and no fast-math, and every multiply-add below is written as separate
+// operations on purpose.
+//
+// Work decomposition.  The input is cut into 128 x 128 BF16 tiles (32 KiB).  A workgroup
+// stages a tile in LDS with coalesced 16-byte loads, then each lane owns one whole
+// 128-element group: lanes 0..127 take the tile's 128 row segments (row layout), lanes
+// 128..255 its 128 column segments (column layout).  With a group in one lane's registers,
+// the 7 butterfly stages of the Hadamard transform, the 1x16 block maxima and the pairwise
+// sums of the EDEN ratio need no cross-lane traffic at all.  The LDS tile is stored with
+// its 16-byte chunks XOR-swizzled by row, so that both the row reads (one 16-byte chunk per
+// lane) and the column reads (one 2-byte element per lane) are free of bank conflicts.
+//
+// The global amax must be known before any scale can be rounded, so a quantization is two
+// passes over X: k_amax (rotate, per-workgroup max, one atomic max per workgroup and
+// layout into the workspace) then k_quant (rotate again, quantize, pack, store).  k_quant
+// walks the tiles in the reverse order, so its first tiles are those k_amax touched last,
+// which are the likeliest to still sit in the last-level cache.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4k {
+
+enum Mode { MODE_RTN = 0, MODE_SR = 1, MODE_EDEN = 2, MODE_FP46 = 3 };
+enum Layouts { LAY_ROW = 1, LAY_COL = 2, LAY_BOTH = 3 };
+
+constexpr uint32_t STREAM_SIGN = 1u, STREAM_SCALE_SR = 2u, STREAM_ELEM_SR = 3u;
+constexpr int TILE = 128;            // tile edge == rotation group size
+constexpr int CHUNKS = TILE / 8;     // 16-byte chunks per tile row
+constexpr float FLT_BIG = 3.40282347e+38f;
+
+// ------------------------------------------------------------------------------ Philox
+// Philox4x32-10 (Salmon et al., SC'11): 10 rounds of two 32x32->64 multiplies, key bumped by
+// the Weyl constants between rounds.
+struct Word4 { uint32_t w[4]; };
+
+__device__ __forceinline__ Word4 philox(uint64_t key, uint32_t c0, uint32_t c1, uint32_t c2,
+                                        uint32_t c3)
+{
+    uint32_t k0 = (uint32_t)key, k1 = (uint32_t)(key >> 32);
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    Word4 r;
+    r.w[0] = c0; r.w[1] = c1; r.w[2] = c2; r.w[3] = c3;
+    return r;
+}
+
+// ------------------------------------------------------------------------------ formats
+// E4M3FN scale byte of t >= 0, round to nearest even, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne(float t)
+{
+    if (!(t < 448.0f)) return 0x7Eu;
+    if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);   // subnormal: k * 2^-9
+    uint32_t u = __float_as_uint(t);
+    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;              // keep 3 mantissa bits
+    return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+}
+
+// Smallest E4M3FN value >= t >= 0, capped at 448.
+__device__ __forceinline__ uint32_t e4m3_up(float t)
+{
+    if (!(t < 448.0f)) return 0x7Eu;
+    if (t < 0.015625f) return (uint32_t)__builtin_ceilf(t * 512.0f);
+    uint32_t u = (__float_as_uint(t) + 0xFFFFFu) & 0xFFF00000u;
+    return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+}
+
+// E4M3 byte of an fp32 value that is already an E4M3 normal number.
+__device__ __forceinline__ uint32_t e4m3_of_exact_normal(uint32_t bits)
+{
+    return (((bits >> 23) - 120u) << 3) | ((bits >> 20) & 7u);
+}
+
+__device__ __forceinline__ float e4m3_val(uint32_t c)
+{
+    const uint32_t e = c >> 3, m = c & 7u;
+    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// E2M1 magnitude index of a >= 0: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even index,
+// anything above 5 -> 7 (saturation).
+__device__ __forceinline__ uint32_t e2m1_rtn(float a)
+{
+    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+           (uint32_t)(a > 5.0f);
+}
+
+// Largest grid index whose magnitude is <= a, for 0 <= a < 6.
+__device__ __forceinline__ uint32_t e2m1_floor(float a)
+{
+    return (uint32_t)(a >= 0.5f) + (uint32_t)(a >= 1.0f) + (uint32_t)(a >= 1.5f) +
+           (uint32_t)(a >= 2.0f) + (uint32_t)(a >= 3.0f) + (uint32_t)(a >= 4.0f);
+}
+
+__device__ __forceinline__ float e2m1_val(uint32_t mag)
+{
+    const uint32_t e = mag >> 1, m = mag & 1u;
+    const uint32_t b = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
+    return __uint_as_float(b);
+}
+
+// Reciprocal rounded once, clamped so a zero / subnormal divisor stays finite.
+__device__ __forceinline__ float clamped_rcp(float d)
+{
+    const float r = 1.0f / d;
+    return r > FLT_BIG ? FLT_BIG : r;
+}
+
+// ------------------------------------------------------------------------------ signs
+struct Signs { uint32_t w[4]; };
+
+__device__ __forceinline__ Signs make_signs(uint64_t rht_seed)
+{
+    const Word4 p = philox(rht_seed, 0u, 0u, STREAM_SIGN, 0u);
+    Signs s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.w[i] = p.w[i];
+    return s;
+}
+
+// sigma_p = -1 iff bit p of the 128-bit sign word; returned as an fp32 sign-bit mask.
+__device__ __forceinline__ uint32_t sign_mask(const Signs &s, int p)
+{
+    return ((s.w[p >> 5] >> (p & 31)) & 1u) << 31;
+}
+
+// ------------------------------------------------------------------------------ tile
+struct Tile { uint4 chunk[TILE * CHUNKS]; };   // 32 KiB, chunk c of row i at i*16 + (c ^ (i&15))
+
+__device__ __forceinline__ int swz(int i, int c) { return i * CHUNKS + (c ^ (i & 15)); }
+
+// Coalesced load of tile (r0, c0); elements outside [0,R) x [0,C) read as zero.
+__device__ __forceinline__ void load_tile(Tile &t, const uint16_t *__restrict__ x, int64_t R,
+                                          int64_t C, int64_t r0, int64_t c0)
+{
+    for (int q = threadIdx.x; q < TILE * CHUNKS; q += blockDim.x) {
+        const int i = q >> 4, c = q & 15;
+        const int64_t row = r0 + i, col = c0 + 8 * c;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (row < R && col < C) v = *reinterpret_cast<const uint4 *>(x + row * C + col);
+        t.chunk[swz(i, c)] = v;
+    }
+}
+
+// Row segment i of the tile -> r[0..127] as fp32 (exact BF16 decode).
+__device__ __forceinline__ void read_row(const Tile &t, int i, float r[TILE])
+{
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        const uint4 v = t.chunk[swz(i, c)];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            r[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
+            r[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    }
+}
+
+// Column segment j of the tile -> r[0..127].
+__device__ __forceinline__ void read_col(const Tile &t, int j, float r[TILE])
+{
+    const uint16_t *t16 = reinterpret_cast<const uint16_t *>(t.chunk);
+#pragma unroll
+    for (int i = 0; i < TILE; ++i) {
+        const uint32_t h = t16[swz(i, j >> 3) * 8 + (j & 7)];
+        r[i] = __uint_as_float(h << 16);
+    }
+}
+
+// r <- H (sigma * r): random signs, then the unnormalised Sylvester Walsh-Hadamard
+// transform with butterfly spans 1, 2, 4, ..., 64 in that order.
+__device__ __forceinline__ void rotate(float r[TILE], const Signs &s)
+{
+#pragma unroll
+    for (int p = 0; p < TILE; ++p) r[p] = __uint_as_float(__float_as_uint(r[p]) ^ sign_mask(s, p));
+#pragma unroll
+    for (int h = 1; h < TILE; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < TILE; ++i) {
+            if ((i & h) == 0) {
+                const float u = r[i], v = r[i + h];
+                r[i] = u + v;
+                r[i + h] = u - v;
+            }
+        }
+    }
+}
+
+// Balanced pairwise sum of 2^k values in natural order, in place.
+template <int N>
+__device__ __forceinline__ float tree(float *v)
+{
+#pragma unroll
+    for (int len = N; len > 1; len >>= 1) {
+#pragma unroll
+        for (int i = 0; i < len / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+    }
+    return v[0];
+}
+
+__device__ __forceinline__ float block_max(const float *r)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(r[i]));
+    return m;
+}
+
+// ------------------------------------------------------------------------------ arguments
+struct LayoutOut {
+    uint8_t *codes;    // [vecs][n/2]
+    uint8_t *scales;   // [vecs][n/16]
+    float *g;          // [1]
+};
+
+struct QuantArgs {
+    const uint16_t *x;
+    int64_t R, C;
+    LayoutOut out[2];          // [0] row layout, [1] column layout
+    uint32_t *amax_bits;       // [0] row, [1] column: fp32 bits of max |r| (phase 1 output)
+    uint64_t seed, rht_seed;
+    int64_t tiles_c, tiles;    // tiles per tile-row, total tiles
+};
+
+// ------------------------------------------------------------------------------ kernels
+__global__ void k_zero_u32(uint32_t *p, int n)
+{
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+// Tensor scales of an empty input: g = amax / D for each requested layout.
+__global__ void k_write_g(const uint32_t *amax_bits, float D, float *g0, float *g1)
+{
+    if (threadIdx.x == 0) {
+        if (g0) *g0 = __uint_as_float(amax_bits[0]) / D;
+        if (g1) *g1 = __uint_as_float(amax_bits[1]) / D;
+    }
+}
+
+// Pass 1: amax of |r| per layout.  One atomicMax per workgroup and layout.
+template <bool ROT, int LAY>
+__global__ void __launch_bounds__(256) k_amax(QuantArgs a)
+{
+    __shared__ Tile tile;
+    __shared__ uint32_t wmax[2];
+    const Signs sg = make_signs(a.rht_seed);
+    const int t = threadIdx.x;
+    // which layout this lane serves
+    const int lay = (LAY == LAY_BOTH) ? (t >> 7) : (LAY == LAY_ROW ? 0 : 1);
+    const int lane_idx = (LAY == LAY_BOTH) ? (t & 127) : t;
+    if (t < 2) wmax[t] = 0u;
+    float local = 0.0f;
+    for (int64_t tid = blockIdx.x; tid < a.tiles; tid += gridDim.x) {
+        const int64_t r0 = (tid / a.tiles_c) * TILE, c0 = (tid % a.tiles_c) * TILE;
+        __syncthreads();
+        load_tile(tile, a.x, a.R, a.C, r0, c0);
+        __syncthreads();
+        const bool valid = (lay == 0) ? (r0 + lane_idx < a.R) : (c0 + lane_idx < a.C);
+        if (valid) {
+            float r[TILE];
+            if (lay == 0) read_row(tile, lane_idx, r);
+            else read_col(tile, lane_idx, r);
+            if (ROT) rotate(r, sg);
+#pragma unroll
+            for (int p = 0; p < TILE; ++p) local = fmaxf(local, fabsf(r[p]));
+        }
+    }
+    // wave max, then one atomic per wave into LDS, one per workgroup and layout into memory
+    for (int off = 32; off > 0; off >>= 1) local = fmaxf(local, __shfl_xor(local, off));
+    __syncthreads();
+    if ((t & 63) == 0) atomicMax(&wmax[lay], __float_as_uint(local));
+    __syncthreads();
+    if (t == 0) {
+        if (LAY & LAY_ROW) atomicMax(&a.amax_bits[0], wmax[0]);
+        if (LAY & LAY_COL) atomicMax(&a.amax_bits[1], wmax[1]);
+    }
+}
+
+// Quantize one group held in r[0..127] (rotated if ROT), nb valid 1x16 blocks (8 unless the
+// vector ends inside this group).  vec = vector index in its layout, n = vector length,
+// gi = group index within the vector.  Writes codes and scales of this group.
+template <int MODE>
+__device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g, uint64_t seed,
+                                               uint32_t axis, int64_t vec, int64_t n, int64_t gi,
+                                               uint8_t *__restrict__ codes,
+                                               uint8_t *__restrict__ scales)
+{
+    uint32_t cw[16];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) cw[w] = 0u;
+    uint32_t sc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) sc[b] = 0u;
+
+    const float rcp6g = clamped_rcp(6.0f * g);
+
+    if constexpr (MODE == MODE_RTN || MODE == MODE_EDEN) {
+        float bp[8], bq[8], sv[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            bp[b] = 0.0f; bq[b] = 0.0f; sv[b] = 0.0f;
+            if (b < nb) {
+                const float m = block_max(r + 16 * b);
+                const uint32_t s = e4m3_rne(m * rcp6g);
+                const float sval = e4m3_val(s);
+                const float den = sval * g;
+                const float rcp = clamped_rcp(den);
+                float P[16], Q[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int p = 16 * b + i;
+                    const float y = r[p] * rcp;
+                    const uint32_t mag = s ? e2m1_rtn(fabsf(y)) : 0u;
+                    const uint32_t sgn = s ? (__float_as_uint(r[p]) >> 31) : 0u;
+                    cw[p >> 3] |= (mag | (sgn << 3)) << (4 * (p & 7));
+                    const float q = s ? den * e2m1_val(mag) : 0.0f;
+                    P[i] = r[p] * r[p];
+                    Q[i] = fabsf(r[p]) * q;
+                }
+                sc[b] = s;
+                sv[b] = sval;
+                if constexpr (MODE == MODE_EDEN) {
+                    bp[b] = tree<16>(P);
+                    bq[b] = tree<16>(Q);
+                }
+            }
+        }
+        if constexpr (MODE == MODE_EDEN) {
+            const float num = tree<8>(bp), den = tree<8>(bq);
+            const float S = den > 0.0f ? num / den : 1.0f;
+            const int64_t k0 = vec * (n >> 4) + gi * 8;     // scale index of block 0
+            const Word4 w0 = philox(seed, (uint32_t)(k0 >> 2), (uint32_t)(k0 >> 34),
+                                    STREAM_SCALE_SR, axis);
+            const Word4 w1 = philox(seed, (uint32_t)((k0 >> 2) + 1),
+                                    (uint32_t)(((k0 >> 2) + 1) >> 32), STREAM_SCALE_SR, axis);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                if (sc[b] == 0u) continue;
+                const float c = S * sv[b];
+                uint32_t out;
+                if (!(c < 448.0f)) {
+                    out = 0x7Eu;
+                } else if (c < 0.015625f) {
+                    out = e4m3_rne(c);
+                } else {
+                    const uint32_t w = (b < 4) ? w0.w[b] : w1.w[b - 4];
+                    out = e4m3_of_exact_normal((__float_as_uint(c) + (w >> 12)) & 0xFFF00000u);
+                }
+                sc[b] = out;
+            }
+        }
+    } else if constexpr (MODE == MODE_SR) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            if (b < nb) {
+                const float m = block_max(r + 16 * b);
+                const uint32_t s = e4m3_up(m * rcp6g);
+                const float den = e4m3_val(s) * g;
+                const float rcp = clamped_rcp(den);
+                sc[b] = s;
+                if (s) {
+                    const int64_t e0 = vec * n + gi * TILE + 16 * b;   // element index, % 4 == 0
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const int64_t j = (e0 >> 2) + qd;
+                        const Word4 w = philox(seed, (uint32_t)j, (uint32_t)(j >> 32),
+                                               STREAM_ELEM_SR, axis);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int p = 16 * b + 4 * qd + k;
+                            const float a = fminf(fabsf(r[p] * rcp), 6.0f);
+                            uint32_t mag;
+                            if (a >= 6.0f) {
+                                mag = 7u;
+                            } else {
+                                const uint32_t lo = e2m1_floor(a);
+                                const float vlo = e2m1_val(lo);
+                                // 1 / (next grid value - vlo): steps 0.5, 1, 2 -> exact
+                                const float inv_step = (lo < 4u) ? 2.0f : (lo < 6u ? 1.0f : 0.5f);
+                                const float frac = (a - vlo) * inv_step;
+                                const uint32_t u = w.w[k] >> 8;
+                                mag = lo + (uint32_t)((float)u < frac * 16777216.0f);
+                            }
+                            const uint32_t sgn = __float_as_uint(r[p]) >> 31;
+                            cw[p >> 3] |= (mag | (sgn << 3)) << (4 * (p & 7));
+                        }
+                    }
+                }
+            }
+        }
+    } else {   // MODE_FP46
+        const float rcp4g = clamped_rcp(4.0f * g);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            if (b < nb) {
+                const float m = block_max(r + 16 * b);
+                const uint32_t sA = e4m3_rne(m * rcp6g), sB = e4m3_rne(m * rcp4g);
+                const float denA = e4m3_val(sA) * g, denB = e4m3_val(sB) * g;
+                const float rcpA = clamped_rcp(denA), rcpB = clamped_rcp(denB);
+                float dA[16], dB[16];
+                uint32_t cA0 = 0, cA1 = 0, cB0 = 0, cB1 = 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int p = 16 * b + i;
+                    const float ar = fabsf(r[p]);
+                    const uint32_t sgn = __float_as_uint(r[p]) >> 31;
+                    const uint32_t mA = sA ? e2m1_rtn(fabsf(r[p] * rcpA)) : 0u;
+                    uint32_t mB = sB ? e2m1_rtn(fabsf(r[p] * rcpB)) : 0u;
+                    mB = mB > 6u ? 6u : mB;
+                    const float qA = sA ? denA * e2m1_val(mA) : 0.0f;
+                    const float qB = sB ? denB * e2m1_val(mB) : 0.0f;
+                    const float eA = qA - ar, eB = qB - ar;
+                    dA[i] = eA * eA;
+                    dB[i] = eB * eB;
+                    const uint32_t codeA = sA ? (mA | (sgn << 3)) : 0u;
+                    const uint32_t codeB = sB ? (mB | (sgn << 3)) : 0u;
+                    if (i < 8) { cA0 |= codeA << (4 * i); cB0 |= codeB << (4 * i); }
+                    else { cA1 |= codeA << (4 * (i - 8)); cB1 |= codeB << (4 * (i - 8)); }
+                }
+                const float errA = tree<16>(dA), errB = tree<16>(dB);
+                const bool pickA = errA <= errB;
+                sc[b] = pickA ? sA : sB;
+                cw[2 * b] = pickA ? cA0 : cB0;
+                cw[2 * b + 1] = pickA ? cA1 : cB1;
+            }
+        }
+    }
+
+    // ---- stores: 64 code bytes + 8 scale bytes for a full, 16-byte aligned group
+    if (nb == 8 && (n & (TILE - 1)) == 0) {
+        uint4 *cp = reinterpret_cast<uint4 *>(codes);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            cp[k] = make_uint4(cw[4 * k], cw[4 * k + 1], cw[4 * k + 2], cw[4 * k + 3]);
+        *reinterpret_cast<uint2 *>(scales) =
+            make_uint2(sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24),
+                       sc[4] | (sc[5] << 8) | (sc[6] << 16) | (sc[7] << 24));
+    } else {
+        uint2 *cp = reinterpret_cast<uint2 *>(codes);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            if (b < nb) {
+                cp[b] = make_uint2(cw[2 * b], cw[2 * b + 1]);
+                scales[b] = (uint8_t)sc[b];
+            }
+        }
+    }
+}
+
+// Pass 2: quantize and pack every group of the requested layouts.
+template <int MODE, bool ROT, int LAY>
+__global__ void __launch_bounds__(256) k_quant(QuantArgs a)
+{
+    __shared__ Tile tile;
+    const Signs sg = make_signs(a.rht_seed);
+    const int t = threadIdx.x;
+    const int lay = (LAY == LAY_BOTH) ? (t >> 7) : (LAY == LAY_ROW ? 0 : 1);
+    const int li = (LAY == LAY_BOTH) ? (t & 127) : t;
+    const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
+    const float g = __uint_as_float(a.amax_bits[lay]) / D;
+    if (blockIdx.x == 0 && li == 0) *a.out[lay].g = g;
+    const int64_t n = lay == 0 ? a.C : a.R;
+    for (int64_t k = blockIdx.x; k < a.tiles; k += gridDim.x) {
+        const int64_t tid = a.tiles - 1 - k;    // reverse order: reuse what pass 1 left cached
+        const int64_t r0 = (tid / a.tiles_c) * TILE, c0 = (tid % a.tiles_c) * TILE;
+        __syncthreads();
+        load_tile(tile, a.x, a.R, a.C, r0, c0);
+        __syncthreads();
+        const int64_t vec = lay == 0 ? r0 + li : c0 + li;
+        const int64_t start = lay == 0 ? c0 : r0;      // first position of this group
+        if (vec < (lay == 0 ? a.R : a.C)) {
+            float r[TILE];
+            if (lay == 0) read_row(tile, li, r);
+            else read_col(tile, li, r);
+            if (ROT) rotate(r, sg);
+            const int64_t left = n - start;
+            const int nb = left >= TILE ? 8 : (int)(left >> 4);
+            const int64_t gi = start / TILE;
+            quantize_group<MODE>(r, nb, g, a.seed, (uint32_t)lay, vec, n, gi,
+                                 a.out[lay].codes + vec * (n >> 1) + (start >> 1),
+                                 a.out[lay].scales + vec * (n >> 4) + (start >> 4));
+        }
+    }
+}
+
+// Dequantize: one lane per (vector, group).  out[vec][pos] fp32.
+template <bool ROT>
+__global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ codes,
+                                                 const uint8_t *__restrict__ scales,
+                                                 const float *__restrict__ gp, int64_t vecs,
+                                                 int64_t n, uint64_t rht_seed,
+                                                 float *__restrict__ out)
+{
+    const int64_t groups_per_vec = (n + TILE - 1) / TILE;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= vecs * groups_per_vec) return;
+    const int64_t vec = id / groups_per_vec, gi = id % groups_per_vec;
+    const int64_t start = gi * TILE;
+    const int len = (n - start) >= TILE ? TILE : (int)(n - start);
+    const float g = *gp;
+    float v[TILE];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        if (16 * b < len) {
+            const float den = e4m3_val(scales[vec * (n >> 4) + (start >> 4) + b]) * g;
+            const uint2 cwd = *reinterpret_cast<const uint2 *>(codes + vec * (n >> 1) +
+                                                                (start >> 1) + 8 * b);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t code = ((i < 8 ? cwd.x : cwd.y) >> (4 * (i & 7))) & 15u;
+                const float q = den * e2m1_val(code & 7u);
+                v[16 * b + i] = (code & 8u) ? -q : q;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[16 * b + i] = 0.0f;
+        }
+    }
+    if (ROT) {
+        const Signs sg = make_signs(rht_seed);
+#pragma unroll
+        for (int h = 1; h < TILE; h <<= 1) {
+#pragma unroll
+            for (int i = 0; i < TILE; ++i) {
+                if ((i & h) == 0) {
+                    const float u = v[i], w = v[i + h];
+                    v[i] = u + w;
+                    v[i + h] = u - w;
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < TILE; ++p)
+            v[p] = __uint_as_float(__float_as_uint(v[p]) ^ sign_mask(sg, p)) * 0.0078125f;
+    }
+    float4 *o = reinterpret_cast<float4 *>(out + vec * n + start);
+#pragma unroll
+    for (int k = 0; k < TILE / 4; ++k)
+        if (4 * k < len) o[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+}
+
+}  // namespace nvfp4k
+
+// ------------------------------------------------------------------------------ launchers
+// Called by the C ABI layer (nvfp4_api.cpp) after argument validation.
+namespace nvfp4k {
+
+// Compute units of the current device, looked up once per device.
+static int cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+static int grid_for(int64_t tiles)
+{
+    const int64_t cap = (int64_t)cu_count() * 8;
+    return (int)(tiles < cap ? tiles : cap);
+}
+
+template <bool ROT, int LAY>
+static void launch_amax(const QuantArgs &a, hipStream_t st)
+{
+    const int threads = (LAY == LAY_BOTH) ? 256 : 128;
+    k_amax<ROT, LAY><<<grid_for(a.tiles), threads, 0, st>>>(a);
+}
+
+template <int MODE, bool ROT, int LAY>
+static void launch_quant(const QuantArgs &a, hipStream_t st)
+{
+    const int threads = (LAY == LAY_BOTH) ? 256 : 128;
+    k_quant<MODE, ROT, LAY><<<grid_for(a.tiles), threads, 0, st>>>(a);
+}
+
+template <int MODE, bool ROT>
+static void quant_lay(const QuantArgs &a, int lay, hipStream_t st)
+{
+    if (lay == LAY_ROW) launch_quant<MODE, ROT, LAY_ROW>(a, st);
+    else if (lay == LAY_COL) launch_quant<MODE, ROT, LAY_COL>(a, st);
+    else launch_quant<MODE, ROT, LAY_BOTH>(a, st);
+}
+
+static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_bits,
+                           uint64_t seed, uint64_t rht_seed)
+{
+    QuantArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.R = R;
+    a.C = C;
+    a.out[0] = {nullptr, nullptr, nullptr};
+    a.out[1] = {nullptr, nullptr, nullptr};
+    a.amax_bits = amax_bits;
+    a.seed = seed;
+    a.rht_seed = rht_seed;
+    a.tiles_c = (C + TILE - 1) / TILE;
+    a.tiles = a.tiles_c * ((R + TILE - 1) / TILE);
+    return a;
+}
+
+}  // namespace nvfp4k
+
+// Phase 1: amax[0..1] <- max |r| of the requested layouts (0 for the others).
+extern "C" hipError_t nvfp4k_amax(int rht, int layouts, const void *x, int64_t R, int64_t C,
+                                  float *amax, uint64_t rht_seed, hipStream_t st)
+{
+    using namespace nvfp4k;
+    QuantArgs a = make_args(x, R, C, reinterpret_cast<uint32_t *>(amax), 0, rht_seed);
+    k_zero_u32<<<1, 64, 0, st>>>(a.amax_bits, 2);
+    if (a.tiles > 0) {
+        if (rht) {
+            if (layouts == LAY_ROW) launch_amax<true, LAY_ROW>(a, st);
+            else if (layouts == LAY_COL) launch_amax<true, LAY_COL>(a, st);
+            else launch_amax<true, LAY_BOTH>(a, st);
+        } else {
+            if (layouts == LAY_ROW) launch_amax<false, LAY_ROW>(a, st);
+            else if (layouts == LAY_COL) launch_amax<false, LAY_COL>(a, st);
+            else launch_amax<false, LAY_BOTH>(a, st);
+        }
+    }
+    return hipGetLastError();
+}
+
+// Phase 2: quantize given the phase-1 maxima.
+extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x, int64_t R,
+                                   int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
+                                   uint8_t *codes1, uint8_t *scales1, float *g1,
+                                   const float *amax, uint64_t seed, uint64_t rht_seed,
+                                   hipStream_t st)
+{
+    using namespace nvfp4k;
+    QuantArgs a = make_args(x, R, C, reinterpret_cast<uint32_t *>(const_cast<float *>(amax)),
+                            seed, rht_seed);
+    a.out[0] = {codes0, scales0, g0};
+    a.out[1] = {codes1, scales1, g1};
+    if (a.tiles == 0) {
+        k_write_g<<<1, 64, 0, st>>>(a.amax_bits, mode == MODE_FP46 ? 1792.0f : 2688.0f,
+                                    (layouts & LAY_ROW) ? g0 : nullptr,
+                                    (layouts & LAY_COL) ? g1 : nullptr);
+        return hipGetLastError();
+    }
+    switch (mode) {
+    case MODE_RTN: rht ? quant_lay<MODE_RTN, true>(a, layouts, st)
+                       : quant_lay<MODE_RTN, false>(a, layouts, st); break;
+    case MODE_SR: rht ? quant_lay<MODE_SR, true>(a, layouts, st)
+                      : quant_lay<MODE_SR, false>(a, layouts, st); break;
+    case MODE_EDEN: quant_lay<MODE_EDEN, true>(a, layouts, st); break;
+    case MODE_FP46: rht ? quant_lay<MODE_FP46, true>(a, layouts, st)
+                        : quant_lay<MODE_FP46, false>(a, layouts, st); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+extern "C" hipError_t nvfp4k_dequantize(const uint8_t *codes, const uint8_t *scales,
+                                        const float *g, int64_t vecs, int64_t n, int rht,
+                                        uint64_t rht_seed, float *out, hipStream_t st)
+{
+    using namespace nvfp4k;
+    const int64_t groups = vecs * ((n + TILE - 1) / TILE);
+    if (groups == 0) return hipSuccess;
+    const int64_t blocks = (groups + 255) / 256;
+    if (rht) k_dequant<true><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, vecs, n, rht_seed, out);
+    else k_dequant<false><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, vecs, n, rht_seed, out);
+    return hipGetLastError();
+}
