@@ -363,6 +363,42 @@ static void rtn_block(const float *r, uint8_t s, float g, int mag_cap, uint8_t *
     }
 }
 
+/* ------------------------------------------------------------------ EDEN scalar products
+ * <r, r> and <r, q> of one 128-group, where q_i = den_b * V_i is the RTN dequantization of
+ * element i of block b (V_i the signed grid value of its code, den_b = s_b * g).  Within a
+ * 1x16 block the terms are accumulated by fused multiply-adds in element order (each term
+ * enters with a single rounding, and den_b is factored out of its block); the 8 block
+ * values are then combined by a balanced pairwise sum. */
+static void eden_dots(const float *r, const uint8_t *codes, const float *den, float *num,
+                      float *dot)
+{
+    float pb[GROUP / BLOCK], qb[GROUP / BLOCK];
+    for (int b = 0; b < GROUP / BLOCK; ++b) {
+        float p = 0.0f, v = 0.0f;
+        for (int i = 0; i < BLOCK; ++i) {
+            float x = r[b * BLOCK + i];
+            p = fmaf(x, x, p);
+            v = fmaf(x, oracle_e2m1_value(codes[b * BLOCK + i]), v);
+        }
+        pb[b] = p;
+        qb[b] = den[b] * v;
+    }
+    *num = tree_sum(pb, GROUP / BLOCK);
+    *dot = tree_sum(qb, GROUP / BLOCK);
+}
+
+/* Squared error of one block's RTN option: sum of d_i^2, d_i = den * V_i - r_i with one
+ * rounding (a fused multiply-add), accumulated by fused multiply-adds in element order. */
+static float block_sq_error(const float *r, const uint8_t *codes, float den)
+{
+    float err = 0.0f;
+    for (int i = 0; i < BLOCK; ++i) {
+        float d = fmaf(den, oracle_e2m1_value(codes[i]), -r[i]);
+        err = fmaf(d, d, err);
+    }
+    return err;
+}
+
 /* ------------------------------------------------------------------ one vector
  * The quantizers of one vector r (already rotated), length n, given the tensor scale.
  * vec is the vector's index in its layout (for the random streams and scale indices). */
@@ -406,13 +442,11 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                 }
                 continue;
             }
-            /* EDEN ratio S = <r, r> / <r, q> over the group of 128 (pairwise sums). */
-            float P[GROUP], Q[GROUP];
-            for (int i = 0; i < GROUP; ++i) {
-                P[i] = r[g0 + i] * r[g0 + i];
-                Q[i] = r[g0 + i] * q[i];
-            }
-            float num = tree_sum(P, GROUP), den = tree_sum(Q, GROUP);
+            /* EDEN ratio S = <r, r> / <r, q> over the group of 128. */
+            float dens[GROUP / BLOCK], num, den;
+            for (int b = 0; b < GROUP / BLOCK; ++b)
+                dens[b] = s[b] ? oracle_e4m3_value(s[b]) * g : 0.0f;
+            eden_dots(r + g0, bcodes, dens, &num, &den);
             float S = (den > 0.0f) ? num / den : 1.0f;
             for (int b = 0; b < GROUP / BLOCK; ++b) {
                 int64_t k = vec * nblk + (g0 / BLOCK) + b;   /* index in the scale array */
@@ -505,16 +539,12 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
         float tA = m * six_g_rcp, tB = m * four_g_rcp;
         uint8_t sA = oracle_e4m3_rne_sat(tA), sB = oracle_e4m3_rne_sat(tB);
         uint8_t cA[BLOCK], cB[BLOCK];
-        float qA[BLOCK], qB[BLOCK], dA[BLOCK], dB[BLOCK];
+        float qA[BLOCK], qB[BLOCK];
         uint32_t mA[BLOCK], mB[BLOCK];
         rtn_block(rb, sA, g, 7, cA, qA, mA);
         rtn_block(rb, sB, g, 6, cB, qB, mB);
-        for (int i = 0; i < BLOCK; ++i) {
-            float ea = qA[i] - rb[i], eb = qB[i] - rb[i];
-            dA[i] = ea * ea;
-            dB[i] = eb * eb;
-        }
-        float errA = tree_sum(dA, BLOCK), errB = tree_sum(dB, BLOCK);
+        float errA = block_sq_error(rb, cA, sA ? oracle_e4m3_value(sA) * g : 0.0f);
+        float errB = block_sq_error(rb, cB, sB ? oracle_e4m3_value(sB) * g : 0.0f);
         int pickA = errA <= errB;
         scales[b] = pickA ? sA : sB;
         if (smargin) {
@@ -633,7 +663,7 @@ int oracle_eden_internals(const uint16_t *x, int64_t rows, int64_t cols, int axi
     const float six_g_rcp = clamped_rcp(6.0f * g);
     for (int64_t g0 = 0; g0 < n; g0 += GROUP) {
         uint8_t bcodes[GROUP], s[GROUP / BLOCK];
-        float q[GROUP], P[GROUP], Q[GROUP];
+        float q[GROUP];
         for (int b = 0; b < GROUP / BLOCK; ++b) {
             const float *rb = buf + g0 + b * BLOCK;
             float m = 0.0f;
@@ -642,13 +672,14 @@ int oracle_eden_internals(const uint16_t *x, int64_t rows, int64_t cols, int axi
             s[b] = oracle_e4m3_rne_sat(m * six_g_rcp);
             rtn_block(rb, s[b], g, 7, bcodes + b * BLOCK, q + b * BLOCK, NULL);
         }
+        float dens[GROUP / BLOCK], num, den;
+        for (int b = 0; b < GROUP / BLOCK; ++b)
+            dens[b] = s[b] ? oracle_e4m3_value(s[b]) * g : 0.0f;
+        eden_dots(buf + g0, bcodes, dens, &num, &den);
         for (int i = 0; i < GROUP; ++i) {
-            P[i] = buf[g0 + i] * buf[g0 + i];
-            Q[i] = buf[g0 + i] * q[i];
             r_out[g0 + i] = buf[g0 + i];
             q_out[g0 + i] = q[i];
         }
-        float num = tree_sum(P, GROUP), den = tree_sum(Q, GROUP);
         float S = (den > 0.0f) ? num / den : 1.0f;
         S_out[g0 / GROUP] = S;
         for (int b = 0; b < GROUP / BLOCK; ++b)

@@ -110,8 +110,9 @@ def test_amax_against_fp64(oracle_mod):
 
 
 def test_eden_ratio_against_fp64(oracle_mod):
-    """S = <r,r>/<r,q>: both sums have non-negative terms, so fp32 pairwise summation over
-    128 terms (7 levels) plus the products and the division stay within 17u relative."""
+    """S = <r,r>/<r,q>: all terms are non-negative; a 16-term fused multiply-add chain per
+    block (<= 16u), the block scale product (u) and a 3-level pairwise sum (3u) bound each
+    sum by 20u, so with the division the ratio stays within 41u of the fp64 value."""
     x = workloads.c1()
     xb = _bits(x)
     g = oracle_mod.tensor_scale("eden", oracle_mod.amax(xb, 0, True, 1))
@@ -122,7 +123,7 @@ def test_eden_ratio_against_fp64(oracle_mod):
         S64 = (r64 * r64).sum(1) / (r64 * q64).sum(1)
         rel = np.abs(S.astype(np.float64) - S64) / S64
         worst = max(worst, rel.max())
-        assert np.all(rel <= 17 * U)
+        assert np.all(rel <= 41 * U)
         assert np.all((S > 0.9) & (S < 1.1))
     assert worst > 0  # the check is not vacuous
 

@@ -24,6 +24,13 @@
 // its 16-byte chunks XOR-swizzled by row, so that both the row reads (one 16-byte chunk per
 // lane) and the column reads (one 2-byte element per lane) are free of bank conflicts.
 //
+// Conversions use gfx950's own instructions where they compute exactly the contract's
+// rounding: v_cvt_scalef32_pk_fp4_f32 with scale 1.0 is round-to-nearest-even onto the E2M1
+// grid with saturation and the sign of its input (two codes per instruction, packed in
+// place), v_cvt_scalef32_pk_f32_fp4 decodes codes exactly, and v_cvt_pk_fp8_f32 is
+// nearest-even E4M3 below 448 (the input is clamped at 448 first).  All other steps are
+// plain binary32 arithmetic.
+//
 // The global amax must be known before any scale can be rounded, so a quantization is two
 // passes over X: k_amax (rotate, per-workgroup max, one atomic max per workgroup and
 // layout into the workspace) then k_quant (rotate again, quantize, pack, store).  k_quant
@@ -53,10 +60,10 @@ __device__ __forceinline__ Word4 philox(uint64_t key, uint32_t c0, uint32_t c1, 
     uint32_t k0 = (uint32_t)key, k1 = (uint32_t)(key >> 32);
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;   // one v_mad_u64_u32 each
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
@@ -120,6 +127,21 @@ __device__ __forceinline__ float e2m1_val(uint32_t mag)
     return __uint_as_float(b);
 }
 
+// Nearest-even E4M3 of t >= 0, saturating: the hardware conversion is exact below 448.
+__device__ __forceinline__ uint32_t e4m3_rne_hw(float t)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// Codes of y0, y1 (nearest-even E2M1, sign of the input) into byte `sel` of w.
+#define CVT_FP4(w, y0, y1, sel) \
+    __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((w), (y0), (y1), 1.0f, (sel))
+
+// Signed grid values of the two codes in byte `sel` of w.
+#define DEC_FP4(w, sel) __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((w), 1.0f, (sel))
+
 // Reciprocal rounded once, clamped so a zero / subnormal divisor stays finite.
 __device__ __forceinline__ float clamped_rcp(float d)
 {
@@ -150,6 +172,26 @@ struct Tile { uint4 chunk[TILE * CHUNKS]; };   // 32 KiB, chunk c of row i at i*
 
 __device__ __forceinline__ int swz(int i, int c) { return i * CHUNKS + (c ^ (i & 15)); }
 
+// Per-position fp32 sign-bit masks of the rotation (sigma_p = -1 -> 0x80000000), built
+// once per workgroup in LDS; lanes read them as broadcasts right before use.
+struct SignTable { uint4 m[TILE / 4]; };
+
+__device__ __forceinline__ void build_sign_table(SignTable &st, uint64_t rht_seed, bool rot)
+{
+    if (threadIdx.x < TILE / 4) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (rot) {
+            const Signs s = make_signs(rht_seed);
+            const int q = threadIdx.x >> 3;                 // sign word holding these 4 bits
+            const uint32_t word = q == 0 ? s.w[0] : q == 1 ? s.w[1] : q == 2 ? s.w[2] : s.w[3];
+            const int b0 = (4 * threadIdx.x) & 31;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = ((word >> (b0 + k)) & 1u) << 31;
+        }
+        st.m[threadIdx.x] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 // Coalesced load of tile (r0, c0); elements outside [0,R) x [0,C) read as zero.
 __device__ __forceinline__ void load_tile(Tile &t, const uint16_t *__restrict__ x, int64_t R,
                                           int64_t C, int64_t r0, int64_t c0)
@@ -163,38 +205,47 @@ __device__ __forceinline__ void load_tile(Tile &t, const uint16_t *__restrict__ 
     }
 }
 
-// Row segment i of the tile -> r[0..127] as fp32 (exact BF16 decode).
-__device__ __forceinline__ void read_row(const Tile &t, int i, float r[TILE])
+// Row segment i of the tile -> r[p] = sigma_p * x (exact BF16 decode, sign folded in).
+__device__ __forceinline__ void read_row(const Tile &t, const SignTable &st, int i,
+                                         float r[TILE])
 {
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
         const uint4 v = t.chunk[swz(i, c)];
+        const uint4 m0 = st.m[2 * c], m1 = st.m[2 * c + 1];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            r[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
-            r[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+            // (w << 16) + mask flips bit 31 exactly when the mask is set
+            r[8 * c + 2 * k] = __uint_as_float((w[k] << 16) + m[2 * k]);
+            r[8 * c + 2 * k + 1] = __uint_as_float((w[k] & 0xFFFF0000u) ^ m[2 * k + 1]);
         }
     }
 }
 
-// Column segment j of the tile -> r[0..127].
-__device__ __forceinline__ void read_col(const Tile &t, int j, float r[TILE])
+// Column segment j of the tile -> r[i] = sigma_i * x.
+__device__ __forceinline__ void read_col(const Tile &t, const SignTable &st, int j,
+                                         float r[TILE])
 {
     const uint16_t *t16 = reinterpret_cast<const uint16_t *>(t.chunk);
 #pragma unroll
-    for (int i = 0; i < TILE; ++i) {
-        const uint32_t h = t16[swz(i, j >> 3) * 8 + (j & 7)];
-        r[i] = __uint_as_float(h << 16);
+    for (int i4 = 0; i4 < TILE / 4; ++i4) {
+        const uint4 m = st.m[i4];
+        const uint32_t mm[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = 4 * i4 + k;
+            const uint32_t h = t16[swz(i, j >> 3) * 8 + (j & 7)];
+            r[i] = __uint_as_float((h << 16) + mm[k]);
+        }
     }
 }
 
-// r <- H (sigma * r): random signs, then the unnormalised Sylvester Walsh-Hadamard
-// transform with butterfly spans 1, 2, 4, ..., 64 in that order.
-__device__ __forceinline__ void rotate(float r[TILE], const Signs &s)
+// r <- H r: unnormalised Sylvester Walsh-Hadamard transform, butterfly spans 1, 2, ..., 64
+// in that order (the random signs are already folded in by read_row / read_col).
+__device__ __forceinline__ void fwht(float r[TILE])
 {
-#pragma unroll
-    for (int p = 0; p < TILE; ++p) r[p] = __uint_as_float(__float_as_uint(r[p]) ^ sign_mask(s, p));
 #pragma unroll
     for (int h = 1; h < TILE; h <<= 1) {
 #pragma unroll
@@ -222,10 +273,22 @@ __device__ __forceinline__ float tree(float *v)
 
 __device__ __forceinline__ float block_max(const float *r)
 {
-    float m = 0.0f;
+    float m = fmaxf(fabsf(r[0]), fabsf(r[1]));     // pairs of fmaxf fold into v_max3_f32
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(r[i]));
+    for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(fabsf(r[i]), fabsf(r[i + 1])));
     return m;
+}
+
+// Per-workgroup table over the 127 E4M3 codes: (scale value s, den = s*g, rcp(den)).
+struct ScaleTable { float4 e[128]; };
+
+__device__ __forceinline__ void build_scale_table(ScaleTable &tb, float g, int tid)
+{
+    if (tid < 128) {
+        const float sv = e4m3_val((uint32_t)tid);
+        const float den = sv * g;
+        tb.e[tid] = make_float4(sv, den, clamped_rcp(den), 0.0f);
+    }
 }
 
 // ------------------------------------------------------------------------------ arguments
@@ -261,15 +324,16 @@ __global__ void k_write_g(const uint32_t *amax_bits, float D, float *g0, float *
 
 // Pass 1: amax of |r| per layout.  One atomicMax per workgroup and layout.
 template <bool ROT, int LAY>
-__global__ void __launch_bounds__(256) k_amax(QuantArgs a)
+__global__ void __launch_bounds__(256, 2) k_amax(QuantArgs a)
 {
     __shared__ Tile tile;
+    __shared__ SignTable st;
     __shared__ uint32_t wmax[2];
-    const Signs sg = make_signs(a.rht_seed);
     const int t = threadIdx.x;
     // which layout this lane serves
     const int lay = (LAY == LAY_BOTH) ? (t >> 7) : (LAY == LAY_ROW ? 0 : 1);
-    const int lane_idx = (LAY == LAY_BOTH) ? (t & 127) : t;
+    const int li = (LAY == LAY_BOTH) ? (t & 127) : t;
+    build_sign_table(st, a.rht_seed, ROT);
     if (t < 2) wmax[t] = 0u;
     float local = 0.0f;
     for (int64_t tid = blockIdx.x; tid < a.tiles; tid += gridDim.x) {
@@ -277,14 +341,19 @@ __global__ void __launch_bounds__(256) k_amax(QuantArgs a)
         __syncthreads();
         load_tile(tile, a.x, a.R, a.C, r0, c0);
         __syncthreads();
-        const bool valid = (lay == 0) ? (r0 + lane_idx < a.R) : (c0 + lane_idx < a.C);
+        const bool valid = (lay == 0) ? (r0 + li < a.R) : (c0 + li < a.C);
         if (valid) {
             float r[TILE];
-            if (lay == 0) read_row(tile, lane_idx, r);
-            else read_col(tile, lane_idx, r);
-            if (ROT) rotate(r, sg);
+            if (lay == 0) read_row(tile, st, li, r);
+            else read_col(tile, st, li, r);
+            if (ROT) fwht(r);
+            float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
-            for (int p = 0; p < TILE; ++p) local = fmaxf(local, fabsf(r[p]));
+            for (int p = 0; p < TILE; p += 4) {
+                m0 = fmaxf(m0, fmaxf(fabsf(r[p]), fabsf(r[p + 1])));
+                m1 = fmaxf(m1, fmaxf(fabsf(r[p + 2]), fabsf(r[p + 3])));
+            }
+            local = fmaxf(local, fmaxf(m0, m1));
         }
     }
     // wave max, then one atomic per wave into LDS, one per workgroup and layout into memory
@@ -298,99 +367,134 @@ __global__ void __launch_bounds__(256) k_amax(QuantArgs a)
     }
 }
 
-// Quantize one group held in r[0..127] (rotated if ROT), nb valid 1x16 blocks (8 unless the
-// vector ends inside this group).  vec = vector index in its layout, n = vector length,
-// gi = group index within the vector.  Writes codes and scales of this group.
+// Round-to-nearest of one 1x16 block rb[0..15] with scale code s (table entry e):
+// packed codes into w0 (elements 0..7) and w1 (8..15); a zero scale gives all-zero codes.
+__device__ __forceinline__ void rtn_block(const float *rb, uint32_t s, const float4 e,
+                                          uint32_t &w0, uint32_t &w1)
+{
+    const float rcp = e.z;
+    uint32_t a = 0u, b = 0u;
+    a = CVT_FP4(a, rb[0] * rcp, rb[1] * rcp, 0);
+    a = CVT_FP4(a, rb[2] * rcp, rb[3] * rcp, 1);
+    a = CVT_FP4(a, rb[4] * rcp, rb[5] * rcp, 2);
+    a = CVT_FP4(a, rb[6] * rcp, rb[7] * rcp, 3);
+    b = CVT_FP4(b, rb[8] * rcp, rb[9] * rcp, 0);
+    b = CVT_FP4(b, rb[10] * rcp, rb[11] * rcp, 1);
+    b = CVT_FP4(b, rb[12] * rcp, rb[13] * rcp, 2);
+    b = CVT_FP4(b, rb[14] * rcp, rb[15] * rcp, 3);
+    w0 = s ? a : 0u;
+    w1 = s ? b : 0u;
+}
+
+// Dequantized values q_i = den * V(code_i) of a block (signed, as the codes).
+template <int K>
+__device__ __forceinline__ void decode_pair(uint32_t w0, uint32_t w1, float den, float q[16])
+{
+    const float2v v0 = DEC_FP4(w0, K), v1 = DEC_FP4(w1, K);
+    q[2 * K] = den * v0.x;
+    q[2 * K + 1] = den * v0.y;
+    q[8 + 2 * K] = den * v1.x;
+    q[8 + 2 * K + 1] = den * v1.y;
+}
+
+// (with den = 1.0f the multiplies fold away and q holds the signed grid values)
+__device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, float den, float q[16])
+{
+    decode_pair<0>(w0, w1, den, q);
+    decode_pair<1>(w0, w1, den, q);
+    decode_pair<2>(w0, w1, den, q);
+    decode_pair<3>(w0, w1, den, q);
+}
+
+// Saturate magnitude 7 (value 6) to 6 (value 4) in every nibble of a packed word.
+__device__ __forceinline__ uint32_t cap_mag6(uint32_t w)
+{
+    const uint32_t seven = w & (w >> 1) & (w >> 2) & 0x11111111u;
+    return w ^ seven;
+}
+
+// Quantize one group held in r[0..127] (rotated if the mode rotates), nb valid 1x16 blocks
+// (8 unless the vector ends inside this group).  vec = vector index in its layout, n =
+// vector length, gi = group index within the vector.  Writes codes and scales.
 template <int MODE>
-__device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g, uint64_t seed,
-                                               uint32_t axis, int64_t vec, int64_t n, int64_t gi,
+__device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g,
+                                               const ScaleTable &tb, float rcp6g, float rcp4g,
+                                               uint64_t seed, uint32_t axis, int64_t vec,
+                                               int64_t n, int64_t gi,
                                                uint8_t *__restrict__ codes,
                                                uint8_t *__restrict__ scales)
 {
     uint32_t cw[16];
-#pragma unroll
-    for (int w = 0; w < 16; ++w) cw[w] = 0u;
     uint32_t sc[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) sc[b] = 0u;
-
-    const float rcp6g = clamped_rcp(6.0f * g);
+    for (int b = 0; b < 8; ++b) { sc[b] = 0u; cw[2 * b] = 0u; cw[2 * b + 1] = 0u; }
 
     if constexpr (MODE == MODE_RTN || MODE == MODE_EDEN) {
         float bp[8], bq[8], sv[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             bp[b] = 0.0f; bq[b] = 0.0f; sv[b] = 0.0f;
-            if (b < nb) {
-                const float m = block_max(r + 16 * b);
-                const uint32_t s = e4m3_rne(m * rcp6g);
-                const float sval = e4m3_val(s);
-                const float den = sval * g;
-                const float rcp = clamped_rcp(den);
-                float P[16], Q[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int p = 16 * b + i;
-                    const float y = r[p] * rcp;
-                    const uint32_t mag = s ? e2m1_rtn(fabsf(y)) : 0u;
-                    const uint32_t sgn = s ? (__float_as_uint(r[p]) >> 31) : 0u;
-                    cw[p >> 3] |= (mag | (sgn << 3)) << (4 * (p & 7));
-                    const float q = s ? den * e2m1_val(mag) : 0.0f;
-                    P[i] = r[p] * r[p];
-                    Q[i] = fabsf(r[p]) * q;
-                }
+            if (MODE == MODE_EDEN || b < nb) {
+                const float *rb = r + 16 * b;
+                const uint32_t s = e4m3_rne_hw(block_max(rb) * rcp6g);
+                const float4 e = tb.e[s];
+                rtn_block(rb, s, e, cw[2 * b], cw[2 * b + 1]);
                 sc[b] = s;
-                sv[b] = sval;
+                sv[b] = e.x;
                 if constexpr (MODE == MODE_EDEN) {
-                    bp[b] = tree<16>(P);
-                    bq[b] = tree<16>(Q);
+                    // <r,r> and <r,V> of the block by fused multiply-add chains in element
+                    // order; den is factored out of the block's <r,q>.
+                    float V[16];
+                    decode_block(cw[2 * b], cw[2 * b + 1], 1.0f, V);
+                    float p = 0.0f, v = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        p = __builtin_fmaf(rb[i], rb[i], p);
+                        v = __builtin_fmaf(rb[i], V[i], v);
+                    }
+                    bp[b] = p;
+                    bq[b] = e.y * v;
                 }
             }
         }
         if constexpr (MODE == MODE_EDEN) {
             const float num = tree<8>(bp), den = tree<8>(bq);
             const float S = den > 0.0f ? num / den : 1.0f;
-            const int64_t k0 = vec * (n >> 4) + gi * 8;     // scale index of block 0
-            const Word4 w0 = philox(seed, (uint32_t)(k0 >> 2), (uint32_t)(k0 >> 34),
+            const int64_t k0 = vec * (n >> 4) + gi * 8;     // scale index of block 0, % 8 == 0
+            const uint64_t j0 = (uint64_t)k0 >> 2;
+            const Word4 w0 = philox(seed, (uint32_t)j0, (uint32_t)(j0 >> 32), STREAM_SCALE_SR, axis);
+            const Word4 w1 = philox(seed, (uint32_t)(j0 + 1), (uint32_t)((j0 + 1) >> 32),
                                     STREAM_SCALE_SR, axis);
-            const Word4 w1 = philox(seed, (uint32_t)((k0 >> 2) + 1),
-                                    (uint32_t)(((k0 >> 2) + 1) >> 32), STREAM_SCALE_SR, axis);
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
-                if (sc[b] == 0u) continue;
                 const float c = S * sv[b];
+                const uint32_t w = (b < 4) ? w0.w[b] : w1.w[b - 4];
                 uint32_t out;
-                if (!(c < 448.0f)) {
-                    out = 0x7Eu;
-                } else if (c < 0.015625f) {
-                    out = e4m3_rne(c);
-                } else {
-                    const uint32_t w = (b < 4) ? w0.w[b] : w1.w[b - 4];
-                    out = e4m3_of_exact_normal((__float_as_uint(c) + (w >> 12)) & 0xFFF00000u);
-                }
-                sc[b] = out;
+                if (!(c < 448.0f)) out = 0x7Eu;
+                else if (c < 0.015625f) out = e4m3_rne_hw(c);      // no SR below 2^-6
+                else out = e4m3_of_exact_normal((__float_as_uint(c) + (w >> 12)) & 0xFFF00000u);
+                sc[b] = sc[b] ? out : 0u;
             }
         }
     } else if constexpr (MODE == MODE_SR) {
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             if (b < nb) {
-                const float m = block_max(r + 16 * b);
-                const uint32_t s = e4m3_up(m * rcp6g);
-                const float den = e4m3_val(s) * g;
-                const float rcp = clamped_rcp(den);
+                const float *rb = r + 16 * b;
+                const uint32_t s = e4m3_up(block_max(rb) * rcp6g);
+                const float rcp = tb.e[s].z;
                 sc[b] = s;
                 if (s) {
                     const int64_t e0 = vec * n + gi * TILE + 16 * b;   // element index, % 4 == 0
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
-                        const int64_t j = (e0 >> 2) + qd;
+                        const uint64_t j = ((uint64_t)e0 >> 2) + qd;
                         const Word4 w = philox(seed, (uint32_t)j, (uint32_t)(j >> 32),
                                                STREAM_ELEM_SR, axis);
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
                             const int p = 16 * b + 4 * qd + k;
-                            const float a = fminf(fabsf(r[p] * rcp), 6.0f);
+                            const float a = fminf(fabsf(rb[4 * qd + k] * rcp), 6.0f);
                             uint32_t mag;
                             if (a >= 6.0f) {
                                 mag = 7u;
@@ -403,7 +507,7 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g, u
                                 const uint32_t u = w.w[k] >> 8;
                                 mag = lo + (uint32_t)((float)u < frac * 16777216.0f);
                             }
-                            const uint32_t sgn = __float_as_uint(r[p]) >> 31;
+                            const uint32_t sgn = __float_as_uint(rb[4 * qd + k]) >> 31;
                             cw[p >> 3] |= (mag | (sgn << 3)) << (4 * (p & 7));
                         }
                     }
@@ -411,39 +515,35 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g, u
             }
         }
     } else {   // MODE_FP46
-        const float rcp4g = clamped_rcp(4.0f * g);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             if (b < nb) {
-                const float m = block_max(r + 16 * b);
-                const uint32_t sA = e4m3_rne(m * rcp6g), sB = e4m3_rne(m * rcp4g);
-                const float denA = e4m3_val(sA) * g, denB = e4m3_val(sB) * g;
-                const float rcpA = clamped_rcp(denA), rcpB = clamped_rcp(denB);
-                float dA[16], dB[16];
-                uint32_t cA0 = 0, cA1 = 0, cB0 = 0, cB1 = 0;
+                const float *rb = r + 16 * b;
+                const float m = block_max(rb);
+                const uint32_t sA = e4m3_rne_hw(m * rcp6g), sB = e4m3_rne_hw(m * rcp4g);
+                const float4 eA = tb.e[sA], eB = tb.e[sB];
+                uint32_t a0, a1, b0, b1;
+                rtn_block(rb, sA, eA, a0, a1);
+                rtn_block(rb, sB, eB, b0, b1);
+                b0 = cap_mag6(b0);
+                b1 = cap_mag6(b1);
+                // squared error of each option: d = den * V - r with one rounding, summed by
+                // fused multiply-adds in element order
+                float VA[16], VB[16];
+                decode_block(a0, a1, 1.0f, VA);
+                decode_block(b0, b1, 1.0f, VB);
+                float errA = 0.0f, errB = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int p = 16 * b + i;
-                    const float ar = fabsf(r[p]);
-                    const uint32_t sgn = __float_as_uint(r[p]) >> 31;
-                    const uint32_t mA = sA ? e2m1_rtn(fabsf(r[p] * rcpA)) : 0u;
-                    uint32_t mB = sB ? e2m1_rtn(fabsf(r[p] * rcpB)) : 0u;
-                    mB = mB > 6u ? 6u : mB;
-                    const float qA = sA ? denA * e2m1_val(mA) : 0.0f;
-                    const float qB = sB ? denB * e2m1_val(mB) : 0.0f;
-                    const float eA = qA - ar, eB = qB - ar;
-                    dA[i] = eA * eA;
-                    dB[i] = eB * eB;
-                    const uint32_t codeA = sA ? (mA | (sgn << 3)) : 0u;
-                    const uint32_t codeB = sB ? (mB | (sgn << 3)) : 0u;
-                    if (i < 8) { cA0 |= codeA << (4 * i); cB0 |= codeB << (4 * i); }
-                    else { cA1 |= codeA << (4 * (i - 8)); cB1 |= codeB << (4 * (i - 8)); }
+                    const float da = __builtin_fmaf(eA.y, VA[i], -rb[i]);
+                    const float db = __builtin_fmaf(eB.y, VB[i], -rb[i]);
+                    errA = __builtin_fmaf(da, da, errA);
+                    errB = __builtin_fmaf(db, db, errB);
                 }
-                const float errA = tree<16>(dA), errB = tree<16>(dB);
                 const bool pickA = errA <= errB;
                 sc[b] = pickA ? sA : sB;
-                cw[2 * b] = pickA ? cA0 : cB0;
-                cw[2 * b + 1] = pickA ? cA1 : cB1;
+                cw[2 * b] = pickA ? a0 : b0;
+                cw[2 * b + 1] = pickA ? a1 : b1;
             }
         }
     }
@@ -471,16 +571,23 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g, u
 
 // Pass 2: quantize and pack every group of the requested layouts.
 template <int MODE, bool ROT, int LAY>
-__global__ void __launch_bounds__(256) k_quant(QuantArgs a)
+__global__ void __launch_bounds__(256, 2) k_quant(QuantArgs a)
 {
     __shared__ Tile tile;
-    const Signs sg = make_signs(a.rht_seed);
+    __shared__ SignTable st;
+    __shared__ ScaleTable tabs[(LAY == LAY_BOTH) ? 2 : 1];
     const int t = threadIdx.x;
     const int lay = (LAY == LAY_BOTH) ? (t >> 7) : (LAY == LAY_ROW ? 0 : 1);
     const int li = (LAY == LAY_BOTH) ? (t & 127) : t;
     const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
-    const float g = __uint_as_float(a.amax_bits[lay]) / D;
-    if (blockIdx.x == 0 && li == 0) *a.out[lay].g = g;
+    const float g = __uint_as_float(lay == 0 ? a.amax_bits[0] : a.amax_bits[1]) / D;
+    const float rcp6g = clamped_rcp(6.0f * g), rcp4g = clamped_rcp(4.0f * g);
+    ScaleTable &tb = tabs[(LAY == LAY_BOTH) ? lay : 0];
+    // select this lane's layout without indexing the argument struct at run time
+    const LayoutOut o = (lay == 0) ? a.out[0] : a.out[1];
+    build_sign_table(st, a.rht_seed, ROT);
+    build_scale_table(tb, g, li);
+    if (blockIdx.x == 0 && li == 0) *o.g = g;
     const int64_t n = lay == 0 ? a.C : a.R;
     for (int64_t k = blockIdx.x; k < a.tiles; k += gridDim.x) {
         const int64_t tid = a.tiles - 1 - k;    // reverse order: reuse what pass 1 left cached
@@ -492,15 +599,15 @@ __global__ void __launch_bounds__(256) k_quant(QuantArgs a)
         const int64_t start = lay == 0 ? c0 : r0;      // first position of this group
         if (vec < (lay == 0 ? a.R : a.C)) {
             float r[TILE];
-            if (lay == 0) read_row(tile, li, r);
-            else read_col(tile, li, r);
-            if (ROT) rotate(r, sg);
+            if (lay == 0) read_row(tile, st, li, r);
+            else read_col(tile, st, li, r);
+            if (ROT) fwht(r);
             const int64_t left = n - start;
             const int nb = left >= TILE ? 8 : (int)(left >> 4);
             const int64_t gi = start / TILE;
-            quantize_group<MODE>(r, nb, g, a.seed, (uint32_t)lay, vec, n, gi,
-                                 a.out[lay].codes + vec * (n >> 1) + (start >> 1),
-                                 a.out[lay].scales + vec * (n >> 4) + (start >> 4));
+            quantize_group<MODE>(r, nb, g, tb, rcp6g, rcp4g, a.seed, (uint32_t)lay, vec, n, gi,
+                                 o.codes + vec * (n >> 1) + (start >> 1),
+                                 o.scales + vec * (n >> 4) + (start >> 4));
         }
     }
 }
