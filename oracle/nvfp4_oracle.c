@@ -22,7 +22,7 @@
  *           1x16 linear groups rather than 16x16 squares.
  *
  * The pages give no formula, order of operations or constant beyond 128, 16, +-6/+-4 and
- * "about 1/32000".  Every step below is the plainest reading; each reading is listed in
+ * roughly 1/32000.  Every step below is the plainest reading; each reading is listed in
  * the design notes.  All arithmetic is IEEE binary32 with round-to-nearest-even, one
  * rounding per operation, no fused multiply-add (build with -ffp-contract=off) and no
  * flushing of subnormals: every floating-point value here decides an integer (a code, a
@@ -460,7 +460,7 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                         out = 0x7E;
                         m2 = umin(m2, ulp_dist(c, 448.0f));
                     } else if (c < 0.015625f) {
-                        /* below 2^-6 = 448 / 28672 ("about 1/32000 of the max"): no SR */
+                        /* below 2^-6 = 448 / 28672, roughly 1/32000 of the top scale: no SR */
                         out = oracle_e4m3_rne_sat(c);
                         m2 = umin(m2, umin(e4m3_rne_margin(c), ulp_dist(c, 0.015625f)));
                     } else {

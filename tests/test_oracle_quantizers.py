@@ -257,7 +257,7 @@ def test_determinism_and_seed_dependence(oracle_mod):
 
 
 def test_skip_of_tiny_scales(oracle_mod):
-    """Corrected scales below 2^-6 (448/28672, 'about 1/32000 of the max') are rounded to
+    """Corrected scales below 2^-6 (448/28672, the pages' skip threshold near 1/32000 of the top scale) are rounded to
     nearest, identically for every seed; larger ones vary with the seed."""
     x = workloads.c3(shape=(1024, 512))
     xb = _bits(x)
