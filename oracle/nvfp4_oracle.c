@@ -24,8 +24,8 @@
  * The pages give no formula, order of operations or constant beyond 128, 16, +-6/+-4 and
  * roughly 1/32000.  Every step below is the plainest reading; each reading is listed in
  * the design notes.  All arithmetic is IEEE binary32 with round-to-nearest-even, one
- * rounding per operation, no fused multiply-add (build with -ffp-contract=off) and no
- * flushing of subnormals: every floating-point value here decides an integer (a code, a
+ * rounding per operation (a fused multiply-add only where fmaf is written; the build
+ * disables contraction with -ffp-contract=off) and no flushing of subnormals: every floating-point value here decides an integer (a code, a
  * scale byte, an SR branch), and the GPU takes those decisions in binary32 too.
  *
  * Pins (tests marked "not gpu"): Philox against rocRAND's engine; the Hadamard transform

@@ -12,8 +12,8 @@
 //     synchronisation point; one producer writes both layouts.
 //
 // Arithmetic is binary32 with one rounding per operation: the library is built with
-// -ffp-contract=off and no fast-math, and every multiply-add below is written as separate
-// operations on purpose.
+// -ffp-contract=off and no fast-math, so a multiply-add is fused only where __builtin_fmaf
+// is written (the scalar-product chains), exactly as the CPU oracle does.
 //
 // Work decomposition.  The input is cut into 128 x 128 BF16 tiles (32 KiB).  A workgroup
 // stages a tile in LDS with coalesced 16-byte loads, then each lane owns one whole
