@@ -192,9 +192,10 @@ __device__ __forceinline__ void build_sign_table(SignTable &st, uint64_t rht_see
     }
 }
 
-// Coalesced load of tile (r0, c0); elements outside [0,R) x [0,C) read as zero.
-__device__ __forceinline__ void load_tile(Tile &t, const uint16_t *__restrict__ x, int64_t R,
-                                          int64_t C, int64_t r0, int64_t c0)
+// Synchronous load of tile (r0, c0) through registers; elements outside [0,R) x [0,C)
+// read as zero.  Used for the ragged edge tiles only.
+__device__ __forceinline__ void load_tile_sync(Tile &t, const uint16_t *__restrict__ x,
+                                               int64_t R, int64_t C, int64_t r0, int64_t c0)
 {
     for (int q = threadIdx.x; q < TILE * CHUNKS; q += blockDim.x) {
         const int i = q >> 4, c = q & 15;
@@ -202,6 +203,31 @@ __device__ __forceinline__ void load_tile(Tile &t, const uint16_t *__restrict__ 
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (row < R && col < C) v = *reinterpret_cast<const uint4 *>(x + row * C + col);
         t.chunk[swz(i, c)] = v;
+    }
+}
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Start loading tile (r0, c0) into t.  A full tile goes straight from memory into LDS
+// (global_load_lds_dwordx4: lane L of a wave instruction fills 16-byte slot base + L), so
+// the load runs while the workgroup computes on its other buffer; each lane fetches the
+// chunk whose swizzled slot it fills.  The data is visible after the next __syncthreads
+// (which waits for this wave's outstanding memory operations).  Edge tiles load
+// synchronously.
+__device__ __forceinline__ void stage_tile(Tile &t, const uint16_t *__restrict__ x, int64_t R,
+                                           int64_t C, int64_t r0, int64_t c0)
+{
+    if (r0 + TILE <= R && c0 + TILE <= C) {
+        const int waves = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const uint16_t *base = x + r0 * C + c0;
+        for (int j = w; j < TILE * CHUNKS / 64; j += waves) {
+            const int q = j * 64 + lane;               // slot filled by this lane
+            const int i = q >> 4, c = (q & 15) ^ (i & 15);
+            __builtin_amdgcn_global_load_lds(base + (int64_t)i * C + 8 * c,
+                                             LDS_PTR(&t.chunk[j * 64]), 16, 0, 0);
+        }
+    } else {
+        load_tile_sync(t, x, R, C, r0, c0);
     }
 }
 
@@ -322,39 +348,73 @@ __global__ void k_write_g(const uint32_t *amax_bits, float D, float *g0, float *
     }
 }
 
-// Pass 1: amax of |r| per layout.  One atomicMax per workgroup and layout.
+// Max |r| over the groups this lane owns in tile (r0, c0).
+template <bool ROT, int LAY>
+__device__ __forceinline__ float tile_amax(const Tile &tile, const SignTable &st,
+                                           const QuantArgs &a, int lay, int li, int64_t r0,
+                                           int64_t c0)
+{
+    const bool valid = (lay == 0) ? (r0 + li < a.R) : (c0 + li < a.C);
+    if (!valid) return 0.0f;
+    float r[TILE];
+    if (lay == 0) read_row(tile, st, li, r);
+    else read_col(tile, st, li, r);
+    if (ROT) fwht(r);
+    float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+    for (int p = 0; p < TILE; p += 4) {
+        m0 = fmaxf(m0, fmaxf(fabsf(r[p]), fabsf(r[p + 1])));
+        m1 = fmaxf(m1, fmaxf(fabsf(r[p + 2]), fabsf(r[p + 3])));
+    }
+    return fmaxf(m0, m1);
+}
+
+__device__ __forceinline__ void tile_origin(const QuantArgs &a, int64_t tid, int64_t &r0,
+                                            int64_t &c0)
+{
+    r0 = (tid / a.tiles_c) * TILE;
+    c0 = (tid % a.tiles_c) * TILE;
+}
+
+// Pass 1: amax of |r| per layout.  Persistent workgroups walk the tiles with two LDS
+// buffers (the next tile streams in while the current one is processed); one atomicMax
+// per workgroup and layout at the end.
 template <bool ROT, int LAY>
 __global__ void __launch_bounds__(256, 2) k_amax(QuantArgs a)
 {
-    __shared__ Tile tile;
+    __shared__ Tile tile0;
+    __shared__ Tile tile1;
     __shared__ SignTable st;
     __shared__ uint32_t wmax[2];
     const int t = threadIdx.x;
-    // which layout this lane serves
     const int lay = (LAY == LAY_BOTH) ? (t >> 7) : (LAY == LAY_ROW ? 0 : 1);
     const int li = (LAY == LAY_BOTH) ? (t & 127) : t;
     build_sign_table(st, a.rht_seed, ROT);
     if (t < 2) wmax[t] = 0u;
     float local = 0.0f;
-    for (int64_t tid = blockIdx.x; tid < a.tiles; tid += gridDim.x) {
-        const int64_t r0 = (tid / a.tiles_c) * TILE, c0 = (tid % a.tiles_c) * TILE;
-        __syncthreads();
-        load_tile(tile, a.x, a.R, a.C, r0, c0);
-        __syncthreads();
-        const bool valid = (lay == 0) ? (r0 + li < a.R) : (c0 + li < a.C);
-        if (valid) {
-            float r[TILE];
-            if (lay == 0) read_row(tile, st, li, r);
-            else read_col(tile, st, li, r);
-            if (ROT) fwht(r);
-            float m0 = 0.0f, m1 = 0.0f;
-#pragma unroll
-            for (int p = 0; p < TILE; p += 4) {
-                m0 = fmaxf(m0, fmaxf(fabsf(r[p]), fabsf(r[p + 1])));
-                m1 = fmaxf(m1, fmaxf(fabsf(r[p + 2]), fabsf(r[p + 3])));
-            }
-            local = fmaxf(local, fmaxf(m0, m1));
+    int64_t k = blockIdx.x, r0, c0;
+    if (k < a.tiles) {
+        tile_origin(a, k, r0, c0);
+        stage_tile(tile0, a.x, a.R, a.C, r0, c0);
+    }
+    while (k < a.tiles) {
+        const int64_t k1 = k + gridDim.x;
+        __syncthreads();                                   // tile0 landed; tile1 is free
+        int64_t r1 = 0, c1 = 0;
+        if (k1 < a.tiles) {
+            tile_origin(a, k1, r1, c1);
+            stage_tile(tile1, a.x, a.R, a.C, r1, c1);
         }
+        local = fmaxf(local, tile_amax<ROT, LAY>(tile0, st, a, lay, li, r0, c0));
+        if (k1 >= a.tiles) break;
+        const int64_t k2 = k1 + gridDim.x;
+        __syncthreads();                                   // tile1 landed; tile0 is free
+        if (k2 < a.tiles) {
+            tile_origin(a, k2, r0, c0);
+            stage_tile(tile0, a.x, a.R, a.C, r0, c0);
+        }
+        local = fmaxf(local, tile_amax<ROT, LAY>(tile1, st, a, lay, li, r1, c1));
+        k = k2;
     }
     // wave max, then one atomic per wave into LDS, one per workgroup and layout into memory
     for (int off = 32; off > 0; off >>= 1) local = fmaxf(local, __shfl_xor(local, off));
@@ -569,11 +629,36 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g,
     }
 }
 
-// Pass 2: quantize and pack every group of the requested layouts.
+// Quantize this lane's group of tile (r0, c0).
+template <int MODE, bool ROT>
+__device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st,
+                                           const ScaleTable &tb, const QuantArgs &a,
+                                           const LayoutOut &o, int lay, int li, float g,
+                                           float rcp6g, float rcp4g, int64_t r0, int64_t c0)
+{
+    const int64_t n = lay == 0 ? a.C : a.R;
+    const int64_t vec = lay == 0 ? r0 + li : c0 + li;
+    const int64_t start = lay == 0 ? c0 : r0;          // first position of this group
+    if (vec >= (lay == 0 ? a.R : a.C)) return;
+    float r[TILE];
+    if (lay == 0) read_row(tile, st, li, r);
+    else read_col(tile, st, li, r);
+    if (ROT) fwht(r);
+    const int64_t left = n - start;
+    const int nb = left >= TILE ? 8 : (int)(left >> 4);
+    quantize_group<MODE>(r, nb, g, tb, rcp6g, rcp4g, a.seed, (uint32_t)lay, vec, n, start / TILE,
+                         o.codes + vec * (n >> 1) + (start >> 1),
+                         o.scales + vec * (n >> 4) + (start >> 4));
+}
+
+// Pass 2: quantize and pack every group of the requested layouts.  Tiles are walked in
+// the reverse order of pass 1 (its last tiles are the likeliest to still be cached), with
+// the same two-buffer streaming.
 template <int MODE, bool ROT, int LAY>
 __global__ void __launch_bounds__(256, 2) k_quant(QuantArgs a)
 {
-    __shared__ Tile tile;
+    __shared__ Tile tile0;
+    __shared__ Tile tile1;
     __shared__ SignTable st;
     __shared__ ScaleTable tabs[(LAY == LAY_BOTH) ? 2 : 1];
     const int t = threadIdx.x;
@@ -588,27 +673,29 @@ __global__ void __launch_bounds__(256, 2) k_quant(QuantArgs a)
     build_sign_table(st, a.rht_seed, ROT);
     build_scale_table(tb, g, li);
     if (blockIdx.x == 0 && li == 0) *o.g = g;
-    const int64_t n = lay == 0 ? a.C : a.R;
-    for (int64_t k = blockIdx.x; k < a.tiles; k += gridDim.x) {
-        const int64_t tid = a.tiles - 1 - k;    // reverse order: reuse what pass 1 left cached
-        const int64_t r0 = (tid / a.tiles_c) * TILE, c0 = (tid % a.tiles_c) * TILE;
-        __syncthreads();
-        load_tile(tile, a.x, a.R, a.C, r0, c0);
-        __syncthreads();
-        const int64_t vec = lay == 0 ? r0 + li : c0 + li;
-        const int64_t start = lay == 0 ? c0 : r0;      // first position of this group
-        if (vec < (lay == 0 ? a.R : a.C)) {
-            float r[TILE];
-            if (lay == 0) read_row(tile, st, li, r);
-            else read_col(tile, st, li, r);
-            if (ROT) fwht(r);
-            const int64_t left = n - start;
-            const int nb = left >= TILE ? 8 : (int)(left >> 4);
-            const int64_t gi = start / TILE;
-            quantize_group<MODE>(r, nb, g, tb, rcp6g, rcp4g, a.seed, (uint32_t)lay, vec, n, gi,
-                                 o.codes + vec * (n >> 1) + (start >> 1),
-                                 o.scales + vec * (n >> 4) + (start >> 4));
+    int64_t k = blockIdx.x, r0, c0;
+    if (k < a.tiles) {
+        tile_origin(a, a.tiles - 1 - k, r0, c0);
+        stage_tile(tile0, a.x, a.R, a.C, r0, c0);
+    }
+    while (k < a.tiles) {
+        const int64_t k1 = k + gridDim.x;
+        __syncthreads();                                   // tile0 landed; tile1 is free
+        int64_t r1 = 0, c1 = 0;
+        if (k1 < a.tiles) {
+            tile_origin(a, a.tiles - 1 - k1, r1, c1);
+            stage_tile(tile1, a.x, a.R, a.C, r1, c1);
         }
+        tile_quant<MODE, ROT>(tile0, st, tb, a, o, lay, li, g, rcp6g, rcp4g, r0, c0);
+        if (k1 >= a.tiles) break;
+        const int64_t k2 = k1 + gridDim.x;
+        __syncthreads();                                   // tile1 landed; tile0 is free
+        if (k2 < a.tiles) {
+            tile_origin(a, a.tiles - 1 - k2, r0, c0);
+            stage_tile(tile0, a.x, a.R, a.C, r0, c0);
+        }
+        tile_quant<MODE, ROT>(tile1, st, tb, a, o, lay, li, g, rcp6g, rcp4g, r1, c1);
+        k = k2;
     }
 }
 
@@ -690,9 +777,16 @@ static int cu_count()
     return cached[dev];
 }
 
-static int grid_for(int64_t tiles)
+// Persistent grid: as many workgroups as can be resident at once (occupancy of this kernel
+// at this block size), never more than there are tiles.
+template <typename K>
+static int grid_for(K kernel, int threads, int64_t tiles)
 {
-    const int64_t cap = (int64_t)cu_count() * 8;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 1;
+    const int64_t cap = (int64_t)cu_count() * per_cu;
     return (int)(tiles < cap ? tiles : cap);
 }
 
@@ -700,14 +794,15 @@ template <bool ROT, int LAY>
 static void launch_amax(const QuantArgs &a, hipStream_t st)
 {
     const int threads = (LAY == LAY_BOTH) ? 256 : 128;
-    k_amax<ROT, LAY><<<grid_for(a.tiles), threads, 0, st>>>(a);
+    k_amax<ROT, LAY><<<grid_for(k_amax<ROT, LAY>, threads, a.tiles), threads, 0, st>>>(a);
 }
 
 template <int MODE, bool ROT, int LAY>
 static void launch_quant(const QuantArgs &a, hipStream_t st)
 {
     const int threads = (LAY == LAY_BOTH) ? 256 : 128;
-    k_quant<MODE, ROT, LAY><<<grid_for(a.tiles), threads, 0, st>>>(a);
+    k_quant<MODE, ROT, LAY><<<grid_for(k_quant<MODE, ROT, LAY>, threads, a.tiles), threads, 0,
+                              st>>>(a);
 }
 
 template <int MODE, bool ROT>
