@@ -37,6 +37,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mse", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (3x): the calibration kernel "
+                         "for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the MS-EDEN quantizer path runs "
@@ -123,6 +126,14 @@ def main():
             "traffic": None,
         },
     }
+
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = {"read": src.numel(), "written": dst.numel()}
 
     if not args.no_mse:
         result["mse_vs_sr"] = mse_vs_sr(nv, workloads, dev)

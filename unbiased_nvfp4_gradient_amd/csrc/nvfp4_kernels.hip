@@ -15,14 +15,17 @@
 // -ffp-contract=off and no fast-math, so a multiply-add is fused only where __builtin_fmaf
 // is written (the scalar-product chains), exactly as the CPU oracle does.
 //
-// Work decomposition.  The input is cut into 128 x 128 BF16 tiles (32 KiB).  A workgroup
-// stages a tile in LDS with coalesced 16-byte loads, then each lane owns one whole
-// 128-element group: lanes 0..127 take the tile's 128 row segments (row layout), lanes
-// 128..255 its 128 column segments (column layout).  With a group in one lane's registers,
-// the 7 butterfly stages of the Hadamard transform, the 1x16 block maxima and the pairwise
-// sums of the EDEN ratio need no cross-lane traffic at all.  The LDS tile is stored with
-// its 16-byte chunks XOR-swizzled by row, so that both the row reads (one 16-byte chunk per
-// lane) and the column reads (one 2-byte element per lane) are free of bank conflicts.
+// Work decomposition.  The input is cut into 128 x 128 BF16 tiles (32 KiB).  Persistent
+// workgroups stream tiles into two LDS buffers with direct global->LDS loads (the next
+// tile lands while the current one is processed).  Each 128-element group is held by a pair
+// of adjacent lanes, 64 values each: lanes 0..255 of a workgroup take the tile's 128 row
+// segments (row layout), lanes 256..511 its 128 column segments (column layout).  Six of
+// the seven butterfly stages of the Hadamard transform, the 1x16 block maxima and all but
+// the last level of the EDEN pairwise sums stay in registers; the span-64 stage and the
+// last sum level cross the lane pair with one DPP swap.  That keeps a kernel under 128
+// registers (4 waves per SIMD).  The LDS tile is stored with its 16-byte chunks
+// XOR-swizzled by row, so that both the row reads (one 16-byte chunk per lane) and the
+// column reads (one 2-byte element per lane) are free of bank conflicts.
 //
 // Conversions use gfx950's own instructions where they compute exactly the contract's
 // rounding: v_cvt_scalef32_pk_fp4_f32 with scale 1.0 is round-to-nearest-even onto the E2M1
@@ -173,22 +176,29 @@ struct Tile { uint4 chunk[TILE * CHUNKS]; };   // 32 KiB, chunk c of row i at i*
 __device__ __forceinline__ int swz(int i, int c) { return i * CHUNKS + (c ^ (i & 15)); }
 
 // Per-position fp32 sign-bit masks of the rotation (sigma_p = -1 -> 0x80000000), built
-// once per workgroup in LDS; lanes read them as broadcasts right before use.
-struct SignTable { uint4 m[TILE / 4]; };
+// once per workgroup in LDS and read as broadcasts right before use.
+//   mr[h][k]  masks of positions 64h + 4k .. 64h + 4k + 3 (row order); the padding word
+//             puts the two halves in different LDS banks.
+//   mc[s][h]  masks of positions 64h + 16q + s for q = 0..3 (column reader order).
+struct SignTable {
+    uint4 mr[2][17];
+    uint4 mc[16][2];
+};
 
 __device__ __forceinline__ void build_sign_table(SignTable &st, uint64_t rht_seed, bool rot)
 {
-    if (threadIdx.x < TILE / 4) {
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
+    const int t = threadIdx.x;
+    if (t < TILE) {
+        uint32_t mask = 0u;
         if (rot) {
             const Signs s = make_signs(rht_seed);
-            const int q = threadIdx.x >> 3;                 // sign word holding these 4 bits
+            const int q = t >> 5;                        // sign word holding bit t
             const uint32_t word = q == 0 ? s.w[0] : q == 1 ? s.w[1] : q == 2 ? s.w[2] : s.w[3];
-            const int b0 = (4 * threadIdx.x) & 31;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) w[k] = ((word >> (b0 + k)) & 1u) << 31;
+            mask = ((word >> (t & 31)) & 1u) << 31;
         }
-        st.m[threadIdx.x] = make_uint4(w[0], w[1], w[2], w[3]);
+        const int h = t >> 6, pl = t & 63;
+        reinterpret_cast<uint32_t *>(&st.mr[h][0])[pl] = mask;
+        reinterpret_cast<uint32_t *>(&st.mc[pl & 15][h])[pl >> 4] = mask;
     }
 }
 
@@ -231,58 +241,91 @@ __device__ __forceinline__ void stage_tile(Tile &t, const uint16_t *__restrict__
     }
 }
 
-// Row segment i of the tile -> r[p] = sigma_p * x (exact BF16 decode, sign folded in).
-__device__ __forceinline__ void read_row(const Tile &t, const SignTable &st, int i,
-                                         float r[TILE])
+// Hide a value from loop-invariant code motion: the swizzled LDS addresses below are
+// recomputed (one v_xor each) per tile instead of being hoisted into dozens of registers
+// that stay live across the whole loop.
+__device__ __forceinline__ uint32_t opaque(uint32_t v)
 {
+    __asm__ volatile("" : "+v"(v));
+    return v;
+}
+
+// ------------------------------------------------------------------------------ half groups
+// A 128-element group is held by a pair of adjacent lanes: lane half h = 0 holds positions
+// 0..63, h = 1 holds 64..127, 64 registers each.
+
+constexpr int HALF = TILE / 2;
+
+// Row segment i, half h of the tile -> r[k] = sigma_p * x_p, p = 64h + k (exact BF16 decode,
+// sign folded in).  Chunk c of row i sits at byte (i*256 + 16*(c ^ (i&15))) = base_i ^ (c<<4).
+__device__ __forceinline__ void read_row_half(const Tile &t, const SignTable &st, int i, int h,
+                                              float r[HALF])
+{
+    const char *t8 = reinterpret_cast<const char *>(t.chunk);
+    const uint32_t base = opaque((uint32_t)(i * 256 + 16 * (i & 15)) ^ (uint32_t)(h << 7));
+    const uint4 *mrow = st.mr[h];
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        const uint4 v = t.chunk[swz(i, c)];
-        const uint4 m0 = st.m[2 * c], m1 = st.m[2 * c + 1];
+    for (int cc = 0; cc < 8; ++cc) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(t8 + (base ^ (uint32_t)(cc << 4)));
+        const uint4 m0 = mrow[2 * cc], m1 = mrow[2 * cc + 1];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         const uint32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             // (w << 16) + mask flips bit 31 exactly when the mask is set
-            r[8 * c + 2 * k] = __uint_as_float((w[k] << 16) + m[2 * k]);
-            r[8 * c + 2 * k + 1] = __uint_as_float((w[k] & 0xFFFF0000u) ^ m[2 * k + 1]);
+            r[8 * cc + 2 * k] = __uint_as_float((w[k] << 16) + m[2 * k]);
+            r[8 * cc + 2 * k + 1] = __uint_as_float((w[k] & 0xFFFF0000u) ^ m[2 * k + 1]);
         }
     }
 }
 
-// Column segment j of the tile -> r[i] = sigma_i * x.
-__device__ __forceinline__ void read_col(const Tile &t, const SignTable &st, int j,
-                                         float r[TILE])
+// Column segment j, half h -> r[k] = sigma_p * x_p, p = 64h + k.  Element (i, j) sits at
+// byte i*256 + 16*((j>>3) ^ (i&15)) + 2*(j&7): for i = 64h + 16q + s that is
+// off(s) + 16384h + 4096q.
+__device__ __forceinline__ void read_col_half(const Tile &t, const SignTable &st, int j, int h,
+                                              float r[HALF])
 {
-    const uint16_t *t16 = reinterpret_cast<const uint16_t *>(t.chunk);
+    const char *t8 = reinterpret_cast<const char *>(t.chunk) + 16384 * h;
+    const uint32_t jc = opaque((uint32_t)(16 * (j >> 3))), je = 2 * (j & 7);
 #pragma unroll
-    for (int i4 = 0; i4 < TILE / 4; ++i4) {
-        const uint4 m = st.m[i4];
+    for (int s16 = 0; s16 < 16; ++s16) {
+        const uint32_t off = (jc ^ (uint32_t)(16 * s16)) + (uint32_t)(256 * s16) + je;
+        const uint4 m = st.mc[s16][h];
         const uint32_t mm[4] = {m.x, m.y, m.z, m.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = 4 * i4 + k;
-            const uint32_t h = t16[swz(i, j >> 3) * 8 + (j & 7)];
-            r[i] = __uint_as_float((h << 16) + mm[k]);
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t v = *reinterpret_cast<const uint16_t *>(t8 + off + 4096 * q);
+            r[16 * q + s16] = __uint_as_float((v << 16) + mm[q]);
         }
     }
 }
 
-// r <- H r: unnormalised Sylvester Walsh-Hadamard transform, butterfly spans 1, 2, ..., 64
-// in that order (the random signs are already folded in by read_row / read_col).
-__device__ __forceinline__ void fwht(float r[TILE])
+// Value held by the other lane of the pair (DPP quad_perm [1,0,3,2]).
+__device__ __forceinline__ float pair_swap(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// r <- H r over the pair: unnormalised Sylvester Walsh-Hadamard transform, butterfly spans
+// 1, 2, ..., 32 inside each half, then span 64 across the pair: the low half gets
+// a + b and the high half a - b, each rounded once (fma with a +-1 multiplier is exact up
+// to that one rounding).  The random signs are already folded in by the readers.
+__device__ __forceinline__ void fwht_pair(float r[HALF], int h)
 {
 #pragma unroll
-    for (int h = 1; h < TILE; h <<= 1) {
+    for (int s = 1; s < HALF; s <<= 1) {
 #pragma unroll
-        for (int i = 0; i < TILE; ++i) {
-            if ((i & h) == 0) {
-                const float u = r[i], v = r[i + h];
+        for (int i = 0; i < HALF; ++i) {
+            if ((i & s) == 0) {
+                const float u = r[i], v = r[i + s];
                 r[i] = u + v;
-                r[i + h] = u - v;
+                r[i + s] = u - v;
             }
         }
     }
+    const float m = h ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) r[i] = __builtin_fmaf(r[i], m, pair_swap(r[i]));
 }
 
 // Balanced pairwise sum of 2^k values in natural order, in place.
@@ -333,6 +376,26 @@ struct QuantArgs {
     int64_t tiles_c, tiles;    // tiles per tile-row, total tiles
 };
 
+// Lane roles: each layout takes 256 lanes (128 groups x 2 halves) of a workgroup.
+struct Role {
+    int lay;   // 0 row layout, 1 column layout (wave-uniform)
+    int g;     // group (row or column) within the tile, 0..127
+    int h;     // half of the group held by this lane
+};
+
+template <int LAY>
+__device__ __forceinline__ Role lane_role()
+{
+    const int t = threadIdx.x;
+    Role ro;
+    // wave-uniform, so the two layouts take scalar branches instead of masked execution
+    ro.lay = __builtin_amdgcn_readfirstlane((LAY == LAY_BOTH) ? (t >> 8)
+                                                               : (LAY == LAY_ROW ? 0 : 1));
+    ro.g = (t & 255) >> 1;
+    ro.h = t & 1;
+    return ro;
+}
+
 // ------------------------------------------------------------------------------ kernels
 __global__ void k_zero_u32(uint32_t *p, int n)
 {
@@ -348,27 +411,6 @@ __global__ void k_write_g(const uint32_t *amax_bits, float D, float *g0, float *
     }
 }
 
-// Max |r| over the groups this lane owns in tile (r0, c0).
-template <bool ROT, int LAY>
-__device__ __forceinline__ float tile_amax(const Tile &tile, const SignTable &st,
-                                           const QuantArgs &a, int lay, int li, int64_t r0,
-                                           int64_t c0)
-{
-    const bool valid = (lay == 0) ? (r0 + li < a.R) : (c0 + li < a.C);
-    if (!valid) return 0.0f;
-    float r[TILE];
-    if (lay == 0) read_row(tile, st, li, r);
-    else read_col(tile, st, li, r);
-    if (ROT) fwht(r);
-    float m0 = 0.0f, m1 = 0.0f;
-#pragma unroll
-    for (int p = 0; p < TILE; p += 4) {
-        m0 = fmaxf(m0, fmaxf(fabsf(r[p]), fabsf(r[p + 1])));
-        m1 = fmaxf(m1, fmaxf(fabsf(r[p + 2]), fabsf(r[p + 3])));
-    }
-    return fmaxf(m0, m1);
-}
-
 __device__ __forceinline__ void tile_origin(const QuantArgs &a, int64_t tid, int64_t &r0,
                                             int64_t &c0)
 {
@@ -376,19 +418,39 @@ __device__ __forceinline__ void tile_origin(const QuantArgs &a, int64_t tid, int
     c0 = (tid % a.tiles_c) * TILE;
 }
 
+// Max |r| over this lane's half group of tile (r0, c0).
+template <bool ROT>
+__device__ __forceinline__ float tile_amax(const Tile &tile, const SignTable &st,
+                                           const QuantArgs &a, const Role &ro, int64_t r0,
+                                           int64_t c0)
+{
+    const bool valid = (ro.lay == 0) ? (r0 + ro.g < a.R) : (c0 + ro.g < a.C);
+    if (!valid) return 0.0f;
+    float r[HALF];
+    if (ro.lay == 0) read_row_half(tile, st, ro.g, ro.h, r);
+    else read_col_half(tile, st, ro.g, ro.h, r);
+    if (ROT) fwht_pair(r, ro.h);
+    float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+    for (int p = 0; p < HALF; p += 4) {
+        m0 = fmaxf(m0, fmaxf(fabsf(r[p]), fabsf(r[p + 1])));
+        m1 = fmaxf(m1, fmaxf(fabsf(r[p + 2]), fabsf(r[p + 3])));
+    }
+    return fmaxf(m0, m1);
+}
+
 // Pass 1: amax of |r| per layout.  Persistent workgroups walk the tiles with two LDS
 // buffers (the next tile streams in while the current one is processed); one atomicMax
 // per workgroup and layout at the end.
 template <bool ROT, int LAY>
-__global__ void __launch_bounds__(256, 2) k_amax(QuantArgs a)
+__global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
 {
     __shared__ Tile tile0;
     __shared__ Tile tile1;
     __shared__ SignTable st;
     __shared__ uint32_t wmax[2];
     const int t = threadIdx.x;
-    const int lay = (LAY == LAY_BOTH) ? (t >> 7) : (LAY == LAY_ROW ? 0 : 1);
-    const int li = (LAY == LAY_BOTH) ? (t & 127) : t;
+    const Role ro = lane_role<LAY>();
     build_sign_table(st, a.rht_seed, ROT);
     if (t < 2) wmax[t] = 0u;
     float local = 0.0f;
@@ -405,7 +467,7 @@ __global__ void __launch_bounds__(256, 2) k_amax(QuantArgs a)
             tile_origin(a, k1, r1, c1);
             stage_tile(tile1, a.x, a.R, a.C, r1, c1);
         }
-        local = fmaxf(local, tile_amax<ROT, LAY>(tile0, st, a, lay, li, r0, c0));
+        local = fmaxf(local, tile_amax<ROT>(tile0, st, a, ro, r0, c0));
         if (k1 >= a.tiles) break;
         const int64_t k2 = k1 + gridDim.x;
         __syncthreads();                                   // tile1 landed; tile0 is free
@@ -413,13 +475,13 @@ __global__ void __launch_bounds__(256, 2) k_amax(QuantArgs a)
             tile_origin(a, k2, r0, c0);
             stage_tile(tile0, a.x, a.R, a.C, r0, c0);
         }
-        local = fmaxf(local, tile_amax<ROT, LAY>(tile1, st, a, lay, li, r1, c1));
+        local = fmaxf(local, tile_amax<ROT>(tile1, st, a, ro, r1, c1));
         k = k2;
     }
     // wave max, then one atomic per wave into LDS, one per workgroup and layout into memory
     for (int off = 32; off > 0; off >>= 1) local = fmaxf(local, __shfl_xor(local, off));
     __syncthreads();
-    if ((t & 63) == 0) atomicMax(&wmax[lay], __float_as_uint(local));
+    if ((t & 63) == 0) atomicMax(&wmax[ro.lay], __float_as_uint(local));
     __syncthreads();
     if (t == 0) {
         if (LAY & LAY_ROW) atomicMax(&a.amax_bits[0], wmax[0]);
@@ -446,24 +508,23 @@ __device__ __forceinline__ void rtn_block(const float *rb, uint32_t s, const flo
     w1 = s ? b : 0u;
 }
 
-// Dequantized values q_i = den * V(code_i) of a block (signed, as the codes).
+// Signed grid values of a block's 16 codes.
 template <int K>
-__device__ __forceinline__ void decode_pair(uint32_t w0, uint32_t w1, float den, float q[16])
+__device__ __forceinline__ void decode_pair(uint32_t w0, uint32_t w1, float V[16])
 {
     const float2v v0 = DEC_FP4(w0, K), v1 = DEC_FP4(w1, K);
-    q[2 * K] = den * v0.x;
-    q[2 * K + 1] = den * v0.y;
-    q[8 + 2 * K] = den * v1.x;
-    q[8 + 2 * K + 1] = den * v1.y;
+    V[2 * K] = v0.x;
+    V[2 * K + 1] = v0.y;
+    V[8 + 2 * K] = v1.x;
+    V[8 + 2 * K + 1] = v1.y;
 }
 
-// (with den = 1.0f the multiplies fold away and q holds the signed grid values)
-__device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, float den, float q[16])
+__device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, float V[16])
 {
-    decode_pair<0>(w0, w1, den, q);
-    decode_pair<1>(w0, w1, den, q);
-    decode_pair<2>(w0, w1, den, q);
-    decode_pair<3>(w0, w1, den, q);
+    decode_pair<0>(w0, w1, V);
+    decode_pair<1>(w0, w1, V);
+    decode_pair<2>(w0, w1, V);
+    decode_pair<3>(w0, w1, V);
 }
 
 // Saturate magnitude 7 (value 6) to 6 (value 4) in every nibble of a packed word.
@@ -473,28 +534,29 @@ __device__ __forceinline__ uint32_t cap_mag6(uint32_t w)
     return w ^ seven;
 }
 
-// Quantize one group held in r[0..127] (rotated if the mode rotates), nb valid 1x16 blocks
-// (8 unless the vector ends inside this group).  vec = vector index in its layout, n =
-// vector length, gi = group index within the vector.  Writes codes and scales.
+// Quantize this lane's half group: blocks 4h..4h+3 of the group in r[0..63] (rotated when
+// the mode rotates); nbl = number of those blocks inside the vector.  vec = vector index in
+// its layout, n = vector length, gi = group index within the vector.  Writes this half's
+// 32 code bytes and 4 scale bytes (codes/scales point at the group's first byte).
 template <int MODE>
-__device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g,
-                                               const ScaleTable &tb, float rcp6g, float rcp4g,
-                                               uint64_t seed, uint32_t axis, int64_t vec,
-                                               int64_t n, int64_t gi,
-                                               uint8_t *__restrict__ codes,
-                                               uint8_t *__restrict__ scales)
+__device__ __forceinline__ void quantize_half(float r[HALF], int h, int nbl, float g,
+                                              const ScaleTable &tb, float rcp6g, float rcp4g,
+                                              uint64_t seed, uint32_t axis, int64_t vec,
+                                              int64_t n, int64_t gi,
+                                              uint8_t *__restrict__ codes,
+                                              uint8_t *__restrict__ scales)
 {
-    uint32_t cw[16];
-    uint32_t sc[8];
+    uint32_t cw[8];
+    uint32_t sc[4];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) { sc[b] = 0u; cw[2 * b] = 0u; cw[2 * b + 1] = 0u; }
+    for (int b = 0; b < 4; ++b) { sc[b] = 0u; cw[2 * b] = 0u; cw[2 * b + 1] = 0u; }
 
     if constexpr (MODE == MODE_RTN || MODE == MODE_EDEN) {
-        float bp[8], bq[8], sv[8];
+        float bp[4], bq[4], sv[4];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < 4; ++b) {
             bp[b] = 0.0f; bq[b] = 0.0f; sv[b] = 0.0f;
-            if (MODE == MODE_EDEN || b < nb) {
+            if (MODE == MODE_EDEN || b < nbl) {
                 const float *rb = r + 16 * b;
                 const uint32_t s = e4m3_rne_hw(block_max(rb) * rcp6g);
                 const float4 e = tb.e[s];
@@ -505,7 +567,7 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g,
                     // <r,r> and <r,V> of the block by fused multiply-add chains in element
                     // order; den is factored out of the block's <r,q>.
                     float V[16];
-                    decode_block(cw[2 * b], cw[2 * b + 1], 1.0f, V);
+                    decode_block(cw[2 * b], cw[2 * b + 1], V);
                     float p = 0.0f, v = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
@@ -518,34 +580,37 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g,
             }
         }
         if constexpr (MODE == MODE_EDEN) {
-            const float num = tree<8>(bp), den = tree<8>(bq);
+            // pairwise sums over the group's 8 blocks: two levels inside the half, the last
+            // level across the pair (low half's sum + high half's sum in both lanes)
+            const float pn = tree<4>(bp), qn = tree<4>(bq);
+            const float po = pair_swap(pn), qo = pair_swap(qn);
+            const float num = h ? po + pn : pn + po;
+            const float den = h ? qo + qn : qn + qo;
             const float S = den > 0.0f ? num / den : 1.0f;
-            const int64_t k0 = vec * (n >> 4) + gi * 8;     // scale index of block 0, % 8 == 0
-            const uint64_t j0 = (uint64_t)k0 >> 2;
-            const Word4 w0 = philox(seed, (uint32_t)j0, (uint32_t)(j0 >> 32), STREAM_SCALE_SR, axis);
-            const Word4 w1 = philox(seed, (uint32_t)(j0 + 1), (uint32_t)((j0 + 1) >> 32),
-                                    STREAM_SCALE_SR, axis);
+            // scale index of this half's first block is a multiple of 4: one Philox block
+            const uint64_t j = ((uint64_t)(vec * (n >> 4) + gi * 8) >> 2) + (uint64_t)h;
+            const Word4 w = philox(seed, (uint32_t)j, (uint32_t)(j >> 32), STREAM_SCALE_SR, axis);
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
+            for (int b = 0; b < 4; ++b) {
                 const float c = S * sv[b];
-                const uint32_t w = (b < 4) ? w0.w[b] : w1.w[b - 4];
                 uint32_t out;
                 if (!(c < 448.0f)) out = 0x7Eu;
                 else if (c < 0.015625f) out = e4m3_rne_hw(c);      // no SR below 2^-6
-                else out = e4m3_of_exact_normal((__float_as_uint(c) + (w >> 12)) & 0xFFF00000u);
+                else out = e4m3_of_exact_normal((__float_as_uint(c) + (w.w[b] >> 12)) & 0xFFF00000u);
                 sc[b] = sc[b] ? out : 0u;
             }
         }
     } else if constexpr (MODE == MODE_SR) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            if (b < nb) {
+        for (int b = 0; b < 4; ++b) {
+            if (b < nbl) {
                 const float *rb = r + 16 * b;
                 const uint32_t s = e4m3_up(block_max(rb) * rcp6g);
                 const float rcp = tb.e[s].z;
                 sc[b] = s;
                 if (s) {
-                    const int64_t e0 = vec * n + gi * TILE + 16 * b;   // element index, % 4 == 0
+                    // element index of the block's first element, a multiple of 4
+                    const int64_t e0 = vec * n + gi * TILE + HALF * h + 16 * b;
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
                         const uint64_t j = ((uint64_t)e0 >> 2) + qd;
@@ -576,8 +641,8 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g,
         }
     } else {   // MODE_FP46
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            if (b < nb) {
+        for (int b = 0; b < 4; ++b) {
+            if (b < nbl) {
                 const float *rb = r + 16 * b;
                 const float m = block_max(rb);
                 const uint32_t sA = e4m3_rne_hw(m * rcp6g), sB = e4m3_rne_hw(m * rcp4g);
@@ -590,8 +655,8 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g,
                 // squared error of each option: d = den * V - r with one rounding, summed by
                 // fused multiply-adds in element order
                 float VA[16], VB[16];
-                decode_block(a0, a1, 1.0f, VA);
-                decode_block(b0, b1, 1.0f, VB);
+                decode_block(a0, a1, VA);
+                decode_block(b0, b1, VB);
                 float errA = 0.0f, errB = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -608,71 +673,71 @@ __device__ __forceinline__ void quantize_group(float r[TILE], int nb, float g,
         }
     }
 
-    // ---- stores: 64 code bytes + 8 scale bytes for a full, 16-byte aligned group
-    if (nb == 8 && (n & (TILE - 1)) == 0) {
-        uint4 *cp = reinterpret_cast<uint4 *>(codes);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            cp[k] = make_uint4(cw[4 * k], cw[4 * k + 1], cw[4 * k + 2], cw[4 * k + 3]);
-        *reinterpret_cast<uint2 *>(scales) =
-            make_uint2(sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24),
-                       sc[4] | (sc[5] << 8) | (sc[6] << 16) | (sc[7] << 24));
+    // ---- stores: this half's 32 code bytes and 4 scale bytes
+    if (nbl == 4 && (n & (TILE - 1)) == 0) {
+        uint4 *cp = reinterpret_cast<uint4 *>(codes + 32 * h);
+        cp[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        cp[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+        *reinterpret_cast<uint32_t *>(scales + 4 * h) =
+            sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24);
     } else {
-        uint2 *cp = reinterpret_cast<uint2 *>(codes);
+        uint2 *cp = reinterpret_cast<uint2 *>(codes + 32 * h);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            if (b < nb) {
+        for (int b = 0; b < 4; ++b) {
+            if (b < nbl) {
                 cp[b] = make_uint2(cw[2 * b], cw[2 * b + 1]);
-                scales[b] = (uint8_t)sc[b];
+                scales[4 * h + b] = (uint8_t)sc[b];
             }
         }
     }
 }
 
-// Quantize this lane's group of tile (r0, c0).
+// Quantize this lane's half group of tile (r0, c0).
 template <int MODE, bool ROT>
 __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st,
                                            const ScaleTable &tb, const QuantArgs &a,
-                                           const LayoutOut &o, int lay, int li, float g,
+                                           const LayoutOut &o, const Role &ro, float g,
                                            float rcp6g, float rcp4g, int64_t r0, int64_t c0)
 {
-    const int64_t n = lay == 0 ? a.C : a.R;
-    const int64_t vec = lay == 0 ? r0 + li : c0 + li;
-    const int64_t start = lay == 0 ? c0 : r0;          // first position of this group
-    if (vec >= (lay == 0 ? a.R : a.C)) return;
-    float r[TILE];
-    if (lay == 0) read_row(tile, st, li, r);
-    else read_col(tile, st, li, r);
-    if (ROT) fwht(r);
+    const int64_t n = ro.lay == 0 ? a.C : a.R;
+    const int64_t vec = ro.lay == 0 ? r0 + ro.g : c0 + ro.g;
+    const int64_t start = ro.lay == 0 ? c0 : r0;       // first position of this group
+    if (vec >= (ro.lay == 0 ? a.R : a.C)) return;
+    float r[HALF];
+    if (ro.lay == 0) read_row_half(tile, st, ro.g, ro.h, r);
+    else read_col_half(tile, st, ro.g, ro.h, r);
+    if (ROT) fwht_pair(r, ro.h);
     const int64_t left = n - start;
     const int nb = left >= TILE ? 8 : (int)(left >> 4);
-    quantize_group<MODE>(r, nb, g, tb, rcp6g, rcp4g, a.seed, (uint32_t)lay, vec, n, start / TILE,
-                         o.codes + vec * (n >> 1) + (start >> 1),
-                         o.scales + vec * (n >> 4) + (start >> 4));
+    const int nbl = nb - 4 * ro.h < 0 ? 0 : (nb - 4 * ro.h > 4 ? 4 : nb - 4 * ro.h);
+    quantize_half<MODE>(r, ro.h, nbl, g, tb, rcp6g, rcp4g, a.seed, (uint32_t)ro.lay, vec, n,
+                        start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
+                        o.scales + vec * (n >> 4) + (start >> 4));
 }
 
 // Pass 2: quantize and pack every group of the requested layouts.  Tiles are walked in
 // the reverse order of pass 1 (its last tiles are the likeliest to still be cached), with
 // the same two-buffer streaming.
+// MS-EDEN fits 128 registers (4 waves per SIMD); the other modes keep more values live and
+// are given 2 waves per SIMD rather than spilling.
 template <int MODE, bool ROT, int LAY>
-__global__ void __launch_bounds__(256, 2) k_quant(QuantArgs a)
+__global__ void __launch_bounds__(512, MODE == MODE_EDEN ? 4 : 2) k_quant(QuantArgs a)
 {
     __shared__ Tile tile0;
     __shared__ Tile tile1;
     __shared__ SignTable st;
     __shared__ ScaleTable tabs[(LAY == LAY_BOTH) ? 2 : 1];
     const int t = threadIdx.x;
-    const int lay = (LAY == LAY_BOTH) ? (t >> 7) : (LAY == LAY_ROW ? 0 : 1);
-    const int li = (LAY == LAY_BOTH) ? (t & 127) : t;
+    const Role ro = lane_role<LAY>();
     const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
-    const float g = __uint_as_float(lay == 0 ? a.amax_bits[0] : a.amax_bits[1]) / D;
+    const float g = __uint_as_float(ro.lay == 0 ? a.amax_bits[0] : a.amax_bits[1]) / D;
     const float rcp6g = clamped_rcp(6.0f * g), rcp4g = clamped_rcp(4.0f * g);
-    ScaleTable &tb = tabs[(LAY == LAY_BOTH) ? lay : 0];
+    ScaleTable &tb = tabs[(LAY == LAY_BOTH) ? ro.lay : 0];
     // select this lane's layout without indexing the argument struct at run time
-    const LayoutOut o = (lay == 0) ? a.out[0] : a.out[1];
+    const LayoutOut o = (ro.lay == 0) ? a.out[0] : a.out[1];
     build_sign_table(st, a.rht_seed, ROT);
-    build_scale_table(tb, g, li);
-    if (blockIdx.x == 0 && li == 0) *o.g = g;
+    build_scale_table(tb, g, t & 255);
+    if (blockIdx.x == 0 && (t & 255) == 0) *o.g = g;
     int64_t k = blockIdx.x, r0, c0;
     if (k < a.tiles) {
         tile_origin(a, a.tiles - 1 - k, r0, c0);
@@ -686,7 +751,7 @@ __global__ void __launch_bounds__(256, 2) k_quant(QuantArgs a)
             tile_origin(a, a.tiles - 1 - k1, r1, c1);
             stage_tile(tile1, a.x, a.R, a.C, r1, c1);
         }
-        tile_quant<MODE, ROT>(tile0, st, tb, a, o, lay, li, g, rcp6g, rcp4g, r0, c0);
+        tile_quant<MODE, ROT>(tile0, st, tb, a, o, ro, g, rcp6g, rcp4g, r0, c0);
         if (k1 >= a.tiles) break;
         const int64_t k2 = k1 + gridDim.x;
         __syncthreads();                                   // tile1 landed; tile0 is free
@@ -694,7 +759,7 @@ __global__ void __launch_bounds__(256, 2) k_quant(QuantArgs a)
             tile_origin(a, a.tiles - 1 - k2, r0, c0);
             stage_tile(tile0, a.x, a.R, a.C, r0, c0);
         }
-        tile_quant<MODE, ROT>(tile1, st, tb, a, o, lay, li, g, rcp6g, rcp4g, r1, c1);
+        tile_quant<MODE, ROT>(tile1, st, tb, a, o, ro, g, rcp6g, rcp4g, r1, c1);
         k = k2;
     }
 }
@@ -793,14 +858,14 @@ static int grid_for(K kernel, int threads, int64_t tiles)
 template <bool ROT, int LAY>
 static void launch_amax(const QuantArgs &a, hipStream_t st)
 {
-    const int threads = (LAY == LAY_BOTH) ? 256 : 128;
+    const int threads = (LAY == LAY_BOTH) ? 512 : 256;
     k_amax<ROT, LAY><<<grid_for(k_amax<ROT, LAY>, threads, a.tiles), threads, 0, st>>>(a);
 }
 
 template <int MODE, bool ROT, int LAY>
 static void launch_quant(const QuantArgs &a, hipStream_t st)
 {
-    const int threads = (LAY == LAY_BOTH) ? 256 : 128;
+    const int threads = (LAY == LAY_BOTH) ? 512 : 256;
     k_quant<MODE, ROT, LAY><<<grid_for(k_quant<MODE, ROT, LAY>, threads, a.tiles), threads, 0,
                               st>>>(a);
 }
