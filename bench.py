@@ -37,6 +37,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mse", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (3x): the calibration kernel "
                          "for HBM byte counters")
@@ -127,6 +128,9 @@ def main():
         },
     }
 
+    if not args.no_gemm:
+        result["gemm_check"] = gemm_check(nv, workloads, dev, out.row, stream)
+
     if args.copy_probe:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -142,6 +146,34 @@ def main():
         result["cpu_baseline"] = cpu_baseline(x_cpu, B)
 
     print(json.dumps(result), flush=True)
+
+
+def gemm_check(nv, workloads, dev, a, stream, reps=5):
+    """The GEMM check consumer on the bench's quantized activations: A = the MS-EDEN row
+    layout of the 16384 x 8192 input, B = the 8192 x 8192 N(0, 0.02) weight quantized by RTN
+    with the same rotation along K; C = A B^T in FP32 (M=16384, N=8192, K=8192)."""
+    import numpy as np
+    import torch
+
+    w = workloads.c4w().to(dev)
+    b = nv.rtn_quantize(w, rht=True, rht_seed=1, layouts=("row",)).row
+    del w
+    c = torch.empty((a.codes.shape[0], b.codes.shape[0]), dtype=torch.float32, device=dev)
+    nv.nvfp4_gemm_check(a, b, rotated_pair=True, out=c, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        nv.nvfp4_gemm_check(a, b, rotated_pair=True, out=c, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    M, K = a.codes.shape[0], a.codes.shape[1] * 2
+    N = b.codes.shape[0]
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"kernel": "k_gemm (dequantize-in-LDS, v_mfma_f32_32x32x16_bf16)", "M": M, "N": N,
+            "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
 
 
 def mse_vs_sr(nv, workloads, dev):

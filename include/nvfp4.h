@@ -158,6 +158,18 @@ int nvfp4_quantize_amax(int mode, const void *x_bf16, int64_t rows, int64_t cols
 int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int block,
                int rht, uint64_t rht_seed, float *out, void *stream);
 
+/* GEMM check consumer (itsolotime.com summary, abstract: every linear layer's products run
+ * on NVFP4 operands): C[m][n] = f * gA * gB * sum_k a(m,k) * b(n,k), where a(m,k) =
+ * sign * E4M3(scale) * magnitude of code (m,k) of `a` and likewise for `b`, and f = 2^-7
+ * when rotated_pair != 0 (both operands rotated along K with the same rht_seed, so
+ * H H = 128 I cancels the rotation) else 1.  a is [M][K] and b is [N][K], both in the
+ * row layout (K contiguous, as the quantizers emit); c is FP32 [M][N] row-major (device,
+ * 4-byte aligned).  Operand values are dequantized exactly to BF16 and multiplied on the
+ * matrix cores with FP32 accumulation (summation order unspecified).  M and N must be
+ * multiples of 32 and K a multiple of 64. */
+int nvfp4_gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
+                     int64_t K, int rotated_pair, float *c, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

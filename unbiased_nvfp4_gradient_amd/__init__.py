@@ -30,7 +30,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_ARG =
     0, -1, -2, -3, -4, -5, -6, -7)
 
 EXPORTED = ("nvfp4_workspace_bytes", "nvfp4_strerror", "eden_quantize", "sr_quantize",
-            "rtn_quantize", "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize")
+            "rtn_quantize", "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize",
+            "nvfp4_gemm_check")
 
 MODE_RTN, MODE_SR, MODE_EDEN, MODE_FP46 = 0, 1, 2, 3
 MODES = {"rtn": MODE_RTN, "sr": MODE_SR, "eden": MODE_EDEN, "fp46": MODE_FP46}
@@ -84,8 +85,9 @@ def lib() -> ctypes.CDLL:
     h.dequantize.argtypes = [TP, i64, i64, i32, i32, i32, u64, P, P]
     h.nvfp4_amax.argtypes = [P, i64, i64, i32, i32, i32, u64, i32, P, P]
     h.nvfp4_quantize_amax.argtypes = [i32, P, i64, i64, i32, i32, u64, i32, u64, P, TP, TP, P]
+    h.nvfp4_gemm_check.argtypes = [TP, TP, i64, i64, i64, i32, P, P]
     for name in ("eden_quantize", "sr_quantize", "rtn_quantize", "fp46_quantize", "dequantize",
-                 "nvfp4_amax", "nvfp4_quantize_amax"):
+                 "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_gemm_check"):
         getattr(h, name).restype = i32
     _lib_handle = h
     return h
@@ -219,6 +221,22 @@ def dequantize(t: NVFP4, rht: bool = False, rht_seed: int = 0,
     return out
 
 
+def nvfp4_gemm_check(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """C = A B^T of two row-layout NVFP4 operands ([M, K] and [N, K]), FP32 [M, N]."""
+    M, K = a.codes.shape[0], a.codes.shape[1] * 2
+    N = b.codes.shape[0]
+    if b.codes.shape[1] * 2 != K:
+        raise ValueError("operands disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+    _check("nvfp4_gemm_check", lib().nvfp4_gemm_check(
+        _ct(a), _ct(b), M, N, K, int(bool(rotated_pair)), out.data_ptr(),
+        _stream_ptr(stream, a.codes.device)))
+    return out
+
+
 __all__ = ["NVFP4", "Quantized", "NVFP4Error", "eden_quantize", "sr_quantize", "rtn_quantize",
-           "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize", "workspace_bytes", "strerror", "empty_layout", "lib",
+           "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize", "nvfp4_gemm_check",
+           "workspace_bytes", "strerror", "empty_layout", "lib",
            "LIB_PATH", "EXPORTED"]

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["nvfp4_kernels.hip", "nvfp4_api.cpp"]
+SOURCES = ["nvfp4_kernels.hip", "nvfp4_gemm.hip", "nvfp4_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -13,6 +13,11 @@ extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x
                                    uint8_t *codes1, uint8_t *scales1, float *g1,
                                    const float *amax, uint64_t seed, uint64_t rht_seed,
                                    hipStream_t st);
+extern "C" hipError_t nvfp4k_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
+                                  const float *a_g, const uint8_t *b_codes,
+                                  const uint8_t *b_scales, const float *b_g, int64_t M,
+                                  int64_t N, int64_t K, int rotated_pair, float *c,
+                                  hipStream_t st);
 extern "C" hipError_t nvfp4k_dequantize(const uint8_t *codes, const uint8_t *scales,
                                         const float *g, int64_t vecs, int64_t n, int rht,
                                         uint64_t rht_seed, float *out, hipStream_t st);
@@ -225,6 +230,29 @@ int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int b
     if (rc) return rc;
     hipError_t e = nvfp4k_dequantize(in->codes, in->scales, in->tensor_scale, vecs, n, rht,
                                      rht_seed, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+int nvfp4_gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
+                     int64_t K, int rotated_pair, float *c, void *stream)
+{
+    if (!a || !b || !a->tensor_scale || !b->tensor_scale) return NVFP4_ERR_NULL;
+    if (rotated_pair != 0 && rotated_pair != 1) return NVFP4_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
+    if (M > MAX_DIM || N > MAX_DIM || K > MAX_DIM || (M > 0 && N > MAX_ELEMS / M) ||
+        (M > 0 && K > MAX_ELEMS / M) || (N > 0 && K > MAX_ELEMS / N))
+        return NVFP4_ERR_ARG;
+    if (M % 32 || N % 32 || K % 64) return NVFP4_ERR_SHAPE;
+    if (M > 0 && N > 0 && (!c || (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
+        return NVFP4_ERR_NULL;
+    if (!aligned(a->codes, 16) || !aligned(b->codes, 16) || !aligned(c, 4) ||
+        !aligned(a->tensor_scale, 4) || !aligned(b->tensor_scale, 4))
+        return NVFP4_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = nvfp4k_gemm(a->codes, a->scales, a->tensor_scale, b->codes, b->scales,
+                               b->tensor_scale, M, N, K, rotated_pair, c,
+                               static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
