@@ -171,9 +171,14 @@ __device__ __forceinline__ uint32_t sign_mask(const Signs &s, int p)
 }
 
 // ------------------------------------------------------------------------------ tile
-struct Tile { uint4 chunk[TILE * CHUNKS]; };   // 32 KiB, chunk c of row i at i*16 + (c ^ (i&15))
+// 32 KiB.  Chunk c (8 BF16) of tile row i sits at slot i*16 + (c ^ S(i)), with
+// S(i) = (i & 15) ^ (8 * bit 6 of i): the low bits spread 16 consecutive rows over all 64
+// LDS banks for the row readers, and bit 6 separates rows i and i + 64, which the two lanes
+// of a pair read in the same instruction.
+struct Tile { uint4 chunk[TILE * CHUNKS]; };
 
-__device__ __forceinline__ int swz(int i, int c) { return i * CHUNKS + (c ^ (i & 15)); }
+__device__ __forceinline__ int swz_key(int i) { return (i & 15) ^ (((i >> 6) & 1) << 3); }
+__device__ __forceinline__ int swz(int i, int c) { return i * CHUNKS + (c ^ swz_key(i)); }
 
 // Per-position fp32 sign-bit masks of the rotation (sigma_p = -1 -> 0x80000000), built
 // once per workgroup in LDS and read as broadcasts right before use.
@@ -232,7 +237,7 @@ __device__ __forceinline__ void stage_tile(Tile &t, const uint16_t *__restrict__
         const uint16_t *base = x + r0 * C + c0;
         for (int j = w; j < TILE * CHUNKS / 64; j += waves) {
             const int q = j * 64 + lane;               // slot filled by this lane
-            const int i = q >> 4, c = (q & 15) ^ (i & 15);
+            const int i = q >> 4, c = (q & 15) ^ swz_key(i);
             __builtin_amdgcn_global_load_lds(base + (int64_t)i * C + 8 * c,
                                              LDS_PTR(&t.chunk[j * 64]), 16, 0, 0);
         }
@@ -257,12 +262,12 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v)
 constexpr int HALF = TILE / 2;
 
 // Row segment i, half h of the tile -> r[k] = sigma_p * x_p, p = 64h + k (exact BF16 decode,
-// sign folded in).  Chunk c of row i sits at byte (i*256 + 16*(c ^ (i&15))) = base_i ^ (c<<4).
+// sign folded in).  Chunk c of row i sits at byte i*256 + 16*(c ^ S(i)) = base_i ^ (c << 4).
 __device__ __forceinline__ void read_row_half(const Tile &t, const SignTable &st, int i, int h,
                                               float r[HALF])
 {
     const char *t8 = reinterpret_cast<const char *>(t.chunk);
-    const uint32_t base = opaque((uint32_t)(i * 256 + 16 * (i & 15)) ^ (uint32_t)(h << 7));
+    const uint32_t base = opaque((uint32_t)(i * 256 + 16 * swz_key(i)) ^ (uint32_t)(h << 7));
     const uint4 *mrow = st.mr[h];
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
@@ -280,13 +285,13 @@ __device__ __forceinline__ void read_row_half(const Tile &t, const SignTable &st
 }
 
 // Column segment j, half h -> r[k] = sigma_p * x_p, p = 64h + k.  Element (i, j) sits at
-// byte i*256 + 16*((j>>3) ^ (i&15)) + 2*(j&7): for i = 64h + 16q + s that is
-// off(s) + 16384h + 4096q.
+// byte i*256 + 16*((j>>3) ^ S(i)) + 2*(j&7): for i = 64h + 16q + s, S(i) = s ^ 8h, so that
+// is off(s) + 16384h + 4096q with the lane's 8h folded into its column chunk.
 __device__ __forceinline__ void read_col_half(const Tile &t, const SignTable &st, int j, int h,
                                               float r[HALF])
 {
     const char *t8 = reinterpret_cast<const char *>(t.chunk) + 16384 * h;
-    const uint32_t jc = opaque((uint32_t)(16 * (j >> 3))), je = 2 * (j & 7);
+    const uint32_t jc = opaque((uint32_t)(16 * ((j >> 3) ^ (h << 3)))), je = 2 * (j & 7);
 #pragma unroll
     for (int s16 = 0; s16 < 16; ++s16) {
         const uint32_t off = (jc ^ (uint32_t)(16 * s16)) + (uint32_t)(256 * s16) + je;
