@@ -308,7 +308,9 @@ __device__ __forceinline__ void read_col_half(const Tile &t, const SignTable &st
 // Value held by the other lane of the pair (DPP quad_perm [1,0,3,2]).
 __device__ __forceinline__ float pair_swap(float v)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    // every lane reads a lane of its own quad, so no lane keeps its old value: mov_dpp
+    // leaves the destination's old contents undefined and needs no copy to seed them
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 
 // r <- H r over the pair: unnormalised Sylvester Walsh-Hadamard transform, butterfly spans
@@ -331,6 +333,53 @@ __device__ __forceinline__ void fwht_pair(float r[HALF], int h)
     const float m = h ? -1.0f : 1.0f;
 #pragma unroll
     for (int i = 0; i < HALF; ++i) r[i] = __builtin_fmaf(r[i], m, pair_swap(r[i]));
+}
+
+// Max |(H r)_p| over the pair's 128 outputs, for the amax pass, which needs |r| only.  The
+// high half computes own - partner = b - a in the span-64 stage instead of a - b: that is
+// -(a - b) (an exact zero may carry the other sign), so every |r| is unchanged, and the
+// partner's value enters as the multiplicand, where the DPP swap and the fused
+// multiply-add are one v_fmac_f32_dpp.  The compiler does not fold a DPP move into
+// v_fmac_f32, so the last stage and the running maximum are written out, eight values per
+// statement; the s_nop gives the two wait states that a DPP read of a register written by
+// the previous VALU instruction needs (inside a statement every DPP read is of a register
+// no earlier instruction of the statement wrote).  Returns this lane's maximum; the pair's
+// two lanes hold the maxima of the a + b and of the a - b outputs.
+__device__ __forceinline__ float fwht_pair_amax(float r[HALF], int h)
+{
+#pragma unroll
+    for (int s = 1; s < HALF; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            if ((i & s) == 0) {
+                const float u = r[i], v = r[i + s];
+                r[i] = u + v;
+                r[i + s] = u - v;
+            }
+        }
+    }
+    const float m = h ? -1.0f : 1.0f;
+    float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < HALF; i += 8) {
+        __asm__("s_nop 1\n\t"
+                "v_fmac_f32_dpp %0, %0, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %1, %1, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %2, %2, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %3, %3, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %4, %4, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %5, %5, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %6, %6, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %7, %7, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                "v_max3_f32 %8, %8, |%0|, |%1|\n\t"
+                "v_max3_f32 %9, %9, |%2|, |%3|\n\t"
+                "v_max3_f32 %8, %8, |%4|, |%5|\n\t"
+                "v_max3_f32 %9, %9, |%6|, |%7|"
+                : "+v"(r[i]), "+v"(r[i + 1]), "+v"(r[i + 2]), "+v"(r[i + 3]), "+v"(r[i + 4]),
+                  "+v"(r[i + 5]), "+v"(r[i + 6]), "+v"(r[i + 7]), "+v"(m0), "+v"(m1)
+                : "v"(m));
+    }
+    return fmaxf(m0, m1);
 }
 
 // Balanced pairwise sum of 2^k values in natural order, in place.
@@ -434,7 +483,7 @@ __device__ __forceinline__ float tile_amax(const Tile &tile, const SignTable &st
     float r[HALF];
     if (ro.lay == 0) read_row_half(tile, st, ro.g, ro.h, r);
     else read_col_half(tile, st, ro.g, ro.h, r);
-    if (ROT) fwht_pair(r, ro.h);
+    if (ROT) return fwht_pair_amax(r, ro.h);
     float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
     for (int p = 0; p < HALF; p += 4) {
