@@ -355,7 +355,8 @@ static void rtn_block(const float *r, uint8_t s, float g, int mag_cap, uint8_t *
         float y = r[i] * rcp;
         int mag = oracle_e2m1_rtn_mag(fabsf(y));
         if (mag > mag_cap) mag = mag_cap;
-        int neg = signbit(r[i]) ? 1 : 0;
+        /* sign bit set iff r < 0: an exact zero, of either sign, encodes as +0 */
+        int neg = r[i] < 0.0f;
         codes[i] = (uint8_t)(mag | (neg << 3));
         float qv = den * E2M1_V[mag];
         q[i] = neg ? -qv : qv;
@@ -519,7 +520,7 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                                                      (E2M1_V[lo + 1] - E2M1_V[lo]);
                         em = ulp_dist(a, (float)ab);
                     }
-                    code = (uint8_t)(mag | ((signbit(rb[i]) ? 1 : 0) << 3));
+                    code = (uint8_t)(mag | ((rb[i] < 0.0f) << 3));
                 }
                 if (e % 2 == 0) codes[e / 2] = code;
                 else codes[e / 2] |= (uint8_t)(code << 4);

@@ -85,6 +85,37 @@ def test_zero_and_empty():
         assert t.codes.numel() == 0 and float(t.tensor_scale.cpu()[0]) == 0.0
 
 
+def _zero_heavy(seed=5):
+    """512 x 512 rows built to produce exact zeros and cancellations inside the rotation:
+    small integers, constant rows, sparse rows filled with +-0, groups whose first half is
+    zero, equal and opposite pairs, all -0 rows, and +-c patterns; N(0,1) rows in between."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((512, 512))
+    x[0:64] = rng.integers(-2, 3, (64, 512))
+    x[64:128] = rng.choice([-1.0, -0.5, 0.5, 1.0, 2.0], (64, 1))
+    sparse = rng.random((64, 512)) < 0.05
+    x[128:192] = np.where(sparse, rng.standard_normal((64, 512)),
+                          rng.choice([0.0, -0.0], (64, 512)))
+    x[192:256].reshape(64, 4, 128)[:, :, :64] = rng.choice([0.0, -0.0], (64, 4, 64))
+    pairs = rng.standard_normal((64, 256))
+    x[256:320, 0::2] = pairs
+    x[256:320, 1::2] = pairs * rng.choice([-1.0, 1.0], (64, 256))
+    x[384:448] = -0.0
+    x[448:512] = rng.choice([-1.5, 1.5], (64, 512)) * rng.integers(1, 3, (64, 1))
+    return workloads.to_bf16(x)
+
+
+@pytest.mark.parametrize("mode,rht", [("eden", True), ("rtn", True), ("rtn", False),
+                                      ("sr", True), ("sr", False), ("fp46", True),
+                                      ("fp46", False)])
+def test_exact_zeros_and_cancellations(mode, rht):
+    print(f"case: zero-heavy 512x512 mode={mode} rht={rht}", flush=True)
+    x = _zero_heavy()
+    assert (workloads.bf16_bits(x) == 0x8000).any()
+    check_full(mode, x, ("row", "col"), seed=4, rht=rht, rht_seed=6,
+               what=f"zero-heavy {mode} rht={rht}")
+
+
 def test_extreme_magnitudes():
     """Tiny values (subnormal products, scales below 2^-6 and zero scales) and large ones."""
     rng = np.random.default_rng(0)

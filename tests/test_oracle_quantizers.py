@@ -89,6 +89,37 @@ def test_eden_ratio_is_one_on_grid(oracle_mod):
         np.testing.assert_array_equal(back, x.astype(np.float32))
 
 
+def test_zero_encoding(oracle_mod):
+    """A code's sign bit is set iff r < 0: exact zeros of either sign encode as 0x0, while a
+    negative r that rounds to magnitude 0 keeps the sign (0x8).  Rotation off, so r = x;
+    the block's max 6 makes its scale 448 and den = 448 * 6/2688 = 1, so y = r."""
+    o = oracle_mod
+    row = np.zeros(128, dtype=np.float32)
+    row[:6] = [6.0, 0.0, -0.0, -0.125, 0.125, -3.0]
+    x = torch.from_numpy(np.tile(row, (4, 1))).to(torch.bfloat16)
+    xb = _bits(x)
+    assert (xb[:, 2] == 0x8000).all()                  # the input really holds -0
+    for mode in ("rtn", "sr", "fp46"):
+        q = o.quantize(mode, xb, axis=0, seed=5, rht=False)
+        c = o.unpack_codes(q.codes)
+        assert (c[:, 1] == 0).all() and (c[:, 2] == 0).all(), mode
+        assert (c[:, 6:] == 0).all(), mode
+        assert (c[:, 3] & 8).all() and (c[:, 5] & 8).all() and not (c[:, 4] & 8).any(), mode
+        if mode == "rtn":
+            np.testing.assert_array_equal(c[:, 3], 8)
+            np.testing.assert_array_equal(c[:, 4], 0)
+    # with the rotation: the on-grid construction's r = c v holds exact zeros
+    rht_seed = 11
+    v, cst = _on_grid_input(rht_seed)
+    sig = o.signs(rht_seed).astype(np.float64)
+    xr = torch.from_numpy((sig * ((cst * v) @ H.T) / 128.0).astype(np.float32)).to(
+        torch.bfloat16)
+    for mode in ("rtn", "eden", "fp46"):
+        q = o.quantize(mode, _bits(xr), axis=0, seed=3, rht=True, rht_seed=rht_seed)
+        c = o.unpack_codes(q.codes)
+        assert (c[v == 0] == 0).all(), mode
+
+
 def test_zero_tensor(oracle_mod):
     x = torch.zeros(256, 256, dtype=torch.bfloat16)
     for mode in ("rtn", "sr", "eden", "fp46"):

@@ -181,7 +181,9 @@ __device__ __forceinline__ int swz_key(int i) { return (i & 15) ^ (((i >> 6) & 1
 __device__ __forceinline__ int swz(int i, int c) { return i * CHUNKS + (c ^ swz_key(i)); }
 
 // Per-position fp32 sign-bit masks of the rotation (sigma_p = -1 -> 0x80000000), built
-// once per workgroup in LDS and read as broadcasts right before use.
+// once per workgroup in LDS and read as broadcasts right before use.  With the rotation,
+// positions 64..127 (the high half of a group) carry the complement, so that half is read
+// as -sigma*x; without it every mask is 0.
 //   mr[h][k]  masks of positions 64h + 4k .. 64h + 4k + 3 (row order); the padding word
 //             puts the two halves in different LDS banks.
 //   mc[s][h]  masks of positions 64h + 16q + s for q = 0..3 (column reader order).
@@ -202,6 +204,9 @@ __device__ __forceinline__ void build_sign_table(SignTable &st, uint64_t rht_see
             mask = ((word >> (t & 31)) & 1u) << 31;
         }
         const int h = t >> 6, pl = t & 63;
+        // with the rotation, the high half of every group is read negated (fwht_pair_blocks
+        // undoes it in its last stage)
+        if (rot && h) mask ^= 0x80000000u;
         reinterpret_cast<uint32_t *>(&st.mr[h][0])[pl] = mask;
         reinterpret_cast<uint32_t *>(&st.mc[pl & 15][h])[pl >> 4] = mask;
     }
@@ -313,11 +318,22 @@ __device__ __forceinline__ float pair_swap(float v)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 
-// r <- H r over the pair: unnormalised Sylvester Walsh-Hadamard transform, butterfly spans
-// 1, 2, ..., 32 inside each half, then span 64 across the pair: the low half gets
-// a + b and the high half a - b, each rounded once (fma with a +-1 multiplier is exact up
-// to that one rounding).  The random signs are already folded in by the readers.
-__device__ __forceinline__ void fwht_pair(float r[HALF], int h)
+// r <- H r over the pair, and the 1x16 block maxima of |r|.  Unnormalised Sylvester
+// Walsh-Hadamard transform: butterfly spans 1, 2, ..., 32 inside each half, then span 64
+// across the pair.  The readers fold the random signs in and read the high half negated,
+// so before the last stage the low lane holds a (the transform of its half) and the high
+// lane holds b' = -b.  The last stage is own + m * partner with m = -1 in the low lane
+// (a - b' = a + b) and m = +1 in the high lane (b' + a = a - b): one v_fmac_f32_dpp, the
+// DPP swap reading the partner's register.  Only the sign of an exact zero can differ from
+// the direct a +- b (a zero's sign does not survive into any nonzero sum, and every
+// consumer treats a zero of either sign alike: codes encode it as +0), so every value is
+// the contract's.
+//
+// The compiler does not fold a DPP move into v_fmac_f32, so the last stage and the block
+// maximum are written out, one 16-value block per statement.  The s_nop gives the two wait
+// states a DPP read of a register written by the previous VALU instruction needs; inside
+// the statement every DPP read is of a register no earlier instruction of it wrote.
+__device__ __forceinline__ void fwht_pair_blocks(float r[HALF], int h, float bmax[4])
 {
 #pragma unroll
     for (int s = 1; s < HALF; s <<= 1) {
@@ -330,56 +346,31 @@ __device__ __forceinline__ void fwht_pair(float r[HALF], int h)
             }
         }
     }
-    const float m = h ? -1.0f : 1.0f;
+    const float m = h ? 1.0f : -1.0f;
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) r[i] = __builtin_fmaf(r[i], m, pair_swap(r[i]));
-}
-
-// Max |(H r)_p| over the pair's 128 outputs, for the amax pass, which needs |r| only.  The
-// high half computes own - partner = b - a in the span-64 stage instead of a - b: that is
-// -(a - b) (an exact zero may carry the other sign), so every |r| is unchanged, and the
-// partner's value enters as the multiplicand, where the DPP swap and the fused
-// multiply-add are one v_fmac_f32_dpp.  The compiler does not fold a DPP move into
-// v_fmac_f32, so the last stage and the running maximum are written out, eight values per
-// statement; the s_nop gives the two wait states that a DPP read of a register written by
-// the previous VALU instruction needs (inside a statement every DPP read is of a register
-// no earlier instruction of the statement wrote).  Returns this lane's maximum; the pair's
-// two lanes hold the maxima of the a + b and of the a - b outputs.
-__device__ __forceinline__ float fwht_pair_amax(float r[HALF], int h)
-{
-#pragma unroll
-    for (int s = 1; s < HALF; s <<= 1) {
-#pragma unroll
-        for (int i = 0; i < HALF; ++i) {
-            if ((i & s) == 0) {
-                const float u = r[i], v = r[i + s];
-                r[i] = u + v;
-                r[i + s] = u - v;
-            }
-        }
-    }
-    const float m = h ? -1.0f : 1.0f;
-    float m0 = 0.0f, m1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < HALF; i += 8) {
+    for (int b = 0; b < 4; ++b) {
+        float *q = r + 16 * b;
+        float mx;
+#define FMAC_DPP(k) "v_fmac_f32_dpp %" #k ", %" #k ", %17 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
         __asm__("s_nop 1\n\t"
-                "v_fmac_f32_dpp %0, %0, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                "v_fmac_f32_dpp %1, %1, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                "v_fmac_f32_dpp %2, %2, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                "v_fmac_f32_dpp %3, %3, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                "v_fmac_f32_dpp %4, %4, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                "v_fmac_f32_dpp %5, %5, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                "v_fmac_f32_dpp %6, %6, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                "v_fmac_f32_dpp %7, %7, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                "v_max3_f32 %8, %8, |%0|, |%1|\n\t"
-                "v_max3_f32 %9, %9, |%2|, |%3|\n\t"
-                "v_max3_f32 %8, %8, |%4|, |%5|\n\t"
-                "v_max3_f32 %9, %9, |%6|, |%7|"
-                : "+v"(r[i]), "+v"(r[i + 1]), "+v"(r[i + 2]), "+v"(r[i + 3]), "+v"(r[i + 4]),
-                  "+v"(r[i + 5]), "+v"(r[i + 6]), "+v"(r[i + 7]), "+v"(m0), "+v"(m1)
+                FMAC_DPP(0) FMAC_DPP(1) FMAC_DPP(2) FMAC_DPP(3) FMAC_DPP(4) FMAC_DPP(5)
+                FMAC_DPP(6) FMAC_DPP(7) FMAC_DPP(8) FMAC_DPP(9) FMAC_DPP(10) FMAC_DPP(11)
+                FMAC_DPP(12) FMAC_DPP(13) FMAC_DPP(14) FMAC_DPP(15)
+                "v_max3_f32 %16, |%0|, |%1|, |%2|\n\t"
+                "v_max3_f32 %16, %16, |%3|, |%4|\n\t"
+                "v_max3_f32 %16, %16, |%5|, |%6|\n\t"
+                "v_max3_f32 %16, %16, |%7|, |%8|\n\t"
+                "v_max3_f32 %16, %16, |%9|, |%10|\n\t"
+                "v_max3_f32 %16, %16, |%11|, |%12|\n\t"
+                "v_max3_f32 %16, %16, |%13|, |%14|\n\t"
+                "v_max_f32 %16, %16, |%15|"
+                : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]),
+                  "+v"(q[6]), "+v"(q[7]), "+v"(q[8]), "+v"(q[9]), "+v"(q[10]), "+v"(q[11]),
+                  "+v"(q[12]), "+v"(q[13]), "+v"(q[14]), "+v"(q[15]), "=&v"(mx)
                 : "v"(m));
+#undef FMAC_DPP
+        bmax[b] = mx;
     }
-    return fmaxf(m0, m1);
 }
 
 // Balanced pairwise sum of 2^k values in natural order, in place.
@@ -483,7 +474,11 @@ __device__ __forceinline__ float tile_amax(const Tile &tile, const SignTable &st
     float r[HALF];
     if (ro.lay == 0) read_row_half(tile, st, ro.g, ro.h, r);
     else read_col_half(tile, st, ro.g, ro.h, r);
-    if (ROT) return fwht_pair_amax(r, ro.h);
+    if (ROT) {
+        float bm[4];
+        fwht_pair_blocks(r, ro.h, bm);
+        return fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
+    }
     float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
     for (int p = 0; p < HALF; p += 4) {
@@ -545,19 +540,23 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
 
 // Round-to-nearest of one 1x16 block rb[0..15] with scale code s (table entry e):
 // packed codes into w0 (elements 0..7) and w1 (8..15); a zero scale gives all-zero codes.
+// y = fma(r, rcp, +0) is r * rcp rounded once, except that an exact zero becomes +0, so
+// the code's sign bit is set iff r < 0.
+__device__ __forceinline__ float scaled(float r, float rcp) { return __builtin_fmaf(r, rcp, 0.0f); }
+
 __device__ __forceinline__ void rtn_block(const float *rb, uint32_t s, const float4 e,
                                           uint32_t &w0, uint32_t &w1)
 {
     const float rcp = e.z;
     uint32_t a = 0u, b = 0u;
-    a = CVT_FP4(a, rb[0] * rcp, rb[1] * rcp, 0);
-    a = CVT_FP4(a, rb[2] * rcp, rb[3] * rcp, 1);
-    a = CVT_FP4(a, rb[4] * rcp, rb[5] * rcp, 2);
-    a = CVT_FP4(a, rb[6] * rcp, rb[7] * rcp, 3);
-    b = CVT_FP4(b, rb[8] * rcp, rb[9] * rcp, 0);
-    b = CVT_FP4(b, rb[10] * rcp, rb[11] * rcp, 1);
-    b = CVT_FP4(b, rb[12] * rcp, rb[13] * rcp, 2);
-    b = CVT_FP4(b, rb[14] * rcp, rb[15] * rcp, 3);
+    a = CVT_FP4(a, scaled(rb[0], rcp), scaled(rb[1], rcp), 0);
+    a = CVT_FP4(a, scaled(rb[2], rcp), scaled(rb[3], rcp), 1);
+    a = CVT_FP4(a, scaled(rb[4], rcp), scaled(rb[5], rcp), 2);
+    a = CVT_FP4(a, scaled(rb[6], rcp), scaled(rb[7], rcp), 3);
+    b = CVT_FP4(b, scaled(rb[8], rcp), scaled(rb[9], rcp), 0);
+    b = CVT_FP4(b, scaled(rb[10], rcp), scaled(rb[11], rcp), 1);
+    b = CVT_FP4(b, scaled(rb[12], rcp), scaled(rb[13], rcp), 2);
+    b = CVT_FP4(b, scaled(rb[14], rcp), scaled(rb[15], rcp), 3);
     w0 = s ? a : 0u;
     w1 = s ? b : 0u;
 }
@@ -589,11 +588,13 @@ __device__ __forceinline__ uint32_t cap_mag6(uint32_t w)
 }
 
 // Quantize this lane's half group: blocks 4h..4h+3 of the group in r[0..63] (rotated when
-// the mode rotates); nbl = number of those blocks inside the vector.  vec = vector index in
+// the mode rotates), their maxima of |r| in bmax; nbl = number of those blocks inside the
+// vector.  vec = vector index in
 // its layout, n = vector length, gi = group index within the vector.  Writes this half's
 // 32 code bytes and 4 scale bytes (codes/scales point at the group's first byte).
 template <int MODE>
-__device__ __forceinline__ void quantize_half(float r[HALF], int h, int nbl, float g,
+__device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4], int h,
+                                              int nbl, float g,
                                               const ScaleTable &tb, float rcp6g, float rcp4g,
                                               uint64_t seed, uint32_t axis, int64_t vec,
                                               int64_t n, int64_t gi,
@@ -612,7 +613,7 @@ __device__ __forceinline__ void quantize_half(float r[HALF], int h, int nbl, flo
             bp[b] = 0.0f; bq[b] = 0.0f; sv[b] = 0.0f;
             if (MODE == MODE_EDEN || b < nbl) {
                 const float *rb = r + 16 * b;
-                const uint32_t s = e4m3_rne_hw(block_max(rb) * rcp6g);
+                const uint32_t s = e4m3_rne_hw(bmax[b] * rcp6g);
                 const float4 e = tb.e[s];
                 rtn_block(rb, s, e, cw[2 * b], cw[2 * b + 1]);
                 sc[b] = s;
@@ -659,7 +660,7 @@ __device__ __forceinline__ void quantize_half(float r[HALF], int h, int nbl, flo
         for (int b = 0; b < 4; ++b) {
             if (b < nbl) {
                 const float *rb = r + 16 * b;
-                const uint32_t s = e4m3_up(block_max(rb) * rcp6g);
+                const uint32_t s = e4m3_up(bmax[b] * rcp6g);
                 const float rcp = tb.e[s].z;
                 sc[b] = s;
                 if (s) {
@@ -673,7 +674,8 @@ __device__ __forceinline__ void quantize_half(float r[HALF], int h, int nbl, flo
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
                             const int p = 16 * b + 4 * qd + k;
-                            const float a = fminf(fabsf(rb[4 * qd + k] * rcp), 6.0f);
+                            const float y = scaled(rb[4 * qd + k], rcp);
+                            const float a = fminf(fabsf(y), 6.0f);
                             uint32_t mag;
                             if (a >= 6.0f) {
                                 mag = 7u;
@@ -686,7 +688,7 @@ __device__ __forceinline__ void quantize_half(float r[HALF], int h, int nbl, flo
                                 const uint32_t u = w.w[k] >> 8;
                                 mag = lo + (uint32_t)((float)u < frac * 16777216.0f);
                             }
-                            const uint32_t sgn = __float_as_uint(rb[4 * qd + k]) >> 31;
+                            const uint32_t sgn = __float_as_uint(y) >> 31;   // r < 0
                             cw[p >> 3] |= (mag | (sgn << 3)) << (4 * (p & 7));
                         }
                     }
@@ -698,7 +700,7 @@ __device__ __forceinline__ void quantize_half(float r[HALF], int h, int nbl, flo
         for (int b = 0; b < 4; ++b) {
             if (b < nbl) {
                 const float *rb = r + 16 * b;
-                const float m = block_max(rb);
+                const float m = bmax[b];
                 const uint32_t sA = e4m3_rne_hw(m * rcp6g), sB = e4m3_rne_hw(m * rcp4g);
                 const float4 eA = tb.e[sA], eB = tb.e[sB];
                 uint32_t a0, a1, b0, b1;
@@ -760,11 +762,17 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
     float r[HALF];
     if (ro.lay == 0) read_row_half(tile, st, ro.g, ro.h, r);
     else read_col_half(tile, st, ro.g, ro.h, r);
-    if (ROT) fwht_pair(r, ro.h);
+    float bm[4];
+    if (ROT) {
+        fwht_pair_blocks(r, ro.h, bm);
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bm[b] = block_max(r + 16 * b);
+    }
     const int64_t left = n - start;
     const int nb = left >= TILE ? 8 : (int)(left >> 4);
     const int nbl = nb - 4 * ro.h < 0 ? 0 : (nb - 4 * ro.h > 4 ? 4 : nb - 4 * ro.h);
-    quantize_half<MODE>(r, ro.h, nbl, g, tb, rcp6g, rcp4g, a.seed, (uint32_t)ro.lay, vec, n,
+    quantize_half<MODE>(r, bm, ro.h, nbl, g, tb, rcp6g, rcp4g, a.seed, (uint32_t)ro.lay, vec, n,
                         start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
                         o.scales + vec * (n >> 4) + (start >> 4));
 }
