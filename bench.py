@@ -9,11 +9,24 @@ resident in HBM.  Throughput counts the algorithmic bytes of the step: the BF16 
 (2 B/element) plus, per layout, 0.5 B of codes + 1/16 B of scales per element and 4 B of
 tensor scale.  The second read of X by phase 2 is not counted.
 
+The dominant kernel is phase 2 (k_quant).  Inside the timed region one pair of HIP events
+brackets each phase-2 launch (a marker placed elsewhere in the step, or two markers in a
+row, adds a dispatch gap of its own).  Phase 2 is bound by VALU issue, so its roofline is
+the ALU one: per element and layout the method performs 14 operations -- the sign flip,
+the 7 butterfly stages, the 1x16 |r| maximum, the scaling, the rounding to E2M1, the grid
+value of the code and the two EDEN multiply-adds -- against a peak of one VALU operation
+per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 Top/s (packed FP32
+instructions are not used).  The HBM view of the same kernel is reported beside it, and
+the HBM bytes it moves come from the committed rocprofv3 counter summary while the kernel
+source is unchanged since those counters were taken.
+
 Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -21,8 +34,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12     # 39.32: one op per lane per clock
+QUANT_OPS_PER_ELEM_LAYOUT = 14                   # MS-EDEN phase 2, see the docstring
 ROWS, COLS = 16384, 8192
 METRIC = "MS-EDEN NVFP4 quantize GB/s & % HBM peak, 16384×8192 bf16; MSE vs SR"
+PMC_PROFILE = os.path.join(ROOT, "profiles", "k_quant_eden_16384x8192_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "unbiased_nvfp4_gradient_amd", "csrc", "nvfp4_kernels.hip"),
+                  os.path.join(ROOT, "unbiased_nvfp4_gradient_amd", "build.py")]
 
 
 def alg_bytes(rows, cols, layouts=2):
@@ -30,11 +48,41 @@ def alg_bytes(rows, cols, layouts=2):
     return 2 * n + layouts * (n // 2 + n // 16 + 4)
 
 
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per k_quant launch from the committed counter summary: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for a device
+    copy of known size.  None when the summary is missing or was taken on other sources."""
+    try:
+        with open(PMC_PROFILE, encoding="utf-8") as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    fetch = d["fetch_kib"] * d["copy_bytes"] / d["copy_fetch_kib"]
+    write = d["write_kib"] * d["copy_bytes"] / d["copy_write_kib"]
+    return int(round(fetch + write))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU leaves its idle clocks over the first ~50 steps: the default warm-up covers
+    # that, so the timed steps run at the steady-state clock
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mse", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
@@ -63,35 +111,38 @@ def main():
     rht_seed = 1
 
     def step(seed, evs=None):
-        if evs:
-            evs[0].record(stream)
         nv.nvfp4_amax(x, True, rht_seed, ("row", "col"), amax=amax, stream=stream)
         if evs:
-            evs[1].record(stream)
+            evs[0].record(stream)
         nv.nvfp4_quantize_amax("eden", x, amax, seed=seed, rht=True, rht_seed=rht_seed,
                                layouts=("row", "col"), out=out, stream=stream)
         if evs:
-            evs[2].record(stream)
+            evs[1].record(stream)
 
     for k in range(args.warmup):
         step(1000 + k)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    Event = torch.cuda.Event
+    events = [[Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    start = Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for k in range(args.steps):
         step(1 + k, events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    amax_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    quant_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    step_ms_ev = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    step_ms_ev = start.elapsed_time(events[-1][1]) / args.steps
     B = alg_bytes(ROWS, COLS)
     value = B / (ms_step * 1e-3) / 1e9
-    achieved = B / (quant_ms * 1e-3) / 1e9
+    n = ROWS * COLS
+    ops = QUANT_OPS_PER_ELEM_LAYOUT * 2 * n
+    tops = ops / (quant_ms * 1e-3) / 1e12
+    quant_gbs = B / (quant_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -115,16 +166,20 @@ def main():
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_step": B,
-        "phase_ms": {"amax": round(amax_ms, 4), "quantize": round(quant_ms, 4),
+        "phase_ms": {"quantize_events": round(quant_ms, 4),
                      "step_events": round(step_ms_ev, 4)},
         "roofline": {
             "kernel": "k_quant (phase 2: rotate, quantize, EDEN, scale SR, pack both layouts)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "bound": "alu",
+            "achieved": round(tops, 2),
+            "peak": round(VALU_PEAK_TOPS, 2),
+            "unit": "Top/s (VALU lane operations; algorithmic, 14 per element and layout)",
+            "frac": round(tops / VALU_PEAK_TOPS, 4),
+            "traffic": measured_traffic(),
+            "ops_per_launch": ops,
+            "hbm_view": {"achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": B},
         },
     }
 
@@ -140,7 +195,7 @@ def main():
         result["copy_probe_bytes"] = {"read": src.numel(), "written": dst.numel()}
 
     if not args.no_mse:
-        result["mse_vs_sr"] = mse_vs_sr(nv, workloads, dev)
+        result["mse_vs_sr"] = mse_vs_sr(nv, workloads, dev, x)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_cpu, B)
@@ -176,44 +231,76 @@ def gemm_check(nv, workloads, dev, a, stream, reps=5):
             "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
 
 
-def mse_vs_sr(nv, workloads, dev):
-    """Relative MSE of MS-EDEN and of SR on the 256 x 1024 N(0,1) tensor (seed 1)."""
+def rel_mse(nv, xd, mode, layout):
+    """Relative squared error sum((dequant - x)^2) / sum(x^2) of one layout, seed 1."""
     import torch
 
-    x = workloads.c1()
-    xd = x.to(dev)
-    xf = x.float().to(dev)
-    res = {}
-    for mode in ("rtn", "sr", "eden"):
-        if mode == "eden":
-            q = nv.eden_quantize(xd, 1, 1, layouts=("row",)).row
-            back = nv.dequantize(q, rht=True, rht_seed=1)
-        elif mode == "sr":
-            back = nv.dequantize(nv.sr_quantize(xd, 1, layouts=("row",)).row)
-        else:
-            back = nv.dequantize(nv.rtn_quantize(xd, layouts=("row",)).row)
-        res[mode] = float(((back - xf) ** 2).sum() / (xf ** 2).sum())
+    lay = (layout,)
+    if mode == "eden":
+        q = nv.eden_quantize(xd, 1, 1, layouts=lay)
+        rot = True
+    elif mode == "sr":
+        q = nv.sr_quantize(xd, 1, layouts=lay)
+        rot = False
+    else:
+        q = nv.rtn_quantize(xd, layouts=lay)
+        rot = False
+    t = q.row if layout == "row" else q.col
+    back = nv.dequantize(t, rht=rot, rht_seed=1)
+    xf = xd.float() if layout == "row" else xd.float().t()
+    err = float(((back.double() - xf.double()) ** 2).sum() / (xf.double() ** 2).sum())
+    del back, q, t
     torch.cuda.synchronize()
-    return {"workload": "256x1024 N(0,1) bf16 (seed 0), row layout, Philox seed 1",
-            "rel_mse": {k: round(v, 6) for k, v in res.items()},
-            "eden_over_sr": round(res["eden"] / res["sr"], 4)}
+    return err
+
+
+def mse_vs_sr(nv, workloads, dev, x_c4):
+    """Relative MSE of RTN, SR and MS-EDEN (Philox seed 1) on the 256 x 1024 N(0,1) tensor
+    (the primary figure, row layout) and, for MS-EDEN over SR, on the three larger
+    configurations in both layouts."""
+    import torch
+
+    x = workloads.c1().to(dev)
+    res = {m: rel_mse(nv, x, m, "row") for m in ("rtn", "sr", "eden")}
+    out = {"workload": "256x1024 N(0,1) bf16 (seed 0), row layout, Philox seed 1",
+           "rel_mse": {k: round(v, 6) for k, v in res.items()},
+           "eden_over_sr": round(res["eden"] / res["sr"], 4), "other_configs": {}}
+    for name, gen in (("4096x4096 t3*0.02 + outliers", workloads.c2),
+                      ("16384x2048 row magnitudes 1e-6..10", workloads.c3),
+                      ("16384x8192 N(0,1) x column lognormal", None)):
+        xd = gen().to(dev) if gen is not None else x_c4
+        ratios = {}
+        for layout in ("row", "col"):
+            e, s = rel_mse(nv, xd, "eden", layout), rel_mse(nv, xd, "sr", layout)
+            ratios[layout] = {"eden": round(e, 6), "sr": round(s, 6),
+                              "eden_over_sr": round(e / s, 4)}
+        out["other_configs"][name] = ratios
+        del xd
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(x_cpu, B):
-    """The CPU oracle on the same workload (all host cores): amax + both layouts."""
+    """The CPU oracle on the same workload (all host cores): amax + both layouts, three
+    passes, median."""
+    import numpy as np
+
     import oracle
     import workloads
 
     xb = workloads.bf16_bits(x_cpu)
     oracle.build()
     threads = oracle.get_threads()
-    t0 = time.perf_counter()
-    for axis in (0, 1):
-        oracle.quantize("eden", xb, axis=axis, seed=1, rht_seed=1, margins=False)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for axis in (0, 1):
+            oracle.quantize("eden", xb, axis=axis, seed=1, rht_seed=1, margins=False)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     return {"value": round(B / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "the full 16384x8192 workload, both layouts, one pass (amax + quantize "
-                      "per layout), wall time %.2f s" % dt}
+            "sample": "the full 16384x8192 workload, both layouts (amax + quantize per "
+                      "layout), median of 3 passes: %.2f s" % dt}
 
 
 if __name__ == "__main__":
