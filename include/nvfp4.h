@@ -39,8 +39,9 @@
  *               for MS-EDEN) and of 16 otherwise.
  *   Output.     nvfp4_tensor for a layout with vecs vectors of length n:
  *                 codes  [vecs][n/2] bytes, byte j = code(2j) | code(2j+1) << 4, where a
- *                        code is sign << 3 | magnitude index into {0,.5,1,1.5,2,3,4,6};
- *                        16-byte aligned;
+ *                        code is sign << 3 | magnitude index into {0,.5,1,1.5,2,3,4,6},
+ *                        the sign bit set iff the rotated value is negative (an exact
+ *                        zero encodes as 0); 16-byte aligned;
  *                 scales [vecs][n/16] OCP E4M3FN bytes (one per 1x16 block), 8-byte aligned;
  *                 tensor_scale: one float g, 4-byte aligned.
  *               A value decodes as sign * (E4M3(scale) * g) * magnitude; with the rotation

@@ -7,6 +7,10 @@ too: every code of a block whose scale rounding is within the band, and (MS-EDEN
 scale of a group in which a code mismatch was excused, since the EDEN ratio then moves.
 Excused mismatches must stay at or below 1e-5 of each output kind; unexcused ones at 0.
 The tensor scale is an exact function of the exact amax and must match exactly.
+
+The kernels compute the contract's binary32 steps in the oracle's order, so the tests hold
+them to the stricter bar: no mismatch at all (STRICT).  The band is still computed, so a
+failure report says whether the differing outputs sit on a rounding boundary.
 """
 from dataclasses import dataclass
 
@@ -16,6 +20,7 @@ import oracle
 
 BAND = 2
 EXCUSED_RATE = 1e-5
+STRICT = True
 
 
 @dataclass
@@ -28,6 +33,8 @@ class Report:
     scale_excused: int
 
     def ok(self) -> bool:
+        if STRICT:
+            return self.code_mismatch == 0 and self.scale_mismatch == 0
         return (self.code_mismatch == self.code_excused and
                 self.scale_mismatch == self.scale_excused and
                 self.code_excused <= EXCUSED_RATE * self.codes + 0 and
