@@ -228,23 +228,61 @@ __device__ __forceinline__ void load_tile_sync(Tile &t, const uint16_t *__restri
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
-// Start loading tile (r0, c0) into t.  A full tile goes straight from memory into LDS
-// (global_load_lds_dwordx4: lane L of a wave instruction fills 16-byte slot base + L), so
-// the load runs while the workgroup computes on its other buffer; each lane fetches the
-// chunk whose swizzled slot it fills.  The data is visible after the next __syncthreads
-// (which waits for this wave's outstanding memory operations).  Edge tiles load
-// synchronously.
+// Byte offsets, from a full tile's first element, of the 16-byte chunks one lane moves in
+// the direct global->LDS load (below).  With W waves, round k of wave w fills LDS slots
+// (w + W k) * 64 + lane, i.e. tile row i = i0 + 4 W k with i0 = 4 w + lane / 16 < 32, and
+// chunk (lane mod 16) XOR S(i): the low bits of S(i) are those of i0 in every round, and
+// bit 6 of i (the 8 in S) is set from row 64 on.  So a lane needs two offsets, one for the
+// rounds above row 64 and one for the rest, plus 4 W rows per round.  They fit 32 bits for
+// C <= 2^26 (2 * 31 * C + 240 < 2^32); wider rows take the general path.
+struct DmaLane { uint32_t a, b; };
+
+constexpr int64_t DMA_FAST_MAX_C = int64_t(1) << 26;
+
+template <int W>
+__device__ __forceinline__ DmaLane dma_lane(int64_t C)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i0 = 4 * w + (lane >> 4);
+    const int c = (lane & 15) ^ (i0 & 15);
+    const uint32_t rowb = 2u * (uint32_t)i0 * (uint32_t)C;
+    DmaLane d;
+    d.a = rowb + 16u * (uint32_t)c;
+    d.b = rowb + 16u * (uint32_t)(c ^ 8);
+    return d;
+}
+
+// Start loading tile (r0, c0) into t (W waves take part).  A full tile goes straight from
+// memory into LDS (global_load_lds_dwordx4: lane L of a wave instruction fills 16-byte slot
+// base + L), so the load runs while the workgroup computes on its other buffer; each lane
+// fetches the chunk whose swizzled slot it fills.  The data is visible after the next
+// __syncthreads (which waits for this wave's outstanding memory operations).  Edge tiles
+// load synchronously.
+template <int W>
 __device__ __forceinline__ void stage_tile(Tile &t, const uint16_t *__restrict__ x, int64_t R,
-                                           int64_t C, int64_t r0, int64_t c0)
+                                           int64_t C, int64_t r0, int64_t c0,
+                                           const DmaLane &dl)
 {
     if (r0 + TILE <= R && c0 + TILE <= C) {
-        const int waves = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-        const uint16_t *base = x + r0 * C + c0;
-        for (int j = w; j < TILE * CHUNKS / 64; j += waves) {
-            const int q = j * 64 + lane;               // slot filled by this lane
-            const int i = q >> 4, c = (q & 15) ^ swz_key(i);
-            __builtin_amdgcn_global_load_lds(base + (int64_t)i * C + 8 * c,
-                                             LDS_PTR(&t.chunk[j * 64]), 16, 0, 0);
+        const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        if (C <= DMA_FAST_MAX_C) {
+            const char *base = reinterpret_cast<const char *>(x + r0 * C + c0);
+            const int64_t step = 8 * W * C;                 // bytes of 4 W rows
+#pragma unroll
+            for (int k = 0; k < 32 / W; ++k) {
+                const char *p = base + k * step + (4 * W * k < 64 ? dl.a : dl.b);
+                __builtin_amdgcn_global_load_lds(p, LDS_PTR(&t.chunk[(w + W * k) * 64]), 16, 0,
+                                                 0);
+            }
+        } else {
+            const int lane = threadIdx.x & 63;
+            const uint16_t *base = x + r0 * C + c0;
+            for (int j = w; j < TILE * CHUNKS / 64; j += W) {
+                const int q = j * 64 + lane;               // slot filled by this lane
+                const int i = q >> 4, c = (q & 15) ^ swz_key(i);
+                __builtin_amdgcn_global_load_lds(base + (int64_t)i * C + 8 * c,
+                                                 LDS_PTR(&t.chunk[j * 64]), 16, 0, 0);
+            }
         }
     } else {
         load_tile_sync(t, x, R, C, r0, c0);
@@ -421,6 +459,9 @@ struct QuantArgs {
     int64_t tiles_c, tiles;    // tiles per tile-row, total tiles
 };
 
+// Waves per workgroup: 4 per layout (128 groups x 2 halves = 256 lanes per layout).
+constexpr int waves_for(int lay) { return lay == LAY_BOTH ? 8 : 4; }
+
 // Lane roles: each layout takes 256 lanes (128 groups x 2 halves) of a workgroup.
 struct Role {
     int lay;   // 0 row layout, 1 column layout (wave-uniform)
@@ -500,13 +541,15 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
     __shared__ uint32_t wmax[2];
     const int t = threadIdx.x;
     const Role ro = lane_role<LAY>();
+    constexpr int WAVES = waves_for(LAY);
+    const DmaLane dl = dma_lane<WAVES>(a.C);
     build_sign_table(st, a.rht_seed, ROT);
     if (t < 2) wmax[t] = 0u;
     float local = 0.0f;
     int64_t k = blockIdx.x, r0, c0;
     if (k < a.tiles) {
         tile_origin(a, k, r0, c0);
-        stage_tile(tile0, a.x, a.R, a.C, r0, c0);
+        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
     }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
@@ -514,7 +557,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         int64_t r1 = 0, c1 = 0;
         if (k1 < a.tiles) {
             tile_origin(a, k1, r1, c1);
-            stage_tile(tile1, a.x, a.R, a.C, r1, c1);
+            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl);
         }
         local = fmaxf(local, tile_amax<ROT>(tile0, st, a, ro, r0, c0));
         if (k1 >= a.tiles) break;
@@ -522,7 +565,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         __syncthreads();                                   // tile1 landed; tile0 is free
         if (k2 < a.tiles) {
             tile_origin(a, k2, r0, c0);
-            stage_tile(tile0, a.x, a.R, a.C, r0, c0);
+            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
         }
         local = fmaxf(local, tile_amax<ROT>(tile1, st, a, ro, r1, c1));
         k = k2;
@@ -791,6 +834,8 @@ __global__ void __launch_bounds__(512, MODE == MODE_EDEN ? 4 : 2) k_quant(QuantA
     __shared__ ScaleTable tabs[(LAY == LAY_BOTH) ? 2 : 1];
     const int t = threadIdx.x;
     const Role ro = lane_role<LAY>();
+    constexpr int WAVES = waves_for(LAY);
+    const DmaLane dl = dma_lane<WAVES>(a.C);
     const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
     const float g = __uint_as_float(ro.lay == 0 ? a.amax_bits[0] : a.amax_bits[1]) / D;
     const float rcp6g = clamped_rcp(6.0f * g), rcp4g = clamped_rcp(4.0f * g);
@@ -803,7 +848,7 @@ __global__ void __launch_bounds__(512, MODE == MODE_EDEN ? 4 : 2) k_quant(QuantA
     int64_t k = blockIdx.x, r0, c0;
     if (k < a.tiles) {
         tile_origin(a, a.tiles - 1 - k, r0, c0);
-        stage_tile(tile0, a.x, a.R, a.C, r0, c0);
+        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
     }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
@@ -811,7 +856,7 @@ __global__ void __launch_bounds__(512, MODE == MODE_EDEN ? 4 : 2) k_quant(QuantA
         int64_t r1 = 0, c1 = 0;
         if (k1 < a.tiles) {
             tile_origin(a, a.tiles - 1 - k1, r1, c1);
-            stage_tile(tile1, a.x, a.R, a.C, r1, c1);
+            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl);
         }
         tile_quant<MODE, ROT>(tile0, st, tb, a, o, ro, g, rcp6g, rcp4g, r0, c0);
         if (k1 >= a.tiles) break;
@@ -819,7 +864,7 @@ __global__ void __launch_bounds__(512, MODE == MODE_EDEN ? 4 : 2) k_quant(QuantA
         __syncthreads();                                   // tile1 landed; tile0 is free
         if (k2 < a.tiles) {
             tile_origin(a, a.tiles - 1 - k2, r0, c0);
-            stage_tile(tile0, a.x, a.R, a.C, r0, c0);
+            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
         }
         tile_quant<MODE, ROT>(tile1, st, tb, a, o, ro, g, rcp6g, rcp4g, r1, c1);
         k = k2;
@@ -920,14 +965,14 @@ static int grid_for(K kernel, int threads, int64_t tiles)
 template <bool ROT, int LAY>
 static void launch_amax(const QuantArgs &a, hipStream_t st)
 {
-    const int threads = (LAY == LAY_BOTH) ? 512 : 256;
+    const int threads = 64 * waves_for(LAY);
     k_amax<ROT, LAY><<<grid_for(k_amax<ROT, LAY>, threads, a.tiles), threads, 0, st>>>(a);
 }
 
 template <int MODE, bool ROT, int LAY>
 static void launch_quant(const QuantArgs &a, hipStream_t st)
 {
-    const int threads = (LAY == LAY_BOTH) ? 512 : 256;
+    const int threads = 64 * waves_for(LAY);
     k_quant<MODE, ROT, LAY><<<grid_for(k_quant<MODE, ROT, LAY>, threads, a.tiles), threads, 0,
                               st>>>(a);
 }
