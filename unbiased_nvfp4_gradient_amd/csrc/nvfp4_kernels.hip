@@ -95,10 +95,14 @@ __device__ __forceinline__ uint32_t e4m3_up(float t)
     return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
 }
 
-// E4M3 byte of an fp32 value that is already an E4M3 normal number.
-__device__ __forceinline__ uint32_t e4m3_of_exact_normal(uint32_t bits)
+// E4M3 byte of a normal c in [2^-6, 448) rounded stochastically: add the top 20 bits of
+// the random word w to the 20 mantissa bits E4M3 drops, keep the 3 that remain.  The fp32
+// bits >> 20 are exponent << 3 | mantissa, so the E4M3 byte is that minus the bias
+// difference (127 - 7) << 3 = 960; a carry out of the mantissa bumps the exponent, and
+// c < 448 cannot carry past 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_sr_normal(uint32_t bits, uint32_t w)
 {
-    return (((bits >> 23) - 120u) << 3) | ((bits >> 20) & 7u);
+    return ((bits + (w >> 12)) >> 20) - 960u;
 }
 
 __device__ __forceinline__ float e4m3_val(uint32_t c)
@@ -431,7 +435,9 @@ __device__ __forceinline__ float block_max(const float *r)
     return m;
 }
 
-// Per-workgroup table over the 127 E4M3 codes: (scale value s, den = s*g, rcp(den)).
+// Per-workgroup table over the 127 E4M3 codes: (scale value s, den = s*g, rcp(den)).  Code
+// 0 gets rcp = 0: a block with scale 0 then scales every element to +0 and rounds it to code
+// 0x0, which is what the contract prescribes for it, without a select.
 struct ScaleTable { float4 e[128]; };
 
 __device__ __forceinline__ void build_scale_table(ScaleTable &tb, float g, int tid)
@@ -439,7 +445,7 @@ __device__ __forceinline__ void build_scale_table(ScaleTable &tb, float g, int t
     if (tid < 128) {
         const float sv = e4m3_val((uint32_t)tid);
         const float den = sv * g;
-        tb.e[tid] = make_float4(sv, den, clamped_rcp(den), 0.0f);
+        tb.e[tid] = make_float4(sv, den, tid ? clamped_rcp(den) : 0.0f, 0.0f);
     }
 }
 
@@ -582,7 +588,8 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
 }
 
 // Round-to-nearest of one 1x16 block rb[0..15] with scale code s (table entry e):
-// packed codes into w0 (elements 0..7) and w1 (8..15); a zero scale gives all-zero codes.
+// packed codes into w0 (elements 0..7) and w1 (8..15); a zero scale gives all-zero codes
+// (its table rcp is 0).
 // y = fma(r, rcp, +0) is r * rcp rounded once, except that an exact zero becomes +0, so
 // the code's sign bit is set iff r < 0.
 __device__ __forceinline__ float scaled(float r, float rcp) { return __builtin_fmaf(r, rcp, 0.0f); }
@@ -600,8 +607,8 @@ __device__ __forceinline__ void rtn_block(const float *rb, uint32_t s, const flo
     b = CVT_FP4(b, scaled(rb[10], rcp), scaled(rb[11], rcp), 1);
     b = CVT_FP4(b, scaled(rb[12], rcp), scaled(rb[13], rcp), 2);
     b = CVT_FP4(b, scaled(rb[14], rcp), scaled(rb[15], rcp), 3);
-    w0 = s ? a : 0u;
-    w1 = s ? b : 0u;
+    w0 = a;      // s = 0: rcp = 0, so every code is 0x0 already
+    w1 = b;
 }
 
 // Signed grid values of a block's 16 codes.
@@ -694,7 +701,8 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
                 uint32_t out;
                 if (!(c < 448.0f)) out = 0x7Eu;
                 else if (c < 0.015625f) out = e4m3_rne_hw(c);      // no SR below 2^-6
-                else out = e4m3_of_exact_normal((__float_as_uint(c) + (w.w[b] >> 12)) & 0xFFF00000u);
+                else out = e4m3_sr_normal(__float_as_uint(c), w.w[b]);
+                // a zero scale stays zero even where S is not finite (inputs beyond 2^56)
                 sc[b] = sc[b] ? out : 0u;
             }
         }
