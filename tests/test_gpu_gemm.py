@@ -5,36 +5,12 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import unbiased_nvfp4_gradient_amd as nv
 import workloads
+from gemm_ref import check_entries
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-U = 2.0 ** -24
-
-E2M1 = np.array([oracle.e2m1_value(c) for c in range(16)], dtype=np.float64)
-E4M3 = np.array([oracle.e4m3_value(c) for c in range(127)] + [np.nan], dtype=np.float64)
-
-
-def exact_rows(t: nv.NVFP4, rows):
-    """fp64 values sign * E4M3(scale) * magnitude of the listed rows (tensor scale apart)."""
-    codes = oracle.unpack_codes(t.codes[rows].cpu().numpy())
-    scales = E4M3[t.scales[rows].cpu().numpy()]
-    return E2M1[codes] * np.repeat(scales, 16, axis=1)
-
-
-def check_entries(c, a, b, rows, cols, f):
-    ga, gb = float(a.tensor_scale.cpu()[0]), float(b.tensor_scale.cpu()[0])
-    A = exact_rows(a, rows)
-    B = exact_rows(b, cols)
-    ref = (A @ B.T) * ga * gb * f
-    mag = (np.abs(A) @ np.abs(B).T) * ga * gb * f
-    K = A.shape[1]
-    got = c[np.ix_(rows, cols)].cpu().numpy().astype(np.float64)
-    bound = 2 * K * U * mag + 4 * U * np.abs(ref) + 1e-30
-    assert np.all(np.abs(got - ref) <= bound), np.max(np.abs(got - ref) / bound)
-    return got, ref
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 256, 384), (96, 160, 64),
