@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mse", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-linear", action="store_true",
+                    help="skip the linear-layer (forward + backward) measurement")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (3x): the calibration kernel "
                          "for HBM byte counters")
@@ -186,6 +188,9 @@ def main():
     if not args.no_gemm:
         result["gemm_check"] = gemm_check(nv, workloads, dev, out.row, stream)
 
+    if not args.no_linear:
+        result["linear_layer"] = linear_layer(nv, dev)
+
     if args.copy_probe:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -229,6 +234,70 @@ def gemm_check(nv, workloads, dev, a, stream, reps=5):
     return {"kernel": "k_gemm (dequantize-in-LDS, v_mfma_f32_32x32x16_bf16)", "M": M, "N": N,
             "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
             "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
+
+
+def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=5):
+    """One Quartet II linear layer's products at the shape of a 1.9B Llama-style model's
+    gate projection (32768 tokens, 2048 -> 8192): forward 4/6 + GEMM, backward MS-EDEN of
+    dY (both layouts), W and X + two GEMMs.  Reports the whole forward + backward, the
+    three GEMMs alone on already-quantized operands, and the same three products as BF16
+    torch.mm (hipBLASLt) for context."""
+    import numpy as np
+    import torch
+
+    from unbiased_nvfp4_gradient_amd import linear
+
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn((t, n_in), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn((n_out, n_in), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    dy = torch.randn((t, n_out), generator=g, device=dev).to(torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    def step():
+        linear.forward_product(x, w, 1)
+        linear.backward_products(dy, x, w, 1, "eden")
+
+    ms_step = timed(step)
+    _, (qx, qw) = linear.forward_product(x, w, 1, operands=True)
+    _, (qdy_r, qw_c, qdy_c, qx_c) = linear.backward_products(dy, x, w, 1, "eden", operands=True)
+    outs = [torch.empty((t, n_out), dtype=torch.float32, device=dev),
+            torch.empty((t, n_in), dtype=torch.float32, device=dev),
+            torch.empty((n_out, n_in), dtype=torch.float32, device=dev)]
+
+    def gemms():
+        nv.nvfp4_gemm_check(qx, qw, True, out=outs[0])
+        nv.nvfp4_gemm_check(qdy_r, qw_c, True, out=outs[1])
+        nv.nvfp4_gemm_check(qdy_c, qx_c, True, out=outs[2])
+
+    ms_gemm = timed(gemms)
+    wt, dyt = w.t().contiguous(), dy.t().contiguous()
+
+    def bf16():
+        torch.mm(x, wt)
+        torch.mm(dy, w)
+        torch.mm(dyt, x)
+
+    ms_bf16 = timed(bf16)
+    flops = 3 * 2.0 * t * n_in * n_out
+    return {"shape": f"T={t}, in={n_in}, out={n_out} (gate projection)",
+            "ms_forward_backward": round(ms_step, 3),
+            "ms_three_gemms": round(ms_gemm, 3),
+            "ms_quantize": round(ms_step - ms_gemm, 3),
+            "gemm_tflops": round(flops / (ms_gemm * 1e-3) / 1e12, 1),
+            "bf16_torch_mm_ms": round(ms_bf16, 3),
+            "bf16_torch_mm_tflops": round(flops / (ms_bf16 * 1e-3) / 1e12, 1)}
 
 
 def rel_mse(nv, xd, mode, layout):
