@@ -88,6 +88,8 @@ def main():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-linear", action="store_true",
                     help="skip the linear-layer (forward + backward) measurement")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the per-quantizer throughput table")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (3x): the calibration kernel "
                          "for HBM byte counters")
@@ -188,6 +190,9 @@ def main():
     if not args.no_gemm:
         result["gemm_check"] = gemm_check(nv, workloads, dev, out.row, stream)
 
+    if not args.no_modes:
+        result["modes"] = modes_table(nv, x, out, amax, stream)
+
     if not args.no_linear:
         result["linear_layer"] = linear_layer(nv, dev)
 
@@ -234,6 +239,41 @@ def gemm_check(nv, workloads, dev, a, stream, reps=5):
     return {"kernel": "k_gemm (dequantize-in-LDS, v_mfma_f32_32x32x16_bf16)", "M": M, "N": N,
             "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
             "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
+
+
+def modes_table(nv, x, out, amax, stream, reps=40):
+    """Throughput of every quantizer on the same 16384 x 8192 input, both layouts: phase 1
+    + phase 2 per call, algorithmic GB/s as in the main line, a pair of events around each
+    call.  The modes take turns call by call, so they see the same clock conditions."""
+    import numpy as np
+    import torch
+
+    modes = (("rtn", "rtn", False), ("rtn+rht", "rtn", True), ("sr", "sr", False),
+             ("sr+rht", "sr", True), ("fp46+rht", "fp46", True), ("eden", "eden", True))
+
+    def call(mode, rht, seed):
+        nv.nvfp4_amax(x, rht, 1, ("row", "col"), amax=amax, stream=stream)
+        nv.nvfp4_quantize_amax(mode, x, amax, seed=seed, rht=rht, rht_seed=1,
+                               layouts=("row", "col"), out=out, stream=stream)
+
+    for k in range(3):
+        for _, mode, rht in modes:
+            call(mode, rht, 100 + k)
+    ev = {name: [] for name, _, _ in modes}
+    for k in range(reps):
+        for name, mode, rht in modes:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(mode, rht, k)
+            e1.record(stream)
+            ev[name].append((e0, e1))
+    torch.cuda.synchronize()
+    table = {}
+    for name, _, _ in modes:
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev[name]]))
+        table[name] = {"ms": round(ms, 4),
+                       "GB/s": round(alg_bytes(ROWS, COLS) / (ms * 1e-3) / 1e9, 1)}
+    return table
 
 
 def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=5):

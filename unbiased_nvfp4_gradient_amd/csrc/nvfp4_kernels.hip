@@ -120,18 +120,30 @@ __device__ __forceinline__ uint32_t e2m1_rtn(float a)
            (uint32_t)(a > 5.0f);
 }
 
-// Largest grid index whose magnitude is <= a, for 0 <= a < 6.
-__device__ __forceinline__ uint32_t e2m1_floor(float a)
-{
-    return (uint32_t)(a >= 0.5f) + (uint32_t)(a >= 1.0f) + (uint32_t)(a >= 1.5f) +
-           (uint32_t)(a >= 2.0f) + (uint32_t)(a >= 3.0f) + (uint32_t)(a >= 4.0f);
-}
-
 __device__ __forceinline__ float e2m1_val(uint32_t mag)
 {
     const uint32_t e = mag >> 1, m = mag & 1u;
     const uint32_t b = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
     return __uint_as_float(b);
+}
+
+// Stochastic rounding of a magnitude 0 <= a <= 6 onto the E2M1 grid with random word w:
+// lo = the largest grid index whose value vlo <= a, frac = (a - vlo) / step to the next
+// value, and the magnitude is lo + 1 iff the top 24 bits of w, u, satisfy u < frac * 2^24.
+// From 1 up, the grid points are a's binade start and its midpoint: vlo is a with all but
+// the top mantissa bit cleared, lo = (bits(a) >> 22) - 252 (2 at 1, 6 at 4), and the step
+// is half the binade, so 1 / step = 2^(128 - biased exponent).  Below 1 the points are 0,
+// 0.5, 1 (step 0.5).  a = 6 is index 7.  Every operation here is exact.
+__device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t w)
+{
+    const uint32_t t = __float_as_uint(a);
+    const bool big = a >= 1.0f, half = a >= 0.5f;
+    const uint32_t lo = big ? (t >> 22) - 252u : (uint32_t)half;
+    const float vlo = big ? __uint_as_float(t & 0xFFC00000u) : (half ? 0.5f : 0.0f);
+    const float inv = big ? __uint_as_float(0x7F800000u - (t & 0x7F800000u)) : 2.0f;
+    const float frac = (a - vlo) * inv;
+    const uint32_t up = (float)(w >> 8) < frac * 16777216.0f;
+    return a >= 6.0f ? 7u : lo + up;
 }
 
 // Nearest-even E4M3 of t >= 0, saturating: the hardware conversion is exact below 448.
@@ -727,18 +739,7 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
                             const int p = 16 * b + 4 * qd + k;
                             const float y = scaled(rb[4 * qd + k], rcp);
                             const float a = fminf(fabsf(y), 6.0f);
-                            uint32_t mag;
-                            if (a >= 6.0f) {
-                                mag = 7u;
-                            } else {
-                                const uint32_t lo = e2m1_floor(a);
-                                const float vlo = e2m1_val(lo);
-                                // 1 / (next grid value - vlo): steps 0.5, 1, 2 -> exact
-                                const float inv_step = (lo < 4u) ? 2.0f : (lo < 6u ? 1.0f : 0.5f);
-                                const float frac = (a - vlo) * inv_step;
-                                const uint32_t u = w.w[k] >> 8;
-                                mag = lo + (uint32_t)((float)u < frac * 16777216.0f);
-                            }
+                            const uint32_t mag = e2m1_sr_mag(a, w.w[k]);
                             const uint32_t sgn = __float_as_uint(y) >> 31;   // r < 0
                             cw[p >> 3] |= (mag | (sgn << 3)) << (4 * (p & 7));
                         }
@@ -831,10 +832,16 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
 // Pass 2: quantize and pack every group of the requested layouts.  Tiles are walked in
 // the reverse order of pass 1 (its last tiles are the likeliest to still be cached), with
 // the same two-buffer streaming.
-// MS-EDEN fits 128 registers (4 waves per SIMD); the other modes keep more values live and
-// are given 2 waves per SIMD rather than spilling.
+// MS-EDEN and RTN fit 128 registers (4 waves per SIMD); SR and 4/6 keep more values live
+// and get 3 waves per SIMD (168 registers) rather than spilling, as does every mode's
+// unrotated column-only variant at 2 waves.
+constexpr int quant_waves_per_simd(int mode, bool rot, int lay)
+{
+    return (!rot && lay == LAY_COL) ? 2 : (mode == MODE_EDEN || mode == MODE_RTN) ? 4 : 3;
+}
+
 template <int MODE, bool ROT, int LAY>
-__global__ void __launch_bounds__(512, MODE == MODE_EDEN ? 4 : 2) k_quant(QuantArgs a)
+__global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_quant(QuantArgs a)
 {
     __shared__ Tile tile0;
     __shared__ Tile tile1;
