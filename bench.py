@@ -390,8 +390,9 @@ def mse_vs_sr(nv, workloads, dev, x_c4):
 
 
 def cpu_baseline(x_cpu, B):
-    """The CPU oracle on the same workload (all host cores): amax + both layouts, three
-    passes, median."""
+    """The CPU oracle on the same workload: on all host cores, amax + both layouts, median
+    of three passes; and on one core, the row layout of the first 2048 rows (1/8 of the
+    tensor), scaled to the same byte accounting."""
     import numpy as np
 
     import oracle
@@ -407,9 +408,20 @@ def cpu_baseline(x_cpu, B):
             oracle.quantize("eden", xb, axis=axis, seed=1, rht_seed=1, margins=False)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
+    sub = np.ascontiguousarray(xb[:2048])
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.quantize("eden", sub, axis=0, seed=1, rht_seed=1, margins=False)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
+    b1 = alg_bytes(2048, COLS, layouts=1)
     return {"value": round(B / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "the full 16384x8192 workload, both layouts (amax + quantize per "
-                      "layout), median of 3 passes: %.2f s" % dt}
+                      "layout), median of 3 passes: %.2f s" % dt,
+            "single_core": {"value": round(b1 / dt1 / 1e9, 4), "unit": "GB/s",
+                            "sample": "rows 0..2047, row layout, one pass: %.2f s" % dt1}}
 
 
 if __name__ == "__main__":
