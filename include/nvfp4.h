@@ -54,6 +54,9 @@
  *   Seeds.      rht_seed selects the rotation's random signs, shared by every group and both
  *               layouts; both operands of one GEMM must use the same rht_seed.  seed drives
  *               stochastic rounding (Philox4x32-10 counter streams).
+ *   Environment. NVFP4_GENERAL_TILE_LOADS=1 (read at every call) makes the quantizers load
+ *               every tile through the general path that rows longer than 2^26 elements
+ *               take; the results are identical.  It exists for testing that path.
  */
 #ifndef NVFP4_H
 #define NVFP4_H

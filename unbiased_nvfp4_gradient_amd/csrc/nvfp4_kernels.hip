@@ -41,6 +41,7 @@
 // which are the likeliest to still sit in the last-level cache.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <cstdlib>
 
 namespace nvfp4k {
 
@@ -277,11 +278,11 @@ __device__ __forceinline__ DmaLane dma_lane(int64_t C)
 template <int W>
 __device__ __forceinline__ void stage_tile(Tile &t, const uint16_t *__restrict__ x, int64_t R,
                                            int64_t C, int64_t r0, int64_t c0,
-                                           const DmaLane &dl)
+                                           const DmaLane &dl, int64_t fast_max_c)
 {
     if (r0 + TILE <= R && c0 + TILE <= C) {
         const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-        if (C <= DMA_FAST_MAX_C) {
+        if (C <= fast_max_c) {
             const char *base = reinterpret_cast<const char *>(x + r0 * C + c0);
             const int64_t step = 8 * W * C;                 // bytes of 4 W rows
 #pragma unroll
@@ -475,6 +476,7 @@ struct QuantArgs {
     uint32_t *amax_bits;       // [0] row, [1] column: fp32 bits of max |r| (phase 1 output)
     uint64_t seed, rht_seed;
     int64_t tiles_c, tiles;    // tiles per tile-row, total tiles
+    int64_t dma_fast_max_c;    // rows up to this many elements use the precomputed loads
 };
 
 // Waves per workgroup: 4 per layout (128 groups x 2 halves = 256 lanes per layout).
@@ -567,7 +569,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
     int64_t k = blockIdx.x, r0, c0;
     if (k < a.tiles) {
         tile_origin(a, k, r0, c0);
-        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
+        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
     }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
@@ -575,7 +577,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         int64_t r1 = 0, c1 = 0;
         if (k1 < a.tiles) {
             tile_origin(a, k1, r1, c1);
-            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl);
+            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
         }
         local = fmaxf(local, tile_amax<ROT>(tile0, st, a, ro, r0, c0));
         if (k1 >= a.tiles) break;
@@ -583,7 +585,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         __syncthreads();                                   // tile1 landed; tile0 is free
         if (k2 < a.tiles) {
             tile_origin(a, k2, r0, c0);
-            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
+            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
         }
         local = fmaxf(local, tile_amax<ROT>(tile1, st, a, ro, r1, c1));
         k = k2;
@@ -863,7 +865,7 @@ __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_q
     int64_t k = blockIdx.x, r0, c0;
     if (k < a.tiles) {
         tile_origin(a, a.tiles - 1 - k, r0, c0);
-        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
+        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
     }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
@@ -871,7 +873,7 @@ __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_q
         int64_t r1 = 0, c1 = 0;
         if (k1 < a.tiles) {
             tile_origin(a, a.tiles - 1 - k1, r1, c1);
-            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl);
+            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
         }
         tile_quant<MODE, ROT>(tile0, st, tb, a, o, ro, g, rcp6g, rcp4g, r0, c0);
         if (k1 >= a.tiles) break;
@@ -879,7 +881,7 @@ __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_q
         __syncthreads();                                   // tile1 landed; tile0 is free
         if (k2 < a.tiles) {
             tile_origin(a, a.tiles - 1 - k2, r0, c0);
-            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
+            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
         }
         tile_quant<MODE, ROT>(tile1, st, tb, a, o, ro, g, rcp6g, rcp4g, r1, c1);
         k = k2;
@@ -1014,6 +1016,10 @@ static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_b
     a.rht_seed = rht_seed;
     a.tiles_c = (C + TILE - 1) / TILE;
     a.tiles = a.tiles_c * ((R + TILE - 1) / TILE);
+    // NVFP4_GENERAL_TILE_LOADS=1 sends every tile through the general load loop (the one
+    // rows longer than 2^26 elements take), so tests can cover it at small sizes
+    const char *general = std::getenv("NVFP4_GENERAL_TILE_LOADS");
+    a.dma_fast_max_c = (general && general[0] == '1') ? 0 : DMA_FAST_MAX_C;
     return a;
 }
 
