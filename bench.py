@@ -236,7 +236,7 @@ def gemm_check(nv, workloads, dev, a, stream, reps=5):
     M, K = a.codes.shape[0], a.codes.shape[1] * 2
     N = b.codes.shape[0]
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-    return {"kernel": "k_gemm (dequantize-in-LDS, v_mfma_f32_32x32x16_bf16)", "M": M, "N": N,
+    return {"kernel": "k_gemm (dequantize into LDS as FP16, v_mfma_f32_32x32x16_f16)", "M": M, "N": N,
             "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
             "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
 

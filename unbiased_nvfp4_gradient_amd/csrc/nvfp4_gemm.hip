@@ -4,29 +4,31 @@
 // Quartet II runs every linear layer's products on NVFP4 operands (itsolotime.com summary,
 // abstract: NVFP4 GEMM kernels up to 4.2x over BF16 on Blackwell).  gfx950's scaled MFMA
 // takes power-of-two (E8M0) scales per 32 elements, not E4M3 scales per 16, so this consumer
-// dequantizes in LDS instead: a code's value V (<= 2 significant bits) times its block's
-// E4M3 scale (<= 4 significant bits) has at most 6 significant bits and an exponent inside
-// BF16's range, so the BF16 operand is exact.  v_mfma_f32_32x32x16_bf16 multiplies exactly
+// dequantizes into LDS instead: a code's value V (<= 2 significant bits) times its block's
+// E4M3 scale (<= 4 significant bits) has at most 6 significant bits and lies in
+// [2^-10, 2688], so the FP16 operand is exact.  v_mfma_f32_32x32x16_f16 multiplies exactly
 // and accumulates in FP32; the two FP32 tensor scales (and 2^-7 when both operands carry
 // the same random-sign Hadamard rotation along K, since H H = 128 I) are applied in the
 // epilogue.
 //
 // Tiling: a C tile of 256 x 256 per workgroup of 8 waves, each wave a 64 x 128 sub-tile
 // (2 x 4 MFMA 32x32 tiles, 128 FP32 accumulators per lane); K in steps of 64 (four 1x16
-// blocks).  Lane layouts of v_mfma_f32_32x32x16_bf16 (checked on
-// the device): lane l supplies A row l%32 and B column l%32, elements k = 8*(l/32) .. +7;
+// blocks) through two LDS stages.  Lane layout of the 32x32x16 MFMA (checked on the
+// device): lane l supplies A row l%32 and B column l%32, elements k = 8*(l/32) .. +7;
 // accumulator r of lane l is C[8*(r/4) + 4*(l/32) + r%4][l%32].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace nvfp4g {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDS_ROW = BK + 8;          // bf16 per LDS row (16-byte pad against bank conflicts)
+constexpr int LDS_ROW = BK + 8;          // halfs per LDS row (16-byte pad against bank conflicts)
+constexpr int STAGE = (BM + BN) * LDS_ROW;   // halfs of one A + B stage
 
 struct Operand {
     const uint8_t *codes;    // [rows][K/2]
@@ -34,78 +36,88 @@ struct Operand {
     const float *g;
 };
 
+// One thread's share of a 256 x 64 operand slice: row t/2, elements 32*(t%2) .. +31,
+// as stored (16 code bytes, 2 scale bytes).
+struct Raw {
+    uint4 codes;
+    uint32_t scales;
+};
+
+__device__ __forceinline__ Raw load_raw(const Operand &op, int64_t rows, int64_t K, int64_t row0,
+                                        int64_t k0)
+{
+    const int t = threadIdx.x, r = t >> 1, half = t & 1;
+    const int64_t row = row0 + r;
+    Raw raw;
+    if (row < rows) {
+        raw.codes = *reinterpret_cast<const uint4 *>(op.codes + row * (K >> 1) + (k0 >> 1) +
+                                                     16 * half);
+        raw.scales = *reinterpret_cast<const uint16_t *>(op.scales + row * (K >> 4) + (k0 >> 4) +
+                                                         2 * half);
+    } else {
+        raw.codes = make_uint4(0u, 0u, 0u, 0u);
+        raw.scales = 0u;
+    }
+    return raw;
+}
+
 __device__ __forceinline__ float e4m3_val(uint32_t c)
 {
     const uint32_t e = c >> 3, m = c & 7u;
     return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-// Two dequantized values -> one packed BF16 pair.  The products are exact and have at most
-// 6 significant bits, so taking the high half of each FP32 is an exact conversion.
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
-{
-    return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
-}
-
+// Eight codes (one 32-bit word) times scale s as four packed FP16 pairs.  The grid values
+// decode exactly to FP32, convert exactly to FP16, and the product of a value (<= 2
+// significant bits) and an E4M3 scale (<= 4) has at most 6 significant bits, between 2^-10
+// and 2688: exact in FP16.
 template <int SEL>
-__device__ __forceinline__ uint32_t dq_pair(uint32_t w, float s)
+__device__ __forceinline__ uint32_t dq_pair(uint32_t w, half2v s)
 {
     const float2v v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-    return pack_bf16(v.x * s, v.y * s);
+    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(v.x, v.y)) * s;
+    return __builtin_bit_cast(uint32_t, h);
 }
 
-// Dequantize 32 consecutive elements of one operand row (16 code bytes + 2 scales) into
-// 16 packed BF16 pairs.
-__device__ __forceinline__ void dequant32(uint4 cw, uint32_t s0, uint32_t s1, uint32_t out[16])
-{
-    const float f0 = e4m3_val(s0), f1 = e4m3_val(s1);
-    const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float f = k < 2 ? f0 : f1;
-        out[4 * k + 0] = dq_pair<0>(w[k], f);
-        out[4 * k + 1] = dq_pair<1>(w[k], f);
-        out[4 * k + 2] = dq_pair<2>(w[k], f);
-        out[4 * k + 3] = dq_pair<3>(w[k], f);
-    }
-}
-
-// Stage one operand's 256 x 64 K-slice into LDS as BF16.  Thread t handles row t/2, elements
-// 32*(t%2) .. +31 of the slice; rows outside [0, rows) are zero.
-__device__ __forceinline__ void stage_operand(const Operand &op, int64_t rows, int64_t K,
-                                              int64_t row0, int64_t k0, uint16_t *lds)
+// Dequantize one thread's 32 elements and write them to its row of an LDS operand tile.
+__device__ __forceinline__ void store_dequant(const Raw &raw, _Float16 *lds)
 {
     const int t = threadIdx.x, r = t >> 1, half = t & 1;
-    uint32_t packed[16];
-    const int64_t row = row0 + r;
-    if (row < rows) {
-        const uint4 cw = *reinterpret_cast<const uint4 *>(op.codes + row * (K >> 1) +
-                                                          (k0 >> 1) + 16 * half);
-        const uint8_t *sp = op.scales + row * (K >> 4) + (k0 >> 4) + 2 * half;
-        dequant32(cw, sp[0], sp[1], packed);
-    } else {
+    const _Float16 f0 = (_Float16)e4m3_val(raw.scales & 0xFFu);
+    const _Float16 f1 = (_Float16)e4m3_val(raw.scales >> 8);
+    const half2v s0 = {f0, f0}, s1 = {f1, f1};
+    const uint32_t w[4] = {raw.codes.x, raw.codes.y, raw.codes.z, raw.codes.w};
+    uint32_t o[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) packed[i] = 0u;
+    for (int k = 0; k < 4; ++k) {
+        const half2v s = k < 2 ? s0 : s1;
+        o[4 * k + 0] = dq_pair<0>(w[k], s);
+        o[4 * k + 1] = dq_pair<1>(w[k], s);
+        o[4 * k + 2] = dq_pair<2>(w[k], s);
+        o[4 * k + 3] = dq_pair<3>(w[k], s);
     }
     uint4 *dst = reinterpret_cast<uint4 *>(lds + r * LDS_ROW + 32 * half);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        dst[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+        dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
 }
 
-__device__ __forceinline__ bf16x8 frag(const uint16_t *lds, int row, int k)
+__device__ __forceinline__ half8 frag(const _Float16 *lds, int row, int k)
 {
-    const uint4 v = *reinterpret_cast<const uint4 *>(lds + row * LDS_ROW + k);
-    return __builtin_bit_cast(bf16x8, v);
+    return *reinterpret_cast<const half8 *>(lds + row * LDS_ROW + k);
 }
 
 // C[M][N] = f * gA * gB * sum_k A[m][k] * B[n][k].  Grid: (ceil(N/256), ceil(M/256)),
 // 512 threads.  M and N multiples of 32, K a multiple of 64.
+//
+// The K loop is software-pipelined over two LDS stages: while the waves run the MFMAs of
+// slice k from one stage, the same iteration dequantizes slice k + 1 (loaded into
+// registers during the previous iteration) into the other stage and starts loading slice
+// k + 2; one barrier per slice.
 __global__ void __launch_bounds__(512, 1) k_gemm(Operand A, Operand B, int64_t M, int64_t N,
                                                  int64_t K, float f, float *__restrict__ C)
 {
-    __shared__ uint16_t As[BM * LDS_ROW];
-    __shared__ uint16_t Bs[BN * LDS_ROW];
+    __shared__ _Float16 lds[2 * STAGE];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int wm = (w >> 1) * 64, wn = (w & 1) * 128;      // this wave's 64 x 128 sub-tile
@@ -115,25 +127,42 @@ __global__ void __launch_bounds__(512, 1) k_gemm(Operand A, Operand B, int64_t M
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    for (int64_t k0 = 0; k0 < K; k0 += BK) {
-        __syncthreads();                                   // previous slice fully consumed
-        stage_operand(A, M, K, m0, k0, As);
-        stage_operand(B, N, K, n0, k0, Bs);
-        __syncthreads();
+    const int64_t nk = K / BK;
+    if (nk > 0) {
+        Raw ra = load_raw(A, M, K, m0, 0), rb = load_raw(B, N, K, n0, 0);
+        store_dequant(ra, lds);
+        store_dequant(rb, lds + BM * LDS_ROW);
+        if (nk > 1) {
+            ra = load_raw(A, M, K, m0, BK);
+            rb = load_raw(B, N, K, n0, BK);
+        }
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            __syncthreads();       // stage kt % 2 written; stage (kt + 1) % 2 no longer read
+            const _Float16 *As = lds + (kt & 1) * STAGE, *Bs = As + BM * LDS_ROW;
+            if (kt + 1 < nk) {
+                _Float16 *nxt = lds + ((kt + 1) & 1) * STAGE;
+                store_dequant(ra, nxt);
+                store_dequant(rb, nxt + BM * LDS_ROW);
+                if (kt + 2 < nk) {
+                    ra = load_raw(A, M, K, m0, (kt + 2) * BK);
+                    rb = load_raw(B, N, K, n0, (kt + 2) * BK);
+                }
+            }
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            const int kl = kk + 8 * (lane >> 5);
-            bf16x8 a[2], b[4];
+            for (int kk = 0; kk < BK; kk += 16) {
+                const int kl = kk + 8 * (lane >> 5);
+                half8 a[2], b[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = frag(As, wm + 32 * i + (lane & 31), kl);
+                for (int i = 0; i < 2; ++i) a[i] = frag(As, wm + 32 * i + (lane & 31), kl);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = frag(Bs, wn + 32 * j + (lane & 31), kl);
+                for (int j = 0; j < 4; ++j) b[j] = frag(Bs, wn + 32 * j + (lane & 31), kl);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j],
-                                                                        0, 0, 0);
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j],
+                                                                           0, 0, 0);
+            }
         }
     }
 
