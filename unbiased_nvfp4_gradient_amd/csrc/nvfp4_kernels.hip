@@ -66,7 +66,17 @@ __device__ __forceinline__ Word4 philox(uint64_t key, uint32_t c0, uint32_t c1, 
     for (int round = 0; round < 10; ++round) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0;   // one v_mad_u64_u32 each
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n0, n2;
+        if (round == 0) {
+            // the first round's inputs are partly wave-uniform: plain XORs let the
+            // compiler keep that part on the scalar unit
+            n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+            n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        } else {
+            // three-input XOR in one v_bitop3_b32 (truth table 0x96: odd parity)
+            n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+            n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+        }
         c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
@@ -834,12 +844,16 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
 // Pass 2: quantize and pack every group of the requested layouts.  Tiles are walked in
 // the reverse order of pass 1 (its last tiles are the likeliest to still be cached), with
 // the same two-buffer streaming.
-// MS-EDEN and RTN fit 128 registers (4 waves per SIMD); SR and 4/6 keep more values live
-// and get 3 waves per SIMD (168 registers) rather than spilling, as does every mode's
-// unrotated column-only variant at 2 waves.
+// Waves per SIMD each variant is compiled for, the most that fit without spilling: MS-EDEN,
+// RTN and the unrotated two-layout SR fit 128 registers (4 waves); the other SR and 4/6
+// variants keep more values live (3 waves, 168 registers); the unrotated column-only
+// variants more still (2 waves).
 constexpr int quant_waves_per_simd(int mode, bool rot, int lay)
 {
-    return (!rot && lay == LAY_COL) ? 2 : (mode == MODE_EDEN || mode == MODE_RTN) ? 4 : 3;
+    if (!rot && lay == LAY_COL) return 2;
+    if (mode == MODE_EDEN || mode == MODE_RTN) return 4;
+    if (mode == MODE_SR && !rot && lay == LAY_BOTH) return 4;
+    return 3;
 }
 
 template <int MODE, bool ROT, int LAY>
