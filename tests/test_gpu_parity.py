@@ -206,3 +206,25 @@ def test_general_tile_loads(monkeypatch, shape, mode, rht, layouts):
     monkeypatch.setenv("NVFP4_GENERAL_TILE_LOADS", "1")
     x = workloads.normal(shape, seed=sum(shape) + 1)
     check_full(mode, x, layouts, seed=5, rht=rht, rht_seed=8, what=f"general {shape} {mode}")
+
+
+# ----------------------------------------------------------------------------- outside the contract
+
+def test_nonfinite_inputs_complete():
+    """NaN, infinities and values beyond 2^56 are outside the contract (their codes are
+    unspecified), but every quantizer must still complete and write in-range scale bytes."""
+    print("case: NaN / inf / huge inputs, every mode, both layouts", flush=True)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((256, 512)).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] = np.nan
+    x[rng.random(x.shape) < 0.01] = np.inf
+    x[rng.random(x.shape) < 0.01] = -np.inf
+    x[rng.random(x.shape) < 0.01] = 3e38
+    xd = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+    bits = workloads.bf16_bits(xd.cpu())
+    assert ((bits & 0x7FFF) > 0x7F80).any() and ((bits & 0x7FFF) == 0x7F80).any()
+    for mode, rht in (("eden", True), ("sr", False), ("sr", True), ("rtn", False),
+                      ("rtn", True), ("fp46", False), ("fp46", True)):
+        got = run_gpu(mode, xd, ("row", "col"), seed=2, rht=rht, rht_seed=2)
+        for axis, (codes, scales, g, _) in got.items():
+            assert scales.max() <= 0x7E, (mode, rht, axis)

@@ -158,9 +158,11 @@ __device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t w)
 }
 
 // Nearest-even E4M3 of t >= 0, saturating: the hardware conversion is exact below 448.
+// Its result indexes the 128-entry scale table: the mask keeps even a NaN input (outside the
+// contract) inside the table; a finite t >= 0 never sets bit 7.
 __device__ __forceinline__ uint32_t e4m3_rne_hw(float t)
 {
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0xFFu;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0x7Fu;
 }
 
 typedef float float2v __attribute__((ext_vector_type(2)));
