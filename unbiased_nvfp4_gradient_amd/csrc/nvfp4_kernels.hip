@@ -656,6 +656,23 @@ __device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, float V[1
     decode_pair<3>(w0, w1, V);
 }
 
+// Squared-error terms of elements 2K and 2K+1 (code byte K of wa / wb) for the two 4/6
+// options, added to the running fused multiply-add chains.
+template <int K>
+__device__ __forceinline__ void fp46_err_pairs(const float *r, uint32_t wa, uint32_t wb,
+                                               float denA, float denB, float &errA, float &errB)
+{
+    const float2v va = DEC_FP4(wa, K), vb = DEC_FP4(wb, K);
+    const float da0 = __builtin_fmaf(denA, va.x, -r[2 * K]);
+    const float db0 = __builtin_fmaf(denB, vb.x, -r[2 * K]);
+    errA = __builtin_fmaf(da0, da0, errA);
+    errB = __builtin_fmaf(db0, db0, errB);
+    const float da1 = __builtin_fmaf(denA, va.y, -r[2 * K + 1]);
+    const float db1 = __builtin_fmaf(denB, vb.y, -r[2 * K + 1]);
+    errA = __builtin_fmaf(da1, da1, errA);
+    errB = __builtin_fmaf(db1, db1, errB);
+}
+
 // Saturate magnitude 7 (value 6) to 6 (value 4) in every nibble of a packed word.
 __device__ __forceinline__ uint32_t cap_mag6(uint32_t w)
 {
@@ -775,18 +792,16 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
                 b0 = cap_mag6(b0);
                 b1 = cap_mag6(b1);
                 // squared error of each option: d = den * V - r with one rounding, summed by
-                // fused multiply-adds in element order
-                float VA[16], VB[16];
-                decode_block(a0, a1, VA);
-                decode_block(b0, b1, VB);
+                // fused multiply-adds in element order, two elements (one code byte) at a time
                 float errA = 0.0f, errB = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float da = __builtin_fmaf(eA.y, VA[i], -rb[i]);
-                    const float db = __builtin_fmaf(eB.y, VB[i], -rb[i]);
-                    errA = __builtin_fmaf(da, da, errA);
-                    errB = __builtin_fmaf(db, db, errB);
-                }
+                fp46_err_pairs<0>(rb, a0, b0, eA.y, eB.y, errA, errB);
+                fp46_err_pairs<1>(rb, a0, b0, eA.y, eB.y, errA, errB);
+                fp46_err_pairs<2>(rb, a0, b0, eA.y, eB.y, errA, errB);
+                fp46_err_pairs<3>(rb, a0, b0, eA.y, eB.y, errA, errB);
+                fp46_err_pairs<0>(rb + 8, a1, b1, eA.y, eB.y, errA, errB);
+                fp46_err_pairs<1>(rb + 8, a1, b1, eA.y, eB.y, errA, errB);
+                fp46_err_pairs<2>(rb + 8, a1, b1, eA.y, eB.y, errA, errB);
+                fp46_err_pairs<3>(rb + 8, a1, b1, eA.y, eB.y, errA, errB);
                 const bool pickA = errA <= errB;
                 sc[b] = pickA ? sA : sB;
                 cw[2 * b] = pickA ? a0 : b0;
@@ -846,16 +861,15 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
 // Pass 2: quantize and pack every group of the requested layouts.  Tiles are walked in
 // the reverse order of pass 1 (its last tiles are the likeliest to still be cached), with
 // the same two-buffer streaming.
-// Waves per SIMD each variant is compiled for, the most that fit without spilling: MS-EDEN,
-// RTN and the unrotated two-layout SR fit 128 registers (4 waves); the other SR and 4/6
-// variants keep more values live (3 waves, 168 registers); the unrotated column-only
-// variants more still (2 waves).
+// Waves per SIMD each variant is compiled for, the most that fit without spilling: 4 (128
+// registers) for MS-EDEN, RTN, 4/6 and the unrotated two-layout SR; 3 (168) for the other
+// SR variants and the unrotated row-only 4/6; 2 for the unrotated column-only variants.
 constexpr int quant_waves_per_simd(int mode, bool rot, int lay)
 {
     if (!rot && lay == LAY_COL) return 2;
-    if (mode == MODE_EDEN || mode == MODE_RTN) return 4;
-    if (mode == MODE_SR && !rot && lay == LAY_BOTH) return 4;
-    return 3;
+    if (mode == MODE_SR) return (!rot && lay == LAY_BOTH) ? 4 : 3;
+    if (mode == MODE_FP46 && !rot && lay == LAY_ROW) return 3;
+    return 4;
 }
 
 template <int MODE, bool ROT, int LAY>
