@@ -87,16 +87,6 @@ __device__ __forceinline__ Word4 philox(uint64_t key, uint32_t c0, uint32_t c1, 
 }
 
 // ------------------------------------------------------------------------------ formats
-// E4M3FN scale byte of t >= 0, round to nearest even, saturating at 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_rne(float t)
-{
-    if (!(t < 448.0f)) return 0x7Eu;
-    if (t < 0.015625f) return (uint32_t)__builtin_rintf(t * 512.0f);   // subnormal: k * 2^-9
-    uint32_t u = __float_as_uint(t);
-    u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;              // keep 3 mantissa bits
-    return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
-}
-
 // Smallest E4M3FN value >= t >= 0, capped at 448.
 __device__ __forceinline__ uint32_t e4m3_up(float t)
 {
@@ -120,15 +110,6 @@ __device__ __forceinline__ float e4m3_val(uint32_t c)
 {
     const uint32_t e = c >> 3, m = c & 7u;
     return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-}
-
-// E2M1 magnitude index of a >= 0: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even index,
-// anything above 5 -> 7 (saturation).
-__device__ __forceinline__ uint32_t e2m1_rtn(float a)
-{
-    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-           (uint32_t)(a > 5.0f);
 }
 
 __device__ __forceinline__ float e2m1_val(uint32_t mag)
