@@ -21,18 +21,19 @@
 // of adjacent lanes, 64 values each: lanes 0..255 of a workgroup take the tile's 128 row
 // segments (row layout), lanes 256..511 its 128 column segments (column layout).  Six of
 // the seven butterfly stages of the Hadamard transform, the 1x16 block maxima and all but
-// the last level of the EDEN pairwise sums stay in registers; the span-64 stage and the
-// last sum level cross the lane pair with one DPP swap.  That keeps a kernel under 128
-// registers (4 waves per SIMD).  The LDS tile is stored with its 16-byte chunks
-// XOR-swizzled by row, so that both the row reads (one 16-byte chunk per lane) and the
-// column reads (one 2-byte element per lane) are free of bank conflicts.
+// the last level of the EDEN pairwise sums stay in registers; the span-64 stage is one
+// v_fmac_f32_dpp per value across the pair (the high half is read negated for it), and the
+// last sum level one DPP swap.  MS-EDEN, RTN and 4/6 fit 128 registers (4 waves per SIMD).
+// The LDS tile's 16-byte chunks are XOR-swizzled by row to spread both the row reads (one
+// 16-byte chunk per lane) and the column reads (one 2-byte element per lane) over the banks.
 //
 // Conversions use gfx950's own instructions where they compute exactly the contract's
 // rounding: v_cvt_scalef32_pk_fp4_f32 with scale 1.0 is round-to-nearest-even onto the E2M1
 // grid with saturation and the sign of its input (two codes per instruction, packed in
 // place), v_cvt_scalef32_pk_f32_fp4 decodes codes exactly, and v_cvt_pk_fp8_f32 is
 // nearest-even E4M3 below 448 (the input is clamped at 448 first).  All other steps are
-// plain binary32 arithmetic.
+// plain binary32 arithmetic.  A scaled element is formed as fma(r, rcp, +0), which turns an
+// exact zero of either sign into +0, so a code's sign bit is set exactly when r < 0.
 //
 // The global amax must be known before any scale can be rounded, so a quantization is two
 // passes over X: k_amax (rotate, per-workgroup max, one atomic max per workgroup and
