@@ -49,10 +49,15 @@ def alg_bytes(rows, cols, layouts=2):
 
 
 def kernel_source_hash():
+    """sha256 of the kernel sources with comments and whitespace removed, so that an edit
+    of a comment does not count as a change of the kernel."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"(//|#(?!include|define|pragma|if|else|endif)).*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()
 
 

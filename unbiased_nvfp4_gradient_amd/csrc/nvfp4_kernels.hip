@@ -182,14 +182,24 @@ __device__ __forceinline__ uint32_t sign_mask(const Signs &s, int p)
 }
 
 // ------------------------------------------------------------------------------ tile
-// 32 KiB.  Chunk c (8 BF16) of tile row i sits at slot i*16 + (c ^ S(i)), with
-// S(i) = (i & 15) ^ (8 * bit 6 of i): the low bits spread 16 consecutive rows over all 64
-// LDS banks for the row readers, and bit 6 separates rows i and i + 64, which the two lanes
-// of a pair read in the same instruction.
+// 32 KiB.  Chunk c (8 BF16) of tile row i sits at slot i*16 + f(i, c), with
+// f(i, c) = c ^ S(i) ^ (4 * bit 3 of c) and S(i) = (i & 15) ^ (4 * bit 6 of i).  The LDS
+// serves 32 banks of 4 bytes, i.e. 8 slots, at a time, so what matters is f mod 8: the low
+// bits of S spread consecutive rows over the banks; bit 3 of c (the row half a lane reads)
+// and bit 6 of i (rows i and i + 64, read by the two lanes of a pair in one column read)
+// each flip bit 2 of the slot, so the two lanes of a pair never share a bank in either
+// reader.
 struct Tile { uint4 chunk[TILE * CHUNKS]; };
 
-__device__ __forceinline__ int swz_key(int i) { return (i & 15) ^ (((i >> 6) & 1) << 3); }
-__device__ __forceinline__ int swz(int i, int c) { return i * CHUNKS + (c ^ swz_key(i)); }
+__device__ __forceinline__ int swz_key(int i) { return (i & 15) ^ (((i >> 6) & 1) << 2); }
+__device__ __forceinline__ int swz_slot(int i, int c) { return c ^ swz_key(i) ^ (((c >> 3) & 1) << 2); }
+__device__ __forceinline__ int swz(int i, int c) { return i * CHUNKS + swz_slot(i, c); }
+// The chunk held in slot s of row i (f(i, .) is its own kind of inverse: bit 3 survives it).
+__device__ __forceinline__ int swz_chunk(int i, int s)
+{
+    const int u = s ^ swz_key(i);
+    return u ^ (((u >> 3) & 1) << 2);
+}
 
 // Per-position fp32 sign-bit masks of the rotation (sigma_p = -1 -> 0x80000000), built
 // once per workgroup in LDS and read as broadcasts right before use.  With the rotation,
@@ -242,9 +252,10 @@ __device__ __forceinline__ void load_tile_sync(Tile &t, const uint16_t *__restri
 // Byte offsets, from a full tile's first element, of the 16-byte chunks one lane moves in
 // the direct global->LDS load (below).  With W waves, round k of wave w fills LDS slots
 // (w + W k) * 64 + lane, i.e. tile row i = i0 + 4 W k with i0 = 4 w + lane / 16 < 32, and
-// chunk (lane mod 16) XOR S(i): the low bits of S(i) are those of i0 in every round, and
-// bit 6 of i (the 8 in S) is set from row 64 on.  So a lane needs two offsets, one for the
-// rounds above row 64 and one for the rest, plus 4 W rows per round.  They fit 32 bits for
+// the chunk held in slot lane mod 16: the low bits of S(i) are those of i0 in every round,
+// and bit 6 of i (the 4 in S) is set from row 64 on, which flips bit 2 of the chunk.  So a
+// lane needs two offsets, one for the rounds above row 64 and one for the rest, plus 4 W
+// rows per round.  They fit 32 bits for
 // C <= 2^26 (2 * 31 * C + 240 < 2^32); wider rows take the general path.
 struct DmaLane { uint32_t a, b; };
 
@@ -255,11 +266,11 @@ __device__ __forceinline__ DmaLane dma_lane(int64_t C)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i0 = 4 * w + (lane >> 4);
-    const int c = (lane & 15) ^ (i0 & 15);
+    const int c = swz_chunk(i0, lane & 15);
     const uint32_t rowb = 2u * (uint32_t)i0 * (uint32_t)C;
     DmaLane d;
     d.a = rowb + 16u * (uint32_t)c;
-    d.b = rowb + 16u * (uint32_t)(c ^ 8);
+    d.b = rowb + 16u * (uint32_t)(c ^ 4);
     return d;
 }
 
@@ -290,7 +301,7 @@ __device__ __forceinline__ void stage_tile(Tile &t, const uint16_t *__restrict__
             const uint16_t *base = x + r0 * C + c0;
             for (int j = w; j < TILE * CHUNKS / 64; j += W) {
                 const int q = j * 64 + lane;               // slot filled by this lane
-                const int i = q >> 4, c = (q & 15) ^ swz_key(i);
+                const int i = q >> 4, c = swz_chunk(i, q & 15);
                 __builtin_amdgcn_global_load_lds(base + (int64_t)i * C + 8 * c,
                                                  LDS_PTR(&t.chunk[j * 64]), 16, 0, 0);
             }
@@ -316,12 +327,13 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v)
 constexpr int HALF = TILE / 2;
 
 // Row segment i, half h of the tile -> r[k] = sigma_p * x_p, p = 64h + k (exact BF16 decode,
-// sign folded in).  Chunk c of row i sits at byte i*256 + 16*(c ^ S(i)) = base_i ^ (c << 4).
+// sign folded in).  Chunk cc + 8h of row i sits at byte i*256 + 16*(cc ^ 8h ^ 4h ^ S(i))
+// = base ^ (cc << 4), with base = (i*256 + 16 S(i)) ^ (192 h).
 __device__ __forceinline__ void read_row_half(const Tile &t, const SignTable &st, int i, int h,
                                               float r[HALF])
 {
     const char *t8 = reinterpret_cast<const char *>(t.chunk);
-    const uint32_t base = opaque((uint32_t)(i * 256 + 16 * swz_key(i)) ^ (uint32_t)(h << 7));
+    const uint32_t base = opaque((uint32_t)(i * 256 + 16 * swz_key(i)) ^ (uint32_t)(h ? 192 : 0));
     const uint4 *mrow = st.mr[h];
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
@@ -339,13 +351,15 @@ __device__ __forceinline__ void read_row_half(const Tile &t, const SignTable &st
 }
 
 // Column segment j, half h -> r[k] = sigma_p * x_p, p = 64h + k.  Element (i, j) sits at
-// byte i*256 + 16*((j>>3) ^ S(i)) + 2*(j&7): for i = 64h + 16q + s, S(i) = s ^ 8h, so that
-// is off(s) + 16384h + 4096q with the lane's 8h folded into its column chunk.
+// byte i*256 + 16*f(i, J) + 2*(j&7), J = j>>3: for i = 64h + 16q + s, S(i) = s ^ 4h, so that
+// is off(s) + 16384h + 4096q with the lane's J ^ (4 * bit 3 of J) ^ 4h as its column chunk.
 __device__ __forceinline__ void read_col_half(const Tile &t, const SignTable &st, int j, int h,
                                               float r[HALF])
 {
     const char *t8 = reinterpret_cast<const char *>(t.chunk) + 16384 * h;
-    const uint32_t jc = opaque((uint32_t)(16 * ((j >> 3) ^ (h << 3)))), je = 2 * (j & 7);
+    const int J = j >> 3;
+    const uint32_t jc = opaque((uint32_t)(16 * (J ^ (((J >> 3) & 1) << 2) ^ (h << 2))));
+    const uint32_t je = 2 * (j & 7);
 #pragma unroll
     for (int s16 = 0; s16 < 16; ++s16) {
         const uint32_t off = (jc ^ (uint32_t)(16 * s16)) + (uint32_t)(256 * s16) + je;
