@@ -228,3 +228,42 @@ def test_nonfinite_inputs_complete():
         got = run_gpu(mode, xd, ("row", "col"), seed=2, rht=rht, rht_seed=2)
         for axis, (codes, scales, g, _) in got.items():
             assert scales.max() <= 0x7E, (mode, rht, axis)
+
+
+# ----------------------------------------------------------------------------- HIP graphs
+
+def test_graph_capture_and_replay():
+    """The entry points allocate nothing and clear their workspace with a kernel, so a call
+    can be captured in a HIP graph.  Each replay (with other quantizer work run eagerly in
+    between) must give the eager result bit for bit."""
+    print("case: HIP graph capture of eden_quantize + dequantize, 4 replays", flush=True)
+    x = workloads.normal((384, 512), seed=77).to(DEV)
+    other = workloads.normal((256, 256), seed=78).to(DEV)
+    ws = torch.empty(nv.workspace_bytes(384, 512, 3), dtype=torch.uint8, device=DEV)
+    out = nv.Quantized(nv.empty_layout(384, 512, DEV), nv.empty_layout(512, 384, DEV))
+    back = torch.empty((384, 512), dtype=torch.float32, device=DEV)
+    ref = nv.eden_quantize(x, 5, 6, layouts=("row", "col"))
+    ref_back = nv.dequantize(ref.row, rht=True, rht_seed=6)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(s):
+        nv.eden_quantize(x, 5, 6, layouts=("row", "col"), out=out, workspace=ws)   # warm-up
+        nv.dequantize(out.row, rht=True, rht_seed=6, out=back)
+    torch.cuda.current_stream(DEV).wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        nv.eden_quantize(x, 5, 6, layouts=("row", "col"), out=out, workspace=ws)
+        nv.dequantize(out.row, rht=True, rht_seed=6, out=back)
+    for rep in range(4):
+        for t in (out.row.codes, out.row.scales, out.col.codes, out.col.scales, back):
+            t.zero_()
+        nv.sr_quantize(other, seed=rep, layouts=("row", "col"))        # eager work between
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in ((out.row.codes, ref.row.codes), (out.row.scales, ref.row.scales),
+                          (out.col.codes, ref.col.codes), (out.col.scales, ref.col.scales),
+                          (out.row.tensor_scale, ref.row.tensor_scale),
+                          (out.col.tensor_scale, ref.col.tensor_scale), (back, ref_back)):
+            assert torch.equal(got, want), rep
