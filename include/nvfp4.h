@@ -47,6 +47,8 @@
  *               A value decodes as sign * (E4M3(scale) * g) * magnitude; with the rotation
  *               on, the decoded vector is in the rotated domain (see dequantize).
  *   group/block Must be 128 and 16 (NVFP4 1x16 blocks; 128-element rotation groups).
+ *   Aliasing.   Output buffers must not overlap one another, the input or the workspace;
+ *               overlapping buffers give undefined results.
  *   Workspace.  Device scratch of at least nvfp4_workspace_bytes() bytes, 256-byte aligned,
  *               owned by the caller.  The library clears what it uses on the stream; its
  *               contents between calls do not matter.  Concurrent calls need distinct
@@ -168,7 +170,7 @@ int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int b
  * when rotated_pair != 0 (both operands rotated along K with the same rht_seed, so
  * H H = 128 I cancels the rotation) else 1.  a is [M][K] and b is [N][K], both in the
  * row layout (K contiguous, as the quantizers emit); c is FP32 [M][N] row-major (device,
- * 4-byte aligned).  Operand values are dequantized exactly to BF16 and multiplied on the
+ * 4-byte aligned).  Operand values are dequantized exactly to FP16 and multiplied on the
  * matrix cores with FP32 accumulation (summation order unspecified).  M and N must be
  * multiples of 32 and K a multiple of 64. */
 int nvfp4_gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
