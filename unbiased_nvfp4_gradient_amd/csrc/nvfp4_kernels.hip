@@ -872,7 +872,6 @@ template <int MODE, bool ROT, int LAY>
 __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_quant(QuantArgs a)
 {
     __shared__ Tile tile0;
-    __shared__ Tile tile1;
     __shared__ SignTable st;
     __shared__ ScaleTable tabs[(LAY == LAY_BOTH) ? 2 : 1];
     const int t = threadIdx.x;
@@ -888,6 +887,21 @@ __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_q
     build_sign_table(st, a.rht_seed, ROT);
     build_scale_table(tb, g, t & 255);
     if (blockIdx.x == 0 && (t & 255) == 0) *o.g = g;
+    if constexpr (LAY != LAY_BOTH) {
+        // one layout: a single tile buffer, so that four workgroups of 4 waves fit a CU and
+        // hide each other's loads (two buffers leave room for two).  The amax pass keeps
+        // two buffers: its lighter work per tile does not cover a load.
+        for (int64_t k = blockIdx.x; k < a.tiles; k += gridDim.x) {
+            int64_t r0, c0;
+            tile_origin(a, a.tiles - 1 - k, r0, c0);
+            __syncthreads();                               // previous tile fully read
+            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+            __syncthreads();                               // tile landed
+            tile_quant<MODE, ROT>(tile0, st, tb, a, o, ro, g, rcp6g, rcp4g, r0, c0);
+        }
+        return;
+    }
+    __shared__ Tile tile1;
     int64_t k = blockIdx.x, r0, c0;
     if (k < a.tiles) {
         tile_origin(a, a.tiles - 1 - k, r0, c0);
