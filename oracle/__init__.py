@@ -71,6 +71,9 @@ def _load():
     lib.oracle_quantize_vectors.restype = i32
     lib.oracle_quantize.argtypes = [i32, P, i64, i64, i32, i32, u64, u64, P, P, P, P, P]
     lib.oracle_quantize.restype = i32
+    lib.oracle_quantize_strips.argtypes = [i32, P, i64, i64, i32, i32, u64, u64, i64, P, P, P,
+                                           P, P]
+    lib.oracle_quantize_strips.restype = i32
     lib.oracle_dequantize.argtypes = [P, P, f32, i64, i64, i32, u64, P]
     lib.oracle_dequantize.restype = i32
     lib.oracle_eden_internals.argtypes = [P, i64, i64, i32, u64, f32, i64, P, P, P, P]
@@ -241,6 +244,46 @@ def quantize(mode: str, x, axis: int = 0, seed: int = 0, rht: bool = False, rht_
     if rc != 0:
         raise ValueError(f"oracle_quantize: unsupported shape {xb.shape} for axis {axis}")
     return Quantized(codes, scales, float(g[0]), em, sm)
+
+
+class StripQuantized(NamedTuple):
+    codes: np.ndarray          # uint8 [vecs, n/2]
+    scales: np.ndarray         # uint8 [vecs, n/16]
+    g: np.ndarray              # fp32 [ceil(vecs / strip)]: strip s covers vectors s*strip ..
+    elem_margin: Optional[np.ndarray]
+    scale_margin: Optional[np.ndarray]
+
+
+def quantize_strips(mode: str, x, axis: int = 0, seed: int = 0, rht: bool = False,
+                    rht_seed: int = 0, strip: int = 128, margins: bool = True) -> StripQuantized:
+    """Strip-local quantization: each run of `strip` consecutive vectors of the layout takes
+    its FP32 scale from its own maximum (the CTA-local variant)."""
+    lib = _load()
+    xb = _bf16_bits(x)
+    rows, cols = xb.shape
+    nvec, n = (rows, cols) if axis == 0 else (cols, rows)
+    codes = np.zeros((nvec, n // 2), dtype=np.uint8)
+    scales = np.zeros((nvec, n // 16), dtype=np.uint8)
+    em = np.zeros((nvec, n), dtype=np.uint32) if margins else None
+    sm = np.zeros((nvec, n // 16), dtype=np.uint32) if margins else None
+    g = np.zeros(-(-nvec // strip), dtype=np.float32)
+    rc = lib.oracle_quantize_strips(MODES[mode], _ptr(xb), rows, cols, axis, int(rht), seed,
+                                    rht_seed, strip, _ptr(codes), _ptr(scales), _ptr(g), _ptr(em),
+                                    _ptr(sm))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_strips: unsupported shape {xb.shape} for axis {axis}")
+    return StripQuantized(codes, scales, g, em, sm)
+
+
+def dequantize_strips(codes: np.ndarray, scales: np.ndarray, g: np.ndarray, strip: int = 128,
+                      rht: bool = False, rht_seed: int = 0) -> np.ndarray:
+    """Decode strip-local outputs: vectors s*strip .. with g[s]."""
+    nvec = codes.shape[0]
+    parts = [dequantize(codes[v0:v0 + strip], scales[v0:v0 + strip], float(g[v0 // strip]),
+                        rht, rht_seed) for v0 in range(0, nvec, strip)]
+    if not parts:
+        return np.zeros((0, codes.shape[1] * 2), dtype=np.float32)
+    return np.concatenate(parts, axis=0)
 
 
 def quantize_vectors(mode: str, x, axis: int, vec_ids, g: float, seed: int = 0,

@@ -13,7 +13,9 @@
  *  [Q2-RU]  Quartet II blog paraphrase (denisavetisyan.com): "NVFP4 and micro-scaling",
  *           "MS-EDEN and randomized methods" (RHT + stochastic rounding).
  *  [FUSE]   "Format-Aware Fusion for Fast FP4 Pretraining" note (rit.work): global NVFP4
- *           max as a synchronisation point; one producer emitting both layouts.
+ *           max as a synchronisation point; one producer emitting both layouts; the
+ *           CTA-local variant (maxima inside a block of work, separate row and column
+ *           corrections applied after the GEMM's sum).
  *  [TG]     quant_prune_distill post 640 (Telegram digest), section "Method": SR definition,
  *           EDEN = random Hadamard rotation + multiplication by the ratio of the vector's
  *           scalar product with itself to the scalar product of the quantized rotated and
@@ -33,7 +35,8 @@
  * torch's float8_e4m3fn cast and brute force; E2M1 rounding against brute-force nearest;
  * SR probabilities by enumeration of every random word; EDEN ratio against fp64; 4/6
  * choice against an fp64 brute force; scaling / sign / layout invariants; MSE ordering and
- * unbiasedness statistics.  Nothing here is "parity unpinned".
+ * unbiasedness statistics; strip-local scales against the global method on one strip and
+ * per-strip power-of-two equivariance.  Nothing here is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -301,17 +304,15 @@ static void rotate_vector(float *v, int64_t n, int rht, const float sigma[GROUP]
 }
 
 /* ------------------------------------------------------------------ amax (the sync point)
- * Largest |r| over the whole layout ([FUSE]: packing waits until partial maxima are
- * collected).  Exact; the order of the max does not matter. */
-float oracle_amax(const uint16_t *x, int64_t rows, int64_t cols, int axis, int rht,
-                  uint64_t rht_seed)
+ * Largest |r| over vectors [v0, v1) of layout `axis`.  Exact; the order of the max does
+ * not matter. */
+static float range_amax(const uint16_t *x, int64_t rows, int64_t cols, int axis, int rht,
+                        const float sigma[GROUP], int64_t v0, int64_t v1)
 {
-    int64_t nvec = axis == 0 ? rows : cols, n = axis == 0 ? cols : rows;
-    float sigma[GROUP];
-    oracle_signs(rht_seed, sigma);
+    int64_t n = axis == 0 ? cols : rows;
     float amax = 0.0f;
 #pragma omp parallel for schedule(static) reduction(max : amax)
-    for (int64_t v = 0; v < nvec; ++v) {
+    for (int64_t v = v0; v < v1; ++v) {
         float buf_stack[4096];
         float *buf = buf_stack;
         float local = 0.0f;
@@ -333,6 +334,16 @@ float oracle_amax(const uint16_t *x, int64_t rows, int64_t cols, int axis, int r
         if (local > amax) amax = local;
     }
     return amax;
+}
+
+/* Largest |r| over the whole layout ([FUSE]: packing waits until the partial maxima of
+ * the whole tensor are collected). */
+float oracle_amax(const uint16_t *x, int64_t rows, int64_t cols, int axis, int rht,
+                  uint64_t rht_seed)
+{
+    float sigma[GROUP];
+    oracle_signs(rht_seed, sigma);
+    return range_amax(x, rows, cols, axis, rht, sigma, 0, axis == 0 ? rows : cols);
 }
 
 /* ------------------------------------------------------------------ one block of 16
@@ -612,6 +623,48 @@ int oracle_quantize(int mode, const uint16_t *x, int64_t rows, int64_t cols, int
     *g_out = g;
     return oracle_quantize_vectors(mode, x, rows, cols, axis, use_rht, seed, rht_seed, g,
                                    NULL, 0, codes, scales, elem_margin, scale_margin);
+}
+
+/* ------------------------------------------------------------------ strip-local scales
+ * The CTA-local variant of [FUSE]: the maximum behind the FP32 second-level scale is
+ * taken inside one block of work rather than over the whole tensor, so no block waits for
+ * the others, and the GEMM applies one correction per row block of its first operand and
+ * one per column block of its second after the sum over K.  A correction that stays fixed
+ * during that sum has to cover whole vectors, so the reading taken here: the vectors of a
+ * layout form strips of `strip` consecutive vectors (128 on the GPU, one tile), strip s
+ * takes g_s = tensor scale of max |r| over its own vectors, and each of its vectors is
+ * quantized exactly as in the global method with g_s in place of g; every random stream
+ * keeps the vector's index in the whole layout.  g_out receives ceil(vecs / strip) floats. */
+int oracle_quantize_strips(int mode, const uint16_t *x, int64_t rows, int64_t cols, int axis,
+                           int rht, uint64_t seed, uint64_t rht_seed, int64_t strip,
+                           uint8_t *codes, uint8_t *scales, float *g_out,
+                           uint32_t *elem_margin, uint32_t *scale_margin)
+{
+    int64_t n = axis == 0 ? cols : rows;
+    int64_t total = axis == 0 ? rows : cols;
+    int use_rht = rht || mode == MODE_EDEN;
+    if (strip <= 0 || n % BLOCK) return -2;
+    if (use_rht && n % GROUP) return -2;
+    float sigma[GROUP];
+    oracle_signs(rht_seed, sigma);
+    for (int64_t v0 = 0; v0 < total; v0 += strip) {
+        int64_t v1 = (total - v0) < strip ? total : v0 + strip;
+        float g = oracle_tensor_scale(mode, range_amax(x, rows, cols, axis, use_rht, sigma,
+                                                       v0, v1));
+        g_out[v0 / strip] = g;
+        if (n == 0) continue;
+        int64_t *ids = (int64_t *)malloc(sizeof(int64_t) * (size_t)(v1 - v0));
+        if (!ids) return -2;
+        for (int64_t v = v0; v < v1; ++v) ids[v - v0] = v;
+        int rc = oracle_quantize_vectors(mode, x, rows, cols, axis, use_rht, seed, rht_seed, g,
+                                         ids, v1 - v0, codes + v0 * (n / 2),
+                                         scales + v0 * (n / BLOCK),
+                                         elem_margin ? elem_margin + v0 * n : NULL,
+                                         scale_margin ? scale_margin + v0 * (n / BLOCK) : NULL);
+        free(ids);
+        if (rc) return rc;
+    }
+    return 0;
 }
 
 /* Dequantize nvec vectors of length n: value = sign * (s * g) * V[mag]; with the
