@@ -3,8 +3,8 @@
  *
  * The library implements the hot path of Quartet II, the MS-EDEN unbiased NVFP4 quantizer,
  * with the plain stochastic-rounding (SR) baseline, round-to-nearest (RTN), the forward-pass
- * "4/6" grid choice, a producer that emits both packed layouts in one pass, and a
- * dequantizer.  Definitions follow the pages summarising "Quartet II: Accurate LLM
+ * "4/6" grid choice, a producer that emits both packed layouts in one pass, a dequantizer,
+ * a GEMM check consumer, and the strip-local ("CTA-local") scaling variant of each.  Definitions follow the pages summarising "Quartet II: Accurate LLM
  * Pre-Training in NVFP4 by Improved Unbiased Gradient Estimation":
  *   - Telegram digest quant_prune_distill post 640, section "Method": SR; EDEN (random
  *     Hadamard rotation, then multiplication by <x,x> / <Q(Rx), Rx>); stochastic rounding of
@@ -175,6 +175,46 @@ int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int b
  * multiples of 32 and K a multiple of 64. */
 int nvfp4_gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
                      int64_t K, int rotated_pair, float *c, void *stream);
+
+/* ------------------------------------------------------------------ strip-local scales
+ * The CTA-local variant in the rit.work note on "Format-Aware Fusion for Fast FP4
+ * Pretraining" (section "speedup is lost between matmuls"): the maximum behind the FP32
+ * second-level scale is taken inside one block of work instead of over the whole tensor, so
+ * no block waits for the tensor-wide maximum, and the GEMM applies separate row and column
+ * corrections after its sum over K.  The note's closing section adds that this changes the
+ * numerical contract and has to be evaluated as a training recipe of its own.  Reading taken here: a correction that stays
+ * fixed during the sum over K covers whole vectors, so each layout's vectors form strips of
+ * 128 consecutive vectors (one tile row of X for the row layout, one tile column for the
+ * column layout), and strip s has its own g_s = max |r| over the strip / 2688 (/ 1792 for
+ * 4/6).  Every vector is then quantized exactly as by the quantizer of the same mode with
+ * g_s in place of g; random streams keep the vector's index in the whole layout.
+ *
+ * Outputs differ from nvfp4_tensor's global form in one field: tensor_scale points to
+ * ceil(vecs / 128) floats (4-byte aligned), g of vector v being tensor_scale[v / 128]. */
+
+/* Workspace bytes of nvfp4_quantize_strips for a rows x cols input: 4 bytes per row strip and
+ * per column strip, at least 256.  Never fails. */
+size_t nvfp4_strip_workspace_bytes(int64_t rows, int64_t cols, int layouts_mask);
+
+/* Quantizer `mode` (NVFP4_MODE_*) with strip-local scales.  Arguments, shapes, seeds, errors
+ * and the two layouts as for the one-call quantizers (rht is taken as 1 for MS-EDEN; seed is
+ * unused by RTN and 4/6); the workspace must hold nvfp4_strip_workspace_bytes() bytes.  Two
+ * launches: the rotated maximum of every strip, then the quantization, whose workgroups each
+ * read the maxima of their tile's strips. */
+int nvfp4_quantize_strips(int mode, const void *x_bf16, int64_t rows, int64_t cols, int group,
+                          int block, uint64_t seed, int rht, uint64_t rht_seed,
+                          const nvfp4_tensor *row_out, const nvfp4_tensor *col_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* dequantize() for strip-local outputs: vector v decodes with tensor_scale[v / 128]. */
+int dequantize_strips(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int block,
+                      int rht, uint64_t rht_seed, float *out, void *stream);
+
+/* nvfp4_gemm_check() for strip-local operands: C[m][n] = f * gA[m / 128] * gB[n / 128] *
+ * sum_k a(m,k) * b(n,k), the row correction of A and the column correction of B applied after
+ * the sum over K.  a and b are row layouts of nvfp4_quantize_strips ([M][K] and [N][K]). */
+int nvfp4_gemm_check_strips(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
+                            int64_t K, int rotated_pair, float *c, void *stream);
 
 #ifdef __cplusplus
 }

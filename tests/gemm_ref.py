@@ -17,9 +17,15 @@ def exact_rows(t, rows):
     return E2M1[codes] * np.repeat(scales, 16, axis=1)
 
 
-def check_entries(c, a, b, rows, cols, f):
-    """C[rows][cols] of C = f * gA * gB * A B^T against the exact product, within the bound."""
-    ga, gb = float(a.tensor_scale.cpu()[0]), float(b.tensor_scale.cpu()[0])
+def check_entries(c, a, b, rows, cols, f, strips=False):
+    """C[rows][cols] of C = f * gA * gB * A B^T against the exact product, within the bound.
+    With strips=True, gA and gB are per 128 rows of each operand (strip-local scales)."""
+    rows, cols = np.asarray(rows), np.asarray(cols)
+    if strips:
+        ga = a.tensor_scale.cpu().numpy().astype(np.float64)[rows // 128][:, None]
+        gb = b.tensor_scale.cpu().numpy().astype(np.float64)[cols // 128][None, :]
+    else:
+        ga, gb = float(a.tensor_scale.cpu()[0]), float(b.tensor_scale.cpu()[0])
     A = exact_rows(a, rows)
     B = exact_rows(b, cols)
     ref = (A @ B.T) * ga * gb * f

@@ -9,7 +9,8 @@ Layouts: ``"row"`` quantizes the rows of X (groups along the columns), ``"col"``
 columns (groups along the rows, i.e. the row layout of X^T); each layout has its own tensor
 scale and random stream.  Results are ``NVFP4`` triples of device tensors:
 codes uint8 [vecs, n/2] (low nibble = even position), scales uint8 [vecs, n/16] (E4M3FN
-bits; ``.view(torch.float8_e4m3fn)`` works), tensor_scale float32 [1].
+bits; ``.view(torch.float8_e4m3fn)`` works), tensor_scale float32 [1] (with strip-local
+scales, ``nvfp4_quantize_strips``: float32 [ceil(vecs / 128)], one per 128 vectors).
 """
 from __future__ import annotations
 
@@ -31,7 +32,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_ARG =
 
 EXPORTED = ("nvfp4_workspace_bytes", "nvfp4_strerror", "eden_quantize", "sr_quantize",
             "rtn_quantize", "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize",
-            "nvfp4_gemm_check")
+            "nvfp4_gemm_check", "nvfp4_strip_workspace_bytes", "nvfp4_quantize_strips",
+            "dequantize_strips", "nvfp4_gemm_check_strips")
 
 MODE_RTN, MODE_SR, MODE_EDEN, MODE_FP46 = 0, 1, 2, 3
 MODES = {"rtn": MODE_RTN, "sr": MODE_SR, "eden": MODE_EDEN, "fp46": MODE_FP46}
@@ -86,8 +88,15 @@ def lib() -> ctypes.CDLL:
     h.nvfp4_amax.argtypes = [P, i64, i64, i32, i32, i32, u64, i32, P, P]
     h.nvfp4_quantize_amax.argtypes = [i32, P, i64, i64, i32, i32, u64, i32, u64, P, TP, TP, P]
     h.nvfp4_gemm_check.argtypes = [TP, TP, i64, i64, i64, i32, P, P]
+    h.nvfp4_strip_workspace_bytes.argtypes = [i64, i64, i32]
+    h.nvfp4_strip_workspace_bytes.restype = sz
+    h.nvfp4_quantize_strips.argtypes = [i32, P, i64, i64, i32, i32, u64, i32, u64, TP, TP, P, sz,
+                                        P]
+    h.dequantize_strips.argtypes = [TP, i64, i64, i32, i32, i32, u64, P, P]
+    h.nvfp4_gemm_check_strips.argtypes = [TP, TP, i64, i64, i64, i32, P, P]
     for name in ("eden_quantize", "sr_quantize", "rtn_quantize", "fp46_quantize", "dequantize",
-                 "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_gemm_check"):
+                 "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_gemm_check",
+                 "nvfp4_quantize_strips", "dequantize_strips", "nvfp4_gemm_check_strips"):
         getattr(h, name).restype = i32
     _lib_handle = h
     return h
@@ -221,6 +230,66 @@ def dequantize(t: NVFP4, rht: bool = False, rht_seed: int = 0,
     return out
 
 
+def strip_workspace_bytes(rows: int, cols: int, layouts_mask: int = 3) -> int:
+    return int(lib().nvfp4_strip_workspace_bytes(rows, cols, layouts_mask))
+
+
+def empty_strip_layout(vecs: int, n: int, device) -> NVFP4:
+    """Caller-side allocation of one strip-local layout (one g per 128 vectors)."""
+    return NVFP4(torch.empty((vecs, n // 2), dtype=torch.uint8, device=device),
+                 torch.empty((vecs, n // BLOCK), dtype=torch.uint8, device=device),
+                 torch.empty(((vecs + GROUP - 1) // GROUP,), dtype=torch.float32, device=device))
+
+
+def nvfp4_quantize_strips(mode: str, x: torch.Tensor, seed: int = 0, rht: bool = False,
+                          rht_seed: int = 0, layouts=("row", "col"),
+                          out: Optional[Quantized] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> Quantized:
+    """Quantizer `mode` ("rtn", "sr", "eden", "fp46") with strip-local scales: each run of
+    128 vectors of a layout has its own tensor_scale entry (the CTA-local variant)."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
+    rows, cols = x.shape
+    if out is None:
+        out = Quantized(empty_strip_layout(rows, cols, x.device) if "row" in layouts else None,
+                        empty_strip_layout(cols, rows, x.device) if "col" in layouts else None)
+    if workspace is None:
+        workspace = torch.empty(strip_workspace_bytes(rows, cols), dtype=torch.uint8,
+                                device=x.device)
+    _check("nvfp4_quantize_strips", lib().nvfp4_quantize_strips(
+        MODES[mode], x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
+        _ct(out.row), _ct(out.col), workspace.data_ptr(), workspace.numel(),
+        _stream_ptr(stream, x.device)))
+    return out
+
+
+def dequantize_strips(t: NVFP4, rht: bool = False, rht_seed: int = 0,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode one strip-local layout to float32 [vecs, n]."""
+    vecs, n = t.codes.shape[0], t.codes.shape[1] * 2
+    if out is None:
+        out = torch.empty((vecs, n), dtype=torch.float32, device=t.codes.device)
+    _check("dequantize_strips", lib().dequantize_strips(
+        _ct(t), vecs, n, GROUP, BLOCK, int(bool(rht)), rht_seed, out.data_ptr(),
+        _stream_ptr(stream, t.codes.device)))
+    return out
+
+
+def nvfp4_gemm_check_strips(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
+                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """C = A B^T of two strip-local row-layout operands, FP32 [M, N]."""
+    M, K = a.codes.shape[0], a.codes.shape[1] * 2
+    N = b.codes.shape[0]
+    if b.codes.shape[1] * 2 != K:
+        raise ValueError("operands disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+    _check("nvfp4_gemm_check_strips", lib().nvfp4_gemm_check_strips(
+        _ct(a), _ct(b), M, N, K, int(bool(rotated_pair)), out.data_ptr(),
+        _stream_ptr(stream, a.codes.device)))
+    return out
+
+
 def nvfp4_gemm_check(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """C = A B^T of two row-layout NVFP4 operands ([M, K] and [N, K]), FP32 [M, N]."""
@@ -238,5 +307,6 @@ def nvfp4_gemm_check(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
 
 __all__ = ["NVFP4", "Quantized", "NVFP4Error", "eden_quantize", "sr_quantize", "rtn_quantize",
            "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize", "nvfp4_gemm_check",
-           "workspace_bytes", "strerror", "empty_layout", "lib",
-           "LIB_PATH", "EXPORTED"]
+           "nvfp4_quantize_strips", "dequantize_strips", "nvfp4_gemm_check_strips",
+           "workspace_bytes", "strip_workspace_bytes", "strerror", "empty_layout",
+           "empty_strip_layout", "lib", "LIB_PATH", "EXPORTED"]

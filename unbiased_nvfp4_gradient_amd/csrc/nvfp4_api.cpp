@@ -6,19 +6,20 @@
 
 #include "nvfp4.h"
 
-extern "C" hipError_t nvfp4k_amax(int rht, int layouts, const void *x, int64_t R, int64_t C,
-                                  float *amax, uint64_t rht_seed, hipStream_t st);
-extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x, int64_t R,
-                                   int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
-                                   uint8_t *codes1, uint8_t *scales1, float *g1,
+extern "C" int64_t nvfp4k_amax_slots(int local, int64_t R, int64_t C);
+extern "C" hipError_t nvfp4k_amax(int local, int rht, int layouts, const void *x, int64_t R,
+                                  int64_t C, float *amax, uint64_t rht_seed, hipStream_t st);
+extern "C" hipError_t nvfp4k_quant(int local, int mode, int rht, int layouts, const void *x,
+                                   int64_t R, int64_t C, uint8_t *codes0, uint8_t *scales0,
+                                   float *g0, uint8_t *codes1, uint8_t *scales1, float *g1,
                                    const float *amax, uint64_t seed, uint64_t rht_seed,
                                    hipStream_t st);
-extern "C" hipError_t nvfp4k_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
+extern "C" hipError_t nvfp4k_gemm(int local, const uint8_t *a_codes, const uint8_t *a_scales,
                                   const float *a_g, const uint8_t *b_codes,
                                   const uint8_t *b_scales, const float *b_g, int64_t M,
                                   int64_t N, int64_t K, int rotated_pair, float *c,
                                   hipStream_t st);
-extern "C" hipError_t nvfp4k_dequantize(const uint8_t *codes, const uint8_t *scales,
+extern "C" hipError_t nvfp4k_dequantize(int local, const uint8_t *codes, const uint8_t *scales,
                                         const float *g, int64_t vecs, int64_t n, int rht,
                                         uint64_t rht_seed, float *out, hipStream_t st);
 
@@ -81,14 +82,14 @@ int check_outputs(const nvfp4_tensor *row_out, const nvfp4_tensor *col_out, int6
     return rc ? rc : check_layout(col_out, empty);
 }
 
-int launch_quant(int mode, const void *x, int64_t rows, int64_t cols, uint64_t seed, int rht,
-                 uint64_t rht_seed, const float *amax, const nvfp4_tensor *row_out,
+int launch_quant(int local, int mode, const void *x, int64_t rows, int64_t cols, uint64_t seed,
+                 int rht, uint64_t rht_seed, const float *amax, const nvfp4_tensor *row_out,
                  const nvfp4_tensor *col_out, void *stream)
 {
     const int layouts = (row_out ? 1 : 0) | (col_out ? 2 : 0);
     const bool rotated = rht || mode == MODE_EDEN;
     hipError_t e = nvfp4k_quant(
-        mode, rotated ? 1 : 0, layouts, x, rows, cols, row_out ? row_out->codes : nullptr,
+        local, mode, rotated ? 1 : 0, layouts, x, rows, cols, row_out ? row_out->codes : nullptr,
         row_out ? row_out->scales : nullptr, row_out ? row_out->tensor_scale : nullptr,
         col_out ? col_out->codes : nullptr, col_out ? col_out->scales : nullptr,
         col_out ? col_out->tensor_scale : nullptr, amax, seed, rht_seed,
@@ -96,27 +97,81 @@ int launch_quant(int mode, const void *x, int64_t rows, int64_t cols, uint64_t s
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-int quantize_common(int mode, const void *x, int64_t rows, int64_t cols, int group, int block,
-                    uint64_t seed, int rht, uint64_t rht_seed, const nvfp4_tensor *row_out,
-                    const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
-                    void *stream)
+// Workspace of the strip-local quantizer: one u32 slot per row strip and per column strip
+// of 128, padded to 256 bytes.
+size_t strip_workspace_bytes(int64_t rows, int64_t cols)
+{
+    if (rows < 0 || cols < 0) return WORKSPACE_BYTES;
+    const size_t b = 4 * (size_t)nvfp4k_amax_slots(1, rows, cols);
+    return b < WORKSPACE_BYTES ? WORKSPACE_BYTES : (b + 255) / 256 * 256;
+}
+
+int quantize_common(int local, int mode, const void *x, int64_t rows, int64_t cols, int group,
+                    int block, uint64_t seed, int rht, uint64_t rht_seed,
+                    const nvfp4_tensor *row_out, const nvfp4_tensor *col_out, void *workspace,
+                    size_t workspace_bytes, void *stream)
 {
     int rc = check_outputs(row_out, col_out, rows, cols);
     if (rc) return rc;
     rc = check_input(mode, x, rows, cols, group, block, rht, row_out != nullptr,
                      col_out != nullptr);
     if (rc) return rc;
-    if (!workspace || workspace_bytes < WORKSPACE_BYTES) return NVFP4_ERR_WORKSPACE;
+    const size_t need = local ? strip_workspace_bytes(rows, cols) : WORKSPACE_BYTES;
+    if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
     rc = check_device();
     if (rc) return rc;
     const int layouts = (row_out ? 1 : 0) | (col_out ? 2 : 0);
     const bool rotated = rht || mode == MODE_EDEN;
     float *amax = static_cast<float *>(workspace);
-    hipError_t e = nvfp4k_amax(rotated ? 1 : 0, layouts, x, rows, cols, amax, rht_seed,
+    hipError_t e = nvfp4k_amax(local, rotated ? 1 : 0, layouts, x, rows, cols, amax, rht_seed,
                                static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return NVFP4_ERR_HIP;
-    return launch_quant(mode, x, rows, cols, seed, rht, rht_seed, amax, row_out, col_out, stream);
+    return launch_quant(local, mode, x, rows, cols, seed, rht, rht_seed, amax, row_out, col_out,
+                        stream);
+}
+
+int dequantize_common(int local, const nvfp4_tensor *in, int64_t vecs, int64_t n, int group,
+                      int block, int rht, uint64_t rht_seed, float *out, void *stream)
+{
+    if (!in || !in->tensor_scale) return NVFP4_ERR_NULL;
+    if ((vecs > 0 && n > 0) && (!out || !in->codes || !in->scales)) return NVFP4_ERR_NULL;
+    if (group != 128 || block != 16) return NVFP4_ERR_GROUP;
+    if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
+    if (vecs < 0 || n < 0) return NVFP4_ERR_SHAPE;
+    if (vecs > MAX_DIM || n > MAX_DIM || (vecs > 0 && n > MAX_ELEMS / vecs)) return NVFP4_ERR_ARG;
+    if (n % (rht ? 128 : 16)) return NVFP4_ERR_SHAPE;
+    if (!aligned(in->codes, 8) || !aligned(in->scales, 1) || !aligned(in->tensor_scale, 4) ||
+        !aligned(out, 16))
+        return NVFP4_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = nvfp4k_dequantize(local, in->codes, in->scales, in->tensor_scale, vecs, n,
+                                     rht, rht_seed, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+int gemm_common(int local, const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
+                int64_t K, int rotated_pair, float *c, void *stream)
+{
+    if (!a || !b || !a->tensor_scale || !b->tensor_scale) return NVFP4_ERR_NULL;
+    if (rotated_pair != 0 && rotated_pair != 1) return NVFP4_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
+    if (M > MAX_DIM || N > MAX_DIM || K > MAX_DIM || (M > 0 && N > MAX_ELEMS / M) ||
+        (M > 0 && K > MAX_ELEMS / M) || (N > 0 && K > MAX_ELEMS / N))
+        return NVFP4_ERR_ARG;
+    if (M % 32 || N % 32 || K % 64) return NVFP4_ERR_SHAPE;
+    if (M > 0 && N > 0 && (!c || (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
+        return NVFP4_ERR_NULL;
+    if (!aligned(a->codes, 16) || !aligned(b->codes, 16) || !aligned(c, 4) ||
+        !aligned(a->tensor_scale, 4) || !aligned(b->tensor_scale, 4))
+        return NVFP4_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    hipError_t e = nvfp4k_gemm(local, a->codes, a->scales, a->tensor_scale, b->codes, b->scales,
+                               b->tensor_scale, M, N, K, rotated_pair, c,
+                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 }  // namespace
@@ -151,7 +206,7 @@ int eden_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int
                   const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
                   void *stream)
 {
-    return quantize_common(MODE_EDEN, x_bf16, rows, cols, group, block, seed, 1, rht_seed,
+    return quantize_common(0, MODE_EDEN, x_bf16, rows, cols, group, block, seed, 1, rht_seed,
                            row_out, col_out, workspace, workspace_bytes, stream);
 }
 
@@ -160,7 +215,7 @@ int sr_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int b
                 const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
                 void *stream)
 {
-    return quantize_common(MODE_SR, x_bf16, rows, cols, group, block, seed, rht, rht_seed,
+    return quantize_common(0, MODE_SR, x_bf16, rows, cols, group, block, seed, rht, rht_seed,
                            row_out, col_out, workspace, workspace_bytes, stream);
 }
 
@@ -168,7 +223,7 @@ int rtn_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int 
                  uint64_t rht_seed, const nvfp4_tensor *row_out, const nvfp4_tensor *col_out,
                  void *workspace, size_t workspace_bytes, void *stream)
 {
-    return quantize_common(MODE_RTN, x_bf16, rows, cols, group, block, 0, rht, rht_seed,
+    return quantize_common(0, MODE_RTN, x_bf16, rows, cols, group, block, 0, rht, rht_seed,
                            row_out, col_out, workspace, workspace_bytes, stream);
 }
 
@@ -176,7 +231,7 @@ int fp46_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int
                   uint64_t rht_seed, const nvfp4_tensor *row_out, const nvfp4_tensor *col_out,
                   void *workspace, size_t workspace_bytes, void *stream)
 {
-    return quantize_common(MODE_FP46, x_bf16, rows, cols, group, block, 0, rht, rht_seed,
+    return quantize_common(0, MODE_FP46, x_bf16, rows, cols, group, block, 0, rht, rht_seed,
                            row_out, col_out, workspace, workspace_bytes, stream);
 }
 
@@ -191,7 +246,7 @@ int nvfp4_amax(const void *x_bf16, int64_t rows, int64_t cols, int group, int bl
     if (!aligned(amax, 4)) return NVFP4_ERR_ALIGN;
     rc = check_device();
     if (rc) return rc;
-    hipError_t e = nvfp4k_amax(rht, layouts_mask, x_bf16, rows, cols, amax, rht_seed,
+    hipError_t e = nvfp4k_amax(0, rht, layouts_mask, x_bf16, rows, cols, amax, rht_seed,
                                static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
@@ -209,51 +264,47 @@ int nvfp4_quantize_amax(int mode, const void *x_bf16, int64_t rows, int64_t cols
     if (!aligned(amax, 4)) return NVFP4_ERR_ALIGN;
     rc = check_device();
     if (rc) return rc;
-    return launch_quant(mode, x_bf16, rows, cols, seed, rht, rht_seed, amax, row_out, col_out,
+    return launch_quant(0, mode, x_bf16, rows, cols, seed, rht, rht_seed, amax, row_out, col_out,
                         stream);
 }
 
 int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int block, int rht,
                uint64_t rht_seed, float *out, void *stream)
 {
-    if (!in || !in->tensor_scale) return NVFP4_ERR_NULL;
-    if ((vecs > 0 && n > 0) && (!out || !in->codes || !in->scales)) return NVFP4_ERR_NULL;
-    if (group != 128 || block != 16) return NVFP4_ERR_GROUP;
-    if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
-    if (vecs < 0 || n < 0) return NVFP4_ERR_SHAPE;
-    if (vecs > MAX_DIM || n > MAX_DIM || (vecs > 0 && n > MAX_ELEMS / vecs)) return NVFP4_ERR_ARG;
-    if (n % (rht ? 128 : 16)) return NVFP4_ERR_SHAPE;
-    if (!aligned(in->codes, 8) || !aligned(in->scales, 1) || !aligned(in->tensor_scale, 4) ||
-        !aligned(out, 16))
-        return NVFP4_ERR_ALIGN;
-    int rc = check_device();
-    if (rc) return rc;
-    hipError_t e = nvfp4k_dequantize(in->codes, in->scales, in->tensor_scale, vecs, n, rht,
-                                     rht_seed, out, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    return dequantize_common(0, in, vecs, n, group, block, rht, rht_seed, out, stream);
 }
 
 int nvfp4_gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
                      int64_t K, int rotated_pair, float *c, void *stream)
 {
-    if (!a || !b || !a->tensor_scale || !b->tensor_scale) return NVFP4_ERR_NULL;
-    if (rotated_pair != 0 && rotated_pair != 1) return NVFP4_ERR_ARG;
-    if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
-    if (M > MAX_DIM || N > MAX_DIM || K > MAX_DIM || (M > 0 && N > MAX_ELEMS / M) ||
-        (M > 0 && K > MAX_ELEMS / M) || (N > 0 && K > MAX_ELEMS / N))
-        return NVFP4_ERR_ARG;
-    if (M % 32 || N % 32 || K % 64) return NVFP4_ERR_SHAPE;
-    if (M > 0 && N > 0 && (!c || (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
-        return NVFP4_ERR_NULL;
-    if (!aligned(a->codes, 16) || !aligned(b->codes, 16) || !aligned(c, 4) ||
-        !aligned(a->tensor_scale, 4) || !aligned(b->tensor_scale, 4))
-        return NVFP4_ERR_ALIGN;
-    int rc = check_device();
-    if (rc) return rc;
-    hipError_t e = nvfp4k_gemm(a->codes, a->scales, a->tensor_scale, b->codes, b->scales,
-                               b->tensor_scale, M, N, K, rotated_pair, c,
-                               static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    return gemm_common(0, a, b, M, N, K, rotated_pair, c, stream);
+}
+
+size_t nvfp4_strip_workspace_bytes(int64_t rows, int64_t cols, int layouts_mask)
+{
+    (void)layouts_mask;
+    return strip_workspace_bytes(rows, cols);
+}
+
+int nvfp4_quantize_strips(int mode, const void *x_bf16, int64_t rows, int64_t cols, int group,
+                          int block, uint64_t seed, int rht, uint64_t rht_seed,
+                          const nvfp4_tensor *row_out, const nvfp4_tensor *col_out,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    return quantize_common(1, mode, x_bf16, rows, cols, group, block, seed, rht, rht_seed,
+                           row_out, col_out, workspace, workspace_bytes, stream);
+}
+
+int dequantize_strips(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int block,
+                      int rht, uint64_t rht_seed, float *out, void *stream)
+{
+    return dequantize_common(1, in, vecs, n, group, block, rht, rht_seed, out, stream);
+}
+
+int nvfp4_gemm_check_strips(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
+                            int64_t K, int rotated_pair, float *c, void *stream)
+{
+    return gemm_common(1, a, b, M, N, K, rotated_pair, c, stream);
 }
 
 }  // extern "C"

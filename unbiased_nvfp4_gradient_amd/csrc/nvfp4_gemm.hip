@@ -9,7 +9,10 @@
 // [2^-10, 2688], so the FP16 operand is exact.  v_mfma_f32_32x32x16_f16 multiplies exactly
 // and accumulates in FP32; the two FP32 tensor scales (and 2^-7 when both operands carry
 // the same random-sign Hadamard rotation along K, since H H = 128 I) are applied in the
-// epilogue.
+// epilogue.  With strip-local scales (the CTA-local variant of the rit.work note on
+// "Format-Aware Fusion for Fast FP4 Pretraining": separate row and column corrections applied
+// after the sum over K) an operand has one g per 128 rows, and the epilogue takes the g of
+// the output row's strip of A and of the output column's strip of B.
 //
 // Tiling: a C tile of 256 x 256 per workgroup of 8 waves, each wave a 64 x 128 sub-tile
 // (2 x 4 MFMA 32x32 tiles, 128 FP32 accumulators per lane); K in steps of 64 (four 1x16
@@ -33,7 +36,8 @@ constexpr int STAGE = (BM + BN) * LDS_ROW;   // halfs of one A + B stage
 struct Operand {
     const uint8_t *codes;    // [rows][K/2]
     const uint8_t *scales;   // [rows][K/16]
-    const float *g;
+    const float *g;          // g of row r: g[r >> g_shift]
+    int g_shift;             // 7 (one g per 128 rows) or 62 (one g)
 };
 
 // One thread's share of a 256 x 64 operand slice: row t/2, elements 32*(t%2) .. +31,
@@ -166,7 +170,11 @@ __global__ void __launch_bounds__(512, 1) k_gemm(Operand A, Operand B, int64_t M
         }
     }
 
-    const float scale = (*A.g * *B.g) * f;
+    // a wave's 64 rows and 128 columns each lie inside one 128-row strip of their operand
+    const int64_t mw = m0 + wm, nw = n0 + wn;
+    const float ga = mw < M ? A.g[mw >> A.g_shift] : 0.0f;
+    const float gb = nw < N ? B.g[nw >> B.g_shift] : 0.0f;
+    const float scale = (ga * gb) * f;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -183,7 +191,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm(Operand A, Operand B, int64_t M
 
 }  // namespace nvfp4g
 
-extern "C" hipError_t nvfp4k_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
+extern "C" hipError_t nvfp4k_gemm(int local, const uint8_t *a_codes, const uint8_t *a_scales,
                                   const float *a_g, const uint8_t *b_codes,
                                   const uint8_t *b_scales, const float *b_g, int64_t M,
                                   int64_t N, int64_t K, int rotated_pair, float *c,
@@ -191,7 +199,8 @@ extern "C" hipError_t nvfp4k_gemm(const uint8_t *a_codes, const uint8_t *a_scale
 {
     using namespace nvfp4g;
     if (M == 0 || N == 0) return hipSuccess;
-    const Operand A{a_codes, a_scales, a_g}, B{b_codes, b_scales, b_g};
+    const int shift = local ? 7 : 62;
+    const Operand A{a_codes, a_scales, a_g, shift}, B{b_codes, b_scales, b_g, shift};
     const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     k_gemm<<<grid, 512, 0, st>>>(A, B, M, N, K, rotated_pair ? 0.0078125f : 1.0f, c);
     return hipGetLastError();

@@ -40,6 +40,13 @@
 // layout into the workspace) then k_quant (rotate again, quantize, pack, store).  k_quant
 // walks the tiles in the reverse order, so its first tiles are those k_amax touched last,
 // which are the likeliest to still sit in the last-level cache.
+//
+// Strip-local scales (the CTA-local variant of the rit.work note on "Format-Aware Fusion for
+// Fast FP4 Pretraining": maxima inside a block of work, row and column corrections applied
+// after the GEMM's sum over K) take the same two passes with LOCAL = true: k_amax folds each
+// tile's maximum into the slot of its strip (128 consecutive vectors: one tile row for the row
+// layout, one tile column for the column layout), and k_quant rebuilds its scale table for
+// every tile from that tile's strip maxima.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <cstdlib>
@@ -458,8 +465,17 @@ __device__ __forceinline__ float block_max(const float *r)
 
 // Per-workgroup table over the 127 E4M3 codes: (scale value s, den = s*g, rcp(den)).  Code
 // 0 gets rcp = 0: a block with scale 0 then scales every element to +0 and rounds it to code
-// 0x0, which is what the contract prescribes for it, without a select.
-struct ScaleTable { float4 e[128]; };
+// 0x0, which is what the contract prescribes for it, without a select.  gs holds the tensor
+// scale itself and the reciprocals of 6g and 4g.
+struct ScaleTable {
+    float4 e[128];
+    float4 gs;     // (g, rcp(6g), rcp(4g), 0)
+};
+
+__device__ __forceinline__ float4 scale_consts(float g)
+{
+    return make_float4(g, clamped_rcp(6.0f * g), clamped_rcp(4.0f * g), 0.0f);
+}
 
 __device__ __forceinline__ void build_scale_table(ScaleTable &tb, float g, int tid)
 {
@@ -467,6 +483,7 @@ __device__ __forceinline__ void build_scale_table(ScaleTable &tb, float g, int t
         const float sv = e4m3_val((uint32_t)tid);
         const float den = sv * g;
         tb.e[tid] = make_float4(sv, den, tid ? clamped_rcp(den) : 0.0f, 0.0f);
+        if (tid == 0) tb.gs = scale_consts(g);
     }
 }
 
@@ -474,16 +491,18 @@ __device__ __forceinline__ void build_scale_table(ScaleTable &tb, float g, int t
 struct LayoutOut {
     uint8_t *codes;    // [vecs][n/2]
     uint8_t *scales;   // [vecs][n/16]
-    float *g;          // [1]
+    float *g;          // [1], or [ceil(vecs/128)] with strip-local scales
 };
 
 struct QuantArgs {
     const uint16_t *x;
     int64_t R, C;
     LayoutOut out[2];          // [0] row layout, [1] column layout
-    uint32_t *amax_bits;       // [0] row, [1] column: fp32 bits of max |r| (phase 1 output)
+    // fp32 bits of max |r| (phase 1 output): [0] row, [1] column; with strip-local scales
+    // [tiles_r] row strips, then [tiles_c] column strips
+    uint32_t *amax_bits;
     uint64_t seed, rht_seed;
-    int64_t tiles_c, tiles;    // tiles per tile-row, total tiles
+    int64_t tiles_r, tiles_c, tiles;   // tile rows, tiles per tile row, total tiles
     int64_t dma_fast_max_c;    // rows up to this many elements use the precomputed loads
 };
 
@@ -511,9 +530,11 @@ __device__ __forceinline__ Role lane_role()
 }
 
 // ------------------------------------------------------------------------------ kernels
-__global__ void k_zero_u32(uint32_t *p, int n)
+__global__ void k_zero_u32(uint32_t *p, int64_t n)
 {
-    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
 }
 
 // Tensor scales of an empty input: g = amax / D for each requested layout.
@@ -557,10 +578,27 @@ __device__ __forceinline__ float tile_amax(const Tile &tile, const SignTable &st
     return fmaxf(m0, m1);
 }
 
+// Slot of the strip that tile (r0, c0) belongs to, for this lane's layout.
+__device__ __forceinline__ int64_t strip_slot(const QuantArgs &a, int lay, int64_t r0,
+                                              int64_t c0)
+{
+    return lay == 0 ? r0 / TILE : a.tiles_r + c0 / TILE;
+}
+
+// Strip-local scales: fold a lane's maximum over one tile into its strip's slot, one atomic
+// per wave (a wave's lanes share the layout and the tile).
+__device__ __forceinline__ void strip_max(const QuantArgs &a, const Role &ro, int64_t r0,
+                                          int64_t c0, float m)
+{
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0)
+        atomicMax(&a.amax_bits[strip_slot(a, ro.lay, r0, c0)], __float_as_uint(m));
+}
+
 // Pass 1: amax of |r| per layout.  Persistent workgroups walk the tiles with two LDS
 // buffers (the next tile streams in while the current one is processed); one atomicMax
-// per workgroup and layout at the end.
-template <bool ROT, int LAY>
+// per workgroup and layout at the end, or per wave and tile into the tile's strip (LOCAL).
+template <bool ROT, int LAY, bool LOCAL>
 __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
 {
     __shared__ Tile tile0;
@@ -587,7 +625,11 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
             tile_origin(a, k1, r1, c1);
             stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
         }
-        local = fmaxf(local, tile_amax<ROT>(tile0, st, a, ro, r0, c0));
+        {
+            const float m = tile_amax<ROT>(tile0, st, a, ro, r0, c0);
+            if constexpr (LOCAL) strip_max(a, ro, r0, c0, m);
+            else local = fmaxf(local, m);
+        }
         if (k1 >= a.tiles) break;
         const int64_t k2 = k1 + gridDim.x;
         __syncthreads();                                   // tile1 landed; tile0 is free
@@ -595,9 +637,14 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
             tile_origin(a, k2, r0, c0);
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
         }
-        local = fmaxf(local, tile_amax<ROT>(tile1, st, a, ro, r1, c1));
+        {
+            const float m = tile_amax<ROT>(tile1, st, a, ro, r1, c1);
+            if constexpr (LOCAL) strip_max(a, ro, r1, c1, m);
+            else local = fmaxf(local, m);
+        }
         k = k2;
     }
+    if constexpr (LOCAL) return;
     // wave max, then one atomic per wave into LDS, one per workgroup and layout into memory
     for (int off = 32; off > 0; off >>= 1) local = fmaxf(local, __shfl_xor(local, off));
     __syncthreads();
@@ -825,12 +872,13 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
     }
 }
 
-// Quantize this lane's half group of tile (r0, c0).
+// Quantize this lane's half group of tile (r0, c0); tb holds the tile's scale table and
+// its (g, rcp(6g), rcp(4g)).
 template <int MODE, bool ROT>
 __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st,
                                            const ScaleTable &tb, const QuantArgs &a,
-                                           const LayoutOut &o, const Role &ro, float g,
-                                           float rcp6g, float rcp4g, int64_t r0, int64_t c0)
+                                           const LayoutOut &o, const Role &ro, int64_t r0,
+                                           int64_t c0)
 {
     const int64_t n = ro.lay == 0 ? a.C : a.R;
     const int64_t vec = ro.lay == 0 ? r0 + ro.g : c0 + ro.g;
@@ -849,7 +897,8 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
     const int64_t left = n - start;
     const int nb = left >= TILE ? 8 : (int)(left >> 4);
     const int nbl = nb - 4 * ro.h < 0 ? 0 : (nb - 4 * ro.h > 4 ? 4 : nb - 4 * ro.h);
-    quantize_half<MODE>(r, bm, ro.h, nbl, g, tb, rcp6g, rcp4g, a.seed, (uint32_t)ro.lay, vec, n,
+    const float4 gs = tb.gs;
+    quantize_half<MODE>(r, bm, ro.h, nbl, gs.x, tb, gs.y, gs.z, a.seed, (uint32_t)ro.lay, vec, n,
                         start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
                         o.scales + vec * (n >> 4) + (start >> 4));
 }
@@ -860,33 +909,57 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
 // Waves per SIMD each variant is compiled for, the most that fit without spilling: 4 (128
 // registers) for MS-EDEN, RTN, 4/6 and the unrotated two-layout SR; 3 (168) for the other
 // SR variants and the unrotated row-only 4/6; 2 for the unrotated column-only variants.
-constexpr int quant_waves_per_simd(int mode, bool rot, int lay)
+// Strip-local scales move two more variants to 3: unrotated two-layout SR and unrotated
+// row-only RTN.
+constexpr int quant_waves_per_simd(int mode, bool rot, int lay, bool local)
 {
     if (!rot && lay == LAY_COL) return 2;
-    if (mode == MODE_SR) return (!rot && lay == LAY_BOTH) ? 4 : 3;
-    if (mode == MODE_FP46 && !rot && lay == LAY_ROW) return 3;
+    if (mode == MODE_SR) return (!rot && lay == LAY_BOTH && !local) ? 4 : 3;
+    if ((mode == MODE_FP46 || (local && mode == MODE_RTN)) && !rot && lay == LAY_ROW) return 3;
     return 4;
 }
 
-template <int MODE, bool ROT, int LAY>
-__global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_quant(QuantArgs a)
+// Strip-local scales: table of tile (r0, c0) for this lane's layout, from the maximum of
+// the tile's strip; the first tile of a strip also stores the strip's g.
+template <int MODE>
+__device__ __forceinline__ void build_strip_table(ScaleTable &tb, const QuantArgs &a,
+                                                  const LayoutOut &o, const Role &ro,
+                                                  int64_t r0, int64_t c0)
 {
+    const int tid = threadIdx.x & 255;
+    if (tid >= 128) return;
+    const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
+    const float g = __uint_as_float(a.amax_bits[strip_slot(a, ro.lay, r0, c0)]) / D;
+    build_scale_table(tb, g, tid);
+    if (tid == 0 && (ro.lay == 0 ? c0 : r0) == 0) o.g[(ro.lay == 0 ? r0 : c0) / TILE] = g;
+}
+
+template <int MODE, bool ROT, int LAY, bool LOCAL>
+__global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY, LOCAL))
+k_quant(QuantArgs a)
+{
+    constexpr int NBUF = (LAY == LAY_BOTH) ? 2 : 1;      // tile buffers
+    constexpr int NLAY = (LAY == LAY_BOTH) ? 2 : 1;
     __shared__ Tile tile0;
     __shared__ SignTable st;
-    __shared__ ScaleTable tabs[(LAY == LAY_BOTH) ? 2 : 1];
+    // one table per layout, and per tile buffer when every tile has its own scale
+    __shared__ ScaleTable tabs[LOCAL ? NBUF : 1][NLAY];
     const int t = threadIdx.x;
     const Role ro = lane_role<LAY>();
     constexpr int WAVES = waves_for(LAY);
     const DmaLane dl = dma_lane<WAVES>(a.C);
-    const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
-    const float g = __uint_as_float(ro.lay == 0 ? a.amax_bits[0] : a.amax_bits[1]) / D;
-    const float rcp6g = clamped_rcp(6.0f * g), rcp4g = clamped_rcp(4.0f * g);
-    ScaleTable &tb = tabs[(LAY == LAY_BOTH) ? ro.lay : 0];
+    const int li = (LAY == LAY_BOTH) ? ro.lay : 0;
+    ScaleTable &tb0 = tabs[0][li];
+    ScaleTable &tb1 = tabs[LOCAL ? NBUF - 1 : 0][li];
     // select this lane's layout without indexing the argument struct at run time
     const LayoutOut o = (ro.lay == 0) ? a.out[0] : a.out[1];
     build_sign_table(st, a.rht_seed, ROT);
-    build_scale_table(tb, g, t & 255);
-    if (blockIdx.x == 0 && (t & 255) == 0) *o.g = g;
+    if constexpr (!LOCAL) {
+        const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
+        const float g = __uint_as_float(ro.lay == 0 ? a.amax_bits[0] : a.amax_bits[1]) / D;
+        build_scale_table(tb0, g, t & 255);
+        if (blockIdx.x == 0 && (t & 255) == 0) *o.g = g;
+    }
     if constexpr (LAY != LAY_BOTH) {
         // one layout: a single tile buffer, so that four workgroups of 4 waves fit a CU and
         // hide each other's loads (two buffers leave room for two).  The amax pass keeps
@@ -894,10 +967,11 @@ __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_q
         for (int64_t k = blockIdx.x; k < a.tiles; k += gridDim.x) {
             int64_t r0, c0;
             tile_origin(a, a.tiles - 1 - k, r0, c0);
-            __syncthreads();                               // previous tile fully read
+            __syncthreads();                               // previous tile and table read
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
-            __syncthreads();                               // tile landed
-            tile_quant<MODE, ROT>(tile0, st, tb, a, o, ro, g, rcp6g, rcp4g, r0, c0);
+            if constexpr (LOCAL) build_strip_table<MODE>(tb0, a, o, ro, r0, c0);
+            __syncthreads();                               // tile landed, table written
+            tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0);
         }
         return;
     }
@@ -906,6 +980,7 @@ __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_q
     if (k < a.tiles) {
         tile_origin(a, a.tiles - 1 - k, r0, c0);
         stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+        if constexpr (LOCAL) build_strip_table<MODE>(tb0, a, o, ro, r0, c0);
     }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
@@ -914,26 +989,29 @@ __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY)) k_q
         if (k1 < a.tiles) {
             tile_origin(a, a.tiles - 1 - k1, r1, c1);
             stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
+            if constexpr (LOCAL) build_strip_table<MODE>(tb1, a, o, ro, r1, c1);
         }
-        tile_quant<MODE, ROT>(tile0, st, tb, a, o, ro, g, rcp6g, rcp4g, r0, c0);
+        tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0);
         if (k1 >= a.tiles) break;
         const int64_t k2 = k1 + gridDim.x;
         __syncthreads();                                   // tile1 landed; tile0 is free
         if (k2 < a.tiles) {
             tile_origin(a, a.tiles - 1 - k2, r0, c0);
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+            if constexpr (LOCAL) build_strip_table<MODE>(tb0, a, o, ro, r0, c0);
         }
-        tile_quant<MODE, ROT>(tile1, st, tb, a, o, ro, g, rcp6g, rcp4g, r1, c1);
+        tile_quant<MODE, ROT>(tile1, st, tb1, a, o, ro, r1, c1);
         k = k2;
     }
 }
 
 // Dequantize: one lane per (vector, group).  out[vec][pos] fp32.
+// g of vector v is gp[v >> g_shift] (one tensor scale: a shift that maps every vector to 0).
 template <bool ROT>
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ codes,
                                                  const uint8_t *__restrict__ scales,
-                                                 const float *__restrict__ gp, int64_t vecs,
-                                                 int64_t n, uint64_t rht_seed,
+                                                 const float *__restrict__ gp, int g_shift,
+                                                 int64_t vecs, int64_t n, uint64_t rht_seed,
                                                  float *__restrict__ out)
 {
     const int64_t groups_per_vec = (n + TILE - 1) / TILE;
@@ -942,7 +1020,7 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
     const int64_t vec = id / groups_per_vec, gi = id % groups_per_vec;
     const int64_t start = gi * TILE;
     const int len = (n - start) >= TILE ? TILE : (int)(n - start);
-    const float g = *gp;
+    const float g = gp[vec >> g_shift];
     float v[TILE];
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -1019,27 +1097,50 @@ static int grid_for(K kernel, int threads, int64_t tiles)
     return (int)(tiles < cap ? tiles : cap);
 }
 
-template <bool ROT, int LAY>
+template <bool ROT, int LAY, bool LOCAL>
 static void launch_amax(const QuantArgs &a, hipStream_t st)
 {
     const int threads = 64 * waves_for(LAY);
-    k_amax<ROT, LAY><<<grid_for(k_amax<ROT, LAY>, threads, a.tiles), threads, 0, st>>>(a);
-}
-
-template <int MODE, bool ROT, int LAY>
-static void launch_quant(const QuantArgs &a, hipStream_t st)
-{
-    const int threads = 64 * waves_for(LAY);
-    k_quant<MODE, ROT, LAY><<<grid_for(k_quant<MODE, ROT, LAY>, threads, a.tiles), threads, 0,
+    k_amax<ROT, LAY, LOCAL><<<grid_for(k_amax<ROT, LAY, LOCAL>, threads, a.tiles), threads, 0,
                               st>>>(a);
 }
 
-template <int MODE, bool ROT>
+template <bool ROT, bool LOCAL>
+static void amax_lay(const QuantArgs &a, int lay, hipStream_t st)
+{
+    if (lay == LAY_ROW) launch_amax<ROT, LAY_ROW, LOCAL>(a, st);
+    else if (lay == LAY_COL) launch_amax<ROT, LAY_COL, LOCAL>(a, st);
+    else launch_amax<ROT, LAY_BOTH, LOCAL>(a, st);
+}
+
+template <int MODE, bool ROT, int LAY, bool LOCAL>
+static void launch_quant(const QuantArgs &a, hipStream_t st)
+{
+    const int threads = 64 * waves_for(LAY);
+    k_quant<MODE, ROT, LAY, LOCAL><<<grid_for(k_quant<MODE, ROT, LAY, LOCAL>, threads, a.tiles),
+                                     threads, 0, st>>>(a);
+}
+
+template <int MODE, bool ROT, bool LOCAL>
 static void quant_lay(const QuantArgs &a, int lay, hipStream_t st)
 {
-    if (lay == LAY_ROW) launch_quant<MODE, ROT, LAY_ROW>(a, st);
-    else if (lay == LAY_COL) launch_quant<MODE, ROT, LAY_COL>(a, st);
-    else launch_quant<MODE, ROT, LAY_BOTH>(a, st);
+    if (lay == LAY_ROW) launch_quant<MODE, ROT, LAY_ROW, LOCAL>(a, st);
+    else if (lay == LAY_COL) launch_quant<MODE, ROT, LAY_COL, LOCAL>(a, st);
+    else launch_quant<MODE, ROT, LAY_BOTH, LOCAL>(a, st);
+}
+
+template <bool LOCAL>
+static void quant_mode(const QuantArgs &a, int mode, int rht, int lay, hipStream_t st)
+{
+    switch (mode) {
+    case MODE_RTN: rht ? quant_lay<MODE_RTN, true, LOCAL>(a, lay, st)
+                       : quant_lay<MODE_RTN, false, LOCAL>(a, lay, st); break;
+    case MODE_SR: rht ? quant_lay<MODE_SR, true, LOCAL>(a, lay, st)
+                      : quant_lay<MODE_SR, false, LOCAL>(a, lay, st); break;
+    case MODE_EDEN: quant_lay<MODE_EDEN, true, LOCAL>(a, lay, st); break;
+    default: rht ? quant_lay<MODE_FP46, true, LOCAL>(a, lay, st)
+                 : quant_lay<MODE_FP46, false, LOCAL>(a, lay, st); break;
+    }
 }
 
 static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_bits,
@@ -1054,8 +1155,9 @@ static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_b
     a.amax_bits = amax_bits;
     a.seed = seed;
     a.rht_seed = rht_seed;
+    a.tiles_r = (R + TILE - 1) / TILE;
     a.tiles_c = (C + TILE - 1) / TILE;
-    a.tiles = a.tiles_c * ((R + TILE - 1) / TILE);
+    a.tiles = a.tiles_c * a.tiles_r;
     // NVFP4_GENERAL_TILE_LOADS=1 sends every tile through the general load loop (the one
     // rows longer than 2^26 elements take), so tests can cover it at small sizes
     const char *general = std::getenv("NVFP4_GENERAL_TILE_LOADS");
@@ -1065,59 +1167,73 @@ static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_b
 
 }  // namespace nvfp4k
 
-// Phase 1: amax[0..1] <- max |r| of the requested layouts (0 for the others).
-extern "C" hipError_t nvfp4k_amax(int rht, int layouts, const void *x, int64_t R, int64_t C,
-                                  float *amax, uint64_t rht_seed, hipStream_t st)
+// Number of amax slots: 2, or one per row strip and one per column strip (LOCAL).
+extern "C" int64_t nvfp4k_amax_slots(int local, int64_t R, int64_t C)
+{
+    return local ? (R + nvfp4k::TILE - 1) / nvfp4k::TILE + (C + nvfp4k::TILE - 1) / nvfp4k::TILE
+                 : 2;
+}
+
+// Phase 1: amax[0..1] <- max |r| of the requested layouts (0 for the others); with local != 0,
+// amax[s] <- max |r| of row strip s and amax[tiles_r + s] <- of column strip s.
+extern "C" hipError_t nvfp4k_amax(int local, int rht, int layouts, const void *x, int64_t R,
+                                  int64_t C, float *amax, uint64_t rht_seed, hipStream_t st)
 {
     using namespace nvfp4k;
     QuantArgs a = make_args(x, R, C, reinterpret_cast<uint32_t *>(amax), 0, rht_seed);
-    k_zero_u32<<<1, 64, 0, st>>>(a.amax_bits, 2);
+    const int64_t slots = nvfp4k_amax_slots(local, R, C);
+    const int64_t zb = (slots + 255) / 256;
+    k_zero_u32<<<(unsigned)(zb < 1024 ? zb : 1024), 256, 0, st>>>(a.amax_bits, slots);
     if (a.tiles > 0) {
-        if (rht) {
-            if (layouts == LAY_ROW) launch_amax<true, LAY_ROW>(a, st);
-            else if (layouts == LAY_COL) launch_amax<true, LAY_COL>(a, st);
-            else launch_amax<true, LAY_BOTH>(a, st);
-        } else {
-            if (layouts == LAY_ROW) launch_amax<false, LAY_ROW>(a, st);
-            else if (layouts == LAY_COL) launch_amax<false, LAY_COL>(a, st);
-            else launch_amax<false, LAY_BOTH>(a, st);
-        }
+        if (local) rht ? amax_lay<true, true>(a, layouts, st) : amax_lay<false, true>(a, layouts, st);
+        else rht ? amax_lay<true, false>(a, layouts, st) : amax_lay<false, false>(a, layouts, st);
     }
     return hipGetLastError();
 }
 
-// Phase 2: quantize given the phase-1 maxima.
-extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x, int64_t R,
-                                   int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
-                                   uint8_t *codes1, uint8_t *scales1, float *g1,
+namespace nvfp4k {
+// Strip-local tensor scales of an input with no tiles: every strip's maximum is 0.
+__global__ void k_zero_g(float *g, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        g[i] = 0.0f;
+}
+}  // namespace nvfp4k
+
+// Phase 2: quantize given the phase-1 maxima (strip maxima when local != 0).
+extern "C" hipError_t nvfp4k_quant(int local, int mode, int rht, int layouts, const void *x,
+                                   int64_t R, int64_t C, uint8_t *codes0, uint8_t *scales0,
+                                   float *g0, uint8_t *codes1, uint8_t *scales1, float *g1,
                                    const float *amax, uint64_t seed, uint64_t rht_seed,
                                    hipStream_t st)
 {
     using namespace nvfp4k;
+    if (mode < MODE_RTN || mode > MODE_FP46) return hipErrorInvalidValue;
     QuantArgs a = make_args(x, R, C, reinterpret_cast<uint32_t *>(const_cast<float *>(amax)),
                             seed, rht_seed);
     a.out[0] = {codes0, scales0, g0};
     a.out[1] = {codes1, scales1, g1};
     if (a.tiles == 0) {
-        k_write_g<<<1, 64, 0, st>>>(a.amax_bits, mode == MODE_FP46 ? 1792.0f : 2688.0f,
-                                    (layouts & LAY_ROW) ? g0 : nullptr,
-                                    (layouts & LAY_COL) ? g1 : nullptr);
+        if (!local) {
+            k_write_g<<<1, 64, 0, st>>>(a.amax_bits, mode == MODE_FP46 ? 1792.0f : 2688.0f,
+                                        (layouts & LAY_ROW) ? g0 : nullptr,
+                                        (layouts & LAY_COL) ? g1 : nullptr);
+        } else {
+            // a layout with vectors but no elements: each of its strips has g = 0
+            if ((layouts & LAY_ROW) && a.tiles_r > 0)
+                k_zero_g<<<(unsigned)((a.tiles_r + 255) / 256), 256, 0, st>>>(g0, a.tiles_r);
+            if ((layouts & LAY_COL) && a.tiles_c > 0)
+                k_zero_g<<<(unsigned)((a.tiles_c + 255) / 256), 256, 0, st>>>(g1, a.tiles_c);
+        }
         return hipGetLastError();
     }
-    switch (mode) {
-    case MODE_RTN: rht ? quant_lay<MODE_RTN, true>(a, layouts, st)
-                       : quant_lay<MODE_RTN, false>(a, layouts, st); break;
-    case MODE_SR: rht ? quant_lay<MODE_SR, true>(a, layouts, st)
-                      : quant_lay<MODE_SR, false>(a, layouts, st); break;
-    case MODE_EDEN: quant_lay<MODE_EDEN, true>(a, layouts, st); break;
-    case MODE_FP46: rht ? quant_lay<MODE_FP46, true>(a, layouts, st)
-                        : quant_lay<MODE_FP46, false>(a, layouts, st); break;
-    default: return hipErrorInvalidValue;
-    }
+    if (local) quant_mode<true>(a, mode, rht, layouts, st);
+    else quant_mode<false>(a, mode, rht, layouts, st);
     return hipGetLastError();
 }
 
-extern "C" hipError_t nvfp4k_dequantize(const uint8_t *codes, const uint8_t *scales,
+extern "C" hipError_t nvfp4k_dequantize(int local, const uint8_t *codes, const uint8_t *scales,
                                         const float *g, int64_t vecs, int64_t n, int rht,
                                         uint64_t rht_seed, float *out, hipStream_t st)
 {
@@ -1125,7 +1241,12 @@ extern "C" hipError_t nvfp4k_dequantize(const uint8_t *codes, const uint8_t *sca
     const int64_t groups = vecs * ((n + TILE - 1) / TILE);
     if (groups == 0) return hipSuccess;
     const int64_t blocks = (groups + 255) / 256;
-    if (rht) k_dequant<true><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, vecs, n, rht_seed, out);
-    else k_dequant<false><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, vecs, n, rht_seed, out);
+    const int shift = local ? 7 : 62;      // vector -> index of its g (all vectors < 2^31)
+    if (rht)
+        k_dequant<true><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, shift, vecs, n,
+                                                          rht_seed, out);
+    else
+        k_dequant<false><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, shift, vecs, n,
+                                                           rht_seed, out);
     return hipGetLastError();
 }
