@@ -211,6 +211,7 @@ def main():
 
     if not args.no_mse:
         result["mse_vs_sr"] = mse_vs_sr(nv, workloads, dev, x)
+        result["strip_scales_mse"] = strip_scales_mse(nv, workloads, dev, x)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_cpu, B)
@@ -254,9 +255,20 @@ def modes_table(nv, x, out, amax, stream, reps=40):
     import torch
 
     modes = (("rtn", "rtn", False), ("rtn+rht", "rtn", True), ("sr", "sr", False),
-             ("sr+rht", "sr", True), ("fp46+rht", "fp46", True), ("eden", "eden", True))
+             ("sr+rht", "sr", True), ("fp46+rht", "fp46", True), ("eden", "eden", True),
+             ("eden, strip scales", "eden-strips", True))
+    dev = x.device
+    rows, cols = x.shape
+    out_s = nv.Quantized(nv.empty_strip_layout(rows, cols, dev),
+                         nv.empty_strip_layout(cols, rows, dev))
+    ws_s = torch.empty(nv.strip_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
 
     def call(mode, rht, seed):
+        if mode == "eden-strips":
+            nv.nvfp4_quantize_strips("eden", x, seed=seed, rht=True, rht_seed=1,
+                                     layouts=("row", "col"), out=out_s, workspace=ws_s,
+                                     stream=stream)
+            return
         nv.nvfp4_amax(x, rht, 1, ("row", "col"), amax=amax, stream=stream)
         nv.nvfp4_quantize_amax(mode, x, amax, seed=seed, rht=rht, rht_seed=1,
                                layouts=("row", "col"), out=out, stream=stream)
@@ -315,6 +327,12 @@ def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=5):
         linear.backward_products(dy, x, w, 1, "eden")
 
     ms_step = timed(step)
+
+    def step_strips():
+        linear.forward_product(x, w, 1, scales="strip")
+        linear.backward_products(dy, x, w, 1, "eden", scales="strip")
+
+    ms_step_strips = timed(step_strips)
     _, (qx, qw) = linear.forward_product(x, w, 1, operands=True)
     _, (qdy_r, qw_c, qdy_c, qx_c) = linear.backward_products(dy, x, w, 1, "eden", operands=True)
     outs = [torch.empty((t, n_out), dtype=torch.float32, device=dev),
@@ -338,6 +356,7 @@ def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=5):
     flops = 3 * 2.0 * t * n_in * n_out
     return {"shape": f"T={t}, in={n_in}, out={n_out} (gate projection)",
             "ms_forward_backward": round(ms_step, 3),
+            "ms_forward_backward_strip_scales": round(ms_step_strips, 3),
             "ms_three_gemms": round(ms_gemm, 3),
             "ms_quantize": round(ms_step - ms_gemm, 3),
             "gemm_tflops": round(flops / (ms_gemm * 1e-3) / 1e12, 1),
@@ -391,6 +410,39 @@ def mse_vs_sr(nv, workloads, dev, x_c4):
         out["other_configs"][name] = ratios
         del xd
         torch.cuda.empty_cache()
+    return out
+
+
+def strip_scales_mse(nv, workloads, dev, x_c4):
+    """Relative MSE of MS-EDEN with one tensor scale and with strip-local scales (one per 128
+    vectors), both layouts, Philox seed 1, on the four synthetic configurations."""
+    import torch
+
+    out = {}
+    for name, gen in (("256x1024 N(0,1)", workloads.c1),
+                      ("4096x4096 t3*0.02 + outliers", workloads.c2),
+                      ("16384x2048 row magnitudes 1e-6..10", workloads.c3),
+                      ("16384x8192 N(0,1) x column lognormal", None)):
+        xd = gen().to(dev) if gen is not None else x_c4
+        res = {}
+        for layout in ("row", "col"):
+            xf = (xd.float() if layout == "row" else xd.float().t()).double()
+            norm = float((xf ** 2).sum())
+            q = nv.eden_quantize(xd, 1, 1, layouts=(layout,))
+            t = q.row if layout == "row" else q.col
+            e_glob = float(((nv.dequantize(t, rht=True, rht_seed=1).double() - xf) ** 2).sum())
+            q = nv.nvfp4_quantize_strips("eden", xd, seed=1, rht=True, rht_seed=1,
+                                         layouts=(layout,))
+            t = q.row if layout == "row" else q.col
+            e_str = float(((nv.dequantize_strips(t, rht=True, rht_seed=1).double() - xf) ** 2)
+                          .sum())
+            res[layout] = {"tensor_scale": round(e_glob / norm, 6),
+                           "strip_scales": round(e_str / norm, 6),
+                           "strip_over_tensor": round(e_str / e_glob, 4)}
+            del q, t, xf
+            torch.cuda.empty_cache()
+        out[name] = res
+        del xd
     return out
 
 

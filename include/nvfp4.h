@@ -192,15 +192,16 @@ int nvfp4_gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, in
  * Outputs differ from nvfp4_tensor's global form in one field: tensor_scale points to
  * ceil(vecs / 128) floats (4-byte aligned), g of vector v being tensor_scale[v / 128]. */
 
-/* Workspace bytes of nvfp4_quantize_strips for a rows x cols input: 4 bytes per row strip and
- * per column strip, at least 256.  Never fails. */
+/* Workspace bytes of nvfp4_quantize_strips for a rows x cols input: a 2 KiB scale table per
+ * row strip and per column strip, plus 32 bytes per 128 x 128 tile (the maxima the strip
+ * reduction reads), rounded up to a multiple of 256.  Never fails. */
 size_t nvfp4_strip_workspace_bytes(int64_t rows, int64_t cols, int layouts_mask);
 
 /* Quantizer `mode` (NVFP4_MODE_*) with strip-local scales.  Arguments, shapes, seeds, errors
  * and the two layouts as for the one-call quantizers (rht is taken as 1 for MS-EDEN; seed is
- * unused by RTN and 4/6); the workspace must hold nvfp4_strip_workspace_bytes() bytes.  Two
- * launches: the rotated maximum of every strip, then the quantization, whose workgroups each
- * read the maxima of their tile's strips. */
+ * unused by RTN and 4/6); the workspace must hold nvfp4_strip_workspace_bytes() bytes.  Three
+ * launches on `stream`: the rotated maxima of every tile, one reduction per strip (which
+ * writes g and the strip's scale table into the workspace), then the quantization. */
 int nvfp4_quantize_strips(int mode, const void *x_bf16, int64_t rows, int64_t cols, int group,
                           int block, uint64_t seed, int rht, uint64_t rht_seed,
                           const nvfp4_tensor *row_out, const nvfp4_tensor *col_out,

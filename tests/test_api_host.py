@@ -100,14 +100,14 @@ def test_no_device_is_a_hip_error(L):
 
 
 def test_strip_entry_points_validate(L):
-    # one u32 per row strip and per column strip of 128, padded to 256 bytes
-    assert nv.strip_workspace_bytes(256, 256) == 256
-    assert nv.strip_workspace_bytes(16384, 8192) == 4 * (128 + 64)
-    assert nv.strip_workspace_bytes(16384, 8192) % 256 == 0
-    assert nv.strip_workspace_bytes(1 << 20, 1 << 20) == 4 * 2 * 8192
+    # a 2 KiB table per row strip and per column strip, 32 bytes per tile, 256-byte multiple
+    assert nv.strip_workspace_bytes(256, 256) == 2048 * 4 + 256        # 8320 rounded up
+    assert nv.strip_workspace_bytes(16384, 8192) == 2048 * (128 + 64) + 32 * 128 * 64
+    assert nv.strip_workspace_bytes(0, 0) == 256
+    assert nv.strip_workspace_bytes(200, 8) == 2048 * 3 + 32 * 2 + 192   # rounded up
     r, c = _layout(), _layout(FAKE + 65536, FAKE + 69632, FAKE + 73728)
 
-    def q(mode=2, rows=256, cols=256, rht=1, ws=FAKE, wsb=256):
+    def q(mode=2, rows=256, cols=256, rht=1, ws=FAKE, wsb=1 << 20):
         return L.nvfp4_quantize_strips(mode, FAKE, rows, cols, 128, 16, 1, rht, 1, r, c, ws, wsb,
                                        None)
     assert q(mode=4) == nv.ERR_ARG
@@ -115,9 +115,9 @@ def test_strip_entry_points_validate(L):
     assert q(rht=2) == nv.ERR_ARG
     assert q(cols=200) == nv.ERR_SHAPE
     assert q(ws=0) == nv.ERR_WORKSPACE
-    assert q(rows=1 << 20, cols=1 << 12, wsb=256) == nv.ERR_WORKSPACE   # needs 33 KiB
+    assert q(wsb=2048 * 4) == nv.ERR_WORKSPACE                         # needs 8448 bytes
     assert q(ws=FAKE + 64) == nv.ERR_ALIGN
-    assert L.nvfp4_quantize_strips(2, FAKE, 256, 256, 128, 16, 1, 1, 1, None, None, FAKE, 256,
+    assert L.nvfp4_quantize_strips(2, FAKE, 256, 256, 128, 16, 1, 1, 1, None, None, FAKE, 1 << 20,
                                    None) == nv.ERR_NULL
     assert L.dequantize_strips(None, 4, 128, 128, 16, 0, 0, FAKE, None) == nv.ERR_NULL
     assert L.dequantize_strips(r, 4, 100, 128, 16, 0, 0, FAKE, None) == nv.ERR_SHAPE

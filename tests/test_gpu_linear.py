@@ -128,3 +128,62 @@ def test_fig9_gradient_mean_converges_as_1_over_b():
                   flush=True)
             bias, expect = pts[b_max][i]
             assert bias > 2.0 * expect, (scheme, name, bias, expect)
+
+
+# ----------------------------------------------------------------------------- strip-local scales
+
+def _strip_parity(mode, q, x_cpu, axis, seed, rht_seed, what):
+    ref = oracle.quantize_strips(mode, workloads.bf16_bits(x_cpu), axis=axis, seed=seed,
+                                 rht=True, rht_seed=rht_seed, margins=False)
+    assert np.array_equal(q.tensor_scale.cpu().numpy(), ref.g), what
+    assert np.array_equal(q.codes.cpu().numpy(), ref.codes), what
+    assert np.array_equal(q.scales.cpu().numpy(), ref.scales), what
+
+
+def test_layer_with_strip_scales():
+    """The layer with strip-local scales on every operand: operands bit-exact against the
+    oracle's strip quantizer, products within the FP32 bound with per-strip corrections."""
+    t, n_in, n_out = 384, 256, 512
+    print(f"case: linear layer, strip scales, T={t} in={n_in} out={n_out}", flush=True)
+    x, w, dy = layer_inputs(t, n_in, n_out, seed=60)
+    xd, wd, dyd = x.to(DEV), w.to(DEV), dy.to(DEV)
+    s = 5
+    y, (qx, qw) = linear.forward_product(xd, wd, s, operands=True, scales="strip")
+    (dx, dw), (qdy_r, qw_c, qdy_c, qx_c) = linear.backward_products(
+        dyd, xd, wd, s, "eden", operands=True, scales="strip")
+    torch.cuda.synchronize()
+    _strip_parity("fp46", qx, x, 0, 0, 2 * s, "X rows")
+    _strip_parity("fp46", qw, w, 0, 0, 2 * s, "W rows")
+    _strip_parity("eden", qdy_r, dy, 0, 3 * s, 2 * s + 1, "dY rows")
+    _strip_parity("eden", qdy_c, dy, 1, 3 * s, 2 * s + 1, "dY columns")
+    _strip_parity("eden", qw_c, w, 1, 3 * s + 1, 2 * s + 1, "W columns")
+    _strip_parity("eden", qx_c, x, 1, 3 * s + 2, 2 * s + 1, "X columns")
+    f = 2.0 ** -7
+    check_entries(y, qx, qw, np.arange(t), np.arange(n_out), f, strips=True)
+    check_entries(dx, qdy_r, qw_c, np.arange(t), np.arange(n_in), f, strips=True)
+    check_entries(dw, qdy_c, qx_c, np.arange(n_out), np.arange(n_in), f, strips=True)
+
+
+def test_fig9_with_strip_scales():
+    """Strip-local MS-EDEN stays unbiased in the layer: the mean of B backward passes tracks
+    mse/B out to B = 256."""
+    print("case: Fig. 9 method with strip scales, 512 x 256 -> 256, B = 1..256", flush=True)
+    t, n_in, n_out = 512, 256, 256
+    x, w, dy = layer_inputs(t, n_in, n_out, seed=70)
+    xd, wd, dyd = x.to(DEV), w.to(DEV), dy.to(DEV)
+    exact = [dyd.double() @ wd.double(), dyd.double().t() @ xd.double()]
+    acc = [torch.zeros_like(e) for e in exact]
+    norms = [float((e * e).sum()) for e in exact]
+    single = [0.0, 0.0]
+    for b in range(1, 257):
+        grads = linear.backward_products(dyd, xd, wd, b, "eden", scales="strip")
+        for i, g in enumerate(grads):
+            g = g.double()
+            acc[i] += g
+            single[i] += float(((g - exact[i]) ** 2).sum()) / norms[i]
+        if b in (1, 16, 256):
+            for i, name in enumerate(("dX", "dW")):
+                bias = float(((acc[i] / b - exact[i]) ** 2).sum()) / norms[i]
+                expect = single[i] / b / b
+                print(name, b, f"{bias:.3e}/{expect:.3e}", flush=True)
+                assert 0.7 * expect < bias < 1.4 * expect, (name, b, bias, expect)

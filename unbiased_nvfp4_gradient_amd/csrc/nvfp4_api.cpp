@@ -6,14 +6,19 @@
 
 #include "nvfp4.h"
 
-extern "C" int64_t nvfp4k_amax_slots(int local, int64_t R, int64_t C);
-extern "C" hipError_t nvfp4k_amax(int local, int rht, int layouts, const void *x, int64_t R,
-                                  int64_t C, float *amax, uint64_t rht_seed, hipStream_t st);
-extern "C" hipError_t nvfp4k_quant(int local, int mode, int rht, int layouts, const void *x,
-                                   int64_t R, int64_t C, uint8_t *codes0, uint8_t *scales0,
-                                   float *g0, uint8_t *codes1, uint8_t *scales1, float *g1,
+extern "C" hipError_t nvfp4k_amax(int rht, int layouts, const void *x, int64_t R, int64_t C,
+                                  float *amax, uint64_t rht_seed, hipStream_t st);
+extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x, int64_t R,
+                                   int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
+                                   uint8_t *codes1, uint8_t *scales1, float *g1,
                                    const float *amax, uint64_t seed, uint64_t rht_seed,
                                    hipStream_t st);
+extern "C" size_t nvfp4k_strip_workspace(int64_t R, int64_t C);
+extern "C" hipError_t nvfp4k_quant_strips(int mode, int rht, int layouts, const void *x,
+                                          int64_t R, int64_t C, uint8_t *codes0,
+                                          uint8_t *scales0, float *g0, uint8_t *codes1,
+                                          uint8_t *scales1, float *g1, void *workspace,
+                                          uint64_t seed, uint64_t rht_seed, hipStream_t st);
 extern "C" hipError_t nvfp4k_gemm(int local, const uint8_t *a_codes, const uint8_t *a_scales,
                                   const float *a_g, const uint8_t *b_codes,
                                   const uint8_t *b_scales, const float *b_g, int64_t M,
@@ -82,14 +87,14 @@ int check_outputs(const nvfp4_tensor *row_out, const nvfp4_tensor *col_out, int6
     return rc ? rc : check_layout(col_out, empty);
 }
 
-int launch_quant(int local, int mode, const void *x, int64_t rows, int64_t cols, uint64_t seed,
-                 int rht, uint64_t rht_seed, const float *amax, const nvfp4_tensor *row_out,
+int launch_quant(int mode, const void *x, int64_t rows, int64_t cols, uint64_t seed, int rht,
+                 uint64_t rht_seed, const float *amax, const nvfp4_tensor *row_out,
                  const nvfp4_tensor *col_out, void *stream)
 {
     const int layouts = (row_out ? 1 : 0) | (col_out ? 2 : 0);
     const bool rotated = rht || mode == MODE_EDEN;
     hipError_t e = nvfp4k_quant(
-        local, mode, rotated ? 1 : 0, layouts, x, rows, cols, row_out ? row_out->codes : nullptr,
+        mode, rotated ? 1 : 0, layouts, x, rows, cols, row_out ? row_out->codes : nullptr,
         row_out ? row_out->scales : nullptr, row_out ? row_out->tensor_scale : nullptr,
         col_out ? col_out->codes : nullptr, col_out ? col_out->scales : nullptr,
         col_out ? col_out->tensor_scale : nullptr, amax, seed, rht_seed,
@@ -97,12 +102,12 @@ int launch_quant(int local, int mode, const void *x, int64_t rows, int64_t cols,
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-// Workspace of the strip-local quantizer: one u32 slot per row strip and per column strip
-// of 128, padded to 256 bytes.
+// Workspace of the strip-local quantizer (a scale table per strip, wave maxima per tile),
+// padded to 256 bytes.
 size_t strip_workspace_bytes(int64_t rows, int64_t cols)
 {
-    if (rows < 0 || cols < 0) return WORKSPACE_BYTES;
-    const size_t b = 4 * (size_t)nvfp4k_amax_slots(1, rows, cols);
+    if (rows < 0 || cols < 0 || rows > MAX_DIM || cols > MAX_DIM) return WORKSPACE_BYTES;
+    const size_t b = nvfp4k_strip_workspace(rows, cols);
     return b < WORKSPACE_BYTES ? WORKSPACE_BYTES : (b + 255) / 256 * 256;
 }
 
@@ -123,12 +128,21 @@ int quantize_common(int local, int mode, const void *x, int64_t rows, int64_t co
     if (rc) return rc;
     const int layouts = (row_out ? 1 : 0) | (col_out ? 2 : 0);
     const bool rotated = rht || mode == MODE_EDEN;
+    hipError_t e;
+    if (local) {
+        e = nvfp4k_quant_strips(
+            mode, rotated ? 1 : 0, layouts, x, rows, cols, row_out ? row_out->codes : nullptr,
+            row_out ? row_out->scales : nullptr, row_out ? row_out->tensor_scale : nullptr,
+            col_out ? col_out->codes : nullptr, col_out ? col_out->scales : nullptr,
+            col_out ? col_out->tensor_scale : nullptr, workspace, seed, rht_seed,
+            static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+    }
     float *amax = static_cast<float *>(workspace);
-    hipError_t e = nvfp4k_amax(local, rotated ? 1 : 0, layouts, x, rows, cols, amax, rht_seed,
-                               static_cast<hipStream_t>(stream));
+    e = nvfp4k_amax(rotated ? 1 : 0, layouts, x, rows, cols, amax, rht_seed,
+                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return NVFP4_ERR_HIP;
-    return launch_quant(local, mode, x, rows, cols, seed, rht, rht_seed, amax, row_out, col_out,
-                        stream);
+    return launch_quant(mode, x, rows, cols, seed, rht, rht_seed, amax, row_out, col_out, stream);
 }
 
 int dequantize_common(int local, const nvfp4_tensor *in, int64_t vecs, int64_t n, int group,
@@ -246,7 +260,7 @@ int nvfp4_amax(const void *x_bf16, int64_t rows, int64_t cols, int group, int bl
     if (!aligned(amax, 4)) return NVFP4_ERR_ALIGN;
     rc = check_device();
     if (rc) return rc;
-    hipError_t e = nvfp4k_amax(0, rht, layouts_mask, x_bf16, rows, cols, amax, rht_seed,
+    hipError_t e = nvfp4k_amax(rht, layouts_mask, x_bf16, rows, cols, amax, rht_seed,
                                static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
@@ -264,7 +278,7 @@ int nvfp4_quantize_amax(int mode, const void *x_bf16, int64_t rows, int64_t cols
     if (!aligned(amax, 4)) return NVFP4_ERR_ALIGN;
     rc = check_device();
     if (rc) return rc;
-    return launch_quant(0, mode, x_bf16, rows, cols, seed, rht, rht_seed, amax, row_out, col_out,
+    return launch_quant(mode, x_bf16, rows, cols, seed, rht, rht_seed, amax, row_out, col_out,
                         stream);
 }
 

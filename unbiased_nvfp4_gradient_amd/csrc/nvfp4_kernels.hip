@@ -43,10 +43,11 @@
 //
 // Strip-local scales (the CTA-local variant of the rit.work note on "Format-Aware Fusion for
 // Fast FP4 Pretraining": maxima inside a block of work, row and column corrections applied
-// after the GEMM's sum over K) take the same two passes with LOCAL = true: k_amax folds each
-// tile's maximum into the slot of its strip (128 consecutive vectors: one tile row for the row
-// layout, one tile column for the column layout), and k_quant rebuilds its scale table for
-// every tile from that tile's strip maxima.
+// after the GEMM's sum over K) take the same two passes with LOCAL = true and a small kernel
+// between them: k_amax stores each wave's maximum over each tile (no atomics), k_strip_tables
+// reduces them per strip (128 consecutive vectors: one tile row for the row layout, one tile
+// column for the column layout) and writes each strip's g and scale table, and k_quant copies
+// the table of each tile's strips into LDS along with the tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <cstdlib>
@@ -463,28 +464,25 @@ __device__ __forceinline__ float block_max(const float *r)
     return m;
 }
 
-// Per-workgroup table over the 127 E4M3 codes: (scale value s, den = s*g, rcp(den)).  Code
-// 0 gets rcp = 0: a block with scale 0 then scales every element to +0 and rounds it to code
-// 0x0, which is what the contract prescribes for it, without a select.  gs holds the tensor
-// scale itself and the reciprocals of 6g and 4g.
-struct ScaleTable {
-    float4 e[128];
-    float4 gs;     // (g, rcp(6g), rcp(4g), 0)
-};
+// Table over the 127 E4M3 codes a scale can take (0x00..0x7E): (scale value s, den = s*g,
+// rcp(den)).  Code 0 gets rcp = 0: a block with scale 0 then scales every element to +0 and
+// rounds it to code 0x0, which is what the contract prescribes for it, without a select.
+// Entry 127 (0x7F is NaN in E4M3, never a scale) holds (g, rcp(6g), rcp(4g)).
+struct ScaleTable { float4 e[128]; };
 
-__device__ __forceinline__ float4 scale_consts(float g)
+constexpr int TAB_G = 127;
+
+__device__ __forceinline__ float4 scale_entry(int j, float g)
 {
-    return make_float4(g, clamped_rcp(6.0f * g), clamped_rcp(4.0f * g), 0.0f);
+    if (j == TAB_G) return make_float4(g, clamped_rcp(6.0f * g), clamped_rcp(4.0f * g), 0.0f);
+    const float sv = e4m3_val((uint32_t)j);
+    const float den = sv * g;
+    return make_float4(sv, den, j ? clamped_rcp(den) : 0.0f, 0.0f);
 }
 
 __device__ __forceinline__ void build_scale_table(ScaleTable &tb, float g, int tid)
 {
-    if (tid < 128) {
-        const float sv = e4m3_val((uint32_t)tid);
-        const float den = sv * g;
-        tb.e[tid] = make_float4(sv, den, tid ? clamped_rcp(den) : 0.0f, 0.0f);
-        if (tid == 0) tb.gs = scale_consts(g);
-    }
+    if (tid < 128) tb.e[tid] = scale_entry(tid, g);
 }
 
 // ------------------------------------------------------------------------------ arguments
@@ -498,9 +496,11 @@ struct QuantArgs {
     const uint16_t *x;
     int64_t R, C;
     LayoutOut out[2];          // [0] row layout, [1] column layout
-    // fp32 bits of max |r| (phase 1 output): [0] row, [1] column; with strip-local scales
-    // [tiles_r] row strips, then [tiles_c] column strips
+    // fp32 bits of max |r| (phase 1 output): [0] row, [1] column; with strip-local scales,
+    // [tile][layout][wave] the maximum of each of the 4 waves of a layout over each tile
     uint32_t *amax_bits;
+    // strip-local scales: [tiles_r row strips, then tiles_c column strips][128] scale tables
+    float4 *tables;
     uint64_t seed, rht_seed;
     int64_t tiles_r, tiles_c, tiles;   // tile rows, tiles per tile row, total tiles
     int64_t dma_fast_max_c;    // rows up to this many elements use the precomputed loads
@@ -578,26 +578,47 @@ __device__ __forceinline__ float tile_amax(const Tile &tile, const SignTable &st
     return fmaxf(m0, m1);
 }
 
-// Slot of the strip that tile (r0, c0) belongs to, for this lane's layout.
+// Strip of tile (r0, c0) for layout lay: its table index among the row strips, then the
+// column strips.
 __device__ __forceinline__ int64_t strip_slot(const QuantArgs &a, int lay, int64_t r0,
                                               int64_t c0)
 {
     return lay == 0 ? r0 / TILE : a.tiles_r + c0 / TILE;
 }
 
-// Strip-local scales: fold a lane's maximum over one tile into its strip's slot, one atomic
-// per wave (a wave's lanes share the layout and the tile).
-__device__ __forceinline__ void strip_max(const QuantArgs &a, const Role &ro, int64_t r0,
-                                          int64_t c0, float m)
+// Maximum over the wave: rotations within each row of 16 lanes (DPP row_ror 1, 2, 4, 8), then
+// the four rows' results read out.  No LDS round trips.
+__device__ __forceinline__ float wave_max(float m)
 {
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if ((threadIdx.x & 63) == 0)
-        atomicMax(&a.amax_bits[strip_slot(a, ro.lay, r0, c0)], __float_as_uint(m));
+#define ROR_MAX(n) { const int v = __builtin_bit_cast(int, m); \
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, 0x120 + (n), \
+                                                                          0xF, 0xF, false))); }
+    ROR_MAX(1);
+    ROR_MAX(2);
+    ROR_MAX(4);
+    ROR_MAX(8);
+#undef ROR_MAX
+    const int b = __builtin_bit_cast(int, m);
+    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+
+// Strip-local scales: each wave stores its maximum over tile (r0, c0) (4 waves per layout).
+__device__ __forceinline__ void store_wave_max(const QuantArgs &a, const Role &ro, int64_t r0,
+                                               int64_t c0, float m)
+{
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) {
+        const int64_t tile = (r0 / TILE) * a.tiles_c + c0 / TILE;
+        a.amax_bits[tile * 8 + 4 * ro.lay + ((threadIdx.x >> 6) & 3)] = __float_as_uint(m);
+    }
 }
 
 // Pass 1: amax of |r| per layout.  Persistent workgroups walk the tiles with two LDS
 // buffers (the next tile streams in while the current one is processed); one atomicMax
-// per workgroup and layout at the end, or per wave and tile into the tile's strip (LOCAL).
+// per workgroup and layout at the end; with LOCAL, one store per wave and tile instead.
 template <bool ROT, int LAY, bool LOCAL>
 __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
 {
@@ -627,7 +648,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         }
         {
             const float m = tile_amax<ROT>(tile0, st, a, ro, r0, c0);
-            if constexpr (LOCAL) strip_max(a, ro, r0, c0, m);
+            if constexpr (LOCAL) store_wave_max(a, ro, r0, c0, m);
             else local = fmaxf(local, m);
         }
         if (k1 >= a.tiles) break;
@@ -639,7 +660,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         }
         {
             const float m = tile_amax<ROT>(tile1, st, a, ro, r1, c1);
-            if constexpr (LOCAL) strip_max(a, ro, r1, c1, m);
+            if constexpr (LOCAL) store_wave_max(a, ro, r1, c1, m);
             else local = fmaxf(local, m);
         }
         k = k2;
@@ -897,7 +918,7 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
     const int64_t left = n - start;
     const int nb = left >= TILE ? 8 : (int)(left >> 4);
     const int nbl = nb - 4 * ro.h < 0 ? 0 : (nb - 4 * ro.h > 4 ? 4 : nb - 4 * ro.h);
-    const float4 gs = tb.gs;
+    const float4 gs = tb.e[TAB_G];
     quantize_half<MODE>(r, bm, ro.h, nbl, gs.x, tb, gs.y, gs.z, a.seed, (uint32_t)ro.lay, vec, n,
                         start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
                         o.scales + vec * (n >> 4) + (start >> 4));
@@ -909,33 +930,56 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
 // Waves per SIMD each variant is compiled for, the most that fit without spilling: 4 (128
 // registers) for MS-EDEN, RTN, 4/6 and the unrotated two-layout SR; 3 (168) for the other
 // SR variants and the unrotated row-only 4/6; 2 for the unrotated column-only variants.
-// Strip-local scales move two more variants to 3: unrotated two-layout SR and unrotated
-// row-only RTN.
-constexpr int quant_waves_per_simd(int mode, bool rot, int lay, bool local)
+constexpr int quant_waves_per_simd(int mode, bool rot, int lay)
 {
     if (!rot && lay == LAY_COL) return 2;
-    if (mode == MODE_SR) return (!rot && lay == LAY_BOTH && !local) ? 4 : 3;
-    if ((mode == MODE_FP46 || (local && mode == MODE_RTN)) && !rot && lay == LAY_ROW) return 3;
+    if (mode == MODE_SR) return (!rot && lay == LAY_BOTH) ? 4 : 3;
+    if (mode == MODE_FP46 && !rot && lay == LAY_ROW) return 3;
     return 4;
 }
 
-// Strip-local scales: table of tile (r0, c0) for this lane's layout, from the maximum of
-// the tile's strip; the first tile of a strip also stores the strip's g.
-template <int MODE>
-__device__ __forceinline__ void build_strip_table(ScaleTable &tb, const QuantArgs &a,
-                                                  const LayoutOut &o, const Role &ro,
-                                                  int64_t r0, int64_t c0)
+// Between the passes with strip-local scales: workgroup `slot` reduces the wave maxima of its
+// strip (row strip s: the tiles of tile row s; column strip s: of tile column s), stores the
+// strip's g into its layout's output and writes the strip's scale table.
+__global__ void __launch_bounds__(256) k_strip_tables(QuantArgs a, int layouts, float D)
 {
-    const int tid = threadIdx.x & 255;
-    if (tid >= 128) return;
-    const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
-    const float g = __uint_as_float(a.amax_bits[strip_slot(a, ro.lay, r0, c0)]) / D;
-    build_scale_table(tb, g, tid);
-    if (tid == 0 && (ro.lay == 0 ? c0 : r0) == 0) o.g[(ro.lay == 0 ? r0 : c0) / TILE] = g;
+    __shared__ float wm[4];
+    const int64_t slot = blockIdx.x;
+    const bool row = slot < a.tiles_r;
+    if (!(layouts & (row ? LAY_ROW : LAY_COL))) return;
+    const int64_t s = row ? slot : slot - a.tiles_r;
+    const int64_t count = 4 * (row ? a.tiles_c : a.tiles_r);
+    float m = 0.0f;
+    for (int64_t i = threadIdx.x; i < count; i += 256) {
+        const int64_t other = i >> 2;
+        const int64_t tile = row ? s * a.tiles_c + other : other * a.tiles_c + s;
+        m = fmaxf(m, __uint_as_float(a.amax_bits[tile * 8 + (row ? 0 : 4) + (i & 3)]));
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float g = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])) / D;
+    const LayoutOut o = row ? a.out[0] : a.out[1];
+    if (threadIdx.x == 0) o.g[s] = g;
+    if (threadIdx.x < 128) a.tables[slot * 128 + threadIdx.x] = scale_entry(threadIdx.x, g);
+}
+
+// Strip-local scales: start copying the scale table of tile (r0, c0)'s strip for this lane's
+// layout into tb: two wave instructions of 64 16-byte chunks, issued by the layout's first two
+// waves.  Visible after the next __syncthreads, like the tile.
+__device__ __forceinline__ void stage_table(ScaleTable &tb, const QuantArgs &a, const Role &ro,
+                                            int64_t r0, int64_t c0)
+{
+    const int w = __builtin_amdgcn_readfirstlane((int)((threadIdx.x >> 6) & 3));
+    if (w < 2) {
+        const float4 *src = a.tables + strip_slot(a, ro.lay, r0, c0) * 128 + 64 * w +
+                            (threadIdx.x & 63);
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(&tb.e[64 * w]), 16, 0, 0);
+    }
 }
 
 template <int MODE, bool ROT, int LAY, bool LOCAL>
-__global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY, LOCAL))
+__global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY))
 k_quant(QuantArgs a)
 {
     constexpr int NBUF = (LAY == LAY_BOTH) ? 2 : 1;      // tile buffers
@@ -969,7 +1013,7 @@ k_quant(QuantArgs a)
             tile_origin(a, a.tiles - 1 - k, r0, c0);
             __syncthreads();                               // previous tile and table read
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
-            if constexpr (LOCAL) build_strip_table<MODE>(tb0, a, o, ro, r0, c0);
+            if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
             __syncthreads();                               // tile landed, table written
             tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0);
         }
@@ -980,7 +1024,7 @@ k_quant(QuantArgs a)
     if (k < a.tiles) {
         tile_origin(a, a.tiles - 1 - k, r0, c0);
         stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
-        if constexpr (LOCAL) build_strip_table<MODE>(tb0, a, o, ro, r0, c0);
+        if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
     }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
@@ -989,7 +1033,7 @@ k_quant(QuantArgs a)
         if (k1 < a.tiles) {
             tile_origin(a, a.tiles - 1 - k1, r1, c1);
             stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
-            if constexpr (LOCAL) build_strip_table<MODE>(tb1, a, o, ro, r1, c1);
+            if constexpr (LOCAL) stage_table(tb1, a, ro, r1, c1);
         }
         tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0);
         if (k1 >= a.tiles) break;
@@ -998,7 +1042,7 @@ k_quant(QuantArgs a)
         if (k2 < a.tiles) {
             tile_origin(a, a.tiles - 1 - k2, r0, c0);
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
-            if constexpr (LOCAL) build_strip_table<MODE>(tb0, a, o, ro, r0, c0);
+            if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
         }
         tile_quant<MODE, ROT>(tile1, st, tb1, a, o, ro, r1, c1);
         k = k2;
@@ -1153,6 +1197,7 @@ static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_b
     a.out[0] = {nullptr, nullptr, nullptr};
     a.out[1] = {nullptr, nullptr, nullptr};
     a.amax_bits = amax_bits;
+    a.tables = nullptr;
     a.seed = seed;
     a.rht_seed = rht_seed;
     a.tiles_r = (R + TILE - 1) / TILE;
@@ -1167,44 +1212,21 @@ static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_b
 
 }  // namespace nvfp4k
 
-// Number of amax slots: 2, or one per row strip and one per column strip (LOCAL).
-extern "C" int64_t nvfp4k_amax_slots(int local, int64_t R, int64_t C)
-{
-    return local ? (R + nvfp4k::TILE - 1) / nvfp4k::TILE + (C + nvfp4k::TILE - 1) / nvfp4k::TILE
-                 : 2;
-}
-
-// Phase 1: amax[0..1] <- max |r| of the requested layouts (0 for the others); with local != 0,
-// amax[s] <- max |r| of row strip s and amax[tiles_r + s] <- of column strip s.
-extern "C" hipError_t nvfp4k_amax(int local, int rht, int layouts, const void *x, int64_t R,
-                                  int64_t C, float *amax, uint64_t rht_seed, hipStream_t st)
+// Phase 1: amax[0..1] <- max |r| of the requested layouts (0 for the others).
+extern "C" hipError_t nvfp4k_amax(int rht, int layouts, const void *x, int64_t R, int64_t C,
+                                  float *amax, uint64_t rht_seed, hipStream_t st)
 {
     using namespace nvfp4k;
     QuantArgs a = make_args(x, R, C, reinterpret_cast<uint32_t *>(amax), 0, rht_seed);
-    const int64_t slots = nvfp4k_amax_slots(local, R, C);
-    const int64_t zb = (slots + 255) / 256;
-    k_zero_u32<<<(unsigned)(zb < 1024 ? zb : 1024), 256, 0, st>>>(a.amax_bits, slots);
-    if (a.tiles > 0) {
-        if (local) rht ? amax_lay<true, true>(a, layouts, st) : amax_lay<false, true>(a, layouts, st);
-        else rht ? amax_lay<true, false>(a, layouts, st) : amax_lay<false, false>(a, layouts, st);
-    }
+    k_zero_u32<<<1, 64, 0, st>>>(a.amax_bits, 2);
+    if (a.tiles > 0) rht ? amax_lay<true, false>(a, layouts, st) : amax_lay<false, false>(a, layouts, st);
     return hipGetLastError();
 }
 
-namespace nvfp4k {
-// Strip-local tensor scales of an input with no tiles: every strip's maximum is 0.
-__global__ void k_zero_g(float *g, int64_t n)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        g[i] = 0.0f;
-}
-}  // namespace nvfp4k
-
-// Phase 2: quantize given the phase-1 maxima (strip maxima when local != 0).
-extern "C" hipError_t nvfp4k_quant(int local, int mode, int rht, int layouts, const void *x,
-                                   int64_t R, int64_t C, uint8_t *codes0, uint8_t *scales0,
-                                   float *g0, uint8_t *codes1, uint8_t *scales1, float *g1,
+// Phase 2: quantize given the phase-1 maxima.
+extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x, int64_t R,
+                                   int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
+                                   uint8_t *codes1, uint8_t *scales1, float *g1,
                                    const float *amax, uint64_t seed, uint64_t rht_seed,
                                    hipStream_t st)
 {
@@ -1215,21 +1237,45 @@ extern "C" hipError_t nvfp4k_quant(int local, int mode, int rht, int layouts, co
     a.out[0] = {codes0, scales0, g0};
     a.out[1] = {codes1, scales1, g1};
     if (a.tiles == 0) {
-        if (!local) {
-            k_write_g<<<1, 64, 0, st>>>(a.amax_bits, mode == MODE_FP46 ? 1792.0f : 2688.0f,
-                                        (layouts & LAY_ROW) ? g0 : nullptr,
-                                        (layouts & LAY_COL) ? g1 : nullptr);
-        } else {
-            // a layout with vectors but no elements: each of its strips has g = 0
-            if ((layouts & LAY_ROW) && a.tiles_r > 0)
-                k_zero_g<<<(unsigned)((a.tiles_r + 255) / 256), 256, 0, st>>>(g0, a.tiles_r);
-            if ((layouts & LAY_COL) && a.tiles_c > 0)
-                k_zero_g<<<(unsigned)((a.tiles_c + 255) / 256), 256, 0, st>>>(g1, a.tiles_c);
-        }
+        k_write_g<<<1, 64, 0, st>>>(a.amax_bits, mode == MODE_FP46 ? 1792.0f : 2688.0f,
+                                    (layouts & LAY_ROW) ? g0 : nullptr,
+                                    (layouts & LAY_COL) ? g1 : nullptr);
         return hipGetLastError();
     }
-    if (local) quant_mode<true>(a, mode, rht, layouts, st);
-    else quant_mode<false>(a, mode, rht, layouts, st);
+    quant_mode<false>(a, mode, rht, layouts, st);
+    return hipGetLastError();
+}
+
+// Workspace of the strip-local quantizer: a 2 KiB scale table per row strip and per column
+// strip, then 32 bytes of wave maxima per tile.
+extern "C" size_t nvfp4k_strip_workspace(int64_t R, int64_t C)
+{
+    const int64_t tr = (R + nvfp4k::TILE - 1) / nvfp4k::TILE;
+    const int64_t tc = (C + nvfp4k::TILE - 1) / nvfp4k::TILE;
+    return 2048 * (size_t)(tr + tc) + 32 * (size_t)(tr * tc);
+}
+
+// Strip-local quantization: wave maxima per tile, strip tables, then the quantize pass.
+extern "C" hipError_t nvfp4k_quant_strips(int mode, int rht, int layouts, const void *x,
+                                          int64_t R, int64_t C, uint8_t *codes0,
+                                          uint8_t *scales0, float *g0, uint8_t *codes1,
+                                          uint8_t *scales1, float *g1, void *workspace,
+                                          uint64_t seed, uint64_t rht_seed, hipStream_t st)
+{
+    using namespace nvfp4k;
+    if (mode < MODE_RTN || mode > MODE_FP46) return hipErrorInvalidValue;
+    QuantArgs a = make_args(x, R, C, nullptr, seed, rht_seed);
+    a.out[0] = {codes0, scales0, g0};
+    a.out[1] = {codes1, scales1, g1};
+    a.tables = static_cast<float4 *>(workspace);
+    a.amax_bits = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
+                                               2048 * (a.tiles_r + a.tiles_c));
+    if (a.tiles > 0) rht ? amax_lay<true, true>(a, layouts, st) : amax_lay<false, true>(a, layouts, st);
+    // strips with no elements (rows or cols == 0) reduce nothing and get g = 0
+    if (a.tiles_r + a.tiles_c > 0)
+        k_strip_tables<<<(unsigned)(a.tiles_r + a.tiles_c), 256, 0, st>>>(
+            a, layouts, mode == MODE_FP46 ? 1792.0f : 2688.0f);
+    if (a.tiles > 0) quant_mode<true>(a, mode, rht, layouts, st);
     return hipGetLastError();
 }
 

@@ -20,17 +20,38 @@ quantizer calls per step run in this package's HIP kernels; this module only ord
 Seeds: a call with seed s uses rotation seed 2s in the forward and 2s + 1 in the backward,
 and stochastic-rounding seeds 3s, 3s + 1, 3s + 2 for dY, W and X.  All three dimensions
 must be multiples of 128 (rotation groups); the GEMM needs M, N % 32 and K % 64, implied.
+
+scales="strip" switches every operand to strip-local scales (the CTA-local variant of the
+rit.work note on "Format-Aware Fusion for Fast FP4 Pretraining"): one FP32 scale per 128
+vectors of each operand, i.e. per block of 128 rows of the product's first operand and 128
+columns of its second, which the GEMM applies after its sum over K.  Every operand's strips
+run along a dimension that is not contracted, so each product keeps one correction per
+output row block and one per output column block.
 """
 from __future__ import annotations
 
 import torch
 
-from . import eden_quantize, fp46_quantize, nvfp4_gemm_check, rtn_quantize, sr_quantize
+from . import (eden_quantize, fp46_quantize, nvfp4_gemm_check, nvfp4_gemm_check_strips,
+               nvfp4_quantize_strips, rtn_quantize, sr_quantize)
 
 BACKWARD_SCHEMES = ("eden", "sr", "rtn", "fp46")
+SCALES = ("tensor", "strip")
 
 
-def _quantize(scheme: str, x: torch.Tensor, seed: int, rht_seed: int, layouts):
+def _gemm(scales: str):
+    if scales not in SCALES:
+        raise ValueError(f"unknown scales {scales!r}; use one of {SCALES}")
+    return nvfp4_gemm_check_strips if scales == "strip" else nvfp4_gemm_check
+
+
+def _quantize(scheme: str, x: torch.Tensor, seed: int, rht_seed: int, layouts,
+              scales: str = "tensor"):
+    if scales == "strip":
+        if scheme not in BACKWARD_SCHEMES:
+            raise ValueError(f"unknown scheme {scheme!r}; use one of {BACKWARD_SCHEMES}")
+        return nvfp4_quantize_strips(scheme, x, seed=seed, rht=True, rht_seed=rht_seed,
+                                     layouts=layouts)
     if scheme == "eden":
         return eden_quantize(x, seed, rht_seed, layouts=layouts)
     if scheme == "sr":
@@ -53,27 +74,30 @@ def _check_shapes(x: torch.Tensor, w: torch.Tensor):
         raise ValueError("x and w must be bfloat16")
 
 
-def forward_product(x: torch.Tensor, w: torch.Tensor, seed: int, operands: bool = False):
+def forward_product(x: torch.Tensor, w: torch.Tensor, seed: int, operands: bool = False,
+                    scales: str = "tensor"):
     """Y = Q46(X) Q46(W)^T in FP32, X and W rotated along in with rotation seed 2s.  With
     operands=True also returns the two quantized operands (X rows, W rows)."""
+    gemm = _gemm(scales)
     rs = 2 * seed
-    qx = fp46_quantize(x, rht=True, rht_seed=rs, layouts=("row",)).row
-    qw = fp46_quantize(w, rht=True, rht_seed=rs, layouts=("row",)).row
-    y = nvfp4_gemm_check(qx, qw, rotated_pair=True)
+    qx = _quantize("fp46", x, 0, rs, ("row",), scales).row
+    qw = _quantize("fp46", w, 0, rs, ("row",), scales).row
+    y = gemm(qx, qw, rotated_pair=True)
     return (y, (qx, qw)) if operands else y
 
 
 def backward_products(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, seed: int,
-                      scheme: str = "eden", operands: bool = False):
+                      scheme: str = "eden", operands: bool = False, scales: str = "tensor"):
     """(dX, dW) in FP32 from bfloat16 dY [T, out], X [T, in], W [out, in].  With
     operands=True also returns the quantized operands (dY rows, W columns, dY columns,
     X columns)."""
+    gemm = _gemm(scales)
     rs = 2 * seed + 1
-    qdy = _quantize(scheme, dy, 3 * seed, rs, ("row", "col"))
-    qw = _quantize(scheme, w, 3 * seed + 1, rs, ("col",)).col
-    qx = _quantize(scheme, x, 3 * seed + 2, rs, ("col",)).col
-    dx = nvfp4_gemm_check(qdy.row, qw, rotated_pair=True)
-    dw = nvfp4_gemm_check(qdy.col, qx, rotated_pair=True)
+    qdy = _quantize(scheme, dy, 3 * seed, rs, ("row", "col"), scales)
+    qw = _quantize(scheme, w, 3 * seed + 1, rs, ("col",), scales).col
+    qx = _quantize(scheme, x, 3 * seed + 2, rs, ("col",), scales).col
+    dx = gemm(qdy.row, qw, rotated_pair=True)
+    dw = gemm(qdy.col, qx, rotated_pair=True)
     return ((dx, dw), (qdy.row, qw, qdy.col, qx)) if operands else (dx, dw)
 
 
@@ -82,19 +106,19 @@ class QuartetLinearFunction(torch.autograd.Function):
     quantizers' input format; the gradients are returned in the dtypes of X and W."""
 
     @staticmethod
-    def forward(ctx, x, w, seed: int, scheme: str = "eden"):
+    def forward(ctx, x, w, seed: int, scheme: str = "eden", scales: str = "tensor"):
         _check_shapes(x, w)
         x, w = x.contiguous(), w.contiguous()
         ctx.save_for_backward(x, w)
-        ctx.seed, ctx.scheme = int(seed), scheme
-        return forward_product(x, w, int(seed))
+        ctx.seed, ctx.scheme, ctx.scales = int(seed), scheme, scales
+        return forward_product(x, w, int(seed), scales=scales)
 
     @staticmethod
     def backward(ctx, dy):
         x, w = ctx.saved_tensors
         dyb = dy.to(torch.bfloat16).contiguous()
-        dx, dw = backward_products(dyb, x, w, ctx.seed, ctx.scheme)
-        return dx.to(x.dtype), dw.to(w.dtype), None, None
+        dx, dw = backward_products(dyb, x, w, ctx.seed, ctx.scheme, scales=ctx.scales)
+        return dx.to(x.dtype), dw.to(w.dtype), None, None, None
 
 
 class QuartetLinear(torch.nn.Module):
@@ -102,10 +126,13 @@ class QuartetLinear(torch.nn.Module):
     seed (a counter started at `seed`), so repeated steps use fresh rotations and roundings."""
 
     def __init__(self, in_features: int, out_features: int, seed: int = 0,
-                 scheme: str = "eden", device=None):
+                 scheme: str = "eden", device=None, scales: str = "tensor"):
         super().__init__()
         if scheme not in BACKWARD_SCHEMES:
             raise ValueError(f"unknown backward scheme {scheme!r}")
+        if scales not in SCALES:
+            raise ValueError(f"unknown scales {scales!r}")
+        self.scales = scales
         self.weight = torch.nn.Parameter(torch.empty(
             (out_features, in_features), dtype=torch.bfloat16, device=device))
         torch.nn.init.normal_(self.weight, std=0.02)
@@ -115,4 +142,4 @@ class QuartetLinear(torch.nn.Module):
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         s = self._seed
         self._seed += 1
-        return QuartetLinearFunction.apply(x, self.weight, s, self.scheme)
+        return QuartetLinearFunction.apply(x, self.weight, s, self.scheme, self.scales)
