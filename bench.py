@@ -192,6 +192,9 @@ def main():
         },
     }
 
+    if not args.copy_probe:          # the counter runs keep one copy size for calibration
+        result["copy_ceiling"] = copy_ceiling(dev, stream)
+
     if not args.no_gemm:
         result["gemm_check"] = gemm_check(nv, workloads, dev, out.row, stream)
 
@@ -217,6 +220,31 @@ def main():
         result["cpu_baseline"] = cpu_baseline(x_cpu, B)
 
     print(json.dumps(result), flush=True)
+
+
+def copy_ceiling(dev, stream, nbytes=1 << 30, reps=20):
+    """Measured HBM ceiling beside the published peak: a plain device-to-device copy of
+    1 GiB (torch copy_), read + write bytes over the median of `reps` timed copies."""
+    import numpy as np
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"bytes_copied": nbytes, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def gemm_check(nv, workloads, dev, a, stream, reps=5):

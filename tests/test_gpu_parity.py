@@ -267,3 +267,31 @@ def test_graph_capture_and_replay():
                           (out.row.tensor_scale, ref.row.tensor_scale),
                           (out.col.tensor_scale, ref.col.tensor_scale), (back, ref_back)):
             assert torch.equal(got, want), rep
+
+
+def test_concurrent_streams():
+    """Calls on two streams at once, each with its own workspace and outputs, give the same
+    results as one after the other: the library keeps no state between calls.  Calls run on
+    the side streams while the default stream goes on; the inputs were made before them."""
+    print("case: eden_quantize and nvfp4_quantize_strips on two streams at once", flush=True)
+    xa = workloads.c4(seed=3, shape=(1024, 2048)).to(DEV)
+    xb = workloads.normal((2048, 1024), seed=4).to(DEV)
+    ref_a = nv.eden_quantize(xa, 1, 2, layouts=("row", "col"))
+    ref_b = nv.nvfp4_quantize_strips("eden", xb, seed=3, rht_seed=4, layouts=("row", "col"))
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(sa):
+            qa = nv.eden_quantize(xa, 1, 2, layouts=("row", "col"))
+        # the stream argument alone: outputs and workspace are allocated on sb too
+        qb = nv.nvfp4_quantize_strips("eden", xb, seed=3, rht_seed=4, layouts=("row", "col"),
+                                      stream=sb)
+        outs.append((qa, qb))
+    torch.cuda.synchronize()
+    for qa, qb in outs:
+        for got, want in ((qa, ref_a), (qb, ref_b)):
+            for lay in ("row", "col"):
+                g, w = getattr(got, lay), getattr(want, lay)
+                assert torch.equal(g.codes, w.codes) and torch.equal(g.scales, w.scales)
+                assert torch.equal(g.tensor_scale, w.tensor_scale)

@@ -115,6 +115,13 @@ def _stream_ptr(stream, device) -> Optional[int]:
     return s.cuda_stream
 
 
+def _on(stream, device):
+    """Context in which the binding allocates outputs and workspaces: the stream the call is
+    enqueued on, so that the caching allocator hands a freed workspace only to later work on
+    that same stream."""
+    return torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(device))
+
+
 def empty_layout(vecs: int, n: int, device) -> NVFP4:
     """Caller-side allocation of one layout's outputs."""
     return NVFP4(torch.empty((vecs, n // 2), dtype=torch.uint8, device=device),
@@ -129,9 +136,15 @@ def _ct(t: Optional[NVFP4]):
                                  t.tensor_scale.data_ptr()))
 
 
-def _prepare(x: torch.Tensor, layouts: Sequence[str], out: Optional[Quantized], workspace):
+def _prepare(x: torch.Tensor, layouts: Sequence[str], out: Optional[Quantized], workspace,
+             stream=None):
     if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
+    with _on(stream, x.device):
+        return _allocate(x, layouts, out, workspace)
+
+
+def _allocate(x, layouts, out, workspace):
     rows, cols = x.shape
     want_row, want_col = "row" in layouts, "col" in layouts
     if out is None:
@@ -153,7 +166,7 @@ def eden_quantize(x: torch.Tensor, seed: int, rht_seed: int, layouts=("row", "co
                   out: Optional[Quantized] = None, workspace: Optional[torch.Tensor] = None,
                   stream=None) -> Quantized:
     """MS-EDEN NVFP4 quantization (see include/nvfp4.h)."""
-    rows, cols, out, ws = _prepare(x, layouts, out, workspace)
+    rows, cols, out, ws = _prepare(x, layouts, out, workspace, stream)
     _check("eden_quantize", lib().eden_quantize(
         x.data_ptr(), rows, cols, GROUP, BLOCK, seed, rht_seed, _ct(out.row), _ct(out.col),
         ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
@@ -164,7 +177,7 @@ def sr_quantize(x: torch.Tensor, seed: int, rht: bool = False, rht_seed: int = 0
                 layouts=("row",), out: Optional[Quantized] = None,
                 workspace: Optional[torch.Tensor] = None, stream=None) -> Quantized:
     """Plain stochastic-rounding NVFP4 quantization (optionally rotated first)."""
-    rows, cols, out, ws = _prepare(x, layouts, out, workspace)
+    rows, cols, out, ws = _prepare(x, layouts, out, workspace, stream)
     _check("sr_quantize", lib().sr_quantize(
         x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed, _ct(out.row),
         _ct(out.col), ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
@@ -175,7 +188,7 @@ def rtn_quantize(x: torch.Tensor, rht: bool = False, rht_seed: int = 0, layouts=
                  out: Optional[Quantized] = None, workspace: Optional[torch.Tensor] = None,
                  stream=None) -> Quantized:
     """Round-to-nearest NVFP4 quantization (optionally rotated first)."""
-    rows, cols, out, ws = _prepare(x, layouts, out, workspace)
+    rows, cols, out, ws = _prepare(x, layouts, out, workspace, stream)
     _check("rtn_quantize", lib().rtn_quantize(
         x.data_ptr(), rows, cols, GROUP, BLOCK, int(bool(rht)), rht_seed, _ct(out.row),
         _ct(out.col), ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
@@ -186,7 +199,7 @@ def fp46_quantize(x: torch.Tensor, rht: bool = False, rht_seed: int = 0,
                   layouts=("row", "col"), out: Optional[Quantized] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None) -> Quantized:
     """Forward-pass 4/6 NVFP4 quantization (optionally rotated first)."""
-    rows, cols, out, ws = _prepare(x, layouts, out, workspace)
+    rows, cols, out, ws = _prepare(x, layouts, out, workspace, stream)
     _check("fp46_quantize", lib().fp46_quantize(
         x.data_ptr(), rows, cols, GROUP, BLOCK, int(bool(rht)), rht_seed, _ct(out.row),
         _ct(out.col), ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
@@ -199,7 +212,8 @@ def nvfp4_amax(x: torch.Tensor, rht: bool, rht_seed: int = 0, layouts=("row", "c
     if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
     if amax is None:
-        amax = torch.empty((2,), dtype=torch.float32, device=x.device)
+        with _on(stream, x.device):
+            amax = torch.empty((2,), dtype=torch.float32, device=x.device)
     mask = (1 if "row" in layouts else 0) | (2 if "col" in layouts else 0)
     _check("nvfp4_amax", lib().nvfp4_amax(
         x.data_ptr(), x.shape[0], x.shape[1], GROUP, BLOCK, int(bool(rht)), rht_seed, mask,
@@ -211,7 +225,7 @@ def nvfp4_quantize_amax(mode: str, x: torch.Tensor, amax: torch.Tensor, seed: in
                         rht: bool = False, rht_seed: int = 0, layouts=("row", "col"),
                         out: Optional[Quantized] = None, stream=None) -> Quantized:
     """Phase 2: quantizer `mode` ("rtn", "sr", "eden", "fp46") given phase-1 maxima."""
-    rows, cols, out, _ = _prepare(x, layouts, out, amax)
+    rows, cols, out, _ = _prepare(x, layouts, out, amax, stream)
     _check("nvfp4_quantize_amax", lib().nvfp4_quantize_amax(
         MODES[mode], x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
         amax.data_ptr(), _ct(out.row), _ct(out.col), _stream_ptr(stream, x.device)))
@@ -223,7 +237,8 @@ def dequantize(t: NVFP4, rht: bool = False, rht_seed: int = 0,
     """Decode one layout to float32 [vecs, n]; undoes the rotation when rht is set."""
     vecs, n = t.codes.shape[0], t.codes.shape[1] * 2
     if out is None:
-        out = torch.empty((vecs, n), dtype=torch.float32, device=t.codes.device)
+        with _on(stream, t.codes.device):
+            out = torch.empty((vecs, n), dtype=torch.float32, device=t.codes.device)
     _check("dequantize", lib().dequantize(
         _ct(t), vecs, n, GROUP, BLOCK, int(bool(rht)), rht_seed, out.data_ptr(),
         _stream_ptr(stream, t.codes.device)))
@@ -250,12 +265,14 @@ def nvfp4_quantize_strips(mode: str, x: torch.Tensor, seed: int = 0, rht: bool =
     if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
     rows, cols = x.shape
-    if out is None:
-        out = Quantized(empty_strip_layout(rows, cols, x.device) if "row" in layouts else None,
-                        empty_strip_layout(cols, rows, x.device) if "col" in layouts else None)
-    if workspace is None:
-        workspace = torch.empty(strip_workspace_bytes(rows, cols), dtype=torch.uint8,
-                                device=x.device)
+    with _on(stream, x.device):
+        if out is None:
+            out = Quantized(
+                empty_strip_layout(rows, cols, x.device) if "row" in layouts else None,
+                empty_strip_layout(cols, rows, x.device) if "col" in layouts else None)
+        if workspace is None:
+            workspace = torch.empty(strip_workspace_bytes(rows, cols), dtype=torch.uint8,
+                                    device=x.device)
     _check("nvfp4_quantize_strips", lib().nvfp4_quantize_strips(
         MODES[mode], x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
         _ct(out.row), _ct(out.col), workspace.data_ptr(), workspace.numel(),
@@ -268,7 +285,8 @@ def dequantize_strips(t: NVFP4, rht: bool = False, rht_seed: int = 0,
     """Decode one strip-local layout to float32 [vecs, n]."""
     vecs, n = t.codes.shape[0], t.codes.shape[1] * 2
     if out is None:
-        out = torch.empty((vecs, n), dtype=torch.float32, device=t.codes.device)
+        with _on(stream, t.codes.device):
+            out = torch.empty((vecs, n), dtype=torch.float32, device=t.codes.device)
     _check("dequantize_strips", lib().dequantize_strips(
         _ct(t), vecs, n, GROUP, BLOCK, int(bool(rht)), rht_seed, out.data_ptr(),
         _stream_ptr(stream, t.codes.device)))
@@ -283,7 +301,8 @@ def nvfp4_gemm_check_strips(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
     if b.codes.shape[1] * 2 != K:
         raise ValueError("operands disagree on K")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+        with _on(stream, a.codes.device):
+            out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
     _check("nvfp4_gemm_check_strips", lib().nvfp4_gemm_check_strips(
         _ct(a), _ct(b), M, N, K, int(bool(rotated_pair)), out.data_ptr(),
         _stream_ptr(stream, a.codes.device)))
@@ -298,7 +317,8 @@ def nvfp4_gemm_check(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
     if b.codes.shape[1] * 2 != K:
         raise ValueError("operands disagree on K")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+        with _on(stream, a.codes.device):
+            out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
     _check("nvfp4_gemm_check", lib().nvfp4_gemm_check(
         _ct(a), _ct(b), M, N, K, int(bool(rotated_pair)), out.data_ptr(),
         _stream_ptr(stream, a.codes.device)))
