@@ -247,7 +247,7 @@ def copy_ceiling(dev, stream, nbytes=1 << 30, reps=20):
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def gemm_check(nv, workloads, dev, a, stream, reps=5):
+def gemm_check(nv, workloads, dev, a, stream, reps=10, warmup=3):
     """The GEMM check consumer on the bench's quantized activations: A = the MS-EDEN row
     layout of the 16384 x 8192 input, B = the 8192 x 8192 N(0, 0.02) weight quantized by RTN
     with the same rotation along K; C = A B^T in FP32 (M=16384, N=8192, K=8192)."""
@@ -258,7 +258,8 @@ def gemm_check(nv, workloads, dev, a, stream, reps=5):
     b = nv.rtn_quantize(w, rht=True, rht_seed=1, layouts=("row",)).row
     del w
     c = torch.empty((a.codes.shape[0], b.codes.shape[0]), dtype=torch.float32, device=dev)
-    nv.nvfp4_gemm_check(a, b, rotated_pair=True, out=c, stream=stream)
+    for _ in range(warmup):
+        nv.nvfp4_gemm_check(a, b, rotated_pair=True, out=c, stream=stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for e0, e1 in ev:
@@ -266,7 +267,7 @@ def gemm_check(nv, workloads, dev, a, stream, reps=5):
         nv.nvfp4_gemm_check(a, b, rotated_pair=True, out=c, stream=stream)
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
     M, K = a.codes.shape[0], a.codes.shape[1] * 2
     N = b.codes.shape[0]
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
@@ -321,7 +322,7 @@ def modes_table(nv, x, out, amax, stream, reps=40):
     return table
 
 
-def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=5):
+def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=7):
     """One Quartet II linear layer's products at the shape of a 1.9B Llama-style model's
     gate projection (32768 tokens, 2048 -> 8192): forward 4/6 + GEMM, backward MS-EDEN of
     dY (both layouts), W and X + two GEMMs.  Reports the whole forward + backward, the
@@ -340,6 +341,7 @@ def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=5):
 
     def timed(fn):
         fn()
+        fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
@@ -348,7 +350,7 @@ def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=5):
             fn()
             e1.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
 
     def step():
         linear.forward_product(x, w, 1)

@@ -30,6 +30,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
+// VALU instructions the scheduler places after each MFMA in the K loop (2 and 3 measured
+// slower on the 16384 x 8192 x 8192 check; 4 to 8 alike within noise).
+constexpr int VALU_PER_MFMA = 4;
 constexpr int LDS_ROW = BK + 8;          // halfs per LDS row (16-byte pad against bank conflicts)
 constexpr int STAGE = (BM + BN) * LDS_ROW;   // halfs of one A + B stage
 
@@ -51,17 +54,14 @@ __device__ __forceinline__ Raw load_raw(const Operand &op, int64_t rows, int64_t
                                         int64_t k0)
 {
     const int t = threadIdx.x, r = t >> 1, half = t & 1;
-    const int64_t row = row0 + r;
+    // rows past the operand re-read its last row: they only feed entries of C that are not
+    // stored, and the K loop keeps no branch
+    const int64_t row = row0 + r < rows ? row0 + r : rows - 1;
     Raw raw;
-    if (row < rows) {
-        raw.codes = *reinterpret_cast<const uint4 *>(op.codes + row * (K >> 1) + (k0 >> 1) +
-                                                     16 * half);
-        raw.scales = *reinterpret_cast<const uint16_t *>(op.scales + row * (K >> 4) + (k0 >> 4) +
-                                                         2 * half);
-    } else {
-        raw.codes = make_uint4(0u, 0u, 0u, 0u);
-        raw.scales = 0u;
-    }
+    raw.codes = *reinterpret_cast<const uint4 *>(op.codes + row * (K >> 1) + (k0 >> 1) +
+                                                 16 * half);
+    raw.scales = *reinterpret_cast<const uint16_t *>(op.scales + row * (K >> 4) + (k0 >> 4) +
+                                                     2 * half);
     return raw;
 }
 
@@ -111,12 +111,80 @@ __device__ __forceinline__ half8 frag(const _Float16 *lds, int row, int k)
     return *reinterpret_cast<const half8 *>(lds + row * LDS_ROW + k);
 }
 
+struct Frame {
+    Operand A, B;
+    int64_t M, N, K, m0, n0, nk;
+    int wm, wn, lane;
+};
+
+// Eight codes (word k of a thread's 32 elements) times its block scale, as 16 bytes of FP16.
+__device__ __forceinline__ uint4 dq_word(uint32_t w, half2v s)
+{
+    return make_uint4(dq_pair<0>(w, s), dq_pair<1>(w, s), dq_pair<2>(w, s), dq_pair<3>(w, s));
+}
+
+// Scale byte SEL of a thread's two block scales as an FP16 pair.  gfx950's FP8 conversion
+// decodes OCP E4M3 exactly.
+template <int SEL>
+__device__ __forceinline__ half2v scale_pair(uint32_t scales)
+{
+    const _Float16 v = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)scales, SEL);
+    return half2v{v, v};
+}
+
+// One step of the K loop: the MFMAs of slice kt from stage rd, while slice kt + 1 (held in
+// ra, rb as raw codes) is dequantized into stage wr and slice kt + 2 is loaded.  rd and wr are
+// distinct LDS arrays, so the two streams of work are independent.  Each of the four 16-wide
+// k sub-steps reads its fragments, dequantizes one of the four code words of ra and rb, and
+// runs its 8 MFMAs; the scheduling hints alternate one MFMA with a few VALU instructions, so
+// the dequantization issues while the matrix core is busy.  Loads past the last slice
+// re-read the last slice, and the stage written on the last step is never read.
+__device__ __forceinline__ void kstep(const Frame &fr, const _Float16 *__restrict__ rd,
+                                      _Float16 *__restrict__ wr, Raw &ra, Raw &rb, int64_t kt,
+                                      f32x16 (&acc)[2][4])
+{
+    __syncthreads();       // rd written; wr no longer read
+    const Raw qa = ra, qb = rb;
+    const int64_t kn = (kt + 2 < fr.nk ? kt + 2 : fr.nk - 1) * BK;
+    ra = load_raw(fr.A, fr.M, fr.K, fr.m0, kn);
+    rb = load_raw(fr.B, fr.N, fr.K, fr.n0, kn);
+    const int t = threadIdx.x, r = t >> 1, half = t & 1;
+    uint4 *dstA = reinterpret_cast<uint4 *>(wr + r * LDS_ROW + 32 * half);
+    uint4 *dstB = reinterpret_cast<uint4 *>(wr + BM * LDS_ROW + r * LDS_ROW + 32 * half);
+    const uint32_t wa[4] = {qa.codes.x, qa.codes.y, qa.codes.z, qa.codes.w};
+    const uint32_t wb[4] = {qb.codes.x, qb.codes.y, qb.codes.z, qb.codes.w};
+    const half2v sa[2] = {scale_pair<0>(qa.scales), scale_pair<1>(qa.scales)};
+    const half2v sb[2] = {scale_pair<0>(qb.scales), scale_pair<1>(qb.scales)};
+    const _Float16 *As = rd, *Bs = rd + BM * LDS_ROW;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int kl = 16 * q + 8 * (fr.lane >> 5);
+        half8 a[2], b[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = frag(As, fr.wm + 32 * i + (fr.lane & 31), kl);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = frag(Bs, fr.wn + 32 * j + (fr.lane & 31), kl);
+        dstA[q] = dq_word(wa[q], sa[q >> 1]);       // words 0, 1: first block; 2, 3: second
+        dstB[q] = dq_word(wb[q], sb[q >> 1]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0);   // then VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);                       // keep sub-steps apart
+    }
+}
+
 // C[M][N] = f * gA * gB * sum_k A[m][k] * B[n][k].  Grid: (ceil(N/256), ceil(M/256)),
 // 512 threads.  M and N multiples of 32, K a multiple of 64.
 //
-// The K loop is software-pipelined over two LDS stages: while the waves run the MFMAs of
-// slice k from one stage, the same iteration dequantizes slice k + 1 (loaded into
-// registers during the previous iteration) into the other stage and starts loading slice
+// The K loop is software-pipelined over two LDS stages (kstep): the waves run the MFMAs of
+// slice k from one stage while dequantizing slice k + 1 into the other and loading slice
 // k + 2; one barrier per slice.
 __global__ void __launch_bounds__(512, 1) k_gemm(Operand A, Operand B, int64_t M, int64_t N,
                                                  int64_t K, float f, float *__restrict__ C)
@@ -131,43 +199,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm(Operand A, Operand B, int64_t M
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    const int64_t nk = K / BK;
-    if (nk > 0) {
+    const Frame fr{A, B, M, N, K, m0, n0, K / BK, wm, wn, lane};
+    if (fr.nk > 0) {
         Raw ra = load_raw(A, M, K, m0, 0), rb = load_raw(B, N, K, n0, 0);
         store_dequant(ra, lds);
         store_dequant(rb, lds + BM * LDS_ROW);
-        if (nk > 1) {
-            ra = load_raw(A, M, K, m0, BK);
-            rb = load_raw(B, N, K, n0, BK);
-        }
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            __syncthreads();       // stage kt % 2 written; stage (kt + 1) % 2 no longer read
-            const _Float16 *As = lds + (kt & 1) * STAGE, *Bs = As + BM * LDS_ROW;
-            if (kt + 1 < nk) {
-                _Float16 *nxt = lds + ((kt + 1) & 1) * STAGE;
-                store_dequant(ra, nxt);
-                store_dequant(rb, nxt + BM * LDS_ROW);
-                if (kt + 2 < nk) {
-                    ra = load_raw(A, M, K, m0, (kt + 2) * BK);
-                    rb = load_raw(B, N, K, n0, (kt + 2) * BK);
-                }
-            }
-#pragma unroll
-            for (int kk = 0; kk < BK; kk += 16) {
-                const int kl = kk + 8 * (lane >> 5);
-                half8 a[2], b[4];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) a[i] = frag(As, wm + 32 * i + (lane & 31), kl);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = frag(Bs, wn + 32 * j + (lane & 31), kl);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j],
-                                                                           0, 0, 0);
-            }
-        }
+        const int64_t k1 = fr.nk > 1 ? BK : 0;
+        ra = load_raw(A, M, K, m0, k1);
+        rb = load_raw(B, N, K, n0, k1);
+        for (int64_t kt = 0; kt < fr.nk; ++kt)
+            kstep(fr, lds + (kt & 1) * STAGE, lds + ((kt + 1) & 1) * STAGE, ra, rb, kt, acc);
     }
 
     // a wave's 64 rows and 128 columns each lie inside one 128-row strip of their operand
