@@ -27,11 +27,10 @@ namespace nvfp4g {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
-// VALU instructions the scheduler places after each MFMA in the K loop (2 and 3 measured
-// slower on the 16384 x 8192 x 8192 check; 4 to 8 alike within noise).
+// VALU instructions the scheduler places after each MFMA in the K loop (on the 16384 x 8192
+// x 8192 check, 2 was measured slower; 3 to 8 alike within noise).
 constexpr int VALU_PER_MFMA = 4;
 constexpr int LDS_ROW = BK + 8;          // halfs per LDS row (16-byte pad against bank conflicts)
 constexpr int STAGE = (BM + BN) * LDS_ROW;   // halfs of one A + B stage
@@ -71,15 +70,16 @@ __device__ __forceinline__ float e4m3_val(uint32_t c)
     return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-// Eight codes (one 32-bit word) times scale s as four packed FP16 pairs.  The grid values
-// decode exactly to FP32, convert exactly to FP16, and the product of a value (<= 2
-// significant bits) and an E4M3 scale (<= 4) has at most 6 significant bits, between 2^-10
-// and 2688: exact in FP16.
+// Codes 2 SEL and 2 SEL + 1 of a 32-bit word times scale s as a packed FP16 pair.  The grid
+// values decode exactly to FP16 (the conversion's scale operand applies only a power of two,
+// so it stays 1 and the E4M3 scale is a separate multiply), and the product of a value
+// (<= 2 significant bits) and an E4M3 scale (<= 4) has at most 6 significant bits, between
+// 2^-10 and 2688: exact in FP16.
 template <int SEL>
 __device__ __forceinline__ uint32_t dq_pair(uint32_t w, half2v s)
 {
-    const float2v v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(v.x, v.y)) * s;
+    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(
+                                                    w, 1.0f, SEL)) * s;
     return __builtin_bit_cast(uint32_t, h);
 }
 
