@@ -169,8 +169,8 @@ int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int b
  * sign * E4M3(scale) * magnitude of code (m,k) of `a` and likewise for `b`, and f = 2^-7
  * when rotated_pair != 0 (both operands rotated along K with the same rht_seed, so
  * H H = 128 I cancels the rotation) else 1.  a is [M][K] and b is [N][K], both in the
- * row layout (K contiguous, as the quantizers emit); c is FP32 [M][N] row-major (device,
- * 4-byte aligned).  Operand values are dequantized exactly to FP16 and multiplied on the
+ * row layout (K contiguous, as the quantizers emit; codes 16-byte and scales 2-byte
+ * aligned); c is FP32 [M][N] row-major (device, 4-byte aligned).  Operand values are dequantized exactly to FP16 and multiplied on the
  * matrix cores with FP32 accumulation (summation order unspecified).  M and N must be
  * multiples of 32 and K a multiple of 64. */
 int nvfp4_gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,

@@ -123,3 +123,11 @@ def test_strip_entry_points_validate(L):
     assert L.dequantize_strips(r, 4, 100, 128, 16, 0, 0, FAKE, None) == nv.ERR_SHAPE
     assert L.nvfp4_gemm_check_strips(r, r, 48, 64, 128, 1, FAKE, None) == nv.ERR_SHAPE
     assert L.nvfp4_gemm_check_strips(r, r, 64, 64, 128, 3, FAKE, None) == nv.ERR_ARG
+
+
+def test_gemm_alignment(L):
+    ok, odd = _layout(), _layout(scales=FAKE + 4097)
+    assert L.nvfp4_gemm_check(ok, odd, 64, 64, 128, 0, FAKE, None) == nv.ERR_ALIGN
+    assert L.nvfp4_gemm_check(_layout(codes=FAKE + 8), ok, 64, 64, 128, 0, FAKE, None) == \
+        nv.ERR_ALIGN
+    assert L.nvfp4_gemm_check(ok, ok, 64, 64, 128, 0, FAKE + 2, None) == nv.ERR_ALIGN

@@ -177,8 +177,9 @@ int gemm_common(int local, const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t
     if (M % 32 || N % 32 || K % 64) return NVFP4_ERR_SHAPE;
     if (M > 0 && N > 0 && (!c || (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
         return NVFP4_ERR_NULL;
-    if (!aligned(a->codes, 16) || !aligned(b->codes, 16) || !aligned(c, 4) ||
-        !aligned(a->tensor_scale, 4) || !aligned(b->tensor_scale, 4))
+    if (!aligned(a->codes, 16) || !aligned(b->codes, 16) || !aligned(a->scales, 2) ||
+        !aligned(b->scales, 2) || !aligned(c, 4) || !aligned(a->tensor_scale, 4) ||
+        !aligned(b->tensor_scale, 4))
         return NVFP4_ERR_ALIGN;
     int rc = check_device();
     if (rc) return rc;
