@@ -157,6 +157,12 @@ def _allocate(x, layouts, out, workspace):
     return rows, cols, out, workspace
 
 
+def _mode(mode: str) -> int:
+    if mode not in MODES:
+        raise ValueError(f"unknown quantizer mode {mode!r}; use one of {tuple(MODES)}")
+    return MODES[mode]
+
+
 def _check(fn: str, status: int):
     if status != OK:
         raise NVFP4Error(fn, status)
@@ -227,7 +233,7 @@ def nvfp4_quantize_amax(mode: str, x: torch.Tensor, amax: torch.Tensor, seed: in
     """Phase 2: quantizer `mode` ("rtn", "sr", "eden", "fp46") given phase-1 maxima."""
     rows, cols, out, _ = _prepare(x, layouts, out, amax, stream)
     _check("nvfp4_quantize_amax", lib().nvfp4_quantize_amax(
-        MODES[mode], x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
+        _mode(mode), x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
         amax.data_ptr(), _ct(out.row), _ct(out.col), _stream_ptr(stream, x.device)))
     return out
 
@@ -274,7 +280,7 @@ def nvfp4_quantize_strips(mode: str, x: torch.Tensor, seed: int = 0, rht: bool =
             workspace = torch.empty(strip_workspace_bytes(rows, cols), dtype=torch.uint8,
                                     device=x.device)
     _check("nvfp4_quantize_strips", lib().nvfp4_quantize_strips(
-        MODES[mode], x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
+        _mode(mode), x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
         _ct(out.row), _ct(out.col), workspace.data_ptr(), workspace.numel(),
         _stream_ptr(stream, x.device)))
     return out
