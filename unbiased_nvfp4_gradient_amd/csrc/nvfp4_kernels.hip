@@ -1049,8 +1049,36 @@ k_quant(QuantArgs a)
     }
 }
 
-// Dequantize: one lane per (vector, group).  out[vec][pos] fp32.
-// g of vector v is gp[v >> g_shift] (one tensor scale: a shift that maps every vector to 0).
+// Lane q ^ m of v within rows of 16 lanes (m = 1, 2, 4, 8): DPP for 1, 2 and 8, a
+// swizzle for 4.
+template <int M>
+__device__ __forceinline__ float xor16(float v)
+{
+    const int b = __builtin_bit_cast(int, v);
+    int r;
+    if constexpr (M == 1) r = __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false);
+    else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false);
+    else if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(b, b, 0x128, 0xF, 0xF, false);
+    else r = __builtin_amdgcn_ds_swizzle(b, (M << 10) | 0x1F);
+    return __builtin_bit_cast(float, r);
+}
+
+// One butterfly stage of span 8 M across lanes: the lower position takes a + b, the upper
+// a - b (lower - upper), as fma(+-1, mine, partner) with one rounding.
+template <int M>
+__device__ __forceinline__ void cross_stage(float v[8], int q)
+{
+    const float sg = (q & M) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(sg, v[i], xor16<M>(v[i]));
+}
+
+// Dequantize: 16 lanes per (vector, group), lane q holding positions 8q .. 8q + 7, so that
+// the codes (4 bytes), the scale byte and the output (32 bytes) of neighbouring lanes are
+// contiguous.  out[vec][pos] fp32.  g of vector v is gp[v >> g_shift] (one tensor scale: a
+// shift that maps every vector to 0).  With the rotation, the butterfly runs spans 1, 2, 4
+// inside the lane and spans 8 .. 64 across lanes q ^ 1 .. q ^ 8, in ascending order, each
+// output a + b or a - b rounded once.
 template <bool ROT>
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ codes,
                                                  const uint8_t *__restrict__ scales,
@@ -1059,36 +1087,34 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
                                                  float *__restrict__ out)
 {
     const int64_t groups_per_vec = (n + TILE - 1) / TILE;
-    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+    const int q = threadIdx.x & 15;
+    // the 16 lanes of a row share id: they leave together
     if (id >= vecs * groups_per_vec) return;
     const int64_t vec = id / groups_per_vec, gi = id % groups_per_vec;
     const int64_t start = gi * TILE;
     const int len = (n - start) >= TILE ? TILE : (int)(n - start);
+    const bool act = 8 * q < len;
     const float g = gp[vec >> g_shift];
-    float v[TILE];
+    float v[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        if (16 * b < len) {
-            const float den = e4m3_val(scales[vec * (n >> 4) + (start >> 4) + b]) * g;
-            const uint2 cwd = *reinterpret_cast<const uint2 *>(codes + vec * (n >> 1) +
-                                                                (start >> 1) + 8 * b);
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    const int64_t e0 = start + 8 * q;               // first element of this lane
+    if (act) {
+        const uint32_t cw = *reinterpret_cast<const uint32_t *>(codes + vec * (n >> 1) + (e0 >> 1));
+        const float den = e4m3_val(scales[vec * (n >> 4) + (e0 >> 4)]) * g;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t code = ((i < 8 ? cwd.x : cwd.y) >> (4 * (i & 7))) & 15u;
-                const float q = den * e2m1_val(code & 7u);
-                v[16 * b + i] = (code & 8u) ? -q : q;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v[16 * b + i] = 0.0f;
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t code = (cw >> (4 * i)) & 15u;
+            const float qv = den * e2m1_val(code & 7u);
+            v[i] = (code & 8u) ? -qv : qv;
         }
     }
     if (ROT) {
-        const Signs sg = make_signs(rht_seed);
 #pragma unroll
-        for (int h = 1; h < TILE; h <<= 1) {
+        for (int h = 1; h < 8; h <<= 1) {                      // spans 1, 2, 4 in the lane
 #pragma unroll
-            for (int i = 0; i < TILE; ++i) {
+            for (int i = 0; i < 8; ++i) {
                 if ((i & h) == 0) {
                     const float u = v[i], w = v[i + h];
                     v[i] = u + w;
@@ -1096,14 +1122,20 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
                 }
             }
         }
+        cross_stage<1>(v, q);                                  // span 8
+        cross_stage<2>(v, q);                                  // span 16
+        cross_stage<4>(v, q);                                  // span 32
+        cross_stage<8>(v, q);                                  // span 64
+        const Signs sgn = make_signs(rht_seed);
 #pragma unroll
-        for (int p = 0; p < TILE; ++p)
-            v[p] = __uint_as_float(__float_as_uint(v[p]) ^ sign_mask(sg, p)) * 0.0078125f;
+        for (int i = 0; i < 8; ++i)
+            v[i] = __uint_as_float(__float_as_uint(v[i]) ^ sign_mask(sgn, 8 * q + i)) * 0.0078125f;
     }
-    float4 *o = reinterpret_cast<float4 *>(out + vec * n + start);
-#pragma unroll
-    for (int k = 0; k < TILE / 4; ++k)
-        if (4 * k < len) o[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    if (act) {
+        float4 *o = reinterpret_cast<float4 *>(out + vec * n + e0);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
 }
 
 }  // namespace nvfp4k
@@ -1286,7 +1318,7 @@ extern "C" hipError_t nvfp4k_dequantize(int local, const uint8_t *codes, const u
     using namespace nvfp4k;
     const int64_t groups = vecs * ((n + TILE - 1) / TILE);
     if (groups == 0) return hipSuccess;
-    const int64_t blocks = (groups + 255) / 256;
+    const int64_t blocks = (groups + 15) / 16;        // 16 groups of 16 lanes per block
     const int shift = local ? 7 : 62;      // vector -> index of its g (all vectors < 2^31)
     if (rht)
         k_dequant<true><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, shift, vecs, n,
