@@ -44,8 +44,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    # NVFP4_ORACLE_LIB names another build of nvfp4_oracle.c to load instead (the mutation
+    # tests use it to check that the pins reject planted mistakes)
+    other = os.environ.get("NVFP4_ORACLE_LIB")
+    if not other:
+        build()
+    lib = ctypes.CDLL(other or _LIB_PATH)
     c = ctypes
     P = c.c_void_p
     i64, u64, i32, f32 = c.c_int64, c.c_uint64, c.c_int, c.c_float

@@ -179,6 +179,11 @@ uint8_t oracle_e4m3_up(float t)
  * Magnitudes V = {0, 0.5, 1, 1.5, 2, 3, 4, 6} ([TG] Method: grid spans (-6, 6)).
  * Round to nearest, ties to the even magnitude code, saturating at 6. */
 static const float E2M1_V[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+/* The two stochastic-rounding steps (defined below, pinned by enumeration of every random
+ * word); the quantizers call them for every decision they make. */
+uint8_t oracle_scale_sr(float c, uint32_t w);
+int oracle_elem_sr_mag(float a, uint32_t u);
 static const float E2M1_THRESH[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
 
 float oracle_e2m1_value(uint8_t code)
@@ -478,9 +483,9 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                     } else {
                         uint32_t w = rand_word(seed, (uint64_t)k, STREAM_SCALE_SR,
                                                (uint32_t)axis);
+                        out = oracle_scale_sr(c, w);
+                        /* margin: distance of the 20 dropped bits plus the draw from a carry */
                         uint32_t low = bits_of(c) & 0xFFFFFu, add = w >> 12;
-                        uint32_t up_bits = (bits_of(c) + add) & 0xFFF00000u;
-                        out = oracle_e4m3_rne_sat(f32_of(up_bits));   /* exact value */
                         uint32_t sum = low + add;
                         uint32_t d = sum > 0x100000u ? sum - 0x100000u : 0x100000u - sum;
                         m2 = umin(m2, umin(d, umin(ulp_dist(c, 0.015625f),
@@ -520,13 +525,12 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                     if (a >= 6.0f) {
                         mag = 7;
                     } else {
-                        int lo = 0;
+                        int lo = 0;                 /* grid point below a, for the margin */
                         while (E2M1_V[lo + 1] <= a) ++lo;
-                        float frac = (a - E2M1_V[lo]) / (E2M1_V[lo + 1] - E2M1_V[lo]);
                         uint32_t w = rand_word(seed, (uint64_t)(vec * n + e), STREAM_ELEM_SR,
                                                (uint32_t)axis);
                         uint32_t u = w >> 8;
-                        mag = ((float)u < frac * 16777216.0f) ? lo + 1 : lo;
+                        mag = oracle_elem_sr_mag(a, u);
                         double ab = E2M1_V[lo] + ((double)u / 16777216.0) *
                                                      (E2M1_V[lo + 1] - E2M1_V[lo]);
                         em = ulp_dist(a, (float)ab);
