@@ -56,6 +56,16 @@ MUTATIONS = [
      [QUANT + "test_fp46_choice_against_fp64"]),
     ("strip scale from the whole layout", "v0, v1));", "0, total));",
      [STRIP + "test_power_of_two_equivariance_per_strip"]),
+    ("MS-EDEN block scale rounded up", "                s[b] = oracle_e4m3_rne_sat(t);",
+     "                s[b] = oracle_e4m3_up(t);", [QUANT + "test_rtn_codes_are_nearest"]),
+    ("EDEN <r,q> uses r for q", "v = fmaf(x, oracle_e2m1_value(codes[b * BLOCK + i]), v);",
+     "v = fmaf(x, x, v);", [QUANT + "test_eden_ratio_against_fp64"]),
+    ("EDEN <r,r> misses the square", "p = fmaf(x, x, p);", "p = fmaf(x, 1.0f, p);",
+     [QUANT + "test_eden_ratio_is_one_on_grid"]),
+    ("4/6 tensor scale divides by 6 * 448",
+     "float d = (mode == MODE_FP46) ? 1792.0f : 2688.0f;",
+     "float d = (mode == MODE_FP46) ? 2688.0f : 2688.0f;",
+     [QUANT + "test_tensor_max_block_gets_top_scale"]),
 ]
 
 
