@@ -168,10 +168,12 @@ def _check(fn: str, status: int):
         raise NVFP4Error(fn, status)
 
 
-def eden_quantize(x: torch.Tensor, seed: int, rht_seed: int, layouts=("row", "col"),
-                  out: Optional[Quantized] = None, workspace: Optional[torch.Tensor] = None,
-                  stream=None) -> Quantized:
-    """MS-EDEN NVFP4 quantization (see include/nvfp4.h)."""
+def eden_quantize(x: torch.Tensor, seed: int, rht_seed: Optional[int] = None,
+                  layouts=("row", "col"), out: Optional[Quantized] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> Quantized:
+    """MS-EDEN NVFP4 quantization (see include/nvfp4.h).  rht_seed defaults to seed; both
+    operands of one GEMM must pass the same rht_seed."""
+    rht_seed = seed if rht_seed is None else rht_seed
     rows, cols, out, ws = _prepare(x, layouts, out, workspace, stream)
     _check("eden_quantize", lib().eden_quantize(
         x.data_ptr(), rows, cols, GROUP, BLOCK, seed, rht_seed, _ct(out.row), _ct(out.col),
