@@ -169,6 +169,26 @@ def test_config4_eden_sampled():
         assert_parity("eden", codes[ids], scales[ids], g, ref, f"c4 axis={axis}")
 
 
+@pytest.mark.parametrize("mode,rht", [("sr", True), ("sr", False), ("rtn", True),
+                                      ("rtn", False), ("fp46", True)])
+def test_config4_other_modes_sampled(mode, rht):
+    """Every other quantizer of the benchmark's modes table on the full 16384 x 8192 input:
+    exact tensor scale, sampled vectors of both layouts."""
+    print(f"case: c4 16384x8192 {mode} rht={rht} both layouts, sampled vectors", flush=True)
+    x = workloads.c4()
+    xb = workloads.bf16_bits(x)
+    got = run_gpu(mode, x, ("row", "col"), seed=3, rht=rht, rht_seed=2)
+    rng = np.random.default_rng(1)
+    for axis in (0, 1):
+        codes, scales, g, _ = got[axis]
+        ref_g = oracle.tensor_scale(mode, oracle.amax(xb, axis, rht, 2))
+        assert np.float32(g) == np.float32(ref_g)
+        nvec = codes.shape[0]
+        ids = np.unique(np.concatenate([[0, nvec - 1], rng.choice(nvec, 32, replace=False)]))
+        ref = oracle.quantize_vectors(mode, xb, axis, ids, ref_g, seed=3, rht=rht, rht_seed=2)
+        assert_parity(mode, codes[ids], scales[ids], g, ref, f"c4 {mode} axis={axis}")
+
+
 # ----------------------------------------------------------------------------- dequantize
 
 @pytest.mark.parametrize("mode,rht", [("eden", True), ("rtn", False), ("fp46", True)])
