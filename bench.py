@@ -95,6 +95,8 @@ def main():
                     help="skip the linear-layer (forward + backward) measurement")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the per-quantizer throughput table")
+    ap.add_argument("--no-training-step", action="store_true",
+                    help="skip the one-training-step quantization batch (504 calls)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (3x): the calibration kernel "
                          "for HBM byte counters")
@@ -203,6 +205,9 @@ def main():
 
     if not args.no_linear:
         result["linear_layer"] = linear_layer(nv, dev)
+
+    if not args.no_training_step:
+        result["training_step_quantizations"] = training_step(nv, dev)
 
     if args.copy_probe:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -392,6 +397,68 @@ def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=7):
             "gemm_tflops": round(flops / (ms_gemm * 1e-3) / 1e12, 1),
             "bf16_torch_mm_ms": round(ms_bf16, 3),
             "bf16_torch_mm_tflops": round(flops / (ms_bf16 * 1e-3) / 1e12, 1)}
+
+
+def training_step(nv, dev, tokens=32768, hidden=2048, ffn=8192, layers=24, reps=3):
+    """One training step's linear-layer quantizations of a 1.9B Llama-style model on one
+    stream: per layer and projection (q, k, v, o, gate, up, down), 4/6 of the weight (both
+    layouts) and of the activation (row layout), MS-EDEN of the grad-output (both layouts),
+    GEMM partners sharing a rotation seed; 504 calls.  Synthetic X, dY ~ N(0,1), W ~
+    N(0, 0.02), one buffer per shape.  Median of `reps` timed steps after one warm-up."""
+    import numpy as np
+    import torch
+
+    proj = [(hidden, hidden)] * 4 + [(ffn, hidden), (ffn, hidden), (hidden, ffn)]
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def randn(shape, std):
+        return (torch.randn(shape, generator=g, device=dev) * std).to(torch.bfloat16)
+
+    acts = {d: randn((tokens, d), 1.0) for d in (hidden, ffn)}
+    grads = {d: randn((tokens, d), 1.0) for d in (hidden, ffn)}
+    weights = {s: randn(s, 0.02) for s in set(proj)}
+    outw = {s: nv.Quantized(nv.empty_layout(s[0], s[1], dev), nv.empty_layout(s[1], s[0], dev))
+            for s in weights}
+    outx = {d: nv.Quantized(nv.empty_layout(tokens, d, dev), None) for d in (hidden, ffn)}
+    outd = {d: nv.Quantized(nv.empty_layout(tokens, d, dev), nv.empty_layout(d, tokens, dev))
+            for d in (hidden, ffn)}
+    ws = torch.empty(nv.workspace_bytes(tokens, ffn, 3), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        for layer in range(layers):
+            for p, (o, i) in enumerate(proj):
+                rs = 1000 * layer + 10 * p
+                nv.fp46_quantize(weights[(o, i)], rht=True, rht_seed=rs, layouts=("row", "col"),
+                                 out=outw[(o, i)], workspace=ws, stream=stream)
+                nv.fp46_quantize(acts[i], rht=True, rht_seed=rs, layouts=("row",),
+                                 out=outx[i], workspace=ws, stream=stream)
+                nv.eden_quantize(grads[o], seed=rs + 3, rht_seed=rs, layouts=("row", "col"),
+                                 out=outd[o], workspace=ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    read = written = 0
+    for o, i in proj:
+        read += 2 * (o * i + tokens * i + tokens * o)
+        written += 2 * (o * i // 2 + o * i // 16) + (tokens * i // 2 + tokens * i // 16)
+        written += 2 * (tokens * o // 2 + tokens * o // 16)
+    read *= layers
+    written *= layers
+    return {"workload": f"{layers} layers x 7 projections x 3 calls, {tokens} tokens, "
+                        f"hidden {hidden}, FFN {ffn}",
+            "calls": 3 * len(proj) * layers, "ms": round(ms, 3),
+            "algorithmic_GB": round((read + written) / 1e9, 2),
+            "GB/s": round((read + written) / (ms * 1e-3) / 1e9, 1)}
 
 
 def rel_mse(nv, xd, mode, layout):
