@@ -50,9 +50,9 @@
  *   Aliasing.   Output buffers must not overlap one another, the input or the workspace;
  *               overlapping buffers give undefined results.
  *   Workspace.  Device scratch of at least nvfp4_workspace_bytes() bytes, 256-byte aligned,
- *               owned by the caller.  The library clears what it uses on the stream; its
- *               contents between calls do not matter.  Concurrent calls need distinct
- *               workspaces.
+ *               owned by the caller.  On the stream, the library writes every byte of it
+ *               that it reads before reading it; its contents between calls do not matter.
+ *               Concurrent calls need distinct workspaces.
  *   Seeds.      rht_seed selects the rotation's random signs, shared by every group and both
  *               layouts; both operands of one GEMM must use the same rht_seed.  seed drives
  *               stochastic rounding (Philox4x32-10 counter streams).
@@ -92,7 +92,9 @@ typedef struct nvfp4_tensor {
 } nvfp4_tensor;
 
 /* Bytes of workspace the quantizers need for a rows x cols input and the layouts in
- * layouts_mask (bit 0 = row, bit 1 = column).  Never fails; 0 means none needed. */
+ * layouts_mask (bit 0 = row, bit 1 = column).  Never fails; 0 means none needed.  Today a
+ * fixed 16 KiB: the two partial maxima (row, column) of each phase-1 workgroup (at most
+ * 2048), which every phase-2 workgroup reduces before it rounds a scale. */
 size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int layouts_mask);
 
 /* Human-readable text for a status code (static storage). */

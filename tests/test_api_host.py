@@ -39,7 +39,7 @@ def test_strerror_and_workspace(L):
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert nv.strerror(s)
     assert nv.strerror(-99) == "unknown status"
-    assert nv.workspace_bytes(16384, 8192, 3) >= 8
+    assert nv.workspace_bytes(16384, 8192, 3) == 16384 == nv.workspace_bytes(0, 0, 1)
 
 
 def _layout(codes=FAKE, scales=FAKE + 4096, g=FAKE + 8192):
@@ -47,7 +47,7 @@ def _layout(codes=FAKE, scales=FAKE + 4096, g=FAKE + 8192):
 
 
 def _eden(L, x=FAKE, rows=256, cols=256, group=128, block=16, row=True, col=True, ws=FAKE,
-          wsb=256, row_t=None, col_t=None):
+          wsb=16384, row_t=None, col_t=None):
     r = row_t if row_t is not None else (_layout() if row else None)
     c = col_t if col_t is not None else (_layout(FAKE + 65536, FAKE + 69632, FAKE + 73728)
                                          if col else None)
@@ -70,6 +70,7 @@ def test_validation_errors(L):
     assert _eden(L, row_t=_layout(scales=FAKE + 4)) == nv.ERR_ALIGN
     assert _eden(L, ws=0) == nv.ERR_WORKSPACE
     assert _eden(L, wsb=8) == nv.ERR_WORKSPACE
+    assert _eden(L, wsb=16384 - 1) == nv.ERR_WORKSPACE       # two floats x 2048 workgroups
     assert _eden(L, rows=1 << 32) == nv.ERR_ARG
     # sr / rtn / fp46 without rotation accept n % 16
     assert L.sr_quantize(FAKE, 256, 200, 128, 16, 1, 0, 1, _layout(), None, FAKE, 256,

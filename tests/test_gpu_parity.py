@@ -252,9 +252,32 @@ def test_nonfinite_inputs_complete():
 
 # ----------------------------------------------------------------------------- HIP graphs
 
+@pytest.mark.parametrize("layouts", [("row", "col"), ("row",), ("col",)])
+def test_workspace_contents_do_not_matter(layouts):
+    """Phase 1 leaves one maximum per workgroup and layout in the workspace and phase 2
+    reduces them: a workspace full of 0xFF bytes (larger than any maximum, compared as
+    unsigned integers) must give the same result as a zeroed one, in every mode."""
+    print(f"case: workspace filled with 0xFF, layouts {layouts}", flush=True)
+    x = workloads.c4(seed=12, shape=(640, 768)).to(DEV)
+    for name, fn, kw in (("eden", nv.eden_quantize, dict(seed=3, rht_seed=4)),
+                         ("sr", nv.sr_quantize, dict(seed=3, rht=True, rht_seed=4)),
+                         ("rtn", nv.rtn_quantize, dict(rht=False)),
+                         ("fp46", nv.fp46_quantize, dict(rht=True, rht_seed=4))):
+        outs = []
+        for fill in (0, 255):
+            ws = torch.full((nv.workspace_bytes(640, 768, 3),), fill, dtype=torch.uint8,
+                            device=DEV)
+            outs.append(fn(x, layouts=layouts, workspace=ws, **kw))
+        torch.cuda.synchronize()
+        for lay in layouts:
+            a, b = getattr(outs[0], lay), getattr(outs[1], lay)
+            for f in ("codes", "scales", "tensor_scale"):
+                assert torch.equal(getattr(a, f), getattr(b, f)), (name, lay, f)
+
+
 def test_graph_capture_and_replay():
-    """The entry points allocate nothing and clear their workspace with a kernel, so a call
-    can be captured in a HIP graph.  Each replay (with other quantizer work run eagerly in
+    """The entry points allocate nothing and write every workspace slot they read (no
+    memset), so a call can be captured in a HIP graph.  Each replay (with other quantizer work run eagerly in
     between) must give the eager result bit for bit."""
     print("case: HIP graph capture of eden_quantize + dequantize, 4 replays", flush=True)
     x = workloads.normal((384, 512), seed=77).to(DEV)

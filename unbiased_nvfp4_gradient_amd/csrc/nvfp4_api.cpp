@@ -13,6 +13,12 @@ extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x
                                    uint8_t *codes1, uint8_t *scales1, float *g1,
                                    const float *amax, uint64_t seed, uint64_t rht_seed,
                                    hipStream_t st);
+extern "C" size_t nvfp4k_workspace(void);
+extern "C" hipError_t nvfp4k_quantize(int mode, int rht, int layouts, const void *x, int64_t R,
+                                      int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
+                                      uint8_t *codes1, uint8_t *scales1, float *g1,
+                                      void *workspace, uint64_t seed, uint64_t rht_seed,
+                                      hipStream_t st);
 extern "C" size_t nvfp4k_strip_workspace(int64_t R, int64_t C);
 extern "C" hipError_t nvfp4k_quant_strips(int mode, int rht, int layouts, const void *x,
                                           int64_t R, int64_t C, uint8_t *codes0,
@@ -32,7 +38,7 @@ namespace {
 
 enum { MODE_RTN = 0, MODE_SR = 1, MODE_EDEN = 2, MODE_FP46 = 3 };
 
-constexpr size_t WORKSPACE_BYTES = 256;       // two u32 amax slots, padded
+constexpr size_t MIN_WORKSPACE_BYTES = 256;   // smallest workspace any quantizer asks for
 constexpr int64_t MAX_DIM = (int64_t)1 << 31; // each dimension
 constexpr int64_t MAX_ELEMS = (int64_t)1 << 40;
 
@@ -106,9 +112,9 @@ int launch_quant(int mode, const void *x, int64_t rows, int64_t cols, uint64_t s
 // padded to 256 bytes.
 size_t strip_workspace_bytes(int64_t rows, int64_t cols)
 {
-    if (rows < 0 || cols < 0 || rows > MAX_DIM || cols > MAX_DIM) return WORKSPACE_BYTES;
+    if (rows < 0 || cols < 0 || rows > MAX_DIM || cols > MAX_DIM) return MIN_WORKSPACE_BYTES;
     const size_t b = nvfp4k_strip_workspace(rows, cols);
-    return b < WORKSPACE_BYTES ? WORKSPACE_BYTES : (b + 255) / 256 * 256;
+    return b < MIN_WORKSPACE_BYTES ? MIN_WORKSPACE_BYTES : (b + 255) / 256 * 256;
 }
 
 int quantize_common(int local, int mode, const void *x, int64_t rows, int64_t cols, int group,
@@ -121,28 +127,20 @@ int quantize_common(int local, int mode, const void *x, int64_t rows, int64_t co
     rc = check_input(mode, x, rows, cols, group, block, rht, row_out != nullptr,
                      col_out != nullptr);
     if (rc) return rc;
-    const size_t need = local ? strip_workspace_bytes(rows, cols) : WORKSPACE_BYTES;
+    const size_t need = local ? strip_workspace_bytes(rows, cols) : nvfp4k_workspace();
     if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
     rc = check_device();
     if (rc) return rc;
     const int layouts = (row_out ? 1 : 0) | (col_out ? 2 : 0);
     const bool rotated = rht || mode == MODE_EDEN;
-    hipError_t e;
-    if (local) {
-        e = nvfp4k_quant_strips(
-            mode, rotated ? 1 : 0, layouts, x, rows, cols, row_out ? row_out->codes : nullptr,
-            row_out ? row_out->scales : nullptr, row_out ? row_out->tensor_scale : nullptr,
-            col_out ? col_out->codes : nullptr, col_out ? col_out->scales : nullptr,
-            col_out ? col_out->tensor_scale : nullptr, workspace, seed, rht_seed,
-            static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
-    }
-    float *amax = static_cast<float *>(workspace);
-    e = nvfp4k_amax(rotated ? 1 : 0, layouts, x, rows, cols, amax, rht_seed,
-                    static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return NVFP4_ERR_HIP;
-    return launch_quant(mode, x, rows, cols, seed, rht, rht_seed, amax, row_out, col_out, stream);
+    const hipError_t e = (local ? nvfp4k_quant_strips : nvfp4k_quantize)(
+        mode, rotated ? 1 : 0, layouts, x, rows, cols, row_out ? row_out->codes : nullptr,
+        row_out ? row_out->scales : nullptr, row_out ? row_out->tensor_scale : nullptr,
+        col_out ? col_out->codes : nullptr, col_out ? col_out->scales : nullptr,
+        col_out ? col_out->tensor_scale : nullptr, workspace, seed, rht_seed,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 int dequantize_common(int local, const nvfp4_tensor *in, int64_t vecs, int64_t n, int group,
@@ -198,7 +196,7 @@ size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int layouts_mask)
     (void)rows;
     (void)cols;
     (void)layouts_mask;
-    return WORKSPACE_BYTES;
+    return nvfp4k_workspace();
 }
 
 const char *nvfp4_strerror(int status)

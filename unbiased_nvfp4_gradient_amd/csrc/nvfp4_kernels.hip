@@ -496,9 +496,12 @@ struct QuantArgs {
     const uint16_t *x;
     int64_t R, C;
     LayoutOut out[2];          // [0] row layout, [1] column layout
-    // fp32 bits of max |r| (phase 1 output): [0] row, [1] column; with strip-local scales,
-    // [tile][layout][wave] the maximum of each of the 4 waves of a layout over each tile
+    // fp32 bits of max |r| (phase 1 output): [0] row, [1] column when nparts == 0; else
+    // [nparts][2] the maxima of each phase-1 workgroup, reduced by every phase-2 workgroup;
+    // with strip-local scales, [tile][layout][wave] the maximum of each of the 4 waves of a
+    // layout over each tile
     uint32_t *amax_bits;
+    int64_t nparts;
     // strip-local scales: [tiles_r row strips, then tiles_c column strips][128] scale tables
     float4 *tables;
     uint64_t seed, rht_seed;
@@ -617,8 +620,10 @@ __device__ __forceinline__ void store_wave_max(const QuantArgs &a, const Role &r
 }
 
 // Pass 1: amax of |r| per layout.  Persistent workgroups walk the tiles with two LDS
-// buffers (the next tile streams in while the current one is processed); one atomicMax
-// per workgroup and layout at the end; with LOCAL, one store per wave and tile instead.
+// buffers (the next tile streams in while the current one is processed).  At the end each
+// workgroup stores its two maxima in its own slots (nparts > 0), or takes one atomicMax per
+// layout into amax_bits[0..1] (nparts == 0: the caller cleared them); with LOCAL, one store
+// per wave and tile instead.
 template <bool ROT, int LAY, bool LOCAL>
 __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
 {
@@ -671,10 +676,39 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
     __syncthreads();
     if ((t & 63) == 0) atomicMax(&wmax[ro.lay], __float_as_uint(local));
     __syncthreads();
-    if (t == 0) {
+    if (a.nparts > 0) {
+        if (t < 2) a.amax_bits[2 * blockIdx.x + t] = wmax[t];    // 0 for a layout not run
+    } else if (t == 0) {
         if (LAY & LAY_ROW) atomicMax(&a.amax_bits[0], wmax[0]);
         if (LAY & LAY_COL) atomicMax(&a.amax_bits[1], wmax[1]);
     }
+}
+
+// fp32 bits of the maximum |r| of layout lay (wave-uniform): the phase-1 result, or the
+// largest of the per-workgroup maxima.  Compared as unsigned integers, as the atomics do.
+__device__ __forceinline__ uint32_t layout_amax_bits(const QuantArgs &a, int lay)
+{
+    if (a.nparts == 0) return a.amax_bits[lay];
+    const int lane = threadIdx.x & 63;
+    uint32_t m0 = 0u, m1 = 0u;
+    int64_t i = lane;
+    for (; i + 64 < a.nparts; i += 128) {
+        m0 = max(m0, a.amax_bits[2 * i + lay]);
+        m1 = max(m1, a.amax_bits[2 * (i + 64) + lay]);
+    }
+    if (i < a.nparts) m0 = max(m0, a.amax_bits[2 * i + lay]);
+    uint32_t m = max(m0, m1);
+#define ROR_UMAX(n) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x120 + (n), \
+                                                                    0xF, 0xF, false));
+    ROR_UMAX(1);
+    ROR_UMAX(2);
+    ROR_UMAX(4);
+    ROR_UMAX(8);
+#undef ROR_UMAX
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0),
+                   (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)m, 32),
+                   (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
 }
 
 // Round-to-nearest of one 1x16 block rb[0..15] with scale code s (table entry e):
@@ -998,9 +1032,18 @@ k_quant(QuantArgs a)
     // select this lane's layout without indexing the argument struct at run time
     const LayoutOut o = (ro.lay == 0) ? a.out[0] : a.out[1];
     build_sign_table(st, a.rht_seed, ROT);
+    int64_t k = blockIdx.x, r0 = 0, c0 = 0;
+    if constexpr (LAY == LAY_BOTH) {
+        // the first tile streams in while the tensor scale is reduced and its table built
+        if (k < a.tiles) {
+            tile_origin(a, a.tiles - 1 - k, r0, c0);
+            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+            if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
+        }
+    }
     if constexpr (!LOCAL) {
         const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
-        const float g = __uint_as_float(ro.lay == 0 ? a.amax_bits[0] : a.amax_bits[1]) / D;
+        const float g = __uint_as_float(layout_amax_bits(a, ro.lay)) / D;
         build_scale_table(tb0, g, t & 255);
         if (blockIdx.x == 0 && (t & 255) == 0) *o.g = g;
     }
@@ -1008,8 +1051,7 @@ k_quant(QuantArgs a)
         // one layout: a single tile buffer, so that four workgroups of 4 waves fit a CU and
         // hide each other's loads (two buffers leave room for two).  The amax pass keeps
         // two buffers: its lighter work per tile does not cover a load.
-        for (int64_t k = blockIdx.x; k < a.tiles; k += gridDim.x) {
-            int64_t r0, c0;
+        for (; k < a.tiles; k += gridDim.x) {
             tile_origin(a, a.tiles - 1 - k, r0, c0);
             __syncthreads();                               // previous tile and table read
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
@@ -1020,12 +1062,6 @@ k_quant(QuantArgs a)
         return;
     }
     __shared__ Tile tile1;
-    int64_t k = blockIdx.x, r0, c0;
-    if (k < a.tiles) {
-        tile_origin(a, a.tiles - 1 - k, r0, c0);
-        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
-        if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
-    }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
         __syncthreads();                                   // tile0 landed; tile1 is free
@@ -1173,20 +1209,26 @@ static int grid_for(K kernel, int threads, int64_t tiles)
     return (int)(tiles < cap ? tiles : cap);
 }
 
+// Phase-1 workgroups at most (their maxima fill the quantizers' workspace).
+constexpr int64_t MAX_PARTS = 2048;
+
+// Returns the number of workgroups launched.
 template <bool ROT, int LAY, bool LOCAL>
-static void launch_amax(const QuantArgs &a, hipStream_t st)
+static int64_t launch_amax(const QuantArgs &a, hipStream_t st)
 {
     const int threads = 64 * waves_for(LAY);
-    k_amax<ROT, LAY, LOCAL><<<grid_for(k_amax<ROT, LAY, LOCAL>, threads, a.tiles), threads, 0,
-                              st>>>(a);
+    int64_t grid = grid_for(k_amax<ROT, LAY, LOCAL>, threads, a.tiles);
+    if (grid > MAX_PARTS) grid = MAX_PARTS;
+    k_amax<ROT, LAY, LOCAL><<<(unsigned)grid, threads, 0, st>>>(a);
+    return grid;
 }
 
 template <bool ROT, bool LOCAL>
-static void amax_lay(const QuantArgs &a, int lay, hipStream_t st)
+static int64_t amax_lay(const QuantArgs &a, int lay, hipStream_t st)
 {
-    if (lay == LAY_ROW) launch_amax<ROT, LAY_ROW, LOCAL>(a, st);
-    else if (lay == LAY_COL) launch_amax<ROT, LAY_COL, LOCAL>(a, st);
-    else launch_amax<ROT, LAY_BOTH, LOCAL>(a, st);
+    if (lay == LAY_ROW) return launch_amax<ROT, LAY_ROW, LOCAL>(a, st);
+    if (lay == LAY_COL) return launch_amax<ROT, LAY_COL, LOCAL>(a, st);
+    return launch_amax<ROT, LAY_BOTH, LOCAL>(a, st);
 }
 
 template <int MODE, bool ROT, int LAY, bool LOCAL>
@@ -1229,6 +1271,7 @@ static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_b
     a.out[0] = {nullptr, nullptr, nullptr};
     a.out[1] = {nullptr, nullptr, nullptr};
     a.amax_bits = amax_bits;
+    a.nparts = 0;
     a.tables = nullptr;
     a.seed = seed;
     a.rht_seed = rht_seed;
@@ -1274,6 +1317,37 @@ extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x
                                     (layouts & LAY_COL) ? g1 : nullptr);
         return hipGetLastError();
     }
+    quant_mode<false>(a, mode, rht, layouts, st);
+    return hipGetLastError();
+}
+
+// Bytes of workspace the one-call quantizers need: two maxima per phase-1 workgroup.
+extern "C" size_t nvfp4k_workspace(void) { return 8 * (size_t)nvfp4k::MAX_PARTS; }
+
+// One-call quantization with one tensor scale per layout: phase 1 leaves each workgroup's
+// maxima in the workspace (no clearing needed: every slot read is written), and each
+// phase-2 workgroup reduces them before it rounds any scale.
+extern "C" hipError_t nvfp4k_quantize(int mode, int rht, int layouts, const void *x, int64_t R,
+                                      int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
+                                      uint8_t *codes1, uint8_t *scales1, float *g1,
+                                      void *workspace, uint64_t seed, uint64_t rht_seed,
+                                      hipStream_t st)
+{
+    using namespace nvfp4k;
+    if (mode < MODE_RTN || mode > MODE_FP46) return hipErrorInvalidValue;
+    uint32_t *parts = static_cast<uint32_t *>(workspace);
+    if (R * C == 0) {
+        // nothing to reduce: amax = 0, so g = 0 for each requested layout
+        k_zero_u32<<<1, 64, 0, st>>>(parts, 2);
+        k_write_g<<<1, 64, 0, st>>>(parts, 1.0f, (layouts & LAY_ROW) ? g0 : nullptr,
+                                    (layouts & LAY_COL) ? g1 : nullptr);
+        return hipGetLastError();
+    }
+    QuantArgs a = make_args(x, R, C, parts, seed, rht_seed);
+    a.out[0] = {codes0, scales0, g0};
+    a.out[1] = {codes1, scales1, g1};
+    a.nparts = 1;                                   // phase 1: store per-workgroup maxima
+    a.nparts = rht ? amax_lay<true, false>(a, layouts, st) : amax_lay<false, false>(a, layouts, st);
     quant_mode<false>(a, mode, rht, layouts, st);
     return hipGetLastError();
 }
