@@ -14,11 +14,17 @@ brackets each phase-2 launch (a marker placed elsewhere in the step, or two mark
 row, adds a dispatch gap of its own).  Phase 2 is bound by VALU issue, so its roofline is
 the ALU one: per element and layout the method performs 14 operations -- the sign flip,
 the 7 butterfly stages, the 1x16 |r| maximum, the scaling, the rounding to E2M1, the grid
-value of the code and the two EDEN multiply-adds -- against a peak of one VALU operation
-per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 Top/s (packed FP32
-instructions are not used).  The HBM view of the same kernel is reported beside it, and
-the HBM bytes it moves come from the committed rocprofv3 counter summary while the kernel
-source is unchanged since those counters were taken.
+value of the code and the two EDEN multiply-adds -- against MI355X's published FP32 vector
+peak, 157.3 TFLOP/s, counted as one operation per FMA lane: 256 CUs x 4 SIMDs x 32 lanes x
+2.4 GHz = 78.64 Top/s.  Plain FP32 add/mul/FMA and XOR/add/bitop3 issue at that width on
+this chip without packed instructions; max, shifts, DPP, permutes and 32-bit multiplies at
+half of it, the FP4/FP8 conversions at a quarter (the package's valu_rates program measures
+each).  So the kernel's own instruction mix caps it well below the peak; the issue view
+reports the VALU instructions the kernel issues per second (per launch from the committed
+counters, over the launch time) against the same peak.  The HBM
+view of the same kernel is reported beside it, and the HBM bytes it moves come from the
+committed rocprofv3 counter summary while the kernel source is unchanged since those
+counters were taken.
 
 Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU.
 """
@@ -34,7 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12     # 39.32: one op per lane per clock
+VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12     # 78.64: 157.3 TFLOP/s FP32, FMA = 1 op
 QUANT_OPS_PER_ELEM_LAYOUT = 14                   # MS-EDEN phase 2, see the docstring
 ROWS, COLS = 16384, 8192
 METRIC = "MS-EDEN NVFP4 quantize GB/s & % HBM peak, 16384×8192 bf16; MSE vs SR"
@@ -61,10 +67,9 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per k_quant launch from the committed counter summary: FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for a device
-    copy of known size.  None when the summary is missing or was taken on other sources."""
+def pmc_record():
+    """The committed counter summary's machine-readable record for k_quant, or None when the
+    summary is missing or was taken on other kernel sources."""
     try:
         with open(PMC_PROFILE, encoding="utf-8") as f:
             text = f.read()
@@ -75,6 +80,14 @@ def measured_traffic():
         return None
     d = json.loads(m.group(1))
     if d.get("source_sha256") != kernel_source_hash():
+        return None
+    return d
+
+
+def measured_traffic(d):
+    """HBM bytes per k_quant launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for a device copy of known size."""
+    if d is None:
         return None
     fetch = d["fetch_kib"] * d["copy_bytes"] / d["copy_fetch_kib"]
     write = d["write_kib"] * d["copy_bytes"] / d["copy_write_kib"]
@@ -145,6 +158,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
+    pmc = pmc_record()
     ms_step = (t1 - t0) * 1e3 / args.steps
     quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     step_ms_ev = start.elapsed_time(events[-1][1]) / args.steps
@@ -186,11 +200,12 @@ def main():
             "peak": round(VALU_PEAK_TOPS, 2),
             "unit": "Top/s (VALU lane operations; algorithmic, 14 per element and layout)",
             "frac": round(tops / VALU_PEAK_TOPS, 4),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic(pmc),
             "ops_per_launch": ops,
             "hbm_view": {"achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes_per_launch": B},
+            "issue_view": issue_view(pmc, quant_ms),
         },
     }
 
@@ -225,6 +240,17 @@ def main():
         result["cpu_baseline"] = cpu_baseline(x_cpu, B)
 
     print(json.dumps(result), flush=True)
+
+
+def issue_view(d, quant_ms):
+    """VALU instructions k_quant issues per launch (SQ_INSTS_VALU from the committed counters)
+    as wave-lane instructions per second, against the 78.64 T peak."""
+    if d is None or "valu_insts" not in d:
+        return None
+    n = d["valu_insts"]
+    rate = n * 64 / (quant_ms * 1e-3) / 1e12
+    return {"valu_wave_instr_per_launch": n, "achieved": round(rate, 2),
+            "unit": "T lane-instructions/s", "frac": round(rate / VALU_PEAK_TOPS, 4)}
 
 
 def copy_ceiling(dev, stream, nbytes=1 << 30, reps=20):
