@@ -444,6 +444,61 @@ __device__ __forceinline__ void fwht_pair_blocks(float r[HALF], int h, float bma
     }
 }
 
+// Phase 1 needs only max |r| over the group, and the signs of the last two stages' inputs
+// do not matter for it.  After the in-lane spans 1..16 the low lane holds quarters q0, q1
+// (positions 0..31, 32..63) and the high lane q2, q3.  Span 32 gives s = q0 + q1, d = q0 - q1
+// in the low lane and s', d' in the high lane, and the group's outputs are s +- s' and
+// d +- d'.  Since max(|u + v|, |u - v|) = |u| + |v| and binary32 rounding is monotone and
+// symmetric in sign, the largest |output| is the largest of fl(|s_k| + |s'_k|) and
+// fl(|d_k| + |d'_k|) over k: 64 sums, not 128 outputs.  The low lane stores (s, d) in
+// registers (k, k + 32), the high lane (d', s') -- A + m*B and A - m*B with m = +-1, one
+// exact FMA each -- so one DPP read of the partner's register k + 32 gives the low lane s'_k
+// and the high lane d_k: each lane forms 32 sums |own k| + |partner k + 32| and their max.
+__device__ __forceinline__ float fwht_pair_absmax(float r[HALF], int h)
+{
+#pragma unroll
+    for (int s = 1; s < HALF / 2; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            if ((i & s) == 0) {
+                const float u = r[i], v = r[i + s];
+                r[i] = u + v;
+                r[i + s] = u - v;
+            }
+        }
+    }
+    const float m = h ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < HALF / 2; ++i) {
+        const float u = r[i], v = r[i + HALF / 2];
+        r[i] = __builtin_fmaf(v, m, u);
+        r[i + HALF / 2] = __builtin_fmaf(v, -m, u);
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < HALF / 2; c += 8) {
+        const float *lo = r + c, *hi = r + HALF / 2 + c;
+        float t0, t1, t2, t3, t4, t5, t6, t7;
+        // operands: 0 = running max, 1..8 = sums, 9..16 = own k, 17..24 = own k + 32 (read
+        // from the partner by DPP).  The s_nop gives the DPP reads their two wait states.
+#define ADD_DPP(t, a, b) "v_add_f32_dpp %" #t ", |%" #b "|, |%" #a "| quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        __asm__("s_nop 1\n\t"
+                ADD_DPP(1, 9, 17) ADD_DPP(2, 10, 18) ADD_DPP(3, 11, 19) ADD_DPP(4, 12, 20)
+                ADD_DPP(5, 13, 21) ADD_DPP(6, 14, 22) ADD_DPP(7, 15, 23) ADD_DPP(8, 16, 24)
+                "v_max3_f32 %0, %0, %1, %2\n\t"
+                "v_max3_f32 %0, %0, %3, %4\n\t"
+                "v_max3_f32 %0, %0, %5, %6\n\t"
+                "v_max3_f32 %0, %0, %7, %8"
+                : "+v"(mx), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5),
+                  "=&v"(t6), "=&v"(t7)
+                : "v"(lo[0]), "v"(lo[1]), "v"(lo[2]), "v"(lo[3]), "v"(lo[4]), "v"(lo[5]),
+                  "v"(lo[6]), "v"(lo[7]), "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]),
+                  "v"(hi[4]), "v"(hi[5]), "v"(hi[6]), "v"(hi[7]));
+#undef ADD_DPP
+    }
+    return mx;
+}
+
 // Balanced pairwise sum of 2^k values in natural order, in place.
 template <int N>
 __device__ __forceinline__ float tree(float *v)
@@ -567,11 +622,7 @@ __device__ __forceinline__ float tile_amax(const Tile &tile, const SignTable &st
     float r[HALF];
     if (ro.lay == 0) read_row_half(tile, st, ro.g, ro.h, r);
     else read_col_half(tile, st, ro.g, ro.h, r);
-    if (ROT) {
-        float bm[4];
-        fwht_pair_blocks(r, ro.h, bm);
-        return fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
-    }
+    if (ROT) return fwht_pair_absmax(r, ro.h);
     float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
     for (int p = 0; p < HALF; p += 4) {
