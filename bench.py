@@ -227,6 +227,7 @@ def main():
 
     if not args.copy_probe:          # the counter runs keep one copy size for calibration
         result["copy_ceiling"] = copy_ceiling(dev, stream)
+        result["cache_states"] = cache_states(nv, x, out, ws, stream)
 
     if not args.no_gemm:
         result["gemm_check"] = gemm_check(nv, workloads, dev, out.row, stream)
@@ -267,6 +268,47 @@ def issue_view(d, quant_ms):
     rate = n * 64 / (quant_ms * 1e-3) / 1e12
     return {"valu_wave_instr_per_launch": n, "achieved": round(rate, 2),
             "unit": "T lane-instructions/s", "frac": round(rate / VALU_PEAK_TOPS, 4)}
+
+
+def cache_states(nv, x, out, ws, stream, reps=100, flush_bytes=1 << 30):
+    """eden_quantize timed call by call with X warm and cold in the 256 MB last-level cache
+    (MALL): 50 calls to bring the GPU to its working clocks, `reps` calls back to back with
+    a pair of HIP events around each (warm), then `reps` calls each preceded by a 1 GiB
+    device write outside its pair (cold: the write evicts X, so both phases read it from
+    HBM, and the event that opens the pair writes the flush's dirty lines back first).  An
+    event pair around every call puts markers between consecutive calls' kernels, so these
+    times run above the main line's back-to-back steps; the warm/cold difference is the
+    cost of reading X from HBM twice.  Median and minimum of each."""
+    import numpy as np
+    import torch
+
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device=x.device)
+
+    def call(seed):
+        nv.eden_quantize(x, seed=seed, rht_seed=1, layouts=("row", "col"), out=out,
+                         workspace=ws, stream=stream)
+
+    for k in range(50):
+        call(3000 + k)
+    pairs = {"warm": [], "cold": []}
+    for state in ("warm", "cold"):
+        for k in range(reps):
+            if state == "cold":
+                flush.fill_(k & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(4000 + k)
+            e1.record(stream)
+            pairs[state].append((e0, e1))
+    torch.cuda.synchronize()
+    B = alg_bytes(ROWS, COLS)
+    res = {"calls": reps, "flush_bytes": flush_bytes}
+    for state, ev in pairs.items():
+        ms = [a.elapsed_time(b) for a, b in ev]
+        med = float(np.median(ms))
+        res[state] = {"median_ms": round(med, 4), "min_ms": round(float(min(ms)), 4),
+                      "GB/s_median": round(B / (med * 1e-3) / 1e9, 1)}
+    return res
 
 
 def copy_ceiling(dev, stream, nbytes=1 << 30, reps=20):
