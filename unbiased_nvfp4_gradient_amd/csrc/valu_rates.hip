@@ -62,6 +62,8 @@ constexpr int THREADS = 256;
 #define I_CVTFP4(k)  "v_cvt_scalef32_pk_fp4_f32 %" STR(k) ", %8, %9, %8\n\t"
 #define I_CVTFP8(k)  "v_cvt_pk_fp8_f32 %" STR(k) ", %8, %9\n\t"
 #define I_RCP(k)     "v_rcp_f32_e32 %" STR(k) ", %" STR(k) "\n\t"
+#define I_XORSDWA(k) "v_xor_b32_sdwa %" STR(k) ", %" STR(k) ", %8 dst_sel:WORD_1 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_1\n\t"
+#define I_ANDSDWA(k) "v_and_b32_sdwa %" STR(k) ", %" STR(k) ", %8 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:DWORD\n\t"
 
 RATE_KERNEL(k_add, I_ADD)
 RATE_KERNEL(k_sub, I_SUB)
@@ -84,6 +86,8 @@ RATE_KERNEL(k_mullo, I_MULLO)
 RATE_KERNEL(k_cvtfp4, I_CVTFP4)
 RATE_KERNEL(k_cvtfp8, I_CVTFP8)
 RATE_KERNEL(k_rcp, I_RCP)
+RATE_KERNEL(k_xorsdwa, I_XORSDWA)
+RATE_KERNEL(k_andsdwa, I_ANDSDWA)
 
 typedef void (*Kernel)(const uint32_t *, uint32_t *);
 struct Entry { const char *instr; Kernel k; };
@@ -110,6 +114,8 @@ const Entry ENTRIES[] = {
     {"v_cvt_scalef32_pk_fp4_f32", k_cvtfp4},
     {"v_cvt_pk_fp8_f32", k_cvtfp8},
     {"v_rcp_f32_e32", k_rcp},
+    {"v_xor_b32_sdwa dst_sel:WORD_1 src0_sel:WORD_0", k_xorsdwa},
+    {"v_and_b32_sdwa src0_sel:WORD_1", k_andsdwa},
 };
 
 #define CHECK(x)                                                                             \
