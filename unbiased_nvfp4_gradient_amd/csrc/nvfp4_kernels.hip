@@ -152,7 +152,12 @@ __device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t w)
 // contract) inside the table; a finite t >= 0 never sets bit 7.
 __device__ __forceinline__ uint32_t e4m3_rne_hw(float t)
 {
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0x7Fu;
+    // bytes 1..3 of the result are masked off, so the instruction's old-value operand (the
+    // bits it leaves in place) can be any live register: t's own bits, rather than a zero
+    // that would cost a move
+    const float c = fminf(t, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, (int)__float_as_uint(c), false) &
+           0x7Fu;
 }
 
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -773,12 +778,16 @@ __device__ __forceinline__ void rtn_block(const float *rb, uint32_t s, const flo
                                           uint32_t &w0, uint32_t &w1)
 {
     const float rcp = e.z;
-    uint32_t a = 0u, b = 0u;
-    a = CVT_FP4(a, scaled(rb[0], rcp), scaled(rb[1], rcp), 0);
+    // the four conversions into a word write its four bytes, so the bits the first one
+    // leaves in place never survive: it is seeded with its own first input instead of a
+    // zero that would cost a move
+    const float y0 = scaled(rb[0], rcp), y8 = scaled(rb[8], rcp);
+    uint32_t a = __float_as_uint(y0), b = __float_as_uint(y8);
+    a = CVT_FP4(a, y0, scaled(rb[1], rcp), 0);
     a = CVT_FP4(a, scaled(rb[2], rcp), scaled(rb[3], rcp), 1);
     a = CVT_FP4(a, scaled(rb[4], rcp), scaled(rb[5], rcp), 2);
     a = CVT_FP4(a, scaled(rb[6], rcp), scaled(rb[7], rcp), 3);
-    b = CVT_FP4(b, scaled(rb[8], rcp), scaled(rb[9], rcp), 0);
+    b = CVT_FP4(b, y8, scaled(rb[9], rcp), 0);
     b = CVT_FP4(b, scaled(rb[10], rcp), scaled(rb[11], rcp), 1);
     b = CVT_FP4(b, scaled(rb[12], rcp), scaled(rb[13], rcp), 2);
     b = CVT_FP4(b, scaled(rb[14], rcp), scaled(rb[15], rcp), 3);
