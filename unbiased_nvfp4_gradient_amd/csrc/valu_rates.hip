@@ -63,6 +63,8 @@ constexpr int THREADS = 256;
 #define I_CVTFP8(k)  "v_cvt_pk_fp8_f32 %" STR(k) ", %8, %9\n\t"
 #define I_RCP(k)     "v_rcp_f32_e32 %" STR(k) ", %" STR(k) "\n\t"
 #define I_XORSDWA(k) "v_xor_b32_sdwa %" STR(k) ", %" STR(k) ", %8 dst_sel:WORD_1 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_1\n\t"
+#define I_PKMAD(k)   "v_pk_mad_u16 %" STR(k) ", %" STR(k) ", %8, %9 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
+#define I_PKADD(k)   "v_pk_add_u16 %" STR(k) ", %" STR(k) ", %8\n\t"
 #define I_ANDSDWA(k) "v_and_b32_sdwa %" STR(k) ", %" STR(k) ", %8 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:DWORD\n\t"
 
 RATE_KERNEL(k_add, I_ADD)
@@ -88,6 +90,8 @@ RATE_KERNEL(k_cvtfp8, I_CVTFP8)
 RATE_KERNEL(k_rcp, I_RCP)
 RATE_KERNEL(k_xorsdwa, I_XORSDWA)
 RATE_KERNEL(k_andsdwa, I_ANDSDWA)
+RATE_KERNEL(k_pkmad, I_PKMAD)
+RATE_KERNEL(k_pkadd, I_PKADD)
 
 typedef void (*Kernel)(const uint32_t *, uint32_t *);
 struct Entry { const char *instr; Kernel k; };
@@ -116,6 +120,8 @@ const Entry ENTRIES[] = {
     {"v_rcp_f32_e32", k_rcp},
     {"v_xor_b32_sdwa dst_sel:WORD_1 src0_sel:WORD_0", k_xorsdwa},
     {"v_and_b32_sdwa src0_sel:WORD_1", k_andsdwa},
+    {"v_pk_mad_u16 op_sel_hi:[0,1,1]", k_pkmad},
+    {"v_pk_add_u16", k_pkadd},
 };
 
 #define CHECK(x)                                                                             \
