@@ -609,11 +609,33 @@ __global__ void k_write_g(const uint32_t *amax_bits, float D, float *g0, float *
     }
 }
 
-__device__ __forceinline__ void tile_origin(const QuantArgs &a, int64_t tid, int64_t &r0,
-                                            int64_t &c0)
+// The tiles a workgroup visits: index idx, idx + s, idx + 2s, ... (s = gridDim.x), or
+// idx, idx - s, ... walking back, as (tile row, tile column).  The stride's quotient and
+// remainder by tiles_c are taken once, so a step is a few wave-uniform additions instead
+// of a 64-bit division per tile.
+struct TileWalk {
+    int64_t tr, tc;      // current tile row and column
+    int64_t dq, dr;      // s / tiles_c, s % tiles_c
+};
+
+__device__ __forceinline__ TileWalk tile_walk(const QuantArgs &a, int64_t idx)
 {
-    r0 = (tid / a.tiles_c) * TILE;
-    c0 = (tid % a.tiles_c) * TILE;
+    const int64_t s = gridDim.x;
+    return TileWalk{idx / a.tiles_c, idx % a.tiles_c, s / a.tiles_c, s % a.tiles_c};
+}
+
+__device__ __forceinline__ void walk_forward(const QuantArgs &a, TileWalk &w)
+{
+    w.tr += w.dq;
+    w.tc += w.dr;
+    if (w.tc >= a.tiles_c) { w.tc -= a.tiles_c; ++w.tr; }
+}
+
+__device__ __forceinline__ void walk_back(const QuantArgs &a, TileWalk &w)
+{
+    w.tr -= w.dq;
+    w.tc -= w.dr;
+    if (w.tc < 0) { w.tc += a.tiles_c; --w.tr; }
 }
 
 // Max |r| over this lane's half group of tile (r0, c0).
@@ -694,17 +716,22 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
     build_sign_table(st, a.rht_seed, ROT);
     if (t < 2) wmax[t] = 0u;
     float local = 0.0f;
-    int64_t k = blockIdx.x, r0, c0;
+    int64_t k = blockIdx.x, r0 = 0, c0 = 0;
+    TileWalk tw{0, 0, 0, 0};
     if (k < a.tiles) {
-        tile_origin(a, k, r0, c0);
+        tw = tile_walk(a, k);
+        r0 = tw.tr * TILE;
+        c0 = tw.tc * TILE;
         stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
     }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
         __syncthreads();                                   // tile0 landed; tile1 is free
         int64_t r1 = 0, c1 = 0;
+        walk_forward(a, tw);                               // tile k1
         if (k1 < a.tiles) {
-            tile_origin(a, k1, r1, c1);
+            r1 = tw.tr * TILE;
+            c1 = tw.tc * TILE;
             stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
         }
         {
@@ -715,8 +742,10 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         if (k1 >= a.tiles) break;
         const int64_t k2 = k1 + gridDim.x;
         __syncthreads();                                   // tile1 landed; tile0 is free
+        walk_forward(a, tw);                               // tile k2
         if (k2 < a.tiles) {
-            tile_origin(a, k2, r0, c0);
+            r0 = tw.tr * TILE;
+            c0 = tw.tc * TILE;
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
         }
         {
@@ -1093,10 +1122,14 @@ k_quant(QuantArgs a)
     const LayoutOut o = (ro.lay == 0) ? a.out[0] : a.out[1];
     build_sign_table(st, a.rht_seed, ROT);
     int64_t k = blockIdx.x, r0 = 0, c0 = 0;
+    // tiles in the reverse order of pass 1: index tiles - 1 - k, walking back
+    TileWalk tw{0, 0, 0, 0};
+    if (k < a.tiles) tw = tile_walk(a, a.tiles - 1 - k);
     if constexpr (LAY == LAY_BOTH) {
         // the first tile streams in while the tensor scale is reduced and its table built
         if (k < a.tiles) {
-            tile_origin(a, a.tiles - 1 - k, r0, c0);
+            r0 = tw.tr * TILE;
+            c0 = tw.tc * TILE;
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
             if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
         }
@@ -1111,8 +1144,9 @@ k_quant(QuantArgs a)
         // one layout: a single tile buffer, so that four workgroups of 4 waves fit a CU and
         // hide each other's loads (two buffers leave room for two).  The amax pass keeps
         // two buffers: its lighter work per tile does not cover a load.
-        for (; k < a.tiles; k += gridDim.x) {
-            tile_origin(a, a.tiles - 1 - k, r0, c0);
+        for (; k < a.tiles; k += gridDim.x, walk_back(a, tw)) {
+            r0 = tw.tr * TILE;
+            c0 = tw.tc * TILE;
             __syncthreads();                               // previous tile and table read
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
             if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
@@ -1126,8 +1160,10 @@ k_quant(QuantArgs a)
         const int64_t k1 = k + gridDim.x;
         __syncthreads();                                   // tile0 landed; tile1 is free
         int64_t r1 = 0, c1 = 0;
+        walk_back(a, tw);                                  // tile tiles - 1 - k1
         if (k1 < a.tiles) {
-            tile_origin(a, a.tiles - 1 - k1, r1, c1);
+            r1 = tw.tr * TILE;
+            c1 = tw.tc * TILE;
             stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
             if constexpr (LOCAL) stage_table(tb1, a, ro, r1, c1);
         }
@@ -1135,8 +1171,10 @@ k_quant(QuantArgs a)
         if (k1 >= a.tiles) break;
         const int64_t k2 = k1 + gridDim.x;
         __syncthreads();                                   // tile1 landed; tile0 is free
+        walk_back(a, tw);                                  // tile tiles - 1 - k2
         if (k2 < a.tiles) {
-            tile_origin(a, a.tiles - 1 - k2, r0, c0);
+            r0 = tw.tr * TILE;
+            c0 = tw.tc * TILE;
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
             if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
         }
