@@ -1207,42 +1207,83 @@ __device__ __forceinline__ void cross_stage(float v[8], int q)
     for (int i = 0; i < 8; ++i) v[i] = __builtin_fmaf(sg, v[i], xor16<M>(v[i]));
 }
 
+// The same stage in one v_fmac_f32_dpp per value, for the spans whose partner lane a DPP
+// pattern reaches (M = 1, 2: quad_perm; M = 8: row_ror 8), on values held up to a per-lane
+// sign c (true value = c * w).  The partner holds the same c before the stage (the lanes
+// differ only in bit M, and c depends on the lower bits), so sg * t_own + t_partner =
+// (sg * c) * (w_own + sg * w_partner): w += sg * partner's w, rounded once, and c picks up sg.
+// The s_nop gives the DPP reads their two wait states after the last write of v.
+template <int M>
+__device__ __forceinline__ void dpp_stage(float v[8], float sg)
+{
+#define DQ_DPP(k, ctl) "v_fmac_f32_dpp %" #k ", %" #k ", %8 " ctl " row_mask:0xf bank_mask:0xf\n\t"
+#define DQ_STAGE(ctl)                                                                          \
+    __asm__("s_nop 1\n\t" DQ_DPP(0, ctl) DQ_DPP(1, ctl) DQ_DPP(2, ctl) DQ_DPP(3, ctl)          \
+            DQ_DPP(4, ctl) DQ_DPP(5, ctl) DQ_DPP(6, ctl) DQ_DPP(7, ctl)                         \
+            : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),         \
+              "+v"(v[6]), "+v"(v[7])                                                          \
+            : "v"(sg))
+    if constexpr (M == 1) DQ_STAGE("quad_perm:[1,0,3,2]");
+    else if constexpr (M == 2) DQ_STAGE("quad_perm:[2,3,0,1]");
+    else DQ_STAGE("row_ror:8");
+#undef DQ_STAGE
+#undef DQ_DPP
+}
+
 // Dequantize: 16 lanes per (vector, group), lane q holding positions 8q .. 8q + 7, so that
 // the codes (4 bytes), the scale byte and the output (32 bytes) of neighbouring lanes are
 // contiguous.  out[vec][pos] fp32.  g of vector v is gp[v >> g_shift] (one tensor scale: a
-// shift that maps every vector to 0).  With the rotation, the butterfly runs spans 1, 2, 4
+// shift that maps every vector to 0).  sgn: the rotation's 128 sign bits, drawn by the
+// launcher (each wave here is too short to draw them itself: the scalar unit, shared by a
+// CU's waves, would spend more on them than the wave spends on its 512 elements).  With
+// the rotation, the butterfly runs spans 1, 2, 4
 // inside the lane and spans 8 .. 64 across lanes q ^ 1 .. q ^ 8, in ascending order, each
-// output a + b or a - b rounded once.
+// output a + b or a - b rounded once.  One group per row of 16 lanes and no loop: the waves
+// end right after their stores, so no wave waits on its own writes (a persistent loop over
+// groups measured 20% slower without the rotation).
 template <bool ROT>
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ codes,
                                                  const uint8_t *__restrict__ scales,
                                                  const float *__restrict__ gp, int g_shift,
-                                                 int64_t vecs, int64_t n, uint64_t rht_seed,
+                                                 int64_t vecs, int64_t n, Signs sgn,
                                                  float *__restrict__ out)
 {
     const int64_t groups_per_vec = (n + TILE - 1) / TILE;
     const int64_t id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
     const int q = threadIdx.x & 15;
     // the 16 lanes of a row share id: they leave together
-    if (id >= vecs * groups_per_vec) return;
-    const int64_t vec = id / groups_per_vec, gi = id % groups_per_vec;
+    const int64_t groups = vecs * groups_per_vec;
+    if (id >= groups) return;
+    int64_t vec, gi;
+    if (groups <= 0xFFFFFFFFll) {       // the usual case: a 32-bit division (uniform branch)
+        const uint32_t id32 = (uint32_t)id, gpv32 = (uint32_t)groups_per_vec;
+        vec = id32 / gpv32;
+        gi = id32 - (uint32_t)vec * gpv32;
+    } else {
+        vec = id / groups_per_vec;
+        gi = id % groups_per_vec;
+    }
     const int64_t start = gi * TILE;
     const int len = (n - start) >= TILE ? TILE : (int)(n - start);
     const bool act = 8 * q < len;
-    const float g = gp[vec >> g_shift];
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     const int64_t e0 = start + 8 * q;               // first element of this lane
     if (act) {
         const uint32_t cw = *reinterpret_cast<const uint32_t *>(codes + vec * (n >> 1) + (e0 >> 1));
-        const float den = e4m3_val(scales[vec * (n >> 4) + (e0 >> 4)]) * g;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t code = (cw >> (4 * i)) & 15u;
-            const float qv = den * e2m1_val(code & 7u);
-            v[i] = (code & 8u) ? -qv : qv;
-        }
+        const float den = e4m3_val(scales[vec * (n >> 4) + (e0 >> 4)]) * gp[vec >> g_shift];
+        // signed grid values of the 8 codes (exact), times den: one rounding each
+        const float2v V0 = DEC_FP4(cw, 0), V1 = DEC_FP4(cw, 1), V2 = DEC_FP4(cw, 2),
+                      V3 = DEC_FP4(cw, 3);
+        v[0] = den * V0.x;
+        v[1] = den * V0.y;
+        v[2] = den * V1.x;
+        v[3] = den * V1.y;
+        v[4] = den * V2.x;
+        v[5] = den * V2.y;
+        v[6] = den * V3.x;
+        v[7] = den * V3.y;
     }
     if (ROT) {
 #pragma unroll
@@ -1256,14 +1297,17 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
                 }
             }
         }
-        cross_stage<1>(v, q);                                  // span 8
-        cross_stage<2>(v, q);                                  // span 16
+        // spans 8, 16 and 64 leave the lane's values times c = sg1 * sg2 * sg8, which the
+        // sign masks take back out
+        dpp_stage<1>(v, (q & 1) ? -1.0f : 1.0f);              // span 8
+        dpp_stage<2>(v, (q & 2) ? -1.0f : 1.0f);              // span 16
         cross_stage<4>(v, q);                                  // span 32
-        cross_stage<8>(v, q);                                  // span 64
-        const Signs sgn = make_signs(rht_seed);
+        dpp_stage<8>(v, (q & 8) ? -1.0f : 1.0f);              // span 64
+        const uint32_t c = (uint32_t)((q ^ (q >> 1) ^ (q >> 3)) & 1) << 31;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            v[i] = __uint_as_float(__float_as_uint(v[i]) ^ sign_mask(sgn, 8 * q + i)) * 0.0078125f;
+            v[i] = __uint_as_float(__float_as_uint(v[i]) ^ sign_mask(sgn, 8 * q + i) ^ c) *
+                   0.0078125f;
     }
     if (act) {
         float4 *o = reinterpret_cast<float4 *>(out + vec * n + e0);
@@ -1483,6 +1527,27 @@ extern "C" hipError_t nvfp4k_quant_strips(int mode, int rht, int layouts, const 
     return hipGetLastError();
 }
 
+// The rotation's sign words, Philox4x32-10 of key rht_seed at counter (0, 0, STREAM_SIGN, 0)
+// -- the words make_signs draws on the device -- computed on the host.
+static nvfp4k::Signs host_signs(uint64_t key)
+{
+    uint32_t c0 = 0u, c1 = 0u, c2 = nvfp4k::STREAM_SIGN, c3 = 0u;
+    uint32_t k0 = (uint32_t)key, k1 = (uint32_t)(key >> 32);
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0;
+        c1 = (uint32_t)p1;
+        c2 = n2;
+        c3 = (uint32_t)p0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return nvfp4k::Signs{{c0, c1, c2, c3}};
+}
+
 extern "C" hipError_t nvfp4k_dequantize(int local, const uint8_t *codes, const uint8_t *scales,
                                         const float *g, int64_t vecs, int64_t n, int rht,
                                         uint64_t rht_seed, float *out, hipStream_t st)
@@ -1494,9 +1559,9 @@ extern "C" hipError_t nvfp4k_dequantize(int local, const uint8_t *codes, const u
     const int shift = local ? 7 : 62;      // vector -> index of its g (all vectors < 2^31)
     if (rht)
         k_dequant<true><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, shift, vecs, n,
-                                                          rht_seed, out);
+                                                          host_signs(rht_seed), out);
     else
         k_dequant<false><<<(unsigned)blocks, 256, 0, st>>>(codes, scales, g, shift, vecs, n,
-                                                           rht_seed, out);
+                                                           Signs{{0u, 0u, 0u, 0u}}, out);
     return hipGetLastError();
 }
