@@ -369,18 +369,24 @@ __device__ __forceinline__ void read_row_half(const Tile &t, const SignTable &st
 __device__ __forceinline__ void read_col_half(const Tile &t, const SignTable &st, int j, int h,
                                               float r[HALF])
 {
-    const char *t8 = reinterpret_cast<const char *>(t.chunk) + 16384 * h;
+    // Every lane-dependent part of the address is in one offset, so that each load is a few
+    // address steps from the tile itself: the compiler tags LDS accesses with the variable
+    // they touch only up to a small depth of such steps, and an untagged read would also wait
+    // for the next tile's loads into the other buffer.  The column chunk (bits 4..7) and the
+    // half and element (bits 14 and 1..3) do not overlap, so the chunk's xor with s16 can be
+    // applied to their sum.
+    const char *t8 = reinterpret_cast<const char *>(t.chunk);
     const int J = j >> 3;
-    const uint32_t jc = opaque((uint32_t)(16 * (J ^ (((J >> 3) & 1) << 2) ^ (h << 2))));
-    const uint32_t je = 2 * (j & 7);
+    const uint32_t lane = opaque((uint32_t)(16 * (J ^ (((J >> 3) & 1) << 2) ^ (h << 2))) +
+                                 (uint32_t)(16384 * h) + 2 * (uint32_t)(j & 7));
 #pragma unroll
     for (int s16 = 0; s16 < 16; ++s16) {
-        const uint32_t off = (jc ^ (uint32_t)(16 * s16)) + (uint32_t)(256 * s16) + je;
+        const char *p = t8 + (lane ^ (uint32_t)(16 * s16)) + 256 * s16;
         const uint4 m = st.mc[s16][h];
         const uint32_t mm[4] = {m.x, m.y, m.z, m.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t v = *reinterpret_cast<const uint16_t *>(t8 + off + 4096 * q);
+            const uint32_t v = *reinterpret_cast<const uint16_t *>(p + 4096 * q);
             r[16 * q + s16] = __uint_as_float((v << 16) + mm[q]);
         }
     }
@@ -1018,19 +1024,27 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
 
 // Quantize this lane's half group of tile (r0, c0); tb holds the tile's scale table and
 // its (g, rcp(6g), rcp(4g)).
-template <int MODE, bool ROT>
+//
+// next() runs once the tile's LDS reads are issued (every lane reads, those past the edge
+// too): the two-buffer loop starts the following tile's loads there.  Issued after the reads,
+// those loads into the other buffer can never hold the reads back, whereas issued before them
+// the compiler may not be able to tell which buffer they fill and wait for them first.
+template <int MODE, bool ROT, typename Next>
 __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st,
                                            const ScaleTable &tb, const QuantArgs &a,
                                            const LayoutOut &o, const Role &ro, int64_t r0,
-                                           int64_t c0)
+                                           int64_t c0, Next next)
 {
     const int64_t n = ro.lay == 0 ? a.C : a.R;
     const int64_t vec = ro.lay == 0 ? r0 + ro.g : c0 + ro.g;
     const int64_t start = ro.lay == 0 ? c0 : r0;       // first position of this group
-    if (vec >= (ro.lay == 0 ? a.R : a.C)) return;
     float r[HALF];
     if (ro.lay == 0) read_row_half(tile, st, ro.g, ro.h, r);
     else read_col_half(tile, st, ro.g, ro.h, r);
+    __asm__ volatile("" ::: "memory");
+    next();
+    __asm__ volatile("" ::: "memory");                 // the loads stay before the stores
+    if (vec >= (ro.lay == 0 ? a.R : a.C)) return;
     float bm[4];
     if (ROT) {
         fwht_pair_blocks(r, ro.h, bm);
@@ -1045,6 +1059,35 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
     quantize_half<MODE>(r, bm, ro.h, nbl, gs.x, tb, gs.y, gs.z, a.seed, (uint32_t)ro.lay, vec, n,
                         start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
                         o.scales + vec * (n >> 4) + (start >> 4));
+}
+
+// Workgroup barrier between tiles of pass 2 that does not wait for the tile's code and scale
+// stores.  __syncthreads would wait for every outstanding memory operation of the wave,
+// stores included, so each tile would pay the write latency.  The vector memory counter
+// retires in issue order, so waiting until at most `stores` operations are outstanding, where
+// the last `stores` the wave issued are its stores of the tile just computed, waits for the
+// wave's loads into LDS (issued before them) and nothing younger; lgkmcnt(0) waits for its
+// LDS reads and writes.  The empty asm statements keep the compiler from moving memory
+// operations across the barrier.
+template <int STORES>
+__device__ __forceinline__ void tile_barrier()
+{
+    // s_waitcnt fields (gfx9): vmcnt bits 3:0 and 15:14, expcnt 6:4 (7 = no wait), lgkmcnt 11:8
+    constexpr int IMM = (STORES & 15) | (7 << 4) | (0 << 8) | (((STORES >> 4) & 3) << 14);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(IMM);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// The barrier before reading a tile whose loads were issued before the wave's last tile
+// computation: that computation issued exactly 3 stores (two 16-byte code stores and one
+// 4-byte scale store, the full-tile path of quantize_half) when the tile was full and the
+// vectors a multiple of 128 long; otherwise wait for everything.
+__device__ __forceinline__ void tile_barrier_after(bool three_stores)
+{
+    if (three_stores) tile_barrier<3>();
+    else tile_barrier<0>();
 }
 
 // Pass 2: quantize and pack every group of the requested layouts.  Tiles are walked in
@@ -1147,38 +1190,52 @@ k_quant(QuantArgs a)
         for (; k < a.tiles; k += gridDim.x, walk_back(a, tw)) {
             r0 = tw.tr * TILE;
             c0 = tw.tc * TILE;
-            __syncthreads();                               // previous tile and table read
+            // previous tile and table read: LDS only, the tile's stores may still drain
+            tile_barrier<63>();
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
             if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
             __syncthreads();                               // tile landed, table written
-            tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0);
+            tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0, [] {});
         }
         return;
     }
     __shared__ Tile tile1;
+    // vectors of this wave's layout a multiple of 128 long: full tiles take the 3-store path
+    const bool n128 = (((ro.lay == 0) ? a.C : a.R) & (TILE - 1)) == 0;
+    bool three = false;               // the wave's last computation issued exactly 3 stores
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
-        __syncthreads();                                   // tile0 landed; tile1 is free
+        tile_barrier_after(three);                         // tile0 landed; tile1 is free
         int64_t r1 = 0, c1 = 0;
         walk_back(a, tw);                                  // tile tiles - 1 - k1
-        if (k1 < a.tiles) {
+        const bool more1 = k1 < a.tiles;
+        if (more1) {
             r1 = tw.tr * TILE;
             c1 = tw.tc * TILE;
-            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
-            if constexpr (LOCAL) stage_table(tb1, a, ro, r1, c1);
         }
-        tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0);
-        if (k1 >= a.tiles) break;
+        tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0, [&] {
+            if (more1) {
+                stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
+                if constexpr (LOCAL) stage_table(tb1, a, ro, r1, c1);
+            }
+        });
+        three = n128 && r0 + TILE <= a.R && c0 + TILE <= a.C;
+        if (!more1) break;
         const int64_t k2 = k1 + gridDim.x;
-        __syncthreads();                                   // tile1 landed; tile0 is free
+        tile_barrier_after(three);                         // tile1 landed; tile0 is free
         walk_back(a, tw);                                  // tile tiles - 1 - k2
-        if (k2 < a.tiles) {
+        const bool more2 = k2 < a.tiles;
+        if (more2) {
             r0 = tw.tr * TILE;
             c0 = tw.tc * TILE;
-            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
-            if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
         }
-        tile_quant<MODE, ROT>(tile1, st, tb1, a, o, ro, r1, c1);
+        tile_quant<MODE, ROT>(tile1, st, tb1, a, o, ro, r1, c1, [&] {
+            if (more2) {
+                stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+                if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
+            }
+        });
+        three = n128 && r1 + TILE <= a.R && c1 + TILE <= a.C;
         k = k2;
     }
 }
