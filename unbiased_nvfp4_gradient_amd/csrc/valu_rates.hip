@@ -65,6 +65,9 @@ constexpr int THREADS = 256;
 #define I_XORSDWA(k) "v_xor_b32_sdwa %" STR(k) ", %" STR(k) ", %8 dst_sel:WORD_1 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_1\n\t"
 #define I_PKMAD(k)   "v_pk_mad_u16 %" STR(k) ", %" STR(k) ", %8, %9 op_sel:[0,0,0] op_sel_hi:[0,1,1]\n\t"
 #define I_PKADD(k)   "v_pk_add_u16 %" STR(k) ", %" STR(k) ", %8\n\t"
+#define I_MADU24(k)  "v_mad_u32_u24 %" STR(k) ", %" STR(k) ", %8, %9\n\t"
+#define I_MULU24(k)  "v_mul_u32_u24_e32 %" STR(k) ", %8, %" STR(k) "\n\t"
+#define I_CVTBF16(k) "v_cvt_f32_bf16_e32 %" STR(k) ", %" STR(k) "\n\t"
 #define I_ANDSDWA(k) "v_and_b32_sdwa %" STR(k) ", %" STR(k) ", %8 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:DWORD\n\t"
 
 RATE_KERNEL(k_add, I_ADD)
@@ -92,6 +95,9 @@ RATE_KERNEL(k_xorsdwa, I_XORSDWA)
 RATE_KERNEL(k_andsdwa, I_ANDSDWA)
 RATE_KERNEL(k_pkmad, I_PKMAD)
 RATE_KERNEL(k_pkadd, I_PKADD)
+RATE_KERNEL(k_madu24, I_MADU24)
+RATE_KERNEL(k_mulu24, I_MULU24)
+RATE_KERNEL(k_cvtbf16, I_CVTBF16)
 
 typedef void (*Kernel)(const uint32_t *, uint32_t *);
 struct Entry { const char *instr; Kernel k; };
@@ -122,6 +128,9 @@ const Entry ENTRIES[] = {
     {"v_and_b32_sdwa src0_sel:WORD_1", k_andsdwa},
     {"v_pk_mad_u16 op_sel_hi:[0,1,1]", k_pkmad},
     {"v_pk_add_u16", k_pkadd},
+    {"v_mad_u32_u24", k_madu24},
+    {"v_mul_u32_u24_e32", k_mulu24},
+    {"v_cvt_f32_bf16_e32", k_cvtbf16},
 };
 
 #define CHECK(x)                                                                             \
