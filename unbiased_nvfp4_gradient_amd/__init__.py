@@ -144,12 +144,24 @@ def _prepare(x: torch.Tensor, layouts: Sequence[str], out: Optional[Quantized], 
         return _allocate(x, layouts, out, workspace)
 
 
+def _select(layouts, out: Quantized) -> Quantized:
+    """The layouts of a caller's `out` that `layouts` asks for; the others are left alone
+    (passed to the library as null, so it neither computes nor writes them)."""
+    want_row, want_col = "row" in layouts, "col" in layouts
+    for name, want, t in (("row", want_row, out.row), ("col", want_col, out.col)):
+        if want and t is None:
+            raise ValueError(f"`layouts` asks for the {name} layout but `out` has none")
+    return Quantized(out.row if want_row else None, out.col if want_col else None)
+
+
 def _allocate(x, layouts, out, workspace):
     rows, cols = x.shape
     want_row, want_col = "row" in layouts, "col" in layouts
     if out is None:
         out = Quantized(empty_layout(rows, cols, x.device) if want_row else None,
                         empty_layout(cols, rows, x.device) if want_col else None)
+    else:
+        out = _select(layouts, out)
     if workspace is None:
         workspace = torch.empty(workspace_bytes(rows, cols, (1 if want_row else 0) |
                                                 (2 if want_col else 0)),
@@ -278,6 +290,8 @@ def nvfp4_quantize_strips(mode: str, x: torch.Tensor, seed: int = 0, rht: bool =
             out = Quantized(
                 empty_strip_layout(rows, cols, x.device) if "row" in layouts else None,
                 empty_strip_layout(cols, rows, x.device) if "col" in layouts else None)
+        else:
+            out = _select(layouts, out)
         if workspace is None:
             workspace = torch.empty(strip_workspace_bytes(rows, cols), dtype=torch.uint8,
                                     device=x.device)

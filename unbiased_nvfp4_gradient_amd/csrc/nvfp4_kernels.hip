@@ -1092,15 +1092,16 @@ __device__ __forceinline__ void tile_barrier_after(bool three_stores)
 
 // Pass 2: quantize and pack every group of the requested layouts.  Tiles are walked in
 // the reverse order of pass 1 (its last tiles are the likeliest to still be cached), with
-// the same two-buffer streaming.
-// Waves per SIMD each variant is compiled for, the most that fit without spilling: 4 (128
-// registers) for MS-EDEN, RTN, 4/6 and the unrotated two-layout SR; 3 (168) for the other
-// SR variants and the unrotated row-only 4/6; 2 for the unrotated column-only variants.
+// the same two-buffer streaming for one layout and for both.
+// Waves per SIMD each variant is compiled for: with both layouts (8 waves per workgroup) the
+// most that fit without spilling, 4 (128 registers) for MS-EDEN, RTN, 4/6 and the unrotated
+// SR, 3 (168) for SR with the rotation.  With one layout (4 waves) the two 32 KiB tile
+// buffers leave room for two workgroups per CU, i.e. 2 waves per SIMD, so those variants may
+// use up to 256 registers.
 constexpr int quant_waves_per_simd(int mode, bool rot, int lay)
 {
-    if (!rot && lay == LAY_COL) return 2;
-    if (mode == MODE_SR) return (!rot && lay == LAY_BOTH) ? 4 : 3;
-    if (mode == MODE_FP46 && !rot && lay == LAY_ROW) return 3;
+    if (lay != LAY_BOTH) return 2;
+    if (mode == MODE_SR && rot) return 3;
     return 4;
 }
 
@@ -1148,19 +1149,19 @@ template <int MODE, bool ROT, int LAY, bool LOCAL>
 __global__ void __launch_bounds__(512, quant_waves_per_simd(MODE, ROT, LAY))
 k_quant(QuantArgs a)
 {
-    constexpr int NBUF = (LAY == LAY_BOTH) ? 2 : 1;      // tile buffers
     constexpr int NLAY = (LAY == LAY_BOTH) ? 2 : 1;
     __shared__ Tile tile0;
+    __shared__ Tile tile1;
     __shared__ SignTable st;
     // one table per layout, and per tile buffer when every tile has its own scale
-    __shared__ ScaleTable tabs[LOCAL ? NBUF : 1][NLAY];
+    __shared__ ScaleTable tabs[LOCAL ? 2 : 1][NLAY];
     const int t = threadIdx.x;
     const Role ro = lane_role<LAY>();
     constexpr int WAVES = waves_for(LAY);
     const DmaLane dl = dma_lane<WAVES>(a.C);
     const int li = (LAY == LAY_BOTH) ? ro.lay : 0;
     ScaleTable &tb0 = tabs[0][li];
-    ScaleTable &tb1 = tabs[LOCAL ? NBUF - 1 : 0][li];
+    ScaleTable &tb1 = tabs[LOCAL ? 1 : 0][li];
     // select this lane's layout without indexing the argument struct at run time
     const LayoutOut o = (ro.lay == 0) ? a.out[0] : a.out[1];
     build_sign_table(st, a.rht_seed, ROT);
@@ -1168,14 +1169,12 @@ k_quant(QuantArgs a)
     // tiles in the reverse order of pass 1: index tiles - 1 - k, walking back
     TileWalk tw{0, 0, 0, 0};
     if (k < a.tiles) tw = tile_walk(a, a.tiles - 1 - k);
-    if constexpr (LAY == LAY_BOTH) {
-        // the first tile streams in while the tensor scale is reduced and its table built
-        if (k < a.tiles) {
-            r0 = tw.tr * TILE;
-            c0 = tw.tc * TILE;
-            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
-            if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
-        }
+    // the first tile streams in while the tensor scale is reduced and its table built
+    if (k < a.tiles) {
+        r0 = tw.tr * TILE;
+        c0 = tw.tc * TILE;
+        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+        if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
     }
     if constexpr (!LOCAL) {
         const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
@@ -1183,23 +1182,6 @@ k_quant(QuantArgs a)
         build_scale_table(tb0, g, t & 255);
         if (blockIdx.x == 0 && (t & 255) == 0) *o.g = g;
     }
-    if constexpr (LAY != LAY_BOTH) {
-        // one layout: a single tile buffer, so that four workgroups of 4 waves fit a CU and
-        // hide each other's loads (two buffers leave room for two).  The amax pass keeps
-        // two buffers: its lighter work per tile does not cover a load.
-        for (; k < a.tiles; k += gridDim.x, walk_back(a, tw)) {
-            r0 = tw.tr * TILE;
-            c0 = tw.tc * TILE;
-            // previous tile and table read: LDS only, the tile's stores may still drain
-            tile_barrier<63>();
-            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
-            if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
-            __syncthreads();                               // tile landed, table written
-            tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0, [] {});
-        }
-        return;
-    }
-    __shared__ Tile tile1;
     // vectors of this wave's layout a multiple of 128 long: full tiles take the 3-store path
     const bool n128 = (((ro.lay == 0) ? a.C : a.R) & (TILE - 1)) == 0;
     bool three = false;               // the wave's last computation issued exactly 3 stores
