@@ -110,6 +110,8 @@ def main():
                     help="skip the linear-layer (forward + backward) measurement")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the per-quantizer throughput table")
+    ap.add_argument("--no-layouts", action="store_true",
+                    help="skip the per-layout phase 1 / phase 2 timing table")
     ap.add_argument("--no-training-step", action="store_true",
                     help="skip the one-training-step quantization batch (504 calls)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -234,6 +236,9 @@ def main():
 
     if not args.no_modes:
         result["modes"] = modes_table(nv, x, out, stream)
+
+    if not args.no_layouts:
+        result["layouts"] = layouts_table(nv, x, out, stream)
 
     if not args.no_linear:
         result["linear_layer"] = linear_layer(nv, dev)
@@ -412,6 +417,46 @@ def modes_table(nv, x, out, stream, reps=40):
         ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev[name]]))
         table[name] = {"ms": round(ms, 4),
                        "GB/s": round(alg_bytes(ROWS, COLS) / (ms * 1e-3) / 1e9, 1)}
+    return table
+
+
+def layouts_table(nv, x, out, stream, reps=100):
+    """Each phase alone through the split entry points, for both layouts, the row layout
+    only and the column layout only: phase 1 (`nvfp4_amax`, rotated or not) and phase 2
+    (`nvfp4_quantize_amax`, per mode), microseconds per call from one pair of events around
+    `reps` back-to-back calls after 30 warm-up calls (the launcher's time per call is
+    included).  A one-layout call gets only its layout's outputs."""
+    import torch
+
+    lays = {"both": ("row", "col"), "row": ("row",), "col": ("col",)}
+    amax = torch.empty(2, dtype=torch.float32, device=x.device)
+
+    def timed(fn):
+        for k in range(30):
+            fn(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(reps):
+            fn(k)
+        e1.record(stream)
+        e1.synchronize()
+        return round(e0.elapsed_time(e1) / reps * 1e3, 1)
+
+    table = {"unit": "us per call", "phase1": {}, "phase2": {}}
+    for rht in (False, True):
+        table["phase1"]["rotated" if rht else "unrotated"] = {
+            name: timed(lambda k, lay=lay: nv.nvfp4_amax(x, rht, 1, lay, amax=amax,
+                                                         stream=stream))
+            for name, lay in lays.items()}
+    for label, mode, rht in (("rtn", "rtn", False), ("rtn+rht", "rtn", True),
+                             ("eden", "eden", True), ("fp46+rht", "fp46", True)):
+        row = {}
+        for name, lay in lays.items():
+            nv.nvfp4_amax(x, rht, 1, ("row", "col"), amax=amax, stream=stream)
+            row[name] = timed(lambda k, lay=lay: nv.nvfp4_quantize_amax(
+                mode, x, amax, seed=k, rht=rht, rht_seed=1, layouts=lay, out=out,
+                stream=stream))
+        table["phase2"][label] = row
     return table
 
 
