@@ -1312,6 +1312,27 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
     }
     const int64_t start = gi * TILE;
     const int len = (n - start) >= TILE ? TILE : (int)(n - start);
+    if constexpr (!ROT) {
+        // Without the rotation a lane may hold any positions: lane q takes 4q .. 4q + 3 and
+        // 64 + 4q .. 64 + 4q + 3, so that each of the two store instructions writes 256
+        // contiguous bytes per row of 16 lanes (whole 32-byte sectors) instead of half of
+        // every sector.  len is a multiple of 16, so each quadruple is inside or outside.
+        const float gv = gp[vec >> g_shift];
+        const uint8_t *cb = codes + vec * (n >> 1) + (start >> 1) + 2 * q;
+        const uint8_t *sb = scales + vec * (n >> 4) + (start >> 4) + (q >> 2);
+        float *ob = out + vec * n + start + 4 * q;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (64 * half + 4 * q < len) {
+                const uint32_t cw = *reinterpret_cast<const uint16_t *>(cb + 32 * half);
+                const float den = e4m3_val(sb[4 * half]) * gv;
+                const float2v V0 = DEC_FP4(cw, 0), V1 = DEC_FP4(cw, 1);
+                *reinterpret_cast<float4 *>(ob + 64 * half) =
+                    make_float4(den * V0.x, den * V0.y, den * V1.x, den * V1.y);
+            }
+        }
+        return;
+    }
     const bool act = 8 * q < len;
     float v[8];
 #pragma unroll
@@ -1357,18 +1378,12 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
                    0.0078125f;
     }
     if (act) {
-        // Streaming stores with the rotation, ordinary ones without: on c4's row layout
-        // the rotated kernel took 114 us with them and 164 us without, the unrotated one
-        // 210 us with them and 146 us without (the same for the quantizer's code stores,
-        // 262 against 173 us per call), so each keeps the faster kind.
+        // Streaming (non-temporal) stores: on c4's row layout this kernel took 114 us with
+        // them and 164 us without (the quantizer's code stores got slower with them, 262
+        // against 173 us per call, and keep ordinary stores).
         float4 *o = reinterpret_cast<float4 *>(out + vec * n + e0);
-        if constexpr (ROT) {
-            store_nt(o, make_float4(v[0], v[1], v[2], v[3]));
-            store_nt(o + 1, make_float4(v[4], v[5], v[6], v[7]));
-        } else {
-            o[0] = make_float4(v[0], v[1], v[2], v[3]);
-            o[1] = make_float4(v[4], v[5], v[6], v[7]);
-        }
+        store_nt(o, make_float4(v[0], v[1], v[2], v[3]));
+        store_nt(o + 1, make_float4(v[4], v[5], v[6], v[7]));
     }
 }
 
