@@ -209,6 +209,24 @@ def test_dequantize_parity(mode, rht):
         assert np.array_equal(o, ref)   # same operations in the same order: bit-exact
 
 
+@pytest.mark.parametrize("shape,mode", [((144, 48), "rtn"), ((112, 1040), "sr"),
+                                        ((48, 208), "rtn"), ((144, 2064), "fp46")])
+def test_dequantize_ragged_unrotated(shape, mode):
+    """Vector lengths that end in a partial group (48, 112, 144 = 128 + 16, 208 = 128 + 80,
+    1040 = 8 x 128 + 16, 2064 = 16 x 128 + 16; rows are the column layout's lengths): the
+    unrotated decoder's lanes hold positions 4q..4q+3 and 64+4q..64+4q+3 of a group, so in a
+    short last group some lanes store one quadruple and some none; both layouts, compared
+    with the oracle bit for bit."""
+    print(f"case: dequantize ragged {shape} {mode} without the rotation", flush=True)
+    x = workloads.normal(shape, seed=11)
+    got = run_gpu(mode, x, ("row", "col"), seed=5, rht=False)
+    for axis, (codes, scales, g, t) in got.items():
+        out = nv.dequantize(t, rht=False)
+        torch.cuda.synchronize()
+        ref = oracle.dequantize(codes, scales, g, rht=False, rht_seed=0)
+        assert np.array_equal(out.cpu().numpy(), ref), (shape, mode, axis)
+
+
 # ----------------------------------------------------------------------------- general loads
 
 @pytest.mark.parametrize("shape,mode,rht,layouts", [
