@@ -1277,15 +1277,15 @@ __device__ __forceinline__ void dpp_stage(float v[8], float sg)
 #undef DQ_DPP
 }
 
-// Dequantize: 16 lanes per (vector, group), lane q holding positions 8q .. 8q + 7, so that
-// the codes (4 bytes), the scale byte and the output (32 bytes) of neighbouring lanes are
-// contiguous.  out[vec][pos] fp32.  g of vector v is gp[v >> g_shift] (one tensor scale: a
+// Dequantize: 16 lanes per (vector, group), lane q holding positions 4q .. 4q + 3 and
+// 64 + 4q .. 64 + 4q + 3, so that the codes (2 + 2 bytes) and the two 16-byte output pieces
+// of neighbouring lanes are contiguous.  out[vec][pos] fp32.  g of vector v is gp[v >> g_shift] (one tensor scale: a
 // shift that maps every vector to 0).  sgn: the rotation's 128 sign bits, drawn by the
 // launcher (each wave here is too short to draw them itself: the scalar unit, shared by a
 // CU's waves, would spend more on them than the wave spends on its 512 elements).  With
-// the rotation, the butterfly runs spans 1, 2, 4
-// inside the lane and spans 8 .. 64 across lanes q ^ 1 .. q ^ 8, in ascending order, each
-// output a + b or a - b rounded once.  One group per row of 16 lanes and no loop: the waves
+// the rotation, the butterfly runs spans 1, 2 and
+// 64 inside the lane and spans 4 .. 32 across lanes q ^ 1 .. q ^ 8, in ascending order,
+// each output a + b or a - b rounded once.  One group per row of 16 lanes and no loop: the waves
 // end right after their stores, so no wave waits on its own writes (a persistent loop over
 // groups measured 20% slower without the rotation).
 template <bool ROT>
@@ -1312,15 +1312,16 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
     }
     const int64_t start = gi * TILE;
     const int len = (n - start) >= TILE ? TILE : (int)(n - start);
+    // Lane q holds positions 4q + (i & 3) + 64 (i >> 2), i = 0..7: each of its two store
+    // instructions then writes 256 contiguous bytes per row of 16 lanes (whole 32-byte
+    // sectors).  len is a multiple of 16, so each quadruple is wholly inside or outside.
+    const float gv = gp[vec >> g_shift];
+    const uint8_t *cb = codes + vec * (n >> 1) + (start >> 1) + 2 * q;
+    const uint8_t *sb = scales + vec * (n >> 4) + (start >> 4) + (q >> 2);
+    float *ob = out + vec * n + start + 4 * q;
     if constexpr (!ROT) {
-        // Without the rotation a lane may hold any positions: lane q takes 4q .. 4q + 3 and
-        // 64 + 4q .. 64 + 4q + 3, so that each of the two store instructions writes 256
-        // contiguous bytes per row of 16 lanes (whole 32-byte sectors) instead of half of
-        // every sector.  len is a multiple of 16, so each quadruple is inside or outside.
-        const float gv = gp[vec >> g_shift];
-        const uint8_t *cb = codes + vec * (n >> 1) + (start >> 1) + 2 * q;
-        const uint8_t *sb = scales + vec * (n >> 4) + (start >> 4) + (q >> 2);
-        float *ob = out + vec * n + start + 4 * q;
+        // decode and store each quadruple in turn (decoding both first, then storing, took
+        // 112 us instead of 101 us on c4's row layout)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             if (64 * half + 4 * q < len) {
@@ -1333,58 +1334,56 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
         }
         return;
     }
-    const bool act = 8 * q < len;
+    // With the rotation every group is whole (len = 128).
     float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    const int64_t e0 = start + 8 * q;               // first element of this lane
-    if (act) {
-        const uint32_t cw = *reinterpret_cast<const uint32_t *>(codes + vec * (n >> 1) + (e0 >> 1));
-        const float den = e4m3_val(scales[vec * (n >> 4) + (e0 >> 4)]) * gp[vec >> g_shift];
-        // signed grid values of the 8 codes (exact), times den: one rounding each
-        const float2v V0 = DEC_FP4(cw, 0), V1 = DEC_FP4(cw, 1), V2 = DEC_FP4(cw, 2),
-                      V3 = DEC_FP4(cw, 3);
-        v[0] = den * V0.x;
-        v[1] = den * V0.y;
-        v[2] = den * V1.x;
-        v[3] = den * V1.y;
-        v[4] = den * V2.x;
-        v[5] = den * V2.y;
-        v[6] = den * V3.x;
-        v[7] = den * V3.y;
+    for (int half = 0; half < 2; ++half) {
+        const uint32_t cw = *reinterpret_cast<const uint16_t *>(cb + 32 * half);
+        const float den = e4m3_val(sb[4 * half]) * gv;
+        // signed grid values of the 4 codes (exact), times den: one rounding each
+        const float2v V0 = DEC_FP4(cw, 0), V1 = DEC_FP4(cw, 1);
+        v[4 * half] = den * V0.x;
+        v[4 * half + 1] = den * V0.y;
+        v[4 * half + 2] = den * V1.x;
+        v[4 * half + 3] = den * V1.y;
     }
-    if (ROT) {
+    // The butterfly in ascending spans, each output a + b or a - b rounded once: spans 1 and 2
+    // inside each quadruple, spans 4 .. 32 across lanes q ^ 1 .. q ^ 8, span 64 between the
+    // lane's two quadruples.
 #pragma unroll
-        for (int h = 1; h < 8; h <<= 1) {                      // spans 1, 2, 4 in the lane
+    for (int h = 1; h < 4; h <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if ((i & h) == 0) {
-                    const float u = v[i], w = v[i + h];
-                    v[i] = u + w;
-                    v[i + h] = u - w;
-                }
+        for (int i = 0; i < 8; ++i) {
+            if ((i & h) == 0) {
+                const float u = v[i], w = v[i + h];
+                v[i] = u + w;
+                v[i + h] = u - w;
             }
         }
-        // spans 8, 16 and 64 leave the lane's values times c = sg1 * sg2 * sg8, which the
-        // sign masks take back out
-        dpp_stage<1>(v, (q & 1) ? -1.0f : 1.0f);              // span 8
-        dpp_stage<2>(v, (q & 2) ? -1.0f : 1.0f);              // span 16
-        cross_stage<4>(v, q);                                  // span 32
-        dpp_stage<8>(v, (q & 8) ? -1.0f : 1.0f);              // span 64
-        const uint32_t c = (uint32_t)((q ^ (q >> 1) ^ (q >> 3)) & 1) << 31;
+    }
+    // spans 4, 8 and 32 leave the lane's values times c = sg1 * sg2 * sg8, which the sign
+    // masks take back out (span 64, inside the lane, keeps the common factor)
+    dpp_stage<1>(v, (q & 1) ? -1.0f : 1.0f);                  // span 4
+    dpp_stage<2>(v, (q & 2) ? -1.0f : 1.0f);                  // span 8
+    cross_stage<4>(v, q);                                      // span 16
+    dpp_stage<8>(v, (q & 8) ? -1.0f : 1.0f);                  // span 32
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            v[i] = __uint_as_float(__float_as_uint(v[i]) ^ sign_mask(sgn, 8 * q + i) ^ c) *
-                   0.0078125f;
+    for (int i = 0; i < 4; ++i) {                              // span 64
+        const float u = v[i], w = v[i + 4];
+        v[i] = u + w;
+        v[i + 4] = u - w;
     }
-    if (act) {
-        // Streaming (non-temporal) stores: on c4's row layout this kernel took 114 us with
-        // them and 164 us without (the quantizer's code stores got slower with them, 262
-        // against 173 us per call, and keep ordinary stores).
-        float4 *o = reinterpret_cast<float4 *>(out + vec * n + e0);
-        store_nt(o, make_float4(v[0], v[1], v[2], v[3]));
-        store_nt(o + 1, make_float4(v[4], v[5], v[6], v[7]));
-    }
+    const uint32_t c = (uint32_t)((q ^ (q >> 1) ^ (q >> 3)) & 1) << 31;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = __uint_as_float(__float_as_uint(v[i]) ^
+                               sign_mask(sgn, 4 * q + (i & 3) + 64 * (i >> 2)) ^ c) *
+               0.0078125f;
+    // Streaming (non-temporal) stores: 100 us on c4's row layout (with lane q writing
+    // positions 8q .. 8q + 7 instead: 114 us with them, 164 us without; the quantizer's code
+    // stores got slower with them and keep ordinary stores).
+    store_nt(reinterpret_cast<float4 *>(ob), make_float4(v[0], v[1], v[2], v[3]));
+    store_nt(reinterpret_cast<float4 *>(ob + 64), make_float4(v[4], v[5], v[6], v[7]));
 }
 
 }  // namespace nvfp4k
