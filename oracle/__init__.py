@@ -90,6 +90,10 @@ def _load():
         getattr(lib, name).argtypes = [P, P, i64]
     lib.oracle_scale_sr_n.argtypes = [f32, P, P, i64]
     lib.oracle_elem_sr_mag_n.argtypes = [f32, P, P, i64]
+    lib.oracle_margin_n.argtypes = [i32, P, P, P, i64]
+    lib.oracle_scale_sr_pairs_n.argtypes = [P, P, P, i64]
+    lib.oracle_elem_sr_pairs_n.argtypes = [P, P, P, i64]
+    lib.oracle_philox_n.argtypes = [P, P, P, i64]
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_get_threads.restype = i32
     _lib = lib
@@ -195,6 +199,49 @@ def elem_sr_mag_n(a: float, draws) -> np.ndarray:
     u = np.ascontiguousarray(np.asarray(draws, dtype=np.uint32))
     out = np.zeros(u.shape, dtype=np.uint8)
     _load().oracle_elem_sr_mag_n(a, _ptr(u), _ptr(out), u.size)
+    return out
+
+
+def scale_sr_pairs_n(c, words) -> np.ndarray:
+    """Scale SR of each c[i] (normal, below 448) with its own random word words[i]."""
+    cc = np.ascontiguousarray(np.asarray(c, dtype=np.float32))
+    w = np.ascontiguousarray(np.asarray(words, dtype=np.uint32))
+    out = np.zeros(cc.shape, dtype=np.uint8)
+    _load().oracle_scale_sr_pairs_n(_ptr(cc), _ptr(w), _ptr(out), cc.size)
+    return out
+
+
+def elem_sr_pairs_n(a, draws) -> np.ndarray:
+    """Element SR magnitude of each a[i] in [0, 6] with its own 24-bit draw draws[i]."""
+    aa = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = np.ascontiguousarray(np.asarray(draws, dtype=np.uint32))
+    out = np.zeros(aa.shape, dtype=np.uint8)
+    _load().oracle_elem_sr_pairs_n(_ptr(aa), _ptr(u), _ptr(out), aa.size)
+    return out
+
+
+def philox_n(keys, ctrs) -> np.ndarray:
+    """Philox4x32-10 words [n, 4] of keys [n] (uint64) and counters [n, 4] (uint32)."""
+    k = np.ascontiguousarray(np.asarray(keys, dtype=np.uint64))
+    c = np.ascontiguousarray(np.asarray(ctrs, dtype=np.uint32))
+    out = np.zeros((k.size, 4), dtype=np.uint32)
+    _load().oracle_philox_n(_ptr(k), _ptr(c), _ptr(out), k.size)
+    return out
+
+
+MARGIN_KINDS = {"e2m1": 0, "e4m3_rne": 1, "e4m3_up": 2, "scale_sr": 3, "elem_sr": 4, "ulp": 5}
+
+
+def margin_n(kind: str, values, aux=None) -> np.ndarray:
+    """Margin (ulps from the value to the boundary of the rounding it feeds) of each value:
+    "e2m1" nearest of |v|, "e4m3_rne" / "e4m3_up" scale roundings of v >= 0, "scale_sr" of v
+    with random word aux, "elem_sr" of v in [0, 6) with 24-bit draw aux, "ulp" the distance
+    between v and the float whose bits are aux."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float32))
+    a = np.zeros(v.shape, dtype=np.uint32) if aux is None else \
+        np.ascontiguousarray(np.broadcast_to(np.asarray(aux, dtype=np.uint32), v.shape))
+    out = np.zeros(v.shape, dtype=np.uint32)
+    _load().oracle_margin_n(MARGIN_KINDS[kind], _ptr(v), _ptr(a), _ptr(out), v.size)
     return out
 
 

@@ -26,17 +26,21 @@
  * The pages give no formula, order of operations or constant beyond 128, 16, +-6/+-4 and
  * roughly 1/32000.  Every step below is the plainest reading; each reading is listed in
  * the design notes.  All arithmetic is IEEE binary32 with round-to-nearest-even, one
- * rounding per operation (a fused multiply-add only where fmaf is written; the build
- * disables contraction with -ffp-contract=off) and no flushing of subnormals: every floating-point value here decides an integer (a code, a
- * scale byte, an SR branch), and the GPU takes those decisions in binary32 too.
+ * rounding per operation, no fused multiply-add (the build disables contraction with
+ * -ffp-contract=off) and no flushing of subnormals: every floating-point value here decides
+ * an integer (a code, a scale byte, an SR branch), and the GPU takes those decisions in
+ * binary32 too.  A scalar product or a sum of squares is its definition written out: each
+ * term rounded once, then a balanced pairwise sum in natural order.
  *
- * Pins (tests marked "not gpu"): Philox against rocRAND's engine; the Hadamard transform
- * against the Sylvester matrix (exact on integers) and H*H = 128 I; E4M3 rounding against
- * torch's float8_e4m3fn cast and brute force; E2M1 rounding against brute-force nearest;
- * SR probabilities by enumeration of every random word; EDEN ratio against fp64; 4/6
- * choice against an fp64 brute force; scaling / sign / layout invariants; MSE ordering and
- * unbiasedness statistics; strip-local scales against the global method on one strip and
- * per-strip power-of-two equivariance.  Nothing here is "parity unpinned".
+ * Pins (tests marked "not gpu"): Philox against rocRAND's engine and the Random123
+ * known-answer vectors; the Hadamard transform against the Sylvester matrix (exact on
+ * integers) and H*H = 128 I; E4M3 rounding against torch's float8_e4m3fn cast and brute
+ * force; E2M1 rounding against brute-force nearest; SR probabilities by enumeration of every
+ * random word; the EDEN ratio against fp64 within the pairwise-sum bound; the 4/6 choice
+ * against an fp64 brute force; every margin (distance to a rounding boundary) against the
+ * number of one-ulp steps that changes the rounding; scaling / sign / layout invariants; MSE
+ * ordering and unbiasedness statistics; strip-local scales against the global method on one
+ * strip and per-strip power-of-two equivariance.  Nothing here is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -243,13 +247,35 @@ static uint32_t e4m3_rne_margin(float t)
     return best;
 }
 
-/* t against the grid points next to its round-up result. */
+/* t against the grid points next to its round-up result: the result moves up once t passes
+ * its own value (except at the top, where every larger t saturates to the same code) and
+ * down once t reaches the value below. */
 static uint32_t e4m3_up_margin(float t)
 {
     uint8_t c = oracle_e4m3_up(t);
-    uint32_t best = ulp_dist(t, oracle_e4m3_value(c));
+    uint32_t best = MARGIN_NONE;
+    if (c < 0x7E) best = ulp_dist(t, oracle_e4m3_value(c));
     if (c > 0) best = umin(best, ulp_dist(t, oracle_e4m3_value(c - 1)));
     return best;
+}
+
+/* Scale SR of c with word w rounds up exactly when the 20 dropped mantissa bits plus the
+ * draw's top 20 bits carry out (reach 2^20): the margin is their sum's distance from 2^20. */
+static uint32_t scale_sr_margin(float c, uint32_t w)
+{
+    uint32_t sum = (bits_of(c) & 0xFFFFFu) + (w >> 12);
+    return sum > 0x100000u ? sum - 0x100000u : 0x100000u - sum;
+}
+
+/* Element SR of a in [0, 6) with 24-bit draw u rounds up exactly when a lies above the
+ * point lo + u * 2^-24 * (hi - lo) between its grid neighbours lo < hi: the margin is a's
+ * distance from that point (computed in fp64, then rounded to binary32). */
+static uint32_t elem_sr_margin(float a, uint32_t u)
+{
+    int lo = 0;
+    while (E2M1_V[lo + 1] <= a) ++lo;
+    double ab = E2M1_V[lo] + ((double)u / 16777216.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);
+    return ulp_dist(a, (float)ab);
 }
 
 /* ------------------------------------------------------------------ pairwise sums
@@ -381,39 +407,34 @@ static void rtn_block(const float *r, uint8_t s, float g, int mag_cap, uint8_t *
 }
 
 /* ------------------------------------------------------------------ EDEN scalar products
- * <r, r> and <r, q> of one 128-group, where q_i = den_b * V_i is the RTN dequantization of
- * element i of block b (V_i the signed grid value of its code, den_b = s_b * g).  Within a
- * 1x16 block the terms are accumulated by fused multiply-adds in element order (each term
- * enters with a single rounding, and den_b is factored out of its block); the 8 block
- * values are then combined by a balanced pairwise sum. */
-static void eden_dots(const float *r, const uint8_t *codes, const float *den, float *num,
-                      float *dot)
+ * <r, r> and <r, q> of one 128-group ([TG] Method: the ratio of the vector's scalar product
+ * with itself to the scalar product of the quantized rotated and the unquantized rotated
+ * vector).  q_i is the RTN dequantization of element i (den_b * V_i, rounded once, signed),
+ * as rtn_block leaves it.  A scalar product is written out as its definition: each term
+ * rounded once, P_i = r_i * r_i and Q_i = r_i * q_i, then a balanced pairwise sum of the 128
+ * terms in natural order. */
+static void eden_dots(const float *r, const float *q, float *num, float *dot)
 {
-    float pb[GROUP / BLOCK], qb[GROUP / BLOCK];
-    for (int b = 0; b < GROUP / BLOCK; ++b) {
-        float p = 0.0f, v = 0.0f;
-        for (int i = 0; i < BLOCK; ++i) {
-            float x = r[b * BLOCK + i];
-            p = fmaf(x, x, p);
-            v = fmaf(x, oracle_e2m1_value(codes[b * BLOCK + i]), v);
-        }
-        pb[b] = p;
-        qb[b] = den[b] * v;
+    float P[GROUP], Q[GROUP];
+    for (int i = 0; i < GROUP; ++i) {
+        P[i] = r[i] * r[i];
+        Q[i] = r[i] * q[i];
     }
-    *num = tree_sum(pb, GROUP / BLOCK);
-    *dot = tree_sum(qb, GROUP / BLOCK);
+    *num = tree_sum(P, GROUP);
+    *dot = tree_sum(Q, GROUP);
 }
 
-/* Squared error of one block's RTN option: sum of d_i^2, d_i = den * V_i - r_i with one
- * rounding (a fused multiply-add), accumulated by fused multiply-adds in element order. */
-static float block_sq_error(const float *r, const uint8_t *codes, float den)
+/* Squared error of one block's RTN option ([TG] Method: the 4/6 choice keeps the grid with
+ * the lower error): d_i = q_i - r_i with q_i the option's dequantized value (rounded once),
+ * each square rounded once, summed by a balanced pairwise sum of the 16 terms. */
+static float block_sq_error(const float *r, const float *q)
 {
-    float err = 0.0f;
+    float d2[BLOCK];
     for (int i = 0; i < BLOCK; ++i) {
-        float d = fmaf(den, oracle_e2m1_value(codes[i]), -r[i]);
-        err = fmaf(d, d, err);
+        float d = q[i] - r[i];
+        d2[i] = d * d;
     }
-    return err;
+    return tree_sum(d2, BLOCK);
 }
 
 /* ------------------------------------------------------------------ one vector
@@ -460,10 +481,8 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                 continue;
             }
             /* EDEN ratio S = <r, r> / <r, q> over the group of 128. */
-            float dens[GROUP / BLOCK], num, den;
-            for (int b = 0; b < GROUP / BLOCK; ++b)
-                dens[b] = s[b] ? oracle_e4m3_value(s[b]) * g : 0.0f;
-            eden_dots(r + g0, bcodes, dens, &num, &den);
+            float num, den;
+            eden_dots(r + g0, q, &num, &den);
             float S = (den > 0.0f) ? num / den : 1.0f;
             for (int b = 0; b < GROUP / BLOCK; ++b) {
                 int64_t k = vec * nblk + (g0 / BLOCK) + b;   /* index in the scale array */
@@ -484,12 +503,8 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                         uint32_t w = rand_word(seed, (uint64_t)k, STREAM_SCALE_SR,
                                                (uint32_t)axis);
                         out = oracle_scale_sr(c, w);
-                        /* margin: distance of the 20 dropped bits plus the draw from a carry */
-                        uint32_t low = bits_of(c) & 0xFFFFFu, add = w >> 12;
-                        uint32_t sum = low + add;
-                        uint32_t d = sum > 0x100000u ? sum - 0x100000u : 0x100000u - sum;
-                        m2 = umin(m2, umin(d, umin(ulp_dist(c, 0.015625f),
-                                                   ulp_dist(c, 448.0f))));
+                        m2 = umin(m2, umin(scale_sr_margin(c, w),
+                                           umin(ulp_dist(c, 0.015625f), ulp_dist(c, 448.0f))));
                     }
                 }
                 scales[(g0 / BLOCK) + b] = out;
@@ -525,15 +540,11 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                     if (a >= 6.0f) {
                         mag = 7;
                     } else {
-                        int lo = 0;                 /* grid point below a, for the margin */
-                        while (E2M1_V[lo + 1] <= a) ++lo;
                         uint32_t w = rand_word(seed, (uint64_t)(vec * n + e), STREAM_ELEM_SR,
                                                (uint32_t)axis);
                         uint32_t u = w >> 8;
                         mag = oracle_elem_sr_mag(a, u);
-                        double ab = E2M1_V[lo] + ((double)u / 16777216.0) *
-                                                     (E2M1_V[lo + 1] - E2M1_V[lo]);
-                        em = ulp_dist(a, (float)ab);
+                        em = elem_sr_margin(a, u);
                     }
                     code = (uint8_t)(mag | ((rb[i] < 0.0f) << 3));
                 }
@@ -559,8 +570,7 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
         uint32_t mA[BLOCK], mB[BLOCK];
         rtn_block(rb, sA, g, 7, cA, qA, mA);
         rtn_block(rb, sB, g, 6, cB, qB, mB);
-        float errA = block_sq_error(rb, cA, sA ? oracle_e4m3_value(sA) * g : 0.0f);
-        float errB = block_sq_error(rb, cB, sB ? oracle_e4m3_value(sB) * g : 0.0f);
+        float errA = block_sq_error(rb, qA), errB = block_sq_error(rb, qB);
         int pickA = errA <= errB;
         scales[b] = pickA ? sA : sB;
         if (smargin) {
@@ -730,10 +740,8 @@ int oracle_eden_internals(const uint16_t *x, int64_t rows, int64_t cols, int axi
             s[b] = oracle_e4m3_rne_sat(m * six_g_rcp);
             rtn_block(rb, s[b], g, 7, bcodes + b * BLOCK, q + b * BLOCK, NULL);
         }
-        float dens[GROUP / BLOCK], num, den;
-        for (int b = 0; b < GROUP / BLOCK; ++b)
-            dens[b] = s[b] ? oracle_e4m3_value(s[b]) * g : 0.0f;
-        eden_dots(buf + g0, bcodes, dens, &num, &den);
+        float num, den;
+        eden_dots(buf + g0, q, &num, &den);
         for (int i = 0; i < GROUP; ++i) {
             r_out[g0 + i] = buf[g0 + i];
             q_out[g0 + i] = q[i];
@@ -812,4 +820,42 @@ void oracle_elem_sr_mag_n(float a, const uint32_t *u, uint8_t *out, int64_t n)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)oracle_elem_sr_mag(a, u[i]);
+}
+
+/* Margins of single roundings, for the pins: kind 0 = E2M1 nearest of |v|, 1 = E4M3 nearest
+ * of v >= 0, 2 = E4M3 round-up of v >= 0, 3 = scale SR of v with word aux[i], 4 = element SR
+ * of v in [0, 6) with 24-bit draw aux[i], 5 = ulp distance between v and aux[i] read as a
+ * float. */
+void oracle_margin_n(int kind, const float *v, const uint32_t *aux, uint32_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        switch (kind) {
+        case 0: out[i] = e2m1_margin(fabsf(v[i])); break;
+        case 1: out[i] = e4m3_rne_margin(v[i]); break;
+        case 2: out[i] = e4m3_up_margin(v[i]); break;
+        case 3: out[i] = scale_sr_margin(v[i], aux[i]); break;
+        case 4: out[i] = elem_sr_margin(v[i], aux[i]); break;
+        default: out[i] = ulp_dist(v[i], f32_of(aux[i])); break;
+        }
+    }
+}
+
+/* Element-wise forms over paired arrays, for checking the GPU's own device functions. */
+void oracle_scale_sr_pairs_n(const float *c, const uint32_t *w, uint8_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_scale_sr(c[i], w[i]);
+}
+
+void oracle_elem_sr_pairs_n(const float *a, const uint32_t *u, uint8_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)oracle_elem_sr_mag(a[i], u[i]);
+}
+
+void oracle_philox_n(const uint64_t *key, const uint32_t *ctr, uint32_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) oracle_philox4x32_10(key[i], ctr + 4 * i, out + 4 * i);
 }

@@ -17,6 +17,7 @@ SRC = os.path.join(ROOT, "oracle", "nvfp4_oracle.c")
 PRIM = "tests/test_oracle_primitives.py::"
 QUANT = "tests/test_oracle_quantizers.py::"
 STRIP = "tests/test_oracle_strips.py::"
+MARG = "tests/test_oracle_margins.py::"
 
 # (name, text in the source, replacement, pins that must notice)
 MUTATIONS = [
@@ -58,10 +59,29 @@ MUTATIONS = [
      [STRIP + "test_power_of_two_equivariance_per_strip"]),
     ("MS-EDEN block scale rounded up", "                s[b] = oracle_e4m3_rne_sat(t);",
      "                s[b] = oracle_e4m3_up(t);", [QUANT + "test_rtn_codes_are_nearest"]),
-    ("EDEN <r,q> uses r for q", "v = fmaf(x, oracle_e2m1_value(codes[b * BLOCK + i]), v);",
-     "v = fmaf(x, x, v);", [QUANT + "test_eden_ratio_against_fp64"]),
-    ("EDEN <r,r> misses the square", "p = fmaf(x, x, p);", "p = fmaf(x, 1.0f, p);",
+    ("EDEN <r,q> uses r for q", "Q[i] = r[i] * q[i];", "Q[i] = r[i] * r[i];",
+     [QUANT + "test_eden_ratio_against_fp64"]),
+    ("EDEN <r,r> misses the square", "P[i] = r[i] * r[i];", "P[i] = r[i];",
      [QUANT + "test_eden_ratio_is_one_on_grid"]),
+    ("pairwise sum drops the last term", "t[i] = t[2 * i] + t[2 * i + 1];",
+     "t[i] = t[2 * i] + (2 * i + 1 < n - 1 ? t[2 * i + 1] : 0.0f);",
+     [QUANT + "test_eden_ratio_against_fp64"]),
+    ("4/6 error adds instead of subtracting", "float d = q[i] - r[i];",
+     "float d = q[i] + r[i];", [QUANT + "test_fp46_choice_against_fp64"]),
+    ("4/6 error is absolute, not squared", "d2[i] = d * d;", "d2[i] = fabsf(d);",
+     [QUANT + "test_fp46_choice_against_fp64"]),
+    ("E2M1 margin misses the top threshold", "for (int i = 0; i < 7; ++i) {\n        uint32_t d",
+     "for (int i = 0; i < 6; ++i) {\n        uint32_t d", [MARG + "test_e2m1_margin"]),
+    ("E4M3 round-up margin counts the saturated top", "if (c < 0x7E) best = ulp_dist(t, oracle_e4m3_value(c));",
+     "best = ulp_dist(t, oracle_e4m3_value(c));", [MARG + "test_e4m3_up_margin"]),
+    ("E4M3 nearest margin skips the midpoint above", "if (c < 0x7E) {\n        float mid",
+     "if (c < 0x7D) {\n        float mid", [MARG + "test_e4m3_rne_margin"]),
+    ("scale SR margin one bit short", "uint32_t sum = (bits_of(c) & 0xFFFFFu) + (w >> 12);",
+     "uint32_t sum = (bits_of(c) & 0xFFFFFu) + (w >> 13);", [MARG + "test_scale_sr_margin"]),
+    ("element SR margin from the wrong grid point",
+     "double ab = E2M1_V[lo] + ((double)u / 16777216.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);",
+     "double ab = E2M1_V[lo + 1] - ((double)u / 16777216.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);",
+     [MARG + "test_elem_sr_margin"]),
     ("4/6 tensor scale divides by 6 * 448",
      "float d = (mode == MODE_FP46) ? 1792.0f : 2688.0f;",
      "float d = (mode == MODE_FP46) ? 2688.0f : 2688.0f;",

@@ -13,7 +13,9 @@
 //
 // Arithmetic is binary32 with one rounding per operation: the library is built with
 // -ffp-contract=off and no fast-math, so a multiply-add is fused only where __builtin_fmaf
-// is written (the scalar-product chains), exactly as the CPU oracle does.
+// is written, and only where the fused form gives the same value as the separate operations
+// (a product by +-1 or a sum with +0).  A scalar product or sum of squares is its definition:
+// each term rounded once, then a balanced pairwise sum in natural order.
 //
 // Work decomposition.  The input is cut into 128 x 128 BF16 tiles (32 KiB).  Persistent
 // workgroups stream tiles into two LDS buffers with direct global->LDS loads (the next
@@ -52,6 +54,8 @@
 #include <stdint.h>
 #include <cstdlib>
 
+#include "nvfp4_device.h"
+
 namespace nvfp4k {
 
 enum Mode { MODE_RTN = 0, MODE_SR = 1, MODE_EDEN = 2, MODE_FP46 = 3 };
@@ -60,121 +64,6 @@ enum Layouts { LAY_ROW = 1, LAY_COL = 2, LAY_BOTH = 3 };
 constexpr uint32_t STREAM_SIGN = 1u, STREAM_SCALE_SR = 2u, STREAM_ELEM_SR = 3u;
 constexpr int TILE = 128;            // tile edge == rotation group size
 constexpr int CHUNKS = TILE / 8;     // 16-byte chunks per tile row
-constexpr float FLT_BIG = 3.40282347e+38f;
-
-// ------------------------------------------------------------------------------ Philox
-// Philox4x32-10 (Salmon et al., SC'11): 10 rounds of two 32x32->64 multiplies, key bumped by
-// the Weyl constants between rounds.
-struct Word4 { uint32_t w[4]; };
-
-__device__ __forceinline__ Word4 philox(uint64_t key, uint32_t c0, uint32_t c1, uint32_t c2,
-                                        uint32_t c3)
-{
-    uint32_t k0 = (uint32_t)key, k1 = (uint32_t)(key >> 32);
-#pragma unroll
-    for (int round = 0; round < 10; ++round) {
-        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;   // one v_mad_u64_u32 each
-        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        uint32_t n0, n2;
-        if (round == 0) {
-            // the first round's inputs are partly wave-uniform: plain XORs let the
-            // compiler keep that part on the scalar unit
-            n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-            n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
-        } else {
-            // three-input XOR in one v_bitop3_b32 (truth table 0x96: odd parity)
-            n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
-            n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
-        }
-        c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
-    }
-    Word4 r;
-    r.w[0] = c0; r.w[1] = c1; r.w[2] = c2; r.w[3] = c3;
-    return r;
-}
-
-// ------------------------------------------------------------------------------ formats
-// Smallest E4M3FN value >= t >= 0, capped at 448.
-__device__ __forceinline__ uint32_t e4m3_up(float t)
-{
-    if (!(t < 448.0f)) return 0x7Eu;
-    if (t < 0.015625f) return (uint32_t)__builtin_ceilf(t * 512.0f);
-    uint32_t u = (__float_as_uint(t) + 0xFFFFFu) & 0xFFF00000u;
-    return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
-}
-
-// E4M3 byte of a normal c in [2^-6, 448) rounded stochastically: add the top 20 bits of
-// the random word w to the 20 mantissa bits E4M3 drops, keep the 3 that remain.  The fp32
-// bits >> 20 are exponent << 3 | mantissa, so the E4M3 byte is that minus the bias
-// difference (127 - 7) << 3 = 960; a carry out of the mantissa bumps the exponent, and
-// c < 448 cannot carry past 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_sr_normal(uint32_t bits, uint32_t w)
-{
-    return ((bits + (w >> 12)) >> 20) - 960u;
-}
-
-__device__ __forceinline__ float e4m3_val(uint32_t c)
-{
-    const uint32_t e = c >> 3, m = c & 7u;
-    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-}
-
-__device__ __forceinline__ float e2m1_val(uint32_t mag)
-{
-    const uint32_t e = mag >> 1, m = mag & 1u;
-    const uint32_t b = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
-    return __uint_as_float(b);
-}
-
-// Stochastic rounding of a magnitude 0 <= a <= 6 onto the E2M1 grid with random word w:
-// lo = the largest grid index whose value vlo <= a, frac = (a - vlo) / step to the next
-// value, and the magnitude is lo + 1 iff the top 24 bits of w, u, satisfy u < frac * 2^24.
-// From 1 up, the grid points are a's binade start and its midpoint: vlo is a with all but
-// the top mantissa bit cleared, lo = (bits(a) >> 22) - 252 (2 at 1, 6 at 4), and the step
-// is half the binade, so 1 / step = 2^(128 - biased exponent).  Below 1 the points are 0,
-// 0.5, 1 (step 0.5).  a = 6 is index 7.  Every operation here is exact.
-__device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t w)
-{
-    const uint32_t t = __float_as_uint(a);
-    const bool big = a >= 1.0f, half = a >= 0.5f;
-    const uint32_t lo = big ? (t >> 22) - 252u : (uint32_t)half;
-    const float vlo = big ? __uint_as_float(t & 0xFFC00000u) : (half ? 0.5f : 0.0f);
-    const float inv = big ? __uint_as_float(0x7F800000u - (t & 0x7F800000u)) : 2.0f;
-    const float frac = (a - vlo) * inv;
-    const uint32_t up = (float)(w >> 8) < frac * 16777216.0f;
-    return a >= 6.0f ? 7u : lo + up;
-}
-
-// Nearest-even E4M3 of t >= 0, saturating: the hardware conversion is exact below 448.
-// Its result indexes the 128-entry scale table: the mask keeps even a NaN input (outside the
-// contract) inside the table; a finite t >= 0 never sets bit 7.
-__device__ __forceinline__ uint32_t e4m3_rne_hw(float t)
-{
-    // bytes 1..3 of the result are masked off, so the instruction's old-value operand (the
-    // bits it leaves in place) can be any live register: t's own bits, rather than a zero
-    // that would cost a move
-    const float c = fminf(t, 448.0f);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, (int)__float_as_uint(c), false) &
-           0x7Fu;
-}
-
-typedef float float2v __attribute__((ext_vector_type(2)));
-
-// Codes of y0, y1 (nearest-even E2M1, sign of the input) into byte `sel` of w.
-#define CVT_FP4(w, y0, y1, sel) \
-    __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((w), (y0), (y1), 1.0f, (sel))
-
-// Signed grid values of the two codes in byte `sel` of w.
-#define DEC_FP4(w, sel) __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((w), 1.0f, (sel))
-
-// Reciprocal rounded once, clamped so a zero / subnormal divisor stays finite.
-__device__ __forceinline__ float clamped_rcp(float d)
-{
-    const float r = 1.0f / d;
-    return r > FLT_BIG ? FLT_BIG : r;
-}
 
 // ------------------------------------------------------------------------------ signs
 struct Signs { uint32_t w[4]; };
@@ -857,21 +746,19 @@ __device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, float V[1
     decode_pair<3>(w0, w1, V);
 }
 
-// Squared-error terms of elements 2K and 2K+1 (code byte K of wa / wb) for the two 4/6
-// options, added to the running fused multiply-add chains.
-template <int K>
-__device__ __forceinline__ void fp46_err_pairs(const float *r, uint32_t wa, uint32_t wb,
-                                               float denA, float denB, float &errA, float &errB)
+// Squared error of one block's RTN option: d_i = q_i - r_i with q_i = den * V_i (the option's
+// dequantized value, rounded once), each d_i^2 rounded once, summed pairwise over the 16.
+__device__ __forceinline__ float block_sq_error(const float *r, uint32_t w0, uint32_t w1,
+                                                float den)
 {
-    const float2v va = DEC_FP4(wa, K), vb = DEC_FP4(wb, K);
-    const float da0 = __builtin_fmaf(denA, va.x, -r[2 * K]);
-    const float db0 = __builtin_fmaf(denB, vb.x, -r[2 * K]);
-    errA = __builtin_fmaf(da0, da0, errA);
-    errB = __builtin_fmaf(db0, db0, errB);
-    const float da1 = __builtin_fmaf(denA, va.y, -r[2 * K + 1]);
-    const float db1 = __builtin_fmaf(denB, vb.y, -r[2 * K + 1]);
-    errA = __builtin_fmaf(da1, da1, errA);
-    errB = __builtin_fmaf(db1, db1, errB);
+    float V[16], d2[16];
+    decode_block(w0, w1, V);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float d = den * V[i] - r[i];
+        d2[i] = d * d;
+    }
+    return tree<16>(d2);
 }
 
 // Saturate magnitude 7 (value 6) to 6 (value 4) in every nibble of a packed word.
@@ -913,24 +800,25 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
                 sc[b] = s;
                 sv[b] = e.x;
                 if constexpr (MODE == MODE_EDEN) {
-                    // <r,r> and <r,V> of the block by fused multiply-add chains in element
-                    // order; den is factored out of the block's <r,q>.
-                    float V[16];
+                    // the block's terms of <r,r> and <r,q>, each rounded once: r_i * r_i and
+                    // r_i * q_i with q_i = den * V_i (the RTN dequantization, rounded once),
+                    // summed pairwise; the block is an aligned subtree of the group's tree
+                    float V[16], P[16], Q[16];
                     decode_block(cw[2 * b], cw[2 * b + 1], V);
-                    float p = 0.0f, v = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        p = __builtin_fmaf(rb[i], rb[i], p);
-                        v = __builtin_fmaf(rb[i], V[i], v);
+                        P[i] = rb[i] * rb[i];
+                        Q[i] = rb[i] * (e.y * V[i]);
                     }
-                    bp[b] = p;
-                    bq[b] = e.y * v;
+                    bp[b] = tree<16>(P);
+                    bq[b] = tree<16>(Q);
                 }
             }
         }
         if constexpr (MODE == MODE_EDEN) {
-            // pairwise sums over the group's 8 blocks: two levels inside the half, the last
-            // level across the pair (low half's sum + high half's sum in both lanes)
+            // the group's 128-term pairwise sums: the blocks' sums (levels 1..4), two more
+            // levels inside the half, the last across the pair (low half + high half in
+            // both lanes)
             const float pn = tree<4>(bp), qn = tree<4>(bq);
             const float po = pair_swap(pn), qo = pair_swap(qn);
             const float num = h ? po + pn : pn + po;
@@ -992,17 +880,8 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
                 rtn_block(rb, sB, eB, b0, b1);
                 b0 = cap_mag6(b0);
                 b1 = cap_mag6(b1);
-                // squared error of each option: d = den * V - r with one rounding, summed by
-                // fused multiply-adds in element order, two elements (one code byte) at a time
-                float errA = 0.0f, errB = 0.0f;
-                fp46_err_pairs<0>(rb, a0, b0, eA.y, eB.y, errA, errB);
-                fp46_err_pairs<1>(rb, a0, b0, eA.y, eB.y, errA, errB);
-                fp46_err_pairs<2>(rb, a0, b0, eA.y, eB.y, errA, errB);
-                fp46_err_pairs<3>(rb, a0, b0, eA.y, eB.y, errA, errB);
-                fp46_err_pairs<0>(rb + 8, a1, b1, eA.y, eB.y, errA, errB);
-                fp46_err_pairs<1>(rb + 8, a1, b1, eA.y, eB.y, errA, errB);
-                fp46_err_pairs<2>(rb + 8, a1, b1, eA.y, eB.y, errA, errB);
-                fp46_err_pairs<3>(rb + 8, a1, b1, eA.y, eB.y, errA, errB);
+                const float errA = block_sq_error(rb, a0, a1, eA.y);
+                const float errB = block_sq_error(rb, b0, b1, eB.y);
                 const bool pickA = errA <= errB;
                 sc[b] = pickA ? sA : sB;
                 cw[2 * b] = pickA ? a0 : b0;
