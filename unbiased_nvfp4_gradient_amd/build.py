@@ -17,9 +17,6 @@ LIB = os.path.join(PKG, "libnvfp4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["nvfp4_kernels.hip", "nvfp4_gemm.hip", "nvfp4_api.cpp"]
-# a standalone measurement program (VALU issue rate per instruction kind), not linked in
-RATES_SRC = "valu_rates.hip"
-RATES_EXE = os.path.join(PKG, "valu_rates")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [
@@ -39,7 +36,6 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append((src, [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]))
-    cmds.append((RATES_SRC, [HIPCC, *COMMON, os.path.join(CSRC, RATES_SRC), "-o", RATES_EXE]))
     for src, cmd in cmds:
         if verbose:
             print(" ".join(cmd), flush=True)
