@@ -65,3 +65,18 @@ def assert_parity(mode, codes, scales, g, ref: oracle.Quantized, what=""):
     rep = compare(mode, codes, scales, ref)
     assert rep.ok(), f"{what}: {rep}"
     return rep
+
+
+def assert_same_floats(got: np.ndarray, ref: np.ndarray, what="", zero_sign_free=False):
+    """Bit patterns equal.  With zero_sign_free, a zero may carry either sign (the rotated
+    dequantizer carries a per-lane sign through its butterfly, so a zero output's sign follows
+    its own order of operations, not the oracle's); every nonzero value must still match bit
+    for bit."""
+    g = np.ascontiguousarray(got, dtype=np.float32).view(np.uint32)
+    r = np.ascontiguousarray(ref, dtype=np.float32).view(np.uint32)
+    same = g == r
+    if zero_sign_free:
+        same |= ((g & 0x7FFFFFFF) == 0) & ((r & 0x7FFFFFFF) == 0)
+    bad = np.flatnonzero(~same)
+    assert bad.size == 0, (f"{what}: {bad.size} values differ, first at {bad[0]}: "
+                           f"{got.reshape(-1)[bad[0]]!r} vs {ref.reshape(-1)[bad[0]]!r}")

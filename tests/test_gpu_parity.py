@@ -8,24 +8,30 @@ import torch
 import oracle
 import unbiased_nvfp4_gradient_amd as nv
 import workloads
-from parity import assert_parity
+from guards import guarded_outputs
+from parity import assert_parity, assert_same_floats
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
 
-def run_gpu(mode, x, layouts, seed=1, rht=False, rht_seed=1):
+def run_gpu(mode, x, layouts, seed=1, rht=False, rht_seed=1, guard=False):
+    """Quantize on the GPU; with guard, into outputs fenced by sentinel margins that must
+    come back untouched."""
     xd = x.to(DEV)
+    out, guards = (guarded_outputs(xd.shape[0], xd.shape[1], layouts, DEV) if guard
+                   else (None, []))
     if mode == "eden":
-        q = nv.eden_quantize(xd, seed, rht_seed, layouts=layouts)
+        q = nv.eden_quantize(xd, seed, rht_seed, layouts=layouts, out=out)
     elif mode == "sr":
-        q = nv.sr_quantize(xd, seed, rht=rht, rht_seed=rht_seed, layouts=layouts)
+        q = nv.sr_quantize(xd, seed, rht=rht, rht_seed=rht_seed, layouts=layouts, out=out)
     elif mode == "rtn":
-        q = nv.rtn_quantize(xd, rht=rht, rht_seed=rht_seed, layouts=layouts)
+        q = nv.rtn_quantize(xd, rht=rht, rht_seed=rht_seed, layouts=layouts, out=out)
     else:
-        q = nv.fp46_quantize(xd, rht=rht, rht_seed=rht_seed, layouts=layouts)
+        q = nv.fp46_quantize(xd, rht=rht, rht_seed=rht_seed, layouts=layouts, out=out)
     torch.cuda.synchronize()
+    assert all(g.intact() for g in guards), "a write landed outside an output buffer"
     out = {}
     for axis, t in ((0, q.row), (1, q.col)):
         if t is not None:
@@ -34,8 +40,8 @@ def run_gpu(mode, x, layouts, seed=1, rht=False, rht_seed=1):
     return out
 
 
-def check_full(mode, x, layouts, seed=1, rht=False, rht_seed=1, what=""):
-    got = run_gpu(mode, x, layouts, seed, rht, rht_seed)
+def check_full(mode, x, layouts, seed=1, rht=False, rht_seed=1, what="", guard=True):
+    got = run_gpu(mode, x, layouts, seed, rht, rht_seed, guard=guard)
     xb = workloads.bf16_bits(x)
     reps = []
     for axis, (codes, scales, g, _) in got.items():
@@ -148,45 +154,38 @@ def test_config3_eden_both_layouts():
     check_full("eden", workloads.c3(), ("row", "col"), seed=1, rht_seed=1, what="c3")
 
 
-# ----------------------------------------------------------------------------- config 4 (sampled)
+# ----------------------------------------------------------------------------- config 4 (full)
 
-def test_config4_eden_sampled():
-    """Full 16384 x 8192 in the benchmark's launch configuration; the oracle computes the
-    exact amax over the whole tensor, then quantizes sampled rows and columns."""
-    print("case: c4 16384x8192 eden both layouts, sampled vectors", flush=True)
+def assert_identical(codes, scales, g, ref, what):
+    """Every code byte, scale byte and the tensor scale equal to the oracle's."""
+    assert np.float32(g) == np.float32(ref.g), f"{what}: tensor scale {g!r} != {ref.g!r}"
+    assert codes.shape == ref.codes.shape and scales.shape == ref.scales.shape, what
+    cm = int(np.count_nonzero(codes != ref.codes))
+    sm = int(np.count_nonzero(scales != ref.scales))
+    assert cm == 0 and sm == 0, f"{what}: {cm} code bytes and {sm} scale bytes differ"
+
+
+@pytest.fixture(scope="module")
+def config4():
     x = workloads.c4()
-    xb = workloads.bf16_bits(x)
-    got = run_gpu("eden", x, ("row", "col"), seed=1, rht_seed=1)
-    rng = np.random.default_rng(0)
+    return x, workloads.bf16_bits(x), x.to(DEV)
+
+
+@pytest.mark.parametrize("mode,rht,seed,rht_seed", [
+    ("eden", True, 1, 1),            # the benchmark's call
+    ("sr", True, 3, 2), ("sr", False, 3, 2), ("rtn", True, 0, 2), ("rtn", False, 0, 2),
+    ("fp46", True, 0, 2)])
+def test_config4_full(config4, mode, rht, seed, rht_seed):
+    """The full 16384 x 8192 input in the benchmark's launch configuration (both layouts in
+    one call): every code, scale and tensor scale of both layouts against the oracle."""
+    print(f"case: c4 16384x8192 {mode} rht={rht} both layouts, every output", flush=True)
+    x, xb, xd = config4
+    got = run_gpu(mode, xd, ("row", "col"), seed=seed, rht=rht, rht_seed=rht_seed)
     for axis in (0, 1):
         codes, scales, g, _ = got[axis]
-        amax = oracle.amax(xb, axis, True, 1)
-        ref_g = oracle.tensor_scale("eden", amax)
-        assert np.float32(g) == np.float32(ref_g)
-        nvec = codes.shape[0]
-        ids = np.unique(np.concatenate([[0, nvec - 1], rng.choice(nvec, 48, replace=False)]))
-        ref = oracle.quantize_vectors("eden", xb, axis, ids, ref_g, seed=1, rht_seed=1)
-        assert_parity("eden", codes[ids], scales[ids], g, ref, f"c4 axis={axis}")
-
-
-@pytest.mark.parametrize("mode,rht", [("sr", True), ("sr", False), ("rtn", True),
-                                      ("rtn", False), ("fp46", True)])
-def test_config4_other_modes_sampled(mode, rht):
-    """Every other quantizer of the benchmark's modes table on the full 16384 x 8192 input:
-    exact tensor scale, sampled vectors of both layouts."""
-    print(f"case: c4 16384x8192 {mode} rht={rht} both layouts, sampled vectors", flush=True)
-    x = workloads.c4()
-    xb = workloads.bf16_bits(x)
-    got = run_gpu(mode, x, ("row", "col"), seed=3, rht=rht, rht_seed=2)
-    rng = np.random.default_rng(1)
-    for axis in (0, 1):
-        codes, scales, g, _ = got[axis]
-        ref_g = oracle.tensor_scale(mode, oracle.amax(xb, axis, rht, 2))
-        assert np.float32(g) == np.float32(ref_g)
-        nvec = codes.shape[0]
-        ids = np.unique(np.concatenate([[0, nvec - 1], rng.choice(nvec, 32, replace=False)]))
-        ref = oracle.quantize_vectors(mode, xb, axis, ids, ref_g, seed=3, rht=rht, rht_seed=2)
-        assert_parity(mode, codes[ids], scales[ids], g, ref, f"c4 {mode} axis={axis}")
+        ref = oracle.quantize(mode, xb, axis=axis, seed=seed, rht=rht, rht_seed=rht_seed,
+                              margins=False)
+        assert_identical(codes, scales, g, ref, f"c4 {mode} rht={rht} axis={axis}")
 
 
 # ----------------------------------------------------------------------------- dequantize
@@ -206,7 +205,8 @@ def test_dequantize_parity(mode, rht):
         scale = np.maximum(np.abs(ref), np.sqrt((ref.reshape(ref.shape[0], -1, 16) ** 2)
                                                  .mean(-1)).repeat(16, -1))
         assert np.all(np.abs(o - ref) <= 1e-6 * scale), (mode, axis)
-        assert np.array_equal(o, ref)   # same operations in the same order: bit-exact
+        # same operations in the same order: bit-exact (a zero's sign aside when rotated)
+        assert_same_floats(o, ref, f"{mode} axis={axis}", zero_sign_free=rot)
 
 
 @pytest.mark.parametrize("shape,mode", [((144, 48), "rtn"), ((112, 1040), "sr"),
@@ -219,12 +219,17 @@ def test_dequantize_ragged_unrotated(shape, mode):
     with the oracle bit for bit."""
     print(f"case: dequantize ragged {shape} {mode} without the rotation", flush=True)
     x = workloads.normal(shape, seed=11)
-    got = run_gpu(mode, x, ("row", "col"), seed=5, rht=False)
+    got = run_gpu(mode, x, ("row", "col"), seed=5, rht=False, guard=True)
     for axis, (codes, scales, g, t) in got.items():
-        out = nv.dequantize(t, rht=False)
+        vecs, n = codes.shape[0], codes.shape[1] * 2
+        # the output is a view into a larger buffer whose margins must stay untouched
+        fence = torch.full((1024 + vecs * n + 1024,), -7.0, dtype=torch.float32, device=DEV)
+        out = fence[1024:1024 + vecs * n].view(vecs, n)
+        nv.dequantize(t, rht=False, out=out)
         torch.cuda.synchronize()
+        assert bool((fence[:1024] == -7.0).all()) and bool((fence[1024 + vecs * n:] == -7.0).all())
         ref = oracle.dequantize(codes, scales, g, rht=False, rht_seed=0)
-        assert np.array_equal(out.cpu().numpy(), ref), (shape, mode, axis)
+        assert_same_floats(out.cpu().numpy(), ref, f"{shape} {mode} axis={axis}")
 
 
 # ----------------------------------------------------------------------------- general loads

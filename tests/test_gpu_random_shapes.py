@@ -36,7 +36,7 @@ def _cases(n, seed):
 def test_random_shape_tensor_scale(mode, rht, layouts, rows, cols, seed):
     print(f"case: {mode} rht={rht} {layouts} {rows}x{cols} seed={seed}", flush=True)
     x = workloads.c4(seed=seed % 1000, shape=(rows, cols))
-    got = run_gpu(mode, x, layouts, seed=seed, rht=rht, rht_seed=seed + 1)
+    got = run_gpu(mode, x, layouts, seed=seed, rht=rht, rht_seed=seed + 1, guard=True)
     xb = workloads.bf16_bits(x)
     for axis, (codes, scales, g, _) in got.items():
         ref = oracle.quantize(mode, xb, axis=axis, seed=seed, rht=rht, rht_seed=seed + 1)

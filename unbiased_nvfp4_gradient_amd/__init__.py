@@ -136,6 +136,64 @@ def _ct(t: Optional[NVFP4]):
                                  t.tensor_scale.data_ptr()))
 
 
+def _check_buffer(t, name: str, dtype, shape, device):
+    """A caller-supplied buffer must be a contiguous tensor of the given dtype and shape on
+    the input's device: the C ABI sees only its pointer, so a smaller or differently typed
+    buffer would be overrun."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or t.device != device or \
+            not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}; got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _scale_count(vecs: int, strips: bool) -> int:
+    return (vecs + GROUP - 1) // GROUP if strips else 1
+
+
+def _check_layout(t: NVFP4, name: str, vecs: int, n: int, device, strips: bool = False):
+    """One layout's outputs (or inputs, for the decoders and the GEMM): codes uint8
+    [vecs, n/2], scales uint8 [vecs, n/16], tensor_scale float32 [1] (strip-local:
+    [ceil(vecs/128)])."""
+    if not isinstance(t, NVFP4):
+        if not (isinstance(t, tuple) and len(t) == 3):
+            raise ValueError(f"{name} must be an NVFP4 (codes, scales, tensor_scale) triple")
+        t = NVFP4(*t)
+    _check_buffer(t.codes, f"{name}.codes", torch.uint8, (vecs, n // 2), device)
+    _check_buffer(t.scales, f"{name}.scales", torch.uint8, (vecs, n // BLOCK), device)
+    _check_buffer(t.tensor_scale, f"{name}.tensor_scale", torch.float32,
+                  (_scale_count(vecs, strips),), device)
+    return t
+
+
+def _check_outputs(x: torch.Tensor, out: Quantized, strips: bool = False) -> Quantized:
+    rows, cols = x.shape
+    row = None if out.row is None else _check_layout(out.row, "out.row", rows, cols, x.device,
+                                                     strips)
+    col = None if out.col is None else _check_layout(out.col, "out.col", cols, rows, x.device,
+                                                     strips)
+    return Quantized(row, col)
+
+
+def _check_workspace(ws, need: int, device):
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1 or \
+            ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous 1-D uint8 tensor on {device}")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes; {need} are needed")
+
+
+def _decoded_shape(t: NVFP4, name: str, strips: bool):
+    """(vecs, n) of an encoded layout, after checking its three tensors agree."""
+    if not isinstance(t.codes, torch.Tensor) or t.codes.dim() != 2:
+        raise ValueError(f"{name}.codes must be a 2-D uint8 tensor")
+    vecs, n = t.codes.shape[0], t.codes.shape[1] * 2
+    _check_layout(t, name, vecs, n, t.codes.device, strips)
+    return vecs, n
+
+
 def _prepare(x: torch.Tensor, layouts: Sequence[str], out: Optional[Quantized], workspace,
              stream=None):
     if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
@@ -161,11 +219,12 @@ def _allocate(x, layouts, out, workspace):
         out = Quantized(empty_layout(rows, cols, x.device) if want_row else None,
                         empty_layout(cols, rows, x.device) if want_col else None)
     else:
-        out = _select(layouts, out)
+        out = _check_outputs(x, _select(layouts, out))
+    need = workspace_bytes(rows, cols, (1 if want_row else 0) | (2 if want_col else 0))
     if workspace is None:
-        workspace = torch.empty(workspace_bytes(rows, cols, (1 if want_row else 0) |
-                                                (2 if want_col else 0)),
-                                dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    else:
+        _check_workspace(workspace, need, x.device)
     return rows, cols, out, workspace
 
 
@@ -234,6 +293,8 @@ def nvfp4_amax(x: torch.Tensor, rht: bool, rht_seed: int = 0, layouts=("row", "c
     if amax is None:
         with _on(stream, x.device):
             amax = torch.empty((2,), dtype=torch.float32, device=x.device)
+    else:
+        _check_buffer(amax, "amax", torch.float32, (2,), x.device)
     mask = (1 if "row" in layouts else 0) | (2 if "col" in layouts else 0)
     _check("nvfp4_amax", lib().nvfp4_amax(
         x.data_ptr(), x.shape[0], x.shape[1], GROUP, BLOCK, int(bool(rht)), rht_seed, mask,
@@ -245,7 +306,16 @@ def nvfp4_quantize_amax(mode: str, x: torch.Tensor, amax: torch.Tensor, seed: in
                         rht: bool = False, rht_seed: int = 0, layouts=("row", "col"),
                         out: Optional[Quantized] = None, stream=None) -> Quantized:
     """Phase 2: quantizer `mode` ("rtn", "sr", "eden", "fp46") given phase-1 maxima."""
-    rows, cols, out, _ = _prepare(x, layouts, out, amax, stream)
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
+    _check_buffer(amax, "amax", torch.float32, (2,), x.device)
+    rows, cols = x.shape
+    with _on(stream, x.device):
+        if out is None:
+            out = Quantized(empty_layout(rows, cols, x.device) if "row" in layouts else None,
+                            empty_layout(cols, rows, x.device) if "col" in layouts else None)
+        else:
+            out = _check_outputs(x, _select(layouts, out))
     _check("nvfp4_quantize_amax", lib().nvfp4_quantize_amax(
         _mode(mode), x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
         amax.data_ptr(), _ct(out.row), _ct(out.col), _stream_ptr(stream, x.device)))
@@ -255,10 +325,12 @@ def nvfp4_quantize_amax(mode: str, x: torch.Tensor, amax: torch.Tensor, seed: in
 def dequantize(t: NVFP4, rht: bool = False, rht_seed: int = 0,
                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Decode one layout to float32 [vecs, n]; undoes the rotation when rht is set."""
-    vecs, n = t.codes.shape[0], t.codes.shape[1] * 2
+    vecs, n = _decoded_shape(t, "t", strips=False)
     if out is None:
         with _on(stream, t.codes.device):
             out = torch.empty((vecs, n), dtype=torch.float32, device=t.codes.device)
+    else:
+        _check_buffer(out, "out", torch.float32, (vecs, n), t.codes.device)
     _check("dequantize", lib().dequantize(
         _ct(t), vecs, n, GROUP, BLOCK, int(bool(rht)), rht_seed, out.data_ptr(),
         _stream_ptr(stream, t.codes.device)))
@@ -291,10 +363,12 @@ def nvfp4_quantize_strips(mode: str, x: torch.Tensor, seed: int = 0, rht: bool =
                 empty_strip_layout(rows, cols, x.device) if "row" in layouts else None,
                 empty_strip_layout(cols, rows, x.device) if "col" in layouts else None)
         else:
-            out = _select(layouts, out)
+            out = _check_outputs(x, _select(layouts, out), strips=True)
+        need = strip_workspace_bytes(rows, cols)
         if workspace is None:
-            workspace = torch.empty(strip_workspace_bytes(rows, cols), dtype=torch.uint8,
-                                    device=x.device)
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        else:
+            _check_workspace(workspace, need, x.device)
     _check("nvfp4_quantize_strips", lib().nvfp4_quantize_strips(
         _mode(mode), x.data_ptr(), rows, cols, GROUP, BLOCK, seed, int(bool(rht)), rht_seed,
         _ct(out.row), _ct(out.col), workspace.data_ptr(), workspace.numel(),
@@ -305,10 +379,12 @@ def nvfp4_quantize_strips(mode: str, x: torch.Tensor, seed: int = 0, rht: bool =
 def dequantize_strips(t: NVFP4, rht: bool = False, rht_seed: int = 0,
                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Decode one strip-local layout to float32 [vecs, n]."""
-    vecs, n = t.codes.shape[0], t.codes.shape[1] * 2
+    vecs, n = _decoded_shape(t, "t", strips=True)
     if out is None:
         with _on(stream, t.codes.device):
             out = torch.empty((vecs, n), dtype=torch.float32, device=t.codes.device)
+    else:
+        _check_buffer(out, "out", torch.float32, (vecs, n), t.codes.device)
     _check("dequantize_strips", lib().dequantize_strips(
         _ct(t), vecs, n, GROUP, BLOCK, int(bool(rht)), rht_seed, out.data_ptr(),
         _stream_ptr(stream, t.codes.device)))
@@ -318,13 +394,17 @@ def dequantize_strips(t: NVFP4, rht: bool = False, rht_seed: int = 0,
 def nvfp4_gemm_check_strips(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
                             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """C = A B^T of two strip-local row-layout operands, FP32 [M, N]."""
-    M, K = a.codes.shape[0], a.codes.shape[1] * 2
-    N = b.codes.shape[0]
-    if b.codes.shape[1] * 2 != K:
+    M, K = _decoded_shape(a, "a", strips=True)
+    N, Kb = _decoded_shape(b, "b", strips=True)
+    if Kb != K:
         raise ValueError("operands disagree on K")
+    if b.codes.device != a.codes.device:
+        raise ValueError("operands must be on one device")
     if out is None:
         with _on(stream, a.codes.device):
             out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+    else:
+        _check_buffer(out, "out", torch.float32, (M, N), a.codes.device)
     _check("nvfp4_gemm_check_strips", lib().nvfp4_gemm_check_strips(
         _ct(a), _ct(b), M, N, K, int(bool(rotated_pair)), out.data_ptr(),
         _stream_ptr(stream, a.codes.device)))
@@ -334,13 +414,17 @@ def nvfp4_gemm_check_strips(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
 def nvfp4_gemm_check(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """C = A B^T of two row-layout NVFP4 operands ([M, K] and [N, K]), FP32 [M, N]."""
-    M, K = a.codes.shape[0], a.codes.shape[1] * 2
-    N = b.codes.shape[0]
-    if b.codes.shape[1] * 2 != K:
+    M, K = _decoded_shape(a, "a", strips=False)
+    N, Kb = _decoded_shape(b, "b", strips=False)
+    if Kb != K:
         raise ValueError("operands disagree on K")
+    if b.codes.device != a.codes.device:
+        raise ValueError("operands must be on one device")
     if out is None:
         with _on(stream, a.codes.device):
             out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+    else:
+        _check_buffer(out, "out", torch.float32, (M, N), a.codes.device)
     _check("nvfp4_gemm_check", lib().nvfp4_gemm_check(
         _ct(a), _ct(b), M, N, K, int(bool(rotated_pair)), out.data_ptr(),
         _stream_ptr(stream, a.codes.device)))
