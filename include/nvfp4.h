@@ -19,8 +19,9 @@
  *
  * Conventions shared by every entry point
  *   Pointers.   Every data pointer is a DEVICE pointer allocated by the caller (e.g. a torch
- *               CUDA/HIP tensor).  The library never allocates and keeps no global state,
- *               so calls are thread-safe; calls on one stream are ordered.
+ *               CUDA/HIP tensor).  The library never allocates.  Its only state is per
+ *               device and fixed once looked up (the compute-unit count), so calls are
+ *               thread-safe; calls on one stream are ordered.
  *   Stream.     `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *               work is enqueued asynchronously on it; results are valid once it is
  *               synchronised.  Nothing is copied to the host: the tensor scale stays on the
@@ -56,9 +57,6 @@
  *   Seeds.      rht_seed selects the rotation's random signs, shared by every group and both
  *               layouts; both operands of one GEMM must use the same rht_seed.  seed drives
  *               stochastic rounding (Philox4x32-10 counter streams).
- *   Environment. NVFP4_GENERAL_TILE_LOADS=1 (read at every call) makes the quantizers load
- *               every tile through the general path that rows longer than 2^26 elements
- *               take; the results are identical.  It exists for testing that path.
  */
 #ifndef NVFP4_H
 #define NVFP4_H

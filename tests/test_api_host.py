@@ -132,3 +132,4 @@ def test_gemm_alignment(L):
     assert L.nvfp4_gemm_check(_layout(codes=FAKE + 8), ok, 64, 64, 128, 0, FAKE, None) == \
         nv.ERR_ALIGN
     assert L.nvfp4_gemm_check(ok, ok, 64, 64, 128, 0, FAKE + 2, None) == nv.ERR_ALIGN
+

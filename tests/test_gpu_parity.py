@@ -232,25 +232,6 @@ def test_dequantize_ragged_unrotated(shape, mode):
         assert_same_floats(out.cpu().numpy(), ref, f"{shape} {mode} axis={axis}")
 
 
-# ----------------------------------------------------------------------------- general loads
-
-@pytest.mark.parametrize("shape,mode,rht,layouts", [
-    ((384, 640), "eden", True, ("row", "col")),
-    ((256, 384), "sr", False, ("row",)),
-    ((640, 256), "fp46", True, ("col",)),
-    ((200, 256), "rtn", True, ("row",)),           # ragged rows: edge tiles load synchronously
-    ((256, 200), "eden", True, ("col",)),          # ragged columns
-])
-def test_general_tile_loads(monkeypatch, shape, mode, rht, layouts):
-    """The load path of rows longer than 2^26 elements (forced at small sizes by
-    NVFP4_GENERAL_TILE_LOADS=1) gives the same codes as the oracle."""
-    print(f"case: general tile loads shape={shape} mode={mode} rht={rht} layouts={layouts}",
-          flush=True)
-    monkeypatch.setenv("NVFP4_GENERAL_TILE_LOADS", "1")
-    x = workloads.normal(shape, seed=sum(shape) + 1)
-    check_full(mode, x, layouts, seed=5, rht=rht, rht_seed=8, what=f"general {shape} {mode}")
-
-
 # ----------------------------------------------------------------------------- outside the contract
 
 def test_nonfinite_inputs_complete():

@@ -52,7 +52,8 @@
 // the table of each tile's strips into LDS along with the tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <cstdlib>
+
+#include <atomic>
 
 #include "nvfp4_device.h"
 
@@ -165,11 +166,8 @@ __device__ __forceinline__ void store_nt(float4 *p, float4 v)
 // the chunk held in slot lane mod 16: the low bits of S(i) are those of i0 in every round,
 // and bit 6 of i (the 4 in S) is set from row 64 on, which flips bit 2 of the chunk.  So a
 // lane needs two offsets, one for the rounds above row 64 and one for the rest, plus 4 W
-// rows per round.  They fit 32 bits for
-// C <= 2^26 (2 * 31 * C + 240 < 2^32); wider rows take the general path.
-struct DmaLane { uint32_t a, b; };
-
-constexpr int64_t DMA_FAST_MAX_C = int64_t(1) << 26;
+// rows per round.  They are 64-bit, so one load path serves every row length.
+struct DmaLane { uint64_t a, b; };
 
 template <int W>
 __device__ __forceinline__ DmaLane dma_lane(int64_t C)
@@ -177,10 +175,10 @@ __device__ __forceinline__ DmaLane dma_lane(int64_t C)
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i0 = 4 * w + (lane >> 4);
     const int c = swz_chunk(i0, lane & 15);
-    const uint32_t rowb = 2u * (uint32_t)i0 * (uint32_t)C;
+    const uint64_t rowb = 2u * (uint64_t)i0 * (uint64_t)C;
     DmaLane d;
-    d.a = rowb + 16u * (uint32_t)c;
-    d.b = rowb + 16u * (uint32_t)(c ^ 4);
+    d.a = rowb + 16u * (uint64_t)c;
+    d.b = rowb + 16u * (uint64_t)(c ^ 4);
     return d;
 }
 
@@ -193,28 +191,16 @@ __device__ __forceinline__ DmaLane dma_lane(int64_t C)
 template <int W>
 __device__ __forceinline__ void stage_tile(Tile &t, const uint16_t *__restrict__ x, int64_t R,
                                            int64_t C, int64_t r0, int64_t c0,
-                                           const DmaLane &dl, int64_t fast_max_c)
+                                           const DmaLane &dl)
 {
     if (r0 + TILE <= R && c0 + TILE <= C) {
         const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-        if (C <= fast_max_c) {
-            const char *base = reinterpret_cast<const char *>(x + r0 * C + c0);
-            const int64_t step = 8 * W * C;                 // bytes of 4 W rows
+        const char *base = reinterpret_cast<const char *>(x + r0 * C + c0);
+        const int64_t step = 8 * W * C;                 // bytes of 4 W rows
 #pragma unroll
-            for (int k = 0; k < 32 / W; ++k) {
-                const char *p = base + k * step + (4 * W * k < 64 ? dl.a : dl.b);
-                __builtin_amdgcn_global_load_lds(p, LDS_PTR(&t.chunk[(w + W * k) * 64]), 16, 0,
-                                                 0);
-            }
-        } else {
-            const int lane = threadIdx.x & 63;
-            const uint16_t *base = x + r0 * C + c0;
-            for (int j = w; j < TILE * CHUNKS / 64; j += W) {
-                const int q = j * 64 + lane;               // slot filled by this lane
-                const int i = q >> 4, c = swz_chunk(i, q & 15);
-                __builtin_amdgcn_global_load_lds(base + (int64_t)i * C + 8 * c,
-                                                 LDS_PTR(&t.chunk[j * 64]), 16, 0, 0);
-            }
+        for (int k = 0; k < 32 / W; ++k) {
+            const char *p = base + k * step + (4 * W * k < 64 ? dl.a : dl.b);
+            __builtin_amdgcn_global_load_lds(p, LDS_PTR(&t.chunk[(w + W * k) * 64]), 16, 0, 0);
         }
     } else {
         load_tile_sync(t, x, R, C, r0, c0);
@@ -469,7 +455,6 @@ struct QuantArgs {
     float4 *tables;
     uint64_t seed, rht_seed;
     int64_t tiles_r, tiles_c, tiles;   // tile rows, tiles per tile row, total tiles
-    int64_t dma_fast_max_c;    // rows up to this many elements use the precomputed loads
 };
 
 // Waves per workgroup: 4 per layout (128 groups x 2 halves = 256 lanes per layout).
@@ -625,7 +610,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         tw = tile_walk(a, k);
         r0 = tw.tr * TILE;
         c0 = tw.tc * TILE;
-        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
     }
     while (k < a.tiles) {
         const int64_t k1 = k + gridDim.x;
@@ -635,7 +620,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         if (k1 < a.tiles) {
             r1 = tw.tr * TILE;
             c1 = tw.tc * TILE;
-            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
+            stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl);
         }
         {
             const float m = tile_amax<ROT>(tile0, st, a, ro, r0, c0);
@@ -649,7 +634,7 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         if (k2 < a.tiles) {
             r0 = tw.tr * TILE;
             c0 = tw.tc * TILE;
-            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+            stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
         }
         {
             const float m = tile_amax<ROT>(tile1, st, a, ro, r1, c1);
@@ -1060,7 +1045,7 @@ k_quant(QuantArgs a)
     if (k < a.tiles) {
         r0 = tw.tr * TILE;
         c0 = tw.tc * TILE;
-        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+        stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
         if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
     }
     if constexpr (!LOCAL) {
@@ -1084,7 +1069,7 @@ k_quant(QuantArgs a)
         }
         tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0, [&] {
             if (more1) {
-                stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl, a.dma_fast_max_c);
+                stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl);
                 if constexpr (LOCAL) stage_table(tb1, a, ro, r1, c1);
             }
         });
@@ -1100,7 +1085,7 @@ k_quant(QuantArgs a)
         }
         tile_quant<MODE, ROT>(tile1, st, tb1, a, o, ro, r1, c1, [&] {
             if (more2) {
-                stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl, a.dma_fast_max_c);
+                stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
                 if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
             }
         });
@@ -1271,20 +1256,23 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t *__restrict__ cod
 // Called by the C ABI layer (nvfp4_api.cpp) after argument validation.
 namespace nvfp4k {
 
-// Compute units of the current device, looked up once per device.
+// Compute units of the current device, looked up once per device.  The cache is a constant
+// of the device: threads that race on a first lookup store the same value.
+constexpr int MAX_DEVICES = 64;
+
 static int cu_count()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[MAX_DEVICES];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 256;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        cached[dev] = cus;
+        cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return cus;
 }
 
 // Persistent grid: as many workgroups as can be resident at once (occupancy of this kernel
@@ -1369,10 +1357,6 @@ static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_b
     a.tiles_r = (R + TILE - 1) / TILE;
     a.tiles_c = (C + TILE - 1) / TILE;
     a.tiles = a.tiles_c * a.tiles_r;
-    // NVFP4_GENERAL_TILE_LOADS=1 sends every tile through the general load loop (the one
-    // rows longer than 2^26 elements take), so tests can cover it at small sizes
-    const char *general = std::getenv("NVFP4_GENERAL_TILE_LOADS");
-    a.dma_fast_max_c = (general && general[0] == '1') ? 0 : DMA_FAST_MAX_C;
     return a;
 }
 
