@@ -20,8 +20,9 @@
  * Conventions shared by every entry point
  *   Pointers.   Every data pointer is a DEVICE pointer allocated by the caller (e.g. a torch
  *               CUDA/HIP tensor).  The library never allocates.  Its only state is per
- *               device and fixed once looked up (the compute-unit count), so calls are
- *               thread-safe; calls on one stream are ordered.
+ *               device and fixed once looked up (the compute-unit count, and for
+ *               eden_quantize_noalloc the address of its device scratch), so calls that
+ *               bring their own workspace are thread-safe; calls on one stream are ordered.
  *   Stream.     `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *               work is enqueued asynchronously on it; results are valid once it is
  *               synchronised.  Nothing is copied to the host: the tensor scale stays on the
@@ -108,6 +109,21 @@ int eden_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int
                   uint64_t seed, uint64_t rht_seed, const nvfp4_tensor *row_out,
                   const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
                   void *stream);
+
+/* eden_quantize() for callers that cannot allocate device memory or bring a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (without the workspace), outputs, errors and results, bit for bit, as
+ * eden_quantize.  The phase-1 maxima go to a 16 KiB array in device memory that the library
+ * owns (one copy per GPU, held until the process ends); 16 KiB covers every shape the
+ * library accepts, and a call that needed more would be rejected with NVFP4_ERR_WORKSPACE.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library routine); its
+ * first call on a device looks up that device's copy of the array.  Every call on one GPU
+ * shares that array and finds it as the last call left it (nothing in it needs clearing):
+ * calls that overlap on one GPU -- on different streams, or from different threads -- race
+ * and give undefined results; calls on one stream are ordered and safe. */
+int eden_quantize_noalloc(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
+                          uint64_t seed, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                          const nvfp4_tensor *col_out, void *stream);
 
 /* Plain stochastic rounding (itsolotime opening paragraph; Telegram "Method"): tensor scale
  * amax / 2688, block scale rounded UP to E4M3 (no element clips), each element rounded to

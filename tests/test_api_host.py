@@ -133,3 +133,19 @@ def test_gemm_alignment(L):
         nv.ERR_ALIGN
     assert L.nvfp4_gemm_check(ok, ok, 64, 64, 128, 0, FAKE + 2, None) == nv.ERR_ALIGN
 
+
+def test_noalloc_validation(L):
+    """eden_quantize_noalloc rejects bad arguments exactly as eden_quantize does, before it
+    looks up its device scratch (so with no device at all, argument errors still come first)."""
+    r, c = _layout(), _layout(FAKE + 65536, FAKE + 69632, FAKE + 73728)
+
+    def q(x=FAKE, rows=256, cols=256, group=128, block=16, row=r, col=c):
+        return L.eden_quantize_noalloc(x, rows, cols, group, block, 1, 1, row, col, None)
+    assert q(x=0) == nv.ERR_NULL
+    assert q(row=None, col=None) == nv.ERR_NULL
+    assert q(group=64) == nv.ERR_GROUP
+    assert q(cols=200) == nv.ERR_SHAPE
+    assert q(x=FAKE + 8) == nv.ERR_ALIGN
+    assert q(rows=1 << 32) == nv.ERR_ARG
+    if not _has_gpu():
+        assert q() == nv.ERR_HIP

@@ -30,7 +30,8 @@ BLOCK = 16
 OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_ARG = (
     0, -1, -2, -3, -4, -5, -6, -7)
 
-EXPORTED = ("nvfp4_workspace_bytes", "nvfp4_strerror", "eden_quantize", "sr_quantize",
+EXPORTED = ("nvfp4_workspace_bytes", "nvfp4_strerror", "eden_quantize",
+            "eden_quantize_noalloc", "sr_quantize",
             "rtn_quantize", "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize",
             "nvfp4_gemm_check", "nvfp4_strip_workspace_bytes", "nvfp4_quantize_strips",
             "dequantize_strips", "nvfp4_gemm_check_strips")
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
     h.nvfp4_strerror.argtypes = [i32]
     h.nvfp4_strerror.restype = ctypes.c_char_p
     h.eden_quantize.argtypes = [P, i64, i64, i32, i32, u64, u64, TP, TP, P, sz, P]
+    h.eden_quantize_noalloc.argtypes = [P, i64, i64, i32, i32, u64, u64, TP, TP, P]
     h.sr_quantize.argtypes = [P, i64, i64, i32, i32, u64, i32, u64, TP, TP, P, sz, P]
     h.rtn_quantize.argtypes = [P, i64, i64, i32, i32, i32, u64, TP, TP, P, sz, P]
     h.fp46_quantize.argtypes = [P, i64, i64, i32, i32, i32, u64, TP, TP, P, sz, P]
@@ -94,7 +96,7 @@ def lib() -> ctypes.CDLL:
                                         P]
     h.dequantize_strips.argtypes = [TP, i64, i64, i32, i32, i32, u64, P, P]
     h.nvfp4_gemm_check_strips.argtypes = [TP, TP, i64, i64, i64, i32, P, P]
-    for name in ("eden_quantize", "sr_quantize", "rtn_quantize", "fp46_quantize", "dequantize",
+    for name in ("eden_quantize", "eden_quantize_noalloc", "sr_quantize", "rtn_quantize", "fp46_quantize", "dequantize",
                  "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_gemm_check",
                  "nvfp4_quantize_strips", "dequantize_strips", "nvfp4_gemm_check_strips"):
         getattr(h, name).restype = i32
@@ -249,6 +251,28 @@ def eden_quantize(x: torch.Tensor, seed: int, rht_seed: Optional[int] = None,
     _check("eden_quantize", lib().eden_quantize(
         x.data_ptr(), rows, cols, GROUP, BLOCK, seed, rht_seed, _ct(out.row), _ct(out.col),
         ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.device)))
+    return out
+
+
+def eden_quantize_noalloc(x: torch.Tensor, seed: int, rht_seed: Optional[int] = None,
+                          layouts=("row", "col"), out: Optional[Quantized] = None,
+                          stream=None) -> Quantized:
+    """eden_quantize through the entry point that allocates nothing: the library keeps the
+    call's workspace in its own device scratch (calls that overlap on one GPU race).  Pass
+    `out` to allocate nothing here either."""
+    rht_seed = seed if rht_seed is None else rht_seed
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
+    rows, cols = x.shape
+    if out is None:
+        with _on(stream, x.device):
+            out = Quantized(empty_layout(rows, cols, x.device) if "row" in layouts else None,
+                            empty_layout(cols, rows, x.device) if "col" in layouts else None)
+    else:
+        out = _check_outputs(x, _select(layouts, out))
+    _check("eden_quantize_noalloc", lib().eden_quantize_noalloc(
+        x.data_ptr(), rows, cols, GROUP, BLOCK, seed, rht_seed, _ct(out.row), _ct(out.col),
+        _stream_ptr(stream, x.device)))
     return out
 
 
@@ -431,7 +455,8 @@ def nvfp4_gemm_check(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
     return out
 
 
-__all__ = ["NVFP4", "Quantized", "NVFP4Error", "eden_quantize", "sr_quantize", "rtn_quantize",
+__all__ = ["NVFP4", "Quantized", "NVFP4Error", "eden_quantize", "eden_quantize_noalloc",
+           "sr_quantize", "rtn_quantize",
            "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize", "nvfp4_gemm_check",
            "nvfp4_quantize_strips", "dequantize_strips", "nvfp4_gemm_check_strips",
            "workspace_bytes", "strip_workspace_bytes", "strerror", "empty_layout",

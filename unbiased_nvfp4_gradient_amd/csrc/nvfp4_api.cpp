@@ -14,6 +14,7 @@ extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x
                                    const float *amax, uint64_t seed, uint64_t rht_seed,
                                    hipStream_t st);
 extern "C" size_t nvfp4k_workspace(void);
+extern "C" hipError_t nvfp4k_scratch(void **ptr, size_t *bytes);
 extern "C" hipError_t nvfp4k_quantize(int mode, int rht, int layouts, const void *x, int64_t R,
                                       int64_t C, uint8_t *codes0, uint8_t *scales0, float *g0,
                                       uint8_t *codes1, uint8_t *scales1, float *g1,
@@ -120,13 +121,23 @@ size_t strip_workspace_bytes(int64_t rows, int64_t cols)
 int quantize_common(int local, int mode, const void *x, int64_t rows, int64_t cols, int group,
                     int block, uint64_t seed, int rht, uint64_t rht_seed,
                     const nvfp4_tensor *row_out, const nvfp4_tensor *col_out, void *workspace,
-                    size_t workspace_bytes, void *stream)
+                    size_t workspace_bytes, void *stream, bool own_scratch = false)
 {
     int rc = check_outputs(row_out, col_out, rows, cols);
     if (rc) return rc;
     rc = check_input(mode, x, rows, cols, group, block, rht, row_out != nullptr,
                      col_out != nullptr);
     if (rc) return rc;
+    if (own_scratch) {
+        // the library's own device scratch (eden_quantize_noalloc), once the arguments are
+        // known to be good: looked up on the current device, never allocated
+        rc = check_device();
+        if (rc) return rc;
+        if (nvfp4k_scratch(&workspace, &workspace_bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return NVFP4_ERR_HIP;
+        }
+    }
     const size_t need = local ? strip_workspace_bytes(rows, cols) : nvfp4k_workspace();
     if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
@@ -221,6 +232,14 @@ int eden_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int
 {
     return quantize_common(0, MODE_EDEN, x_bf16, rows, cols, group, block, seed, 1, rht_seed,
                            row_out, col_out, workspace, workspace_bytes, stream);
+}
+
+int eden_quantize_noalloc(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
+                          uint64_t seed, uint64_t rht_seed, const nvfp4_tensor *row_out,
+                          const nvfp4_tensor *col_out, void *stream)
+{
+    return quantize_common(0, MODE_EDEN, x_bf16, rows, cols, group, block, seed, 1, rht_seed,
+                           row_out, col_out, nullptr, 0, stream, true);
 }
 
 int sr_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,

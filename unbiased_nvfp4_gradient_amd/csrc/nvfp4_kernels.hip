@@ -54,6 +54,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "nvfp4_device.h"
 
@@ -1398,6 +1399,44 @@ extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x
 
 // Bytes of workspace the one-call quantizers need: two maxima per phase-1 workgroup.
 extern "C" size_t nvfp4k_workspace(void) { return 8 * (size_t)nvfp4k::MAX_PARTS; }
+
+// ------------------------------------------------------------------------------ scratch
+// Workspace in device memory the library owns, for callers that cannot allocate: the phase-1
+// maxima of one call of eden_quantize_noalloc.  Every GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: its address on a device comes from hipGetSymbolAddress with that device
+// current, looked up once per device and kept.  Every call on one GPU shares its copy, so
+// calls that overlap on one GPU race.  No slot needs clearing: each call's phase 2 reads only
+// slots its own phase 1 wrote.
+namespace nvfp4k {
+constexpr size_t SCRATCH_BYTES = 16384;
+static_assert(8 * MAX_PARTS <= SCRATCH_BYTES, "the scratch must hold every phase-1 maximum");
+}  // namespace nvfp4k
+
+static __device__ __align__(256) uint8_t scratch[nvfp4k::SCRATCH_BYTES];
+
+// The current device's copy of the scratch array and its size.
+extern "C" hipError_t nvfp4k_scratch(void **ptr, size_t *bytes)
+{
+    using namespace nvfp4k;
+    static std::mutex lock;
+    static void *addr[MAX_DEVICES] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(lock);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = SCRATCH_BYTES;
+    return hipSuccess;
+}
 
 // One-call quantization with one tensor scale per layout: phase 1 leaves each workgroup's
 // maxima in the workspace (no clearing needed: every slot read is written), and each
