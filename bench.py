@@ -5,28 +5,31 @@
 One step = one call of eden_quantize, the product entry point: phase 1 (rotated amax of
 both layouts, the tensor-wide synchronisation point) then phase 2 (rotate, scale, round,
 EDEN-correct, stochastically round the scales, pack, store both layouts), on the current
-stream with the input already resident in HBM.  Throughput counts the algorithmic bytes of the step: the BF16 read once
-(2 B/element) plus, per layout, 0.5 B of codes + 1/16 B of scales per element and 4 B of
-tensor scale.  The second read of X by phase 2 is not counted.
+stream with the input already resident in HBM.  `value` counts the algorithmic bytes of the
+step -- the BF16 read once (2 B/element) plus, per layout, 0.5 B of codes + 1/16 B of
+scales per element and 4 B of tensor scale: 419,430,408 B -- over the wall-clock mean of
+the K timed steps.  Phase 2's second read of X and phase 1's first are not counted.
 
-The dominant kernel is phase 2 (k_quant).  A call of eden_quantize has no point between
-its two kernels where a marker could go, so after the K timed steps K more steps run through
-the split entry points (nvfp4_amax, then nvfp4_quantize_amax: the same two kernels), with
-one pair of HIP events on the launch stream bracketing each phase-2 launch; the roofline
-takes that kernel's mean duration from them.  Phase 2 is bound by VALU issue, so its roofline is
-the ALU one: per element and layout the method performs 14 operations -- the sign flip,
-the 7 butterfly stages, the 1x16 |r| maximum, the scaling, the rounding to E2M1, the grid
-value of the code and the two EDEN multiply-adds -- against MI355X's published FP32 vector
-peak, 157.3 TFLOP/s, counted as one operation per FMA lane: 256 CUs x 4 SIMDs x 32 lanes x
-2.4 GHz = 78.64 Top/s.  Plain FP32 add/mul/FMA and XOR/add/bitop3 issue at that width on
-this chip without packed instructions; max, shifts, DPP, permutes and 32-bit multiplies at
-half of it, the FP4/FP8 conversions at a quarter (the package's valu_rates program measures
-each).  So the kernel's own instruction mix caps it well below the peak; the issue view
-reports the VALU instructions the kernel issues per second (per launch from the committed
-counters, over the launch time) against the same peak.  The HBM
-view of the same kernel is reported beside it, and the HBM bytes it moves come from the
-committed rocprofv3 counter summary while the kernel source is unchanged since those
-counters were taken.
+Roofline (HBM bandwidth, the bound the method has: codec work, no dense contraction).  The
+dominant kernel is phase 2, k_quant: it reads X once and writes every output, so its
+algorithmic bytes per launch are the step's 419,430,408 B.  A call of eden_quantize has no
+point between its two kernels where a marker could go, so after the timed steps K more steps
+run through the split entry points (nvfp4_amax, then nvfp4_quantize_amax: the same two
+kernels), with one pair of HIP events on the launch stream bracketing each phase-2 launch;
+achieved = 419,430,408 B / that mean launch time, against MI355X's published 8 TB/s.  The
+kernel is in fact bound by VALU issue at this bandwidth, so two more views are reported
+beside it: the ALU view (the 14 operations per element and layout the method defines --
+sign flip, 7 butterfly stages, block maximum, scaling, E2M1 rounding, grid value, EDEN
+terms -- against the 157.3 TFLOP/s FP32 vector peak counted as 78.64 T lane-operations/s)
+and the issue view (VALU instructions per launch from the committed counters, when they were
+taken on the current kernel sources).  `traffic` is the HBM bytes per k_quant launch from the
+committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the
+same counter reads for a device copy of known size), or null when the kernel sources have
+changed since.
+
+A further K steps run with a pair of HIP events around each call (`per_step_events`): their
+median is the steady-state cost of one call, beside the wall-clock mean of the timed steps
+(which includes the clock ramp of the first steps after idle when the warm-up is short).
 
 Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU.
 """
@@ -48,6 +51,7 @@ ROWS, COLS = 16384, 8192
 METRIC = "MS-EDEN NVFP4 quantize GB/s & % HBM peak, 16384×8192 bf16; MSE vs SR"
 PMC_PROFILE = os.path.join(ROOT, "profiles", "k_quant_eden_16384x8192_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "unbiased_nvfp4_gradient_amd", "csrc", "nvfp4_kernels.hip"),
+                  os.path.join(ROOT, "unbiased_nvfp4_gradient_amd", "csrc", "nvfp4_device.h"),
                   os.path.join(ROOT, "unbiased_nvfp4_gradient_amd", "build.py")]
 
 
@@ -176,16 +180,27 @@ def main():
         step_split(1 + k, events[k])
     torch.cuda.synchronize()
 
+    # one pair of HIP events around each of K more calls: the per-call median
+    per_step = [[Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        per_step[k][0].record(stream)
+        step(3000 + k)
+        per_step[k][1].record(stream)
+    torch.cuda.synchronize()
+
     pmc = pmc_record()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    quant_ms_all = [e[0].elapsed_time(e[1]) for e in events]
+    quant_ms = float(np.mean(quant_ms_all))
     step_ms_ev = start.elapsed_time(stop) / args.steps
+    per_step_ms = [e[0].elapsed_time(e[1]) for e in per_step]
     B = alg_bytes(ROWS, COLS)
     value = B / (ms_step * 1e-3) / 1e9
     n = ROWS * COLS
     ops = QUANT_OPS_PER_ELEM_LAYOUT * 2 * n
     tops = ops / (quant_ms * 1e-3) / 1e12
     quant_gbs = B / (quant_ms * 1e-3) / 1e9
+    med_step = float(np.median(per_step_ms))
 
     result = {
         "metric": METRIC,
@@ -209,20 +224,28 @@ def main():
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_step": B,
-        "phase_ms": {"quantize_events": round(quant_ms, 4),
+        "per_step_events": {"median_ms": round(med_step, 4),
+                            "min_ms": round(float(min(per_step_ms)), 4),
+                            "GB/s_median": round(B / (med_step * 1e-3) / 1e9, 1),
+                            "pct_hbm_peak_median": round(100.0 * B / (med_step * 1e-3) / 1e9
+                                                         / HBM_PEAK_GBS, 2)},
+        "phase_ms": {"quantize_events_mean": round(quant_ms, 4),
+                     "quantize_events_median": round(float(np.median(quant_ms_all)), 4),
                      "step_events": round(step_ms_ev, 4)},
         "roofline": {
             "kernel": "k_quant (phase 2: rotate, quantize, EDEN, scale SR, pack both layouts)",
-            "bound": "alu",
-            "achieved": round(tops, 2),
-            "peak": round(VALU_PEAK_TOPS, 2),
-            "unit": "Top/s (VALU lane operations; algorithmic, 14 per element and layout)",
-            "frac": round(tops / VALU_PEAK_TOPS, 4),
+            "bound": "hbm",
+            "achieved": round(quant_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(pmc),
-            "ops_per_launch": ops,
-            "hbm_view": {"achieved": round(quant_gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
-                         "algorithmic_bytes_per_launch": B},
+            "algorithmic_bytes_per_launch": B,
+            "launch_ms_mean": round(quant_ms, 4),
+            "alu_view": {"achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2),
+                         "unit": "T lane-ops/s (14 algorithmic operations per element and "
+                                 "layout)",
+                         "frac": round(tops / VALU_PEAK_TOPS, 4), "ops_per_launch": ops},
             "issue_view": issue_view(pmc, quant_ms),
         },
     }

@@ -456,6 +456,8 @@ struct QuantArgs {
     float4 *tables;
     uint64_t seed, rht_seed;
     int64_t tiles_r, tiles_c, tiles;   // tile rows, tiles per tile row, total tiles
+    int64_t blk_c;             // blocks of blk x blk tiles per block row (tiles_c / blk)
+    int blk;                   // block edge of the visiting order, 4 or 1
 };
 
 // Waves per workgroup: 4 per layout (128 groups x 2 halves = 256 lanes per layout).
@@ -498,33 +500,65 @@ __global__ void k_write_g(const uint32_t *amax_bits, float D, float *g0, float *
     }
 }
 
-// The tiles a workgroup visits: index idx, idx + s, idx + 2s, ... (s = gridDim.x), or
-// idx, idx - s, ... walking back, as (tile row, tile column).  The stride's quotient and
-// remainder by tiles_c are taken once, so a step is a few wave-uniform additions instead
-// of a 64-bit division per tile.
+// The order in which the tiles are visited.  Order index o names a tile: when both tile
+// counts are multiples of 4 (a.blk = 4) the tiles are taken in 4 x 4 blocks, block by block
+// in row-major order and row-major inside a block; otherwise (a.blk = 1) plainly row-major.
+// A workgroup visits o = j, j + s, j + 2s, ... (s = gridDim.x, a multiple of 16 when
+// blocked), or the same indices counted back from the last, so it keeps one place inside
+// every block it visits and moves a fixed number of blocks per step: a step is a few
+// wave-uniform additions instead of a 64-bit division per tile.
+//
+// j is the workgroup's place in a step.  Workgroups are dispatched to the 8 XCDs round robin
+// (workgroup w on XCD w mod 8), so when a step holds whole groups of 8 x 16 workgroups
+// the 16 tiles of each block go to 16 workgroups of one XCD, which process them at the same
+// time: the four 8-byte scale pieces of a 32-byte sector (a vector's scales from 4 tiles in
+// a row of a block for the row layout, in a column for the column layout) then meet in that
+// XCD's L2 and leave it as one sector.
 struct TileWalk {
-    int64_t tr, tc;      // current tile row and column
-    int64_t dq, dr;      // s / tiles_c, s % tiles_c
+    int64_t br, bc;      // current block row and column
+    int64_t dq, dr;      // blocks per step: (s / blk^2) / blk_c, (s / blk^2) % blk_c
+    int ir, ic;          // the tile's place inside its block
 };
 
-__device__ __forceinline__ TileWalk tile_walk(const QuantArgs &a, int64_t idx)
+__device__ __forceinline__ int64_t first_order_index(const QuantArgs &a)
 {
-    const int64_t s = gridDim.x;
-    return TileWalk{idx / a.tiles_c, idx % a.tiles_c, s / a.tiles_c, s % a.tiles_c};
+    const int64_t w = blockIdx.x, s = gridDim.x;
+    if (a.blk == 1 || (s & 127)) return w;
+    const int64_t xcd = w & 7, slot = w >> 3;
+    return 16 * ((slot >> 4) * 8 + xcd) + (slot & 15);
+}
+
+__device__ __forceinline__ TileWalk tile_walk(const QuantArgs &a, int64_t o)
+{
+    const int bb = a.blk * a.blk;
+    const int64_t blk_idx = o / bb, sb = (int64_t)gridDim.x / bb;
+    const int i = (int)(o - blk_idx * bb);
+    return TileWalk{blk_idx / a.blk_c, blk_idx % a.blk_c, sb / a.blk_c, sb % a.blk_c,
+                    i / a.blk, i % a.blk};
+}
+
+__device__ __forceinline__ int64_t walk_r0(const QuantArgs &a, const TileWalk &w)
+{
+    return (w.br * a.blk + w.ir) * TILE;
+}
+
+__device__ __forceinline__ int64_t walk_c0(const QuantArgs &a, const TileWalk &w)
+{
+    return (w.bc * a.blk + w.ic) * TILE;
 }
 
 __device__ __forceinline__ void walk_forward(const QuantArgs &a, TileWalk &w)
 {
-    w.tr += w.dq;
-    w.tc += w.dr;
-    if (w.tc >= a.tiles_c) { w.tc -= a.tiles_c; ++w.tr; }
+    w.br += w.dq;
+    w.bc += w.dr;
+    if (w.bc >= a.blk_c) { w.bc -= a.blk_c; ++w.br; }
 }
 
 __device__ __forceinline__ void walk_back(const QuantArgs &a, TileWalk &w)
 {
-    w.tr -= w.dq;
-    w.tc -= w.dr;
-    if (w.tc < 0) { w.tc += a.tiles_c; --w.tr; }
+    w.br -= w.dq;
+    w.bc -= w.dr;
+    if (w.bc < 0) { w.bc += a.blk_c; --w.br; }
 }
 
 // Max |r| over this lane's half group of tile (r0, c0).
@@ -605,12 +639,12 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
     build_sign_table(st, a.rht_seed, ROT);
     if (t < 2) wmax[t] = 0u;
     float local = 0.0f;
-    int64_t k = blockIdx.x, r0 = 0, c0 = 0;
-    TileWalk tw{0, 0, 0, 0};
+    int64_t k = first_order_index(a), r0 = 0, c0 = 0;
+    TileWalk tw{0, 0, 0, 0, 0, 0};
     if (k < a.tiles) {
         tw = tile_walk(a, k);
-        r0 = tw.tr * TILE;
-        c0 = tw.tc * TILE;
+        r0 = walk_r0(a, tw);
+        c0 = walk_c0(a, tw);
         stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
     }
     while (k < a.tiles) {
@@ -619,8 +653,8 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         int64_t r1 = 0, c1 = 0;
         walk_forward(a, tw);                               // tile k1
         if (k1 < a.tiles) {
-            r1 = tw.tr * TILE;
-            c1 = tw.tc * TILE;
+            r1 = walk_r0(a, tw);
+            c1 = walk_c0(a, tw);
             stage_tile<WAVES>(tile1, a.x, a.R, a.C, r1, c1, dl);
         }
         {
@@ -633,8 +667,8 @@ __global__ void __launch_bounds__(512, 4) k_amax(QuantArgs a)
         __syncthreads();                                   // tile1 landed; tile0 is free
         walk_forward(a, tw);                               // tile k2
         if (k2 < a.tiles) {
-            r0 = tw.tr * TILE;
-            c0 = tw.tc * TILE;
+            r0 = walk_r0(a, tw);
+            c0 = walk_c0(a, tw);
             stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
         }
         {
@@ -1038,14 +1072,14 @@ k_quant(QuantArgs a)
     // select this lane's layout without indexing the argument struct at run time
     const LayoutOut o = (ro.lay == 0) ? a.out[0] : a.out[1];
     build_sign_table(st, a.rht_seed, ROT);
-    int64_t k = blockIdx.x, r0 = 0, c0 = 0;
-    // tiles in the reverse order of pass 1: index tiles - 1 - k, walking back
-    TileWalk tw{0, 0, 0, 0};
+    int64_t k = first_order_index(a), r0 = 0, c0 = 0;
+    // tiles in the reverse order of pass 1: order index tiles - 1 - k, walking back
+    TileWalk tw{0, 0, 0, 0, 0, 0};
     if (k < a.tiles) tw = tile_walk(a, a.tiles - 1 - k);
     // the first tile streams in while the tensor scale is reduced and its table built
     if (k < a.tiles) {
-        r0 = tw.tr * TILE;
-        c0 = tw.tc * TILE;
+        r0 = walk_r0(a, tw);
+        c0 = walk_c0(a, tw);
         stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
         if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
     }
@@ -1065,8 +1099,8 @@ k_quant(QuantArgs a)
         walk_back(a, tw);                                  // tile tiles - 1 - k1
         const bool more1 = k1 < a.tiles;
         if (more1) {
-            r1 = tw.tr * TILE;
-            c1 = tw.tc * TILE;
+            r1 = walk_r0(a, tw);
+            c1 = walk_c0(a, tw);
         }
         tile_quant<MODE, ROT>(tile0, st, tb0, a, o, ro, r0, c0, [&] {
             if (more1) {
@@ -1081,8 +1115,8 @@ k_quant(QuantArgs a)
         walk_back(a, tw);                                  // tile tiles - 1 - k2
         const bool more2 = k2 < a.tiles;
         if (more2) {
-            r0 = tw.tr * TILE;
-            c0 = tw.tc * TILE;
+            r0 = walk_r0(a, tw);
+            c0 = walk_c0(a, tw);
         }
         tile_quant<MODE, ROT>(tile1, st, tb1, a, o, ro, r1, c1, [&] {
             if (more2) {
@@ -1292,13 +1326,29 @@ static int grid_for(K kernel, int threads, int64_t tiles)
 // Phase-1 workgroups at most (their maxima fill the quantizers' workspace).
 constexpr int64_t MAX_PARTS = 2048;
 
+// A grid for the blocked visiting order must be a multiple of 16 workgroups (each keeps
+// one place inside the blocks it visits): round it down, or visit row-major if it would
+// vanish.
+static void fit_grid(QuantArgs &a, int64_t &grid)
+{
+    if (a.blk == 1) return;
+    if (grid >= 16) {
+        grid -= grid % 16;
+    } else {
+        a.blk = 1;
+        a.blk_c = a.tiles_c;
+    }
+}
+
 // Returns the number of workgroups launched.
 template <bool ROT, int LAY, bool LOCAL>
-static int64_t launch_amax(const QuantArgs &a, hipStream_t st)
+static int64_t launch_amax(const QuantArgs &args, hipStream_t st)
 {
+    QuantArgs a = args;
     const int threads = 64 * waves_for(LAY);
     int64_t grid = grid_for(k_amax<ROT, LAY, LOCAL>, threads, a.tiles);
     if (grid > MAX_PARTS) grid = MAX_PARTS;
+    fit_grid(a, grid);
     k_amax<ROT, LAY, LOCAL><<<(unsigned)grid, threads, 0, st>>>(a);
     return grid;
 }
@@ -1312,11 +1362,13 @@ static int64_t amax_lay(const QuantArgs &a, int lay, hipStream_t st)
 }
 
 template <int MODE, bool ROT, int LAY, bool LOCAL>
-static void launch_quant(const QuantArgs &a, hipStream_t st)
+static void launch_quant(const QuantArgs &args, hipStream_t st)
 {
+    QuantArgs a = args;
     const int threads = 64 * waves_for(LAY);
-    k_quant<MODE, ROT, LAY, LOCAL><<<grid_for(k_quant<MODE, ROT, LAY, LOCAL>, threads, a.tiles),
-                                     threads, 0, st>>>(a);
+    int64_t grid = grid_for(k_quant<MODE, ROT, LAY, LOCAL>, threads, a.tiles);
+    fit_grid(a, grid);
+    k_quant<MODE, ROT, LAY, LOCAL><<<(unsigned)grid, threads, 0, st>>>(a);
 }
 
 template <int MODE, bool ROT, bool LOCAL>
@@ -1358,6 +1410,8 @@ static QuantArgs make_args(const void *x, int64_t R, int64_t C, uint32_t *amax_b
     a.tiles_r = (R + TILE - 1) / TILE;
     a.tiles_c = (C + TILE - 1) / TILE;
     a.tiles = a.tiles_c * a.tiles_r;
+    a.blk = (a.tiles_r % 4 == 0 && a.tiles_c % 4 == 0) ? 4 : 1;
+    a.blk_c = a.tiles_c / a.blk;
     return a;
 }
 
