@@ -618,16 +618,17 @@ def training_step(nv, dev, tokens=32768, hidden=2048, ffn=8192, layers=24, reps=
 
 
 def rel_mse(nv, xd, mode, layout):
-    """Relative squared error sum((dequant - x)^2) / sum(x^2) of one layout, seed 1."""
+    """Relative squared error sum((dequant - x)^2) / sum(x^2) of one layout, seed 1; mode
+    "sr+rht" is SR after the same random-sign Hadamard rotation MS-EDEN uses."""
     import torch
 
     lay = (layout,)
     if mode == "eden":
         q = nv.eden_quantize(xd, 1, 1, layouts=lay)
         rot = True
-    elif mode == "sr":
-        q = nv.sr_quantize(xd, 1, layouts=lay)
-        rot = False
+    elif mode in ("sr", "sr+rht"):
+        rot = mode == "sr+rht"
+        q = nv.sr_quantize(xd, 1, rht=rot, rht_seed=1, layouts=lay)
     else:
         q = nv.rtn_quantize(xd, layouts=lay)
         rot = False
@@ -641,16 +642,20 @@ def rel_mse(nv, xd, mode, layout):
 
 
 def mse_vs_sr(nv, workloads, dev, x_c4):
-    """Relative MSE of RTN, SR and MS-EDEN (Philox seed 1) on the 256 x 1024 N(0,1) tensor
-    (the primary figure, row layout) and, for MS-EDEN over SR, on the three larger
-    configurations in both layouts."""
+    """Relative MSE of RTN, SR, SR with the rotation and MS-EDEN (Philox seed 1) on the
+    256 x 1024 N(0,1) tensor (the primary figure, row layout) and, for MS-EDEN over SR, on the
+    three larger configurations in both layouts.  Two SR baselines: plain SR, and SR after the
+    same random-sign Hadamard rotation, the baseline the pages compare MS-EDEN with (the
+    itsolotime.com summary, Q2: the GPU-feasible core of TetraJet-v2, SR with the rotation
+    along the inner dimension)."""
     import torch
 
     x = workloads.c1().to(dev)
-    res = {m: rel_mse(nv, x, m, "row") for m in ("rtn", "sr", "eden")}
+    res = {m: rel_mse(nv, x, m, "row") for m in ("rtn", "sr", "sr+rht", "eden")}
     out = {"workload": "256x1024 N(0,1) bf16 (seed 0), row layout, Philox seed 1",
            "rel_mse": {k: round(v, 6) for k, v in res.items()},
-           "eden_over_sr": round(res["eden"] / res["sr"], 4), "other_configs": {}}
+           "eden_over_sr": round(res["eden"] / res["sr"], 4),
+           "eden_over_sr_rht": round(res["eden"] / res["sr+rht"], 4), "other_configs": {}}
     for name, gen in (("4096x4096 t3*0.02 + outliers", workloads.c2),
                       ("16384x2048 row magnitudes 1e-6..10", workloads.c3),
                       ("16384x8192 N(0,1) x column lognormal", None)):
@@ -658,8 +663,10 @@ def mse_vs_sr(nv, workloads, dev, x_c4):
         ratios = {}
         for layout in ("row", "col"):
             e, s = rel_mse(nv, xd, "eden", layout), rel_mse(nv, xd, "sr", layout)
-            ratios[layout] = {"eden": round(e, 6), "sr": round(s, 6),
-                              "eden_over_sr": round(e / s, 4)}
+            sr = rel_mse(nv, xd, "sr+rht", layout)
+            ratios[layout] = {"eden": round(e, 6), "sr": round(s, 6), "sr+rht": round(sr, 6),
+                              "eden_over_sr": round(e / s, 4),
+                              "eden_over_sr_rht": round(e / sr, 4)}
         out["other_configs"][name] = ratios
         del xd
         torch.cuda.empty_cache()

@@ -82,6 +82,11 @@ MUTATIONS = [
      "double ab = E2M1_V[lo] + ((double)u / 16777216.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);",
      "double ab = E2M1_V[lo + 1] - ((double)u / 16777216.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);",
      [MARG + "test_elem_sr_margin"]),
+    ("decoder drops the sign", "o[e] = (code & 8) ? -qv : qv;", "o[e] = qv;",
+     [QUANT + "test_dequantize_round_trips_on_grid_inputs"]),
+    ("decoder swaps the nibbles", "uint8_t code = (e % 2 == 0) ? (byte & 15) : (byte >> 4);",
+     "uint8_t code = (e % 2 == 0) ? (byte >> 4) : (byte & 15);",
+     [QUANT + "test_dequantize_round_trips_on_grid_inputs"]),
     ("4/6 tensor scale divides by 6 * 448",
      "float d = (mode == MODE_FP46) ? 1792.0f : 2688.0f;",
      "float d = (mode == MODE_FP46) ? 2688.0f : 2688.0f;",

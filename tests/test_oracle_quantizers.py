@@ -307,17 +307,42 @@ def test_skip_of_tiny_scales(oracle_mod):
     assert np.mean(qs[1].scales[big] != qs[0].scales[big]) > 0.05
 
 
-def test_dequantize_matches_decode(oracle_mod):
-    x = workloads.c1()
-    q = oracle_mod.quantize("rtn", _bits(x), axis=0)
-    out = oracle_mod.dequantize(q.codes, q.scales, q.g)
-    codes = oracle_mod.unpack_codes(q.codes)
-    vals = np.array([oracle_mod.e4m3_value(int(c)) for c in range(127)], dtype=np.float32)
-    s = np.repeat(vals[q.scales], 16, axis=1)
-    mag = MAGS.astype(np.float32)[codes & 7]
-    ref = (s * np.float32(q.g)) * mag
-    ref = np.where(codes & 8, -ref, ref)
-    np.testing.assert_array_equal(out, ref)
+def test_e4m3_values_against_torch(oracle_mod):
+    """The decoder's scale values: every non-negative finite E4M3FN code against torch's own
+    float8_e4m3fn decode (a library routine)."""
+    codes = torch.arange(127, dtype=torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).float().numpy()
+    got = np.array([oracle_mod.e4m3_value(int(c)) for c in range(127)], dtype=np.float32)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_dequantize_round_trips_on_grid_inputs(oracle_mod):
+    """Closed form: an input every element of which is sign * V * s_b * g (V on the E2M1 grid,
+    s_b an E4M3 value, g a power of two, each block's largest |V| equal to 6 and one block at
+    the top scale 448) is quantized by RTN without loss, so decoding returns it bit for bit --
+    signs, zeros, subnormal scales and all-zero blocks included."""
+    rng = np.random.default_rng(7)
+    vals = np.array([oracle_mod.e4m3_value(c) for c in range(127)], dtype=np.float64)
+    rows, cols = 64, 256
+    k = -5
+    x = np.zeros((rows, cols))
+    for r in range(rows):
+        for b in range(cols // 16):
+            if rng.random() < 0.1:
+                continue                                   # an all-zero block
+            s = vals[rng.integers(1, 127)]                 # any nonzero scale, subnormal too
+            v = rng.choice(MAGS, 16) * rng.choice([-1.0, 1.0], 16)
+            v[rng.integers(16)] = 6.0 * rng.choice([-1.0, 1.0])
+            x[r, 16 * b:16 * b + 16] = v * s * 2.0 ** k
+    x[0, :16] = 0.0
+    x[0, 3] = -6.0 * 448.0 * 2.0 ** k                      # the tensor max: g = 2^k
+    xt = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(xt.double().numpy(), x), "construction must be bf16-exact"
+    q = oracle_mod.quantize("rtn", _bits(xt), axis=0)
+    assert q.g == 2.0 ** k
+    back = oracle_mod.dequantize(q.codes, q.scales, q.g)
+    np.testing.assert_array_equal(back.astype(np.float64), x)
+    assert np.signbit(back[x < 0]).all() and not np.signbit(back[x > 0]).any()
 
 
 # ----------------------------------------------------------------------------- statistics
