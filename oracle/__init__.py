@@ -91,6 +91,12 @@ def _load():
     lib.oracle_scale_sr_n.argtypes = [f32, P, P, i64]
     lib.oracle_elem_sr_mag_n.argtypes = [f32, P, P, i64]
     lib.oracle_margin_n.argtypes = [i32, P, P, P, i64]
+    lib.oracle_mx_scale_exp.argtypes = [f32]
+    lib.oracle_mx_scale_exp.restype = i32
+    lib.oracle_mx_quantize.argtypes = [i32, P, i64, i64, i32, i32, u64, u64, P, P]
+    lib.oracle_mx_quantize.restype = i32
+    lib.oracle_mx_dequantize.argtypes = [P, P, i64, i64, i32, u64, P]
+    lib.oracle_mx_dequantize.restype = i32
     lib.oracle_scale_sr_pairs_n.argtypes = [P, P, P, i64]
     lib.oracle_elem_sr_pairs_n.argtypes = [P, P, P, i64]
     lib.oracle_philox_n.argtypes = [P, P, P, i64]
@@ -394,3 +400,45 @@ def unpack_codes(codes: np.ndarray) -> np.ndarray:
     lo = codes & 0x0F
     hi = codes >> 4
     return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+# ---------------------------------------------------------------------------- MXFP4 contract
+
+class MXQuantized(NamedTuple):
+    codes: np.ndarray          # uint8 [vecs, n/2], low nibble = even position
+    scales: np.ndarray         # uint8 [vecs, n/32], E8M0: 2^(byte - 127)
+
+
+def mx_scale_exp(m: float) -> int:
+    """Smallest e with 6 * 2^e >= m (clamped to [-127, 127]; -127 for m = 0)."""
+    return int(_load().oracle_mx_scale_exp(m))
+
+
+def mx_quantize(x, axis: int = 0, sr: bool = False, seed: int = 0, rht: bool = False,
+                rht_seed: int = 0) -> MXQuantized:
+    """MXFP4 (E2M1 elements, one E8M0 scale per 32) of one layout, RTN or SR."""
+    lib = _load()
+    xb = _bf16_bits(x)
+    rows, cols = xb.shape
+    nvec, n = (rows, cols) if axis == 0 else (cols, rows)
+    codes = np.zeros((nvec, n // 2), dtype=np.uint8)
+    scales = np.zeros((nvec, n // 32), dtype=np.uint8)
+    rc = lib.oracle_mx_quantize(int(bool(sr)), _ptr(xb), rows, cols, axis, int(bool(rht)), seed,
+                                rht_seed, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_mx_quantize: unsupported shape {xb.shape} for axis {axis}")
+    return MXQuantized(codes, scales)
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, rht: bool = False,
+                  rht_seed: int = 0) -> np.ndarray:
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    nvec, n = codes.shape[0], codes.shape[1] * 2
+    out = np.zeros((nvec, n), dtype=np.float32)
+    rc = lib.oracle_mx_dequantize(_ptr(codes), _ptr(scales), nvec, n, int(bool(rht)), rht_seed,
+                                  _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_mx_dequantize: bad shape")
+    return out

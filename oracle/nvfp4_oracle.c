@@ -859,3 +859,105 @@ void oracle_philox_n(const uint64_t *key, const uint32_t *ctr, uint32_t *out, in
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) oracle_philox4x32_10(key[i], ctr + 4 * i, out + 4 * i);
 }
+
+/* ------------------------------------------------------------------ MXFP4 block contract
+ * The recipe of the native FP4 matrix-core consumer.  gfx950's scaled matrix instructions
+ * multiply E2M1 elements that carry one power-of-two (E8M0) scale per 32 consecutive elements
+ * along K, and nothing per 16: an NVFP4 operand's E4M3 block scales (3 mantissa bits) cannot
+ * be carried by them.  This contract is the plainest one they can consume: the vectors and
+ * layouts, rotation and random streams of the NVFP4 quantizers; blocks of 32; block scale
+ * 2^e with e the smallest integer such that 6 * 2^e >= max |r| over the block (the grid's top,
+ * 6, covers the block: nothing clips, so SR stays unbiased, as with the NVFP4 SR scale),
+ * e clamped to [-127, 127] (E8M0 byte = e + 127; an all-zero block gets byte 0); elements
+ * y = r * 2^-e (one rounding; the scaling is exact unless y is subnormal) rounded to the E2M1
+ * grid by RTN ([TG] Method: round to nearest) or SR ([Q2-TH] opening paragraph). */
+
+/* Smallest e with 6 * 2^e >= m, clamped; -127 for m = 0. */
+int oracle_mx_scale_exp(float m)
+{
+    if (!(m > 0.0f)) return -127;
+    int E;
+    frexpf(m, &E);                          /* m = f 2^E, f in [0.5, 1) */
+    int e = E - 4;                          /* 6 * 2^(E-4) = 0.375 * 2^E < m */
+    while (ldexp(6.0, e) < (double)m) ++e;  /* exact in double */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+int oracle_mx_quantize(int sr, const uint16_t *x, int64_t rows, int64_t cols, int axis,
+                       int rht, uint64_t seed, uint64_t rht_seed, uint8_t *codes,
+                       uint8_t *scales)
+{
+    int64_t n = axis == 0 ? cols : rows;
+    int64_t nvec = axis == 0 ? rows : cols;
+    if (n % 32) return -2;
+    if (rht && n % GROUP) return -2;
+    float sigma[GROUP];
+    oracle_signs(rht_seed, sigma);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t vec = 0; vec < nvec; ++vec) {
+        float *r = (float *)malloc(sizeof(float) * (size_t)(n ? n : 1));
+        if (!r) { bad = 1; continue; }
+        load_vector(x, rows, cols, axis, vec, r);
+        rotate_vector(r, n, rht, sigma);
+        for (int64_t b = 0; b < n / 32; ++b) {
+            const float *rb = r + 32 * b;
+            float m = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(rb[i]) > m) m = fabsf(rb[i]);
+            int e = oracle_mx_scale_exp(m);
+            scales[vec * (n / 32) + b] = (uint8_t)(e + 127);
+            float p = ldexpf(1.0f, -e);     /* exact: -e in [-127, 127] */
+            for (int i = 0; i < 32; ++i) {
+                int64_t pos = 32 * b + i;
+                float y = rb[i] * p;
+                int mag;
+                if (sr) {
+                    uint32_t w = rand_word(seed, (uint64_t)(vec * n + pos), STREAM_ELEM_SR,
+                                           (uint32_t)axis);
+                    mag = oracle_elem_sr_mag(fminf(fabsf(y), 6.0f), w >> 8);
+                } else {
+                    mag = oracle_e2m1_rtn_mag(fabsf(y));
+                }
+                uint8_t code = (uint8_t)(mag | ((rb[i] < 0.0f) << 3));
+                uint8_t *dst = codes + vec * (n / 2) + pos / 2;
+                if (pos % 2 == 0) *dst = code;
+                else *dst |= (uint8_t)(code << 4);
+            }
+        }
+        free(r);
+    }
+    return bad ? -2 : 0;
+}
+
+/* value = sign * V[mag] * 2^e; with the rotation, x_j = sigma_j * (H q)_j * 2^-7. */
+int oracle_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t nvec, int64_t n,
+                         int rht, uint64_t rht_seed, float *out)
+{
+    if (n % 32) return -2;
+    if (rht && n % GROUP) return -2;
+    float sigma[GROUP];
+    oracle_signs(rht_seed, sigma);
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < nvec; ++v) {
+        float *o = out + v * n;
+        for (int64_t pos = 0; pos < n; ++pos) {
+            uint8_t byte = codes[v * (n / 2) + pos / 2];
+            uint8_t code = (pos % 2 == 0) ? (byte & 15) : (byte >> 4);
+            float s = ldexpf(1.0f, (int)scales[v * (n / 32) + pos / 32] - 127);
+            float qv = E2M1_V[code & 7] * s;
+            o[pos] = (code & 8) ? -qv : qv;
+        }
+        if (rht) {
+            for (int64_t g0 = 0; g0 < n; g0 += GROUP) {
+                float a[GROUP];
+                memcpy(a, o + g0, sizeof a);
+                oracle_fwht128(a);
+                for (int j = 0; j < GROUP; ++j) o[g0 + j] = (sigma[j] * a[j]) * 0.0078125f;
+            }
+        }
+    }
+    return 0;
+}

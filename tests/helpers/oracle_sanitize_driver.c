@@ -51,6 +51,12 @@ void oracle_elem_sr_mag_n(float a, const uint32_t *u, uint8_t *out, int64_t n);
 void oracle_scale_sr_pairs_n(const float *c, const uint32_t *w, uint8_t *out, int64_t n);
 void oracle_elem_sr_pairs_n(const float *a, const uint32_t *u, uint8_t *out, int64_t n);
 void oracle_philox_n(const uint64_t *key, const uint32_t *ctr, uint32_t *out, int64_t n);
+int oracle_mx_scale_exp(float m);
+int oracle_mx_quantize(int sr, const uint16_t *x, int64_t rows, int64_t cols, int axis,
+                       int rht, uint64_t seed, uint64_t rht_seed, uint8_t *codes,
+                       uint8_t *scales);
+int oracle_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t nvec, int64_t n,
+                         int rht, uint64_t rht_seed, float *out);
 
 static int failures = 0;
 #define CHECK(cond, ...) do { if (!(cond)) { fprintf(stderr, __VA_ARGS__); \
@@ -138,6 +144,23 @@ static void run_shape(int64_t rows, int64_t cols)
                 }
                 free(c1); free(s1); free(c2); free(s2); free(em); free(sm);
             }
+    /* the MXFP4 contract: blocks of 32 */
+    for (int sr = 0; sr < 2; ++sr)
+        for (int axis = 0; axis < 2; ++axis)
+            for (int rht = 0; rht < 2; ++rht) {
+                int64_t n = axis == 0 ? cols : rows, vecs = axis == 0 ? rows : cols;
+                int valid = n % 32 == 0 && (!rht || n % 128 == 0);
+                size_t nc = (size_t)(vecs * (n / 2)), ns = (size_t)(vecs * (n / 32));
+                uint8_t *c = xmalloc(nc), *sc = xmalloc(ns);
+                int rc = oracle_mx_quantize(sr, x, rows, cols, axis, rht, 3, 4, c, sc);
+                CHECK(rc == (valid ? 0 : -2), "mx quantize %dx%d rc %d", (int)rows, (int)cols, rc);
+                if (valid && rc == 0) {
+                    float *out = xmalloc((size_t)(vecs * n) * 4);
+                    CHECK(oracle_mx_dequantize(c, sc, vecs, n, rht, 4, out) == 0, "mx dequantize");
+                    free(out);
+                }
+                free(c); free(sc);
+            }
     float amax = oracle_amax(x, rows, cols, 0, 1, 3);
     CHECK(amax >= 0 || cols % 128, "amax");
     free(x);
@@ -201,6 +224,8 @@ static void run_scalars(void)
     CHECK(oracle_elem_sr_mag(6.0f, 0) == 7, "element SR at 6");
     CHECK(oracle_e2m1_rtn_mag(0.25f) == 0, "E2M1 tie");
     CHECK(oracle_tensor_scale(3, 1792.0f) == 1.0f, "4/6 tensor scale");
+    for (int i = 0; i < N; ++i) (void)oracle_mx_scale_exp(fabsf(v[i]));
+    CHECK(oracle_mx_scale_exp(6.0f) == 0 && oracle_mx_scale_exp(0.0f) == -127, "MX scale");
     free(v); free(w); free(m); free(b); free(c); free(a); free(u);
 }
 

@@ -17,6 +17,7 @@ SRC = os.path.join(ROOT, "oracle", "nvfp4_oracle.c")
 PRIM = "tests/test_oracle_primitives.py::"
 QUANT = "tests/test_oracle_quantizers.py::"
 STRIP = "tests/test_oracle_strips.py::"
+MX = "tests/test_oracle_mx.py::"
 MARG = "tests/test_oracle_margins.py::"
 
 # (name, text in the source, replacement, pins that must notice)
@@ -87,6 +88,16 @@ MUTATIONS = [
     ("decoder swaps the nibbles", "uint8_t code = (e % 2 == 0) ? (byte & 15) : (byte >> 4);",
      "uint8_t code = (e % 2 == 0) ? (byte >> 4) : (byte & 15);",
      [QUANT + "test_dequantize_round_trips_on_grid_inputs"]),
+    ("MX scale one binade high on exact fits", "while (ldexp(6.0, e) < (double)m) ++e;",
+     "while (ldexp(6.0, e) <= (double)m) ++e;", [MX + "test_scale_exponent_brute_force"]),
+    ("MX elements scaled by the wrong power", "float p = ldexpf(1.0f, -e);",
+     "float p = ldexpf(1.0f, 1 - e);", [MX + "test_rtn_codes_are_nearest_and_never_clip"]),
+    ("MX decoder ignores the scale bias", "float s = ldexpf(1.0f, (int)scales[v * (n / 32) + pos / 32] - 127);",
+     "float s = ldexpf(1.0f, (int)scales[v * (n / 32) + pos / 32] - 126);",
+     [MX + "test_round_trip_on_grid_inputs"]),
+    ("MX SR draws from the scale stream", "uint32_t w = rand_word(seed, (uint64_t)(vec * n + pos), STREAM_ELEM_SR,",
+     "uint32_t w = rand_word(seed, (uint64_t)(vec * n + pos) / 4, STREAM_ELEM_SR,",
+     [MX + "test_sr_draws_are_independent_per_element"]),
     ("4/6 tensor scale divides by 6 * 448",
      "float d = (mode == MODE_FP46) ? 1792.0f : 2688.0f;",
      "float d = (mode == MODE_FP46) ? 2688.0f : 2688.0f;",
