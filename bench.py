@@ -388,9 +388,39 @@ def gemm_check(nv, workloads, dev, a, stream, reps=10, warmup=3):
     M, K = a.codes.shape[0], a.codes.shape[1] * 2
     N = b.codes.shape[0]
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-    return {"kernel": "k_gemm (dequantize into LDS as FP16, v_mfma_f32_32x32x16_f16)", "M": M, "N": N,
-            "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
-            "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
+    res = {"kernel": "k_gemm (dequantize into LDS as FP16, v_mfma_f32_32x32x16_f16)", "M": M,
+           "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
+           "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
+    res["native_fp4"] = mx_gemm(nv, workloads, dev, stream, reps, warmup)
+    return res
+
+
+def mx_gemm(nv, workloads, dev, stream, reps=10, warmup=3):
+    """The native FP4 consumer on the same shape: the 16384 x 8192 input quantized to MXFP4
+    (SR after the rotation) against the 8192 x 8192 weight (RTN after the same rotation),
+    C = A B^T on v_mfma_scale_f32_32x32x64_f8f6f4, against MI355X's 10.1 PFLOP/s dense FP4."""
+    import numpy as np
+    import torch
+
+    a = nv.mxfp4_quantize(workloads.c4().to(dev), sr=True, seed=1, rht=True, rht_seed=1).row
+    b = nv.mxfp4_quantize(workloads.c4w().to(dev), rht=True, rht_seed=1).row
+    c = torch.empty((a.codes.shape[0], b.codes.shape[0]), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        nv.mxfp4_gemm(a, b, rotated_pair=True, out=c, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        nv.mxfp4_gemm(a, b, rotated_pair=True, out=c, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    M, K = a.codes.shape[0], a.codes.shape[1] * 2
+    N = b.codes.shape[0]
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"kernel": "k_gemm_mx (MXFP4 operands, v_mfma_scale_f32_32x32x64_f8f6f4)", "M": M,
+            "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "frac_of_fp4_dense_peak": round(tflops / 10100.0, 4)}
 
 
 def modes_table(nv, x, out, stream, reps=40):

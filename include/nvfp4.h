@@ -233,6 +233,42 @@ int dequantize_strips(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group
 int nvfp4_gemm_check_strips(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t M, int64_t N,
                             int64_t K, int rotated_pair, float *c, void *stream);
 
+/* ------------------------------------------------------------------ MXFP4 (native FP4)
+ * The recipe of the native FP4 matrix-core consumer.  Quartet II runs its linear layers on
+ * FP4 matrix cores (itsolotime.com summary, abstract: NVFP4 GEMM kernels up to 4.2x over
+ * BF16).  gfx950's scaled matrix instructions multiply E2M1 elements that carry one power-of-
+ * two (E8M0) scale per 32 elements along K; an NVFP4 operand's E4M3 scales per 16 (3 mantissa
+ * bits) cannot ride on them, so this recipe has a block contract of its own ("MXFP4"): the
+ * vectors, layouts, rotation (rht, rht_seed as for the NVFP4 quantizers) and random streams of
+ * the NVFP4 quantizers; blocks of 32; block scale 2^e with e the smallest integer such that
+ * 6 * 2^e >= max |r| over the block (nothing clips, so SR stays unbiased), clamped to
+ * [-127, 127]; elements y = r * 2^-e rounded to the E2M1 grid by round-to-nearest-even
+ * (sr == 0; Telegram digest "Method") or stochastically (sr == 1; itsolotime opening
+ * paragraph; the draw of element e of a layout is word e mod 4 of Philox(seed, (e/4 lo,
+ * e/4 hi, 3, layout))).  MS-EDEN has no MXFP4 form here: stochastic rounding of its corrected
+ * scales onto powers of two would add several percent of variance.  No tensor scale. */
+typedef struct mxfp4_tensor {
+    uint8_t *codes;      /* [vecs][n/2]  packed E2M1 codes, low nibble first; 16-byte aligned */
+    uint8_t *scales;     /* [vecs][n/32] E8M0 bytes, scale = 2^(byte - 127); 4-byte aligned */
+} mxfp4_tensor;
+
+/* MXFP4 quantization of x (as for the NVFP4 quantizers: BF16 row-major, 16-byte aligned,
+ * cols % 8 == 0) in one or both layouts, one pass (no tensor-wide maximum is needed).
+ * block must be 32; each requested layout's n a multiple of 32 (128 with the rotation).  No
+ * workspace; errors as in the conventions above. */
+int mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int block, int sr,
+                   uint64_t seed, int rht, uint64_t rht_seed, const mxfp4_tensor *row_out,
+                   const mxfp4_tensor *col_out, void *stream);
+
+/* C[m][n] = f * sum_k a(m,k) * b(n,k) on the FP4 matrix cores (v_mfma_scale_f32_32x32x64_
+ * f8f6f4), a(m,k) = sign * magnitude * 2^(scale byte - 127) of `a` [M][K] and likewise of `b`
+ * [N][K] (row layouts, K contiguous); f = 2^-7 when rotated_pair != 0 (both operands rotated
+ * along K with the same rht_seed) else 1.  Products exact, FP32 accumulation (order
+ * unspecified).  c is FP32 [M][N] row-major (device, 4-byte aligned).  M and N multiples of
+ * 32, K a multiple of 128. */
+int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, int64_t M, int64_t N, int64_t K,
+               int rotated_pair, float *c, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

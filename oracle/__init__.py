@@ -93,6 +93,7 @@ def _load():
     lib.oracle_margin_n.argtypes = [i32, P, P, P, i64]
     lib.oracle_mx_scale_exp.argtypes = [f32]
     lib.oracle_mx_scale_exp.restype = i32
+    lib.oracle_mx_scale_exp_n.argtypes = [P, P, i64]
     lib.oracle_mx_quantize.argtypes = [i32, P, i64, i64, i32, i32, u64, u64, P, P]
     lib.oracle_mx_quantize.restype = i32
     lib.oracle_mx_dequantize.argtypes = [P, P, i64, i64, i32, u64, P]
@@ -412,6 +413,11 @@ class MXQuantized(NamedTuple):
 def mx_scale_exp(m: float) -> int:
     """Smallest e with 6 * 2^e >= m (clamped to [-127, 127]; -127 for m = 0)."""
     return int(_load().oracle_mx_scale_exp(m))
+
+
+def mx_scale_byte_n(m) -> np.ndarray:
+    """E8M0 bytes (e + 127) of the MXFP4 block scale for each block maximum m."""
+    return _map_u8("oracle_mx_scale_exp_n", m)
 
 
 def mx_quantize(x, axis: int = 0, sr: bool = False, seed: int = 0, rht: bool = False,

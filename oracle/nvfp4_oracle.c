@@ -961,3 +961,9 @@ int oracle_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t nv
     }
     return 0;
 }
+
+void oracle_mx_scale_exp_n(const float *m, uint8_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)(oracle_mx_scale_exp(m[i]) + 127);
+}

@@ -106,6 +106,14 @@ __global__ void k_elem_sr(const float *a, const uint32_t *w, uint64_t n, uint8_t
         out[i] = (uint8_t)e2m1_sr_mag(a[i], w[i]);
 }
 
+// MXFP4 scale byte (e + 127) of the floats with bits start + i.
+__global__ void k_mx_exp(uint32_t start, uint64_t count, uint8_t *out)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        out[i] = (uint8_t)(mx_scale_exp(__uint_as_float(start + (uint32_t)i)) + 127);
+}
+
 // Philox4x32-10 words of (key, counter) pairs: ctr [n][4], out [n][4].
 __global__ void k_philox(const uint64_t *key, const uint32_t *ctr, uint64_t n, uint32_t *out)
 {
@@ -163,6 +171,12 @@ int conv_scale_sr(const float *c, const uint32_t *w, uint64_t n, uint8_t *out, v
 int conv_elem_sr(const float *a, const uint32_t *w, uint64_t n, uint8_t *out, void *stream)
 {
     k_elem_sr<<<grid_for(n), THREADS, 0, (hipStream_t)stream>>>(a, w, n, out);
+    return status();
+}
+
+int conv_mx_exp(uint32_t start, uint64_t count, uint8_t *out, void *stream)
+{
+    k_mx_exp<<<grid_for(count), THREADS, 0, (hipStream_t)stream>>>(start, count, out);
     return status();
 }
 

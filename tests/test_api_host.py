@@ -149,3 +149,24 @@ def test_noalloc_validation(L):
     assert q(rows=1 << 32) == nv.ERR_ARG
     if not _has_gpu():
         assert q() == nv.ERR_HIP
+
+
+def test_mxfp4_validation(L):
+    r = ctypes.byref(nv._CMx(FAKE, FAKE + 4096))
+    c = ctypes.byref(nv._CMx(FAKE + 65536, FAKE + 69632))
+
+    def q(x=FAKE, rows=256, cols=256, block=32, sr=0, rht=0, row=r, col=c):
+        return L.mxfp4_quantize(x, rows, cols, block, sr, 1, rht, 1, row, col, None)
+    assert q(row=None, col=None) == nv.ERR_NULL
+    assert q(x=0) == nv.ERR_NULL
+    assert q(block=16) == nv.ERR_GROUP
+    assert q(sr=2) == nv.ERR_ARG
+    assert q(cols=200) == nv.ERR_SHAPE                    # row layout needs cols % 32
+    assert q(rows=160, cols=256, rht=1) == nv.ERR_SHAPE   # rotation needs rows % 128 (col)
+    assert q(row=ctypes.byref(nv._CMx(FAKE + 8, FAKE))) == nv.ERR_ALIGN
+    assert q(row=ctypes.byref(nv._CMx(FAKE, FAKE + 2))) == nv.ERR_ALIGN
+    assert L.mxfp4_gemm(r, r, 64, 64, 64, 0, FAKE, None) == nv.ERR_SHAPE      # K % 128
+    assert L.mxfp4_gemm(r, r, 48, 64, 128, 0, FAKE, None) == nv.ERR_SHAPE     # M % 32
+    assert L.mxfp4_gemm(r, r, 64, 64, 128, 2, FAKE, None) == nv.ERR_ARG
+    assert L.mxfp4_gemm(None, r, 64, 64, 128, 0, FAKE, None) == nv.ERR_NULL
+    assert L.mxfp4_gemm(r, r, 64, 64, 128, 0, FAKE + 2, None) == nv.ERR_ALIGN

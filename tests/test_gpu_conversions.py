@@ -10,7 +10,8 @@ unbiased_nvfp4_gradient_amd/csrc/nvfp4_device.h, the code the kernels include):
 * E2M1 decode (v_cvt_scalef32_pk_f32_fp4): all 256 code bytes at all four byte positions,
   bit for bit (so -0 for code 8);
 * E4M3 values of the 128 codes;
-* scale SR, element SR and Philox4x32-10 on sampled inputs.
+* scale SR, element SR and Philox4x32-10 on sampled inputs;
+* the MXFP4 block-scale exponent over every non-negative finite binary32.
 
 These roundings are the whole of the contract's element and scale decisions (Telegram digest
 quant_prune_distill post 640, "Method": round-to-nearest onto the +-6 grid, FP8 scales; the
@@ -41,7 +42,8 @@ def conv():
     for name, args in (("conv_fp4_encode", [u32, u64, P, P, P]), ("conv_e4m3_rne", [u32, u64, P, P]),
                        ("conv_e4m3_up", [u32, u64, P, P]), ("conv_fp4_decode", [P, P]),
                        ("conv_e4m3_val", [P, P]), ("conv_scale_sr", [P, P, u64, P, P]),
-                       ("conv_elem_sr", [P, P, u64, P, P]), ("conv_philox", [P, P, u64, P, P])):
+                       ("conv_elem_sr", [P, P, u64, P, P]), ("conv_philox", [P, P, u64, P, P]),
+                       ("conv_mx_exp", [u32, u64, P, P])):
         getattr(h, name).argtypes = args
         getattr(h, name).restype = ctypes.c_int
     return h
@@ -175,3 +177,20 @@ def test_philox_sampled(conv):
     out = torch.empty((n, 4), dtype=torch.int32, device=DEV)
     assert conv.conv_philox(kd.data_ptr(), cd.data_ptr(), n, out.data_ptr(), _stream()) == 0
     assert np.array_equal(out.cpu().numpy().view(np.uint32), oracle.philox_n(keys, ctr))
+
+
+def test_mx_scale_exponent_every_float(conv):
+    """The MXFP4 block-scale exponent (frexp on the device) over every non-negative finite
+    binary32, subnormals included, against the oracle's definition (the smallest e with
+    6 * 2^e >= m, clamped to [-127, 127])."""
+    end = 0x7F800000
+    print(f"case: MXFP4 scale exponent, {end} floats", flush=True)
+    buf = torch.empty(CHUNK, dtype=torch.uint8, device=DEV)
+    for lo in range(0, end, CHUNK):
+        n = min(CHUNK, end - lo)
+        assert conv.conv_mx_exp(lo, n, buf.data_ptr(), _stream()) == 0
+        got = buf[:n].cpu().numpy()
+        want = oracle.mx_scale_byte_n(_bits(lo, n).view(np.float32))
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, (f"{bad.size} differ, first at bits {lo + int(bad[0]):#010x}: "
+                               f"{got[bad[0]]} vs {want[bad[0]]}")

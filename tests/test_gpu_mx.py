@@ -1,0 +1,167 @@
+"""The MXFP4 recipe on the GPU: the producer (mxfp4_quantize) against the oracle's MXFP4
+quantizer bit for bit, and the native FP4 matrix-core consumer (mxfp4_gemm) against an fp64
+product of the exact operand values, within the bound of FP32 accumulation
+(|dC| <= 2 K u sum_k |a_k b_k| + 4 u |C|, u = 2^-24)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import unbiased_nvfp4_gradient_amd as nv
+import workloads
+from guards import MARGIN, SENTINEL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U = 2.0 ** -24
+E2M1 = np.array([oracle.e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def _guarded_mx(vecs, n):
+    """An MXFP4 layout whose two tensors sit inside sentinel margins."""
+    bufs = []
+    views = []
+    for nbytes, shape in ((vecs * (n // 2), (vecs, n // 2)), (vecs * (n // 32), (vecs, n // 32))):
+        buf = torch.full((MARGIN + nbytes + MARGIN,), SENTINEL, dtype=torch.uint8, device=DEV)
+        bufs.append((buf, nbytes))
+        views.append(buf[MARGIN:MARGIN + nbytes].view(shape))
+    return nv.MXFP4(*views), bufs
+
+
+def _intact(bufs):
+    return all(bool((b[:MARGIN] == SENTINEL).all()) and bool((b[MARGIN + n:] == SENTINEL).all())
+               for b, n in bufs)
+
+
+def check_mx(x, layouts, sr, rht, seed=5, rht_seed=7, what=""):
+    xd = x.to(DEV)
+    rows, cols = xd.shape
+    row, bufs_r = _guarded_mx(rows, cols) if "row" in layouts else (None, [])
+    col, bufs_c = _guarded_mx(cols, rows) if "col" in layouts else (None, [])
+    q = nv.mxfp4_quantize(xd, sr=sr, seed=seed, rht=rht, rht_seed=rht_seed, layouts=layouts,
+                          out=nv.MXQuantized(row, col))
+    torch.cuda.synchronize()
+    assert _intact(bufs_r + bufs_c), f"{what}: a write landed outside an output buffer"
+    xb = workloads.bf16_bits(x)
+    for axis, t in ((0, q.row), (1, q.col)):
+        if t is None:
+            continue
+        ref = oracle.mx_quantize(xb, axis=axis, sr=sr, seed=seed, rht=rht, rht_seed=rht_seed)
+        codes, scales = t.codes.cpu().numpy(), t.scales.cpu().numpy()
+        cm = int(np.count_nonzero(codes != ref.codes))
+        sm = int(np.count_nonzero(scales != ref.scales))
+        assert cm == 0 and sm == 0, f"{what} axis={axis}: {cm} code bytes, {sm} scales differ"
+    return q
+
+
+@pytest.mark.parametrize("sr,rht", [(False, False), (True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("layouts", [("row",), ("col",), ("row", "col")])
+def test_mx_quantize_config1(sr, rht, layouts):
+    print(f"case: MXFP4 c1 sr={sr} rht={rht} {layouts}", flush=True)
+    check_mx(workloads.c1(), layouts, sr, rht, what="c1")
+
+
+@pytest.mark.parametrize("shape,sr,rht,layouts", [
+    ((200, 256), True, True, ("row",)),            # ragged rows: partial tiles
+    ((256, 200), False, False, ("col",)),          # n = 256, rows % 128 != 0 elsewhere
+    ((96, 160), True, False, ("row", "col")),      # n % 128 != 0: partial groups, odd n/32
+    ((32, 32), False, False, ("row", "col")),      # one block
+    ((384, 640), True, True, ("row", "col")),      # several tiles
+])
+def test_mx_quantize_ragged(shape, sr, rht, layouts):
+    print(f"case: MXFP4 {shape} sr={sr} rht={rht} {layouts}", flush=True)
+    check_mx(workloads.normal(shape, seed=sum(shape)), layouts, sr, rht, what=f"{shape}")
+
+
+def test_mx_quantize_extremes_and_zeros():
+    """Per-row magnitudes 1e-30..1e30 (scale exponents at the clamp), all-zero rows, -0."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((256, 512)) * 10.0 ** rng.uniform(-30, 30, (256, 1))
+    x[:16] = 0.0
+    x[16:32] = -0.0
+    xt = workloads.to_bf16(x)
+    print("case: MXFP4 extremes and zeros", flush=True)
+    for sr, rht in ((False, False), (True, True), (True, False)):
+        check_mx(xt, ("row", "col"), sr, rht, what=f"extremes sr={sr} rht={rht}")
+
+
+def test_mx_quantize_config4_full():
+    """16384 x 8192, SR with the rotation, both layouts in one call: every output."""
+    print("case: MXFP4 c4 sr+rht both layouts, every output", flush=True)
+    check_mx(workloads.c4(), ("row", "col"), True, True, seed=1, rht_seed=1, what="c4")
+
+
+def _exact(t, rows):
+    codes = oracle.unpack_codes(t.codes[rows].cpu().numpy())
+    scale = np.exp2(t.scales[rows].cpu().numpy().astype(np.float64) - 127)
+    return E2M1[codes] * np.repeat(scale, 32, axis=1)
+
+
+def check_gemm(c, a, b, rows, cols, f):
+    A, B = _exact(a, rows), _exact(b, cols)
+    ref = (A @ B.T) * f
+    mag = (np.abs(A) @ np.abs(B).T) * f
+    K = A.shape[1]
+    got = c[np.ix_(rows, cols)].cpu().numpy().astype(np.float64)
+    bound = 2 * K * U * mag + 4 * U * np.abs(ref) + 1e-300
+    worst = float(np.max(np.abs(got - ref) / bound))
+    assert worst <= 1.0, worst
+    return got, ref
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 256, 384), (96, 160, 256),
+                                   (288, 544, 1024)])
+def test_mx_gemm_small(M, N, K):
+    print(f"case: MXFP4 gemm M={M} N={N} K={K}", flush=True)
+    x = workloads.normal((M, K), seed=M + K).to(DEV)
+    w = workloads.normal((N, K), seed=N + K + 1, scale=0.02).to(DEV)
+    a = nv.mxfp4_quantize(x, sr=True, seed=3, rht=True, rht_seed=9).row
+    b = nv.mxfp4_quantize(w, rht=True, rht_seed=9).row
+    c = nv.mxfp4_gemm(a, b, rotated_pair=True)
+    torch.cuda.synchronize()
+    got, _ = check_gemm(c, a, b, np.arange(M), np.arange(N), 2.0 ** -7)
+    xw = (x.float() @ w.float().T).cpu().numpy()
+    assert np.linalg.norm(got - xw) / np.linalg.norm(xw) < 0.25
+
+
+def test_mx_gemm_wide_scales():
+    """Operands whose 32-blocks span 2^-60..2^60: the matrix core applies every block's own
+    power-of-two scale (no tensor scale to hide a wrong one)."""
+    print("case: MXFP4 gemm with wide block scales", flush=True)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((128, 512)) * np.exp2(rng.integers(-30, 30, (128, 16))).repeat(32, 1)
+    w = rng.standard_normal((96, 512)) * np.exp2(rng.integers(-30, 30, (96, 16))).repeat(32, 1)
+    a = nv.mxfp4_quantize(workloads.to_bf16(x).to(DEV)).row
+    b = nv.mxfp4_quantize(workloads.to_bf16(w).to(DEV)).row
+    c = nv.mxfp4_gemm(a, b)
+    torch.cuda.synchronize()
+    check_gemm(c, a, b, np.arange(128), np.arange(96), 1.0)
+
+
+def test_mx_gemm_config4_sampled():
+    """M = 16384, N = 8192, K = 8192 (the benchmark's GEMM shape): SR+RHT activations against
+    an RTN+RHT weight, sampled rows and columns of C."""
+    print("case: MXFP4 gemm c4 M=16384 N=8192 K=8192 sampled", flush=True)
+    a = nv.mxfp4_quantize(workloads.c4().to(DEV), sr=True, seed=1, rht=True, rht_seed=1).row
+    b = nv.mxfp4_quantize(workloads.c4w().to(DEV), rht=True, rht_seed=1).row
+    c = nv.mxfp4_gemm(a, b, rotated_pair=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 16383], rng.choice(16384, 40, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 40, replace=False)]))
+    check_gemm(c, a, b, rows, cols, 2.0 ** -7)
+
+
+def test_mx_errors():
+    print("case: MXFP4 argument errors", flush=True)
+    x = workloads.normal((256, 200), seed=1).to(DEV)
+    with pytest.raises(nv.NVFP4Error) as e:
+        nv.mxfp4_quantize(x, rht=True)                     # 200 % 128 != 0
+    assert e.value.status == nv.ERR_SHAPE
+    q = nv.mxfp4_quantize(workloads.normal((64, 256), seed=2).to(DEV)).row
+    r = nv.MXFP4(q.codes[:, :64].contiguous(), q.scales[:, :4].contiguous())  # K = 128
+    with pytest.raises(nv.NVFP4Error):
+        nv.mxfp4_gemm(q, nv.MXFP4(q.codes[:48].contiguous(), q.scales[:48].contiguous()))
+    c = nv.mxfp4_gemm(r, r)
+    torch.cuda.synchronize()
+    assert c.shape == (64, 64)

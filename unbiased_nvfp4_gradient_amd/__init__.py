@@ -34,7 +34,7 @@ EXPORTED = ("nvfp4_workspace_bytes", "nvfp4_strerror", "eden_quantize",
             "eden_quantize_noalloc", "sr_quantize",
             "rtn_quantize", "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize",
             "nvfp4_gemm_check", "nvfp4_strip_workspace_bytes", "nvfp4_quantize_strips",
-            "dequantize_strips", "nvfp4_gemm_check_strips")
+            "dequantize_strips", "nvfp4_gemm_check_strips", "mxfp4_quantize", "mxfp4_gemm")
 
 MODE_RTN, MODE_SR, MODE_EDEN, MODE_FP46 = 0, 1, 2, 3
 MODES = {"rtn": MODE_RTN, "sr": MODE_SR, "eden": MODE_EDEN, "fp46": MODE_FP46}
@@ -43,6 +43,20 @@ MODES = {"rtn": MODE_RTN, "sr": MODE_SR, "eden": MODE_EDEN, "fp46": MODE_FP46}
 class _CTensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("tensor_scale", ctypes.c_void_p)]
+
+
+class _CMx(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class MXFP4(NamedTuple):
+    codes: torch.Tensor         # uint8 [vecs, n/2]
+    scales: torch.Tensor        # uint8 [vecs, n/32], E8M0 bits: 2^(byte - 127)
+
+
+class MXQuantized(NamedTuple):
+    row: Optional[MXFP4]
+    col: Optional[MXFP4]
 
 
 class NVFP4(NamedTuple):
@@ -96,9 +110,13 @@ def lib() -> ctypes.CDLL:
                                         P]
     h.dequantize_strips.argtypes = [TP, i64, i64, i32, i32, i32, u64, P, P]
     h.nvfp4_gemm_check_strips.argtypes = [TP, TP, i64, i64, i64, i32, P, P]
+    MP = ctypes.POINTER(_CMx)
+    h.mxfp4_quantize.argtypes = [P, i64, i64, i32, i32, u64, i32, u64, MP, MP, P]
+    h.mxfp4_gemm.argtypes = [MP, MP, i64, i64, i64, i32, P, P]
     for name in ("eden_quantize", "eden_quantize_noalloc", "sr_quantize", "rtn_quantize", "fp46_quantize", "dequantize",
                  "nvfp4_amax", "nvfp4_quantize_amax", "nvfp4_gemm_check",
-                 "nvfp4_quantize_strips", "dequantize_strips", "nvfp4_gemm_check_strips"):
+                 "nvfp4_quantize_strips", "dequantize_strips", "nvfp4_gemm_check_strips",
+                 "mxfp4_quantize", "mxfp4_gemm"):
         getattr(h, name).restype = i32
     _lib_handle = h
     return h
@@ -455,7 +473,78 @@ def nvfp4_gemm_check(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
     return out
 
 
-__all__ = ["NVFP4", "Quantized", "NVFP4Error", "eden_quantize", "eden_quantize_noalloc",
+def empty_mx_layout(vecs: int, n: int, device) -> MXFP4:
+    """Caller-side allocation of one MXFP4 layout's outputs."""
+    return MXFP4(torch.empty((vecs, n // 2), dtype=torch.uint8, device=device),
+                 torch.empty((vecs, n // 32), dtype=torch.uint8, device=device))
+
+
+def _cmx(t: Optional[MXFP4]):
+    if t is None:
+        return None
+    return ctypes.byref(_CMx(t.codes.data_ptr(), t.scales.data_ptr()))
+
+
+def _check_mx_layout(t, name: str, vecs: int, n: int, device) -> MXFP4:
+    if not isinstance(t, MXFP4):
+        if not (isinstance(t, tuple) and len(t) == 2):
+            raise ValueError(f"{name} must be an MXFP4 (codes, scales) pair")
+        t = MXFP4(*t)
+    _check_buffer(t.codes, f"{name}.codes", torch.uint8, (vecs, n // 2), device)
+    _check_buffer(t.scales, f"{name}.scales", torch.uint8, (vecs, n // 32), device)
+    return t
+
+
+def mxfp4_quantize(x: torch.Tensor, sr: bool = False, seed: int = 0, rht: bool = False,
+                   rht_seed: int = 0, layouts=("row",), out: Optional[MXQuantized] = None,
+                   stream=None) -> MXQuantized:
+    """MXFP4 quantization (E2M1 codes, one E8M0 scale per 32), RTN or SR, optionally after the
+    random-sign Hadamard rotation; the operand format of the native FP4 matrix cores."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
+    rows, cols = x.shape
+    want_row, want_col = "row" in layouts, "col" in layouts
+    if out is None:
+        with _on(stream, x.device):
+            out = MXQuantized(empty_mx_layout(rows, cols, x.device) if want_row else None,
+                              empty_mx_layout(cols, rows, x.device) if want_col else None)
+    else:
+        for name, want, t in (("row", want_row, out.row), ("col", want_col, out.col)):
+            if want and t is None:
+                raise ValueError(f"`layouts` asks for the {name} layout but `out` has none")
+        out = MXQuantized(
+            _check_mx_layout(out.row, "out.row", rows, cols, x.device) if want_row else None,
+            _check_mx_layout(out.col, "out.col", cols, rows, x.device) if want_col else None)
+    _check("mxfp4_quantize", lib().mxfp4_quantize(
+        x.data_ptr(), rows, cols, 32, int(bool(sr)), seed, int(bool(rht)), rht_seed,
+        _cmx(out.row), _cmx(out.col), _stream_ptr(stream, x.device)))
+    return out
+
+
+def mxfp4_gemm(a: MXFP4, b: MXFP4, rotated_pair: bool = False,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """C = A B^T of two MXFP4 row-layout operands ([M, K] and [N, K]) on the FP4 matrix
+    cores, FP32 [M, N]."""
+    if not isinstance(a.codes, torch.Tensor) or not isinstance(b.codes, torch.Tensor) or \
+            a.codes.dim() != 2 or b.codes.dim() != 2:
+        raise ValueError("operands must hold 2-D uint8 code tensors")
+    M, K = a.codes.shape[0], a.codes.shape[1] * 2
+    N = b.codes.shape[0]
+    dev = a.codes.device
+    a = _check_mx_layout(a, "a", M, K, dev)
+    b = _check_mx_layout(b, "b", N, K, dev)
+    if out is None:
+        with _on(stream, dev):
+            out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    else:
+        _check_buffer(out, "out", torch.float32, (M, N), dev)
+    _check("mxfp4_gemm", lib().mxfp4_gemm(_cmx(a), _cmx(b), M, N, K, int(bool(rotated_pair)),
+                                          out.data_ptr(), _stream_ptr(stream, dev)))
+    return out
+
+
+__all__ = ["MXFP4", "MXQuantized", "mxfp4_quantize", "mxfp4_gemm", "empty_mx_layout",
+           "NVFP4", "Quantized", "NVFP4Error", "eden_quantize", "eden_quantize_noalloc",
            "sr_quantize", "rtn_quantize",
            "fp46_quantize", "nvfp4_amax", "nvfp4_quantize_amax", "dequantize", "nvfp4_gemm_check",
            "nvfp4_quantize_strips", "dequantize_strips", "nvfp4_gemm_check_strips",

@@ -128,4 +128,17 @@ __device__ __forceinline__ float clamped_rcp(float d)
     return r > FLT_BIG ? FLT_BIG : r;
 }
 
+// Exponent of the MXFP4 block scale: the smallest e with 6 * 2^e >= m (m the block's max |r|,
+// finite, >= 0), clamped to [-127, 127]; -127 for m = 0.
+// frexp gives m = f * 2^E with f in [0.5, 1) (subnormal m too); 6 * 2^(E-3) = 0.75 * 2^E covers
+// m exactly when f <= 0.75, else 6 * 2^(E-2) = 1.5 * 2^E is the smallest that does.
+__device__ __forceinline__ int mx_scale_exp(float m)
+{
+    if (!(m > 0.0f)) return -127;
+    const int E = __builtin_amdgcn_frexp_expf(m);
+    const float f = __builtin_amdgcn_frexp_mantf(m);
+    const int e = E - 3 + (f > 0.75f ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 }  // namespace nvfp4k

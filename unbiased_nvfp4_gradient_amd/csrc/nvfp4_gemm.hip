@@ -246,3 +246,168 @@ extern "C" hipError_t nvfp4k_gemm(int local, const uint8_t *a_codes, const uint8
     k_gemm<<<grid, 512, 0, st>>>(A, B, M, N, K, rotated_pair ? 0.0078125f : 1.0f, c);
     return hipGetLastError();
 }
+
+// ------------------------------------------------------------------------------ MXFP4 GEMM
+// The native FP4 consumer: C = f * A * B^T of two MXFP4 operands (E2M1 codes, one E8M0 scale
+// per 32 elements along K) on gfx950's scaled matrix instruction
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in FP4: the matrix core multiplies the
+// codes' grid values exactly, applies each lane's power-of-two block scales, and accumulates
+// in FP32.  f = 2^-7 when both operands carry the same random-sign Hadamard rotation along K.
+//
+// Lane layout of the instruction (32 x 32 x 64): lane l supplies row l%32 of A (column l%32 of
+// B) and its elements k = 32*(l/32) .. +31, 16 bytes of packed codes (low nibble first, as
+// the quantizers store them), and the E8M0 scale of exactly that 32-block; accumulator r of
+// lane l is C[8*(r/4) + 4*(l/32) + r%4][l%32], as for the other 32 x 32 instructions.
+//
+// Tiling: a C tile of 256 x 256 per workgroup of 8 waves, each wave a 64 x 128 sub-tile (2 x 4
+// instructions, 128 FP32 accumulators per lane); K in steps of 128 (two instructions deep).
+// Each step's codes, 64 bytes per row of A and of B, go straight from memory into one of two
+// LDS stages (global_load_lds_dwordx4, 16 bytes per lane) while the other stage feeds the
+// matrix cores, together with the rows' 4 scale bytes per step; chunk c of row i sits in slot
+// 4 i + (c ^ ((i >> 1) & 3)), so the eight rows a 16-byte LDS read serves at a time hit eight
+// distinct 16-byte bank groups.  The only wait on memory is at the top of each step.
+namespace nvfp4g {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int MX_BK = 128;                    // K elements per step
+constexpr int MX_ROW = MX_BK / 2;             // code bytes per row and step
+constexpr int MX_CODES = (BM + BN) * MX_ROW;  // code bytes of one A + B stage (32 KiB)
+constexpr int MX_STAGE = MX_CODES + 4 * (BM + BN);   // + 4 scale bytes per row and step
+
+struct MxOperand {
+    const uint8_t *codes;    // [rows][K/2]
+    const uint8_t *scales;   // [rows][K/32]
+};
+
+#define MX_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+__device__ __forceinline__ int mx_slot(int i, int c) { return 4 * i + (c ^ ((i >> 1) & 3)); }
+
+// Start loading step kt of the 256 rows from row0 into one operand's part of a stage: the
+// codes, 1024 slots of 16 bytes (lane L of wave w fills slot 512 k + 64 w + L in round k),
+// and the 256 rows' 4 scale bytes (waves 4 w0 .. 4 w0 + 3, 4 bytes per lane, row = 64 w + L).
+// Rows past the operand re-read its last row (they feed only entries of C not stored).
+__device__ __forceinline__ void mx_stage(const MxOperand &op, int64_t rows, int64_t K,
+                                         int64_t row0, int64_t kt, uint8_t *codes_lds,
+                                         uint8_t *scales_lds, int w0)
+{
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int s = 512 * k + 64 * w + lane;
+        const int i = s >> 2, c = (s & 3) ^ ((i >> 1) & 3);
+        const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
+        const uint8_t *src = op.codes + row * (K >> 1) + kt * MX_ROW + 16 * c;
+        __builtin_amdgcn_global_load_lds(src, MX_LDS(codes_lds + 16 * (512 * k + 64 * w)), 16, 0,
+                                         0);
+    }
+    const int ws = w - w0;
+    if (ws >= 0 && ws < 4) {
+        const int i = 64 * ws + lane;
+        const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
+        __builtin_amdgcn_global_load_lds(op.scales + row * (K >> 5) + 4 * kt,
+                                         MX_LDS(scales_lds + 4 * 64 * ws), 4, 0, 0);
+    }
+}
+
+__device__ __forceinline__ v8i mx_frag(const uint8_t *lds, int i, int c)
+{
+    const v4i v = *reinterpret_cast<const v4i *>(lds + 16 * mx_slot(i, c));
+    return v8i{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+}
+
+// Wait for this wave's loads into LDS, then for every wave: the stage just loaded is complete.
+__device__ __forceinline__ void mx_barrier()
+{
+    __asm__ volatile("" ::: "memory");
+    // s_waitcnt fields (gfx9): vmcnt bits 3:0 and 15:14, expcnt 6:4 (7 = no wait), lgkmcnt
+    // 11:8: vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// C[M][N] = f * sum_k A[m][k] * B[n][k].  Grid (ceil(N/256), ceil(M/256)), 512 threads.
+// M and N multiples of 32, K a multiple of 128.
+__global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, int64_t M,
+                                                    int64_t N, int64_t K, float f,
+                                                    float *__restrict__ C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * MX_STAGE];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, half = lane >> 5;
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+    const int wm = (w >> 1) * 64, wn = (w & 1) * 128;
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    const int64_t nk = K / MX_BK;
+    auto stage = [&](int64_t kt) {
+        uint8_t *st = lds + (kt & 1) * MX_STAGE;
+        mx_stage(A, M, K, m0, kt, st, st + MX_CODES, 0);
+        mx_stage(B, N, K, n0, kt, st + BM * MX_ROW, st + MX_CODES + 4 * BM, 4);
+    };
+    if (nk > 0) stage(0);
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        mx_barrier();                    // stage kt & 1 landed; the other one is free
+        if (kt + 1 < nk) stage(kt + 1);
+        const uint8_t *As = lds + (kt & 1) * MX_STAGE, *Bs = As + BM * MX_ROW;
+        const uint32_t *Ss = reinterpret_cast<const uint32_t *>(As + MX_CODES);
+        // each lane's scale bytes, shifted so that byte 2q is its 32-block's in sub-step q
+        uint32_t sa[2], sb[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sa[i] = Ss[wm + 32 * i + (lane & 31)] >> (8 * half);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sb[j] = Ss[BM + wn + 32 * j + (lane & 31)] >> (8 * half);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            v8i a[2], b[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = mx_frag(As, wm + 32 * i + (lane & 31), 2 * q + half);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = mx_frag(Bs, wn + 32 * j + (lane & 31), 2 * q + half);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (q == 0)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a[i], b[j], acc[i][j], 4, 4, 0, (int)sa[i], 0, (int)sb[j]);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a[i], b[j], acc[i][j], 4, 4, 2, (int)sa[i], 2, (int)sb[j]);
+                }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + wn + 32 * j + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < M && n < N) C[m * N + n] = acc[i][j][r] * f;
+            }
+        }
+    }
+}
+
+}  // namespace nvfp4g
+
+extern "C" hipError_t nvfp4k_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales,
+                                     const uint8_t *b_codes, const uint8_t *b_scales,
+                                     int64_t M, int64_t N, int64_t K, int rotated_pair,
+                                     float *c, hipStream_t st)
+{
+    using namespace nvfp4g;
+    if (M == 0 || N == 0) return hipSuccess;
+    const MxOperand A{a_codes, a_scales}, B{b_codes, b_scales};
+    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+    k_gemm_mx<<<grid, 512, 0, st>>>(A, B, M, N, K, rotated_pair ? 0.0078125f : 1.0f, c);
+    return hipGetLastError();
+}

@@ -60,7 +60,10 @@
 
 namespace nvfp4k {
 
-enum Mode { MODE_RTN = 0, MODE_SR = 1, MODE_EDEN = 2, MODE_FP46 = 3 };
+enum Mode { MODE_RTN = 0, MODE_SR = 1, MODE_EDEN = 2, MODE_FP46 = 3,
+            MODE_MX_RTN = 4, MODE_MX_SR = 5 };   // the last two: the MXFP4 block contract
+
+constexpr bool is_mx(int mode) { return mode == MODE_MX_RTN || mode == MODE_MX_SR; }
 enum Layouts { LAY_ROW = 1, LAY_COL = 2, LAY_BOTH = 3 };
 
 constexpr uint32_t STREAM_SIGN = 1u, STREAM_SCALE_SR = 2u, STREAM_ELEM_SR = 3u;
@@ -929,6 +932,81 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
     }
 }
 
+// ------------------------------------------------------------------------------ MXFP4
+// The MXFP4 block contract, the operand format of gfx950's scaled matrix instructions: blocks
+// of 32 with one power-of-two (E8M0) scale 2^e, e the smallest integer with 6 * 2^e >= max |r|
+// over the block (clamped to [-127, 127]; an all-zero block gets -127), elements
+// y = r * 2^-e rounded onto the E2M1 grid by RTN or SR.
+//
+// This lane's two 32-blocks of a group (positions 64h .. 64h + 63 of r, their 16-block maxima
+// in bmax); nbl = 16-blocks inside the vector (even).  Writes 32 code bytes and 2 scale bytes.
+template <bool SR>
+__device__ __forceinline__ void quantize_half_mx(const float r[HALF], const float bmax[4],
+                                                 int h, int nbl, uint64_t seed, uint32_t axis,
+                                                 int64_t vec, int64_t n, int64_t gi,
+                                                 uint8_t *__restrict__ codes,
+                                                 uint8_t *__restrict__ scales, bool aligned)
+{
+    uint32_t cw[8];
+    uint32_t sc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        sc[b] = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cw[4 * b + k] = 0u;
+        if (2 * b < nbl) {
+            const float *rb = r + 32 * b;
+            const int e = mx_scale_exp(fmaxf(bmax[2 * b], bmax[2 * b + 1]));
+            sc[b] = (uint32_t)(e + 127);
+            const float p = __builtin_amdgcn_ldexpf(1.0f, -e);     // exact, normal
+            if constexpr (!SR) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float *q = rb + 8 * k;
+                    const float y0 = scaled(q[0], p);
+                    uint32_t w = __float_as_uint(y0);
+                    w = CVT_FP4(w, y0, scaled(q[1], p), 0);
+                    w = CVT_FP4(w, scaled(q[2], p), scaled(q[3], p), 1);
+                    w = CVT_FP4(w, scaled(q[4], p), scaled(q[5], p), 2);
+                    w = CVT_FP4(w, scaled(q[6], p), scaled(q[7], p), 3);
+                    cw[4 * b + k] = w;
+                }
+            } else {
+                // element index of the block's first element, a multiple of 4
+                const int64_t e0 = vec * n + gi * TILE + HALF * h + 32 * b;
+#pragma unroll
+                for (int qd = 0; qd < 8; ++qd) {
+                    const uint64_t j = ((uint64_t)e0 >> 2) + qd;
+                    const Word4 w = philox(seed, (uint32_t)j, (uint32_t)(j >> 32),
+                                           STREAM_ELEM_SR, axis);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int p4 = 4 * qd + k;
+                        const float y = scaled(rb[p4], p);
+                        const uint32_t mag = e2m1_sr_mag(fminf(fabsf(y), 6.0f), w.w[k]);
+                        const uint32_t sgn = __float_as_uint(y) >> 31;   // r < 0
+                        cw[4 * b + (p4 >> 3)] |= (mag | (sgn << 3)) << (4 * (p4 & 7));
+                    }
+                }
+            }
+        }
+    }
+    if (nbl == 4 && aligned) {
+        uint4 *cp = reinterpret_cast<uint4 *>(codes + 32 * h);
+        cp[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        cp[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+        *reinterpret_cast<uint16_t *>(scales + 2 * h) = (uint16_t)(sc[0] | (sc[1] << 8));
+    } else {
+        uint2 *cp = reinterpret_cast<uint2 *>(codes + 32 * h);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (b < nbl) cp[b] = make_uint2(cw[2 * b], cw[2 * b + 1]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            if (2 * b < nbl) scales[2 * h + b] = (uint8_t)sc[b];
+    }
+}
+
 // Quantize this lane's half group of tile (r0, c0); tb holds the tile's scale table and
 // its (g, rcp(6g), rcp(4g)).
 //
@@ -962,10 +1040,17 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
     const int64_t left = n - start;
     const int nb = left >= TILE ? 8 : (int)(left >> 4);
     const int nbl = nb - 4 * ro.h < 0 ? 0 : (nb - 4 * ro.h > 4 ? 4 : nb - 4 * ro.h);
-    const float4 gs = tb.e[TAB_G];
-    quantize_half<MODE>(r, bm, ro.h, nbl, gs.x, tb, gs.y, gs.z, a.seed, (uint32_t)ro.lay, vec, n,
-                        start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
-                        o.scales + vec * (n >> 4) + (start >> 4));
+    if constexpr (is_mx(MODE)) {
+        quantize_half_mx<MODE == MODE_MX_SR>(r, bm, ro.h, nbl, a.seed, (uint32_t)ro.lay, vec, n,
+                                             start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
+                                             o.scales + vec * (n >> 5) + (start >> 5),
+                                             (n & (TILE - 1)) == 0);
+    } else {
+        const float4 gs = tb.e[TAB_G];
+        quantize_half<MODE>(r, bm, ro.h, nbl, gs.x, tb, gs.y, gs.z, a.seed, (uint32_t)ro.lay, vec,
+                            n, start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
+                            o.scales + vec * (n >> 4) + (start >> 4));
+    }
 }
 
 // Workgroup barrier between tiles of pass 2 that does not wait for the tile's code and scale
@@ -1008,7 +1093,7 @@ __device__ __forceinline__ void tile_barrier_after(bool three_stores)
 constexpr int quant_waves_per_simd(int mode, bool rot, int lay)
 {
     if (lay != LAY_BOTH) return 2;
-    if (mode == MODE_SR && rot) return 3;
+    if ((mode == MODE_SR || mode == MODE_MX_SR) && rot) return 3;
     return 4;
 }
 
@@ -1083,7 +1168,7 @@ k_quant(QuantArgs a)
         stage_tile<WAVES>(tile0, a.x, a.R, a.C, r0, c0, dl);
         if constexpr (LOCAL) stage_table(tb0, a, ro, r0, c0);
     }
-    if constexpr (!LOCAL) {
+    if constexpr (!LOCAL && !is_mx(MODE)) {
         const float D = (MODE == MODE_FP46) ? 1792.0f : 2688.0f;
         const float g = __uint_as_float(layout_amax_bits(a, ro.lay)) / D;
         build_scale_table(tb0, g, t & 255);
@@ -1448,6 +1533,24 @@ extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x
         return hipGetLastError();
     }
     quant_mode<false>(a, mode, rht, layouts, st);
+    return hipGetLastError();
+}
+
+// MXFP4 quantization, one pass (the E8M0 scales need no tensor-wide maximum).
+extern "C" hipError_t nvfp4k_quant_mx(int sr, int rht, int layouts, const void *x, int64_t R,
+                                      int64_t C, uint8_t *codes0, uint8_t *scales0,
+                                      uint8_t *codes1, uint8_t *scales1, uint64_t seed,
+                                      uint64_t rht_seed, hipStream_t st)
+{
+    using namespace nvfp4k;
+    QuantArgs a = make_args(x, R, C, nullptr, seed, rht_seed);
+    a.out[0] = {codes0, scales0, nullptr};
+    a.out[1] = {codes1, scales1, nullptr};
+    if (a.tiles == 0) return hipSuccess;
+    if (sr) rht ? quant_lay<MODE_MX_SR, true, false>(a, layouts, st)
+                : quant_lay<MODE_MX_SR, false, false>(a, layouts, st);
+    else rht ? quant_lay<MODE_MX_RTN, true, false>(a, layouts, st)
+             : quant_lay<MODE_MX_RTN, false, false>(a, layouts, st);
     return hipGetLastError();
 }
 
