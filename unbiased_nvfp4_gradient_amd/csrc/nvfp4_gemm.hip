@@ -261,11 +261,12 @@ extern "C" hipError_t nvfp4k_gemm(int local, const uint8_t *a_codes, const uint8
 //
 // Tiling: a C tile of 256 x 256 per workgroup of 8 waves, each wave a 64 x 128 sub-tile (2 x 4
 // instructions, 128 FP32 accumulators per lane); K in steps of 128 (two instructions deep).
-// Each step's codes, 64 bytes per row of A and of B, go straight from memory into one of two
-// LDS stages (global_load_lds_dwordx4, 16 bytes per lane) while the other stage feeds the
-// matrix cores, together with the rows' 4 scale bytes per step; chunk c of row i sits in slot
+// Each step's codes, 64 bytes per row of A and of B, go straight from memory into one of four
+// LDS stages (global_load_lds_dwordx4, 16 bytes per lane), three steps ahead of the stage that
+// feeds the matrix cores, together with the rows' 4 scale bytes per step; chunk c of row i sits in slot
 // 4 i + (c ^ ((i >> 1) & 3)), so the eight rows a 16-byte LDS read serves at a time hit eight
-// distinct 16-byte bank groups.  The only wait on memory is at the top of each step.
+// distinct 16-byte bank groups.  The only wait on memory is at the top of each step, for that
+// step's own loads.
 namespace nvfp4g {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -285,32 +286,40 @@ struct MxOperand {
 
 __device__ __forceinline__ int mx_slot(int i, int c) { return 4 * i + (c ^ ((i >> 1) & 3)); }
 
-// Start loading step kt of the 256 rows from row0 into one operand's part of a stage: the
-// codes, 1024 slots of 16 bytes (lane L of wave w fills slot 512 k + 64 w + L in round k),
-// and the 256 rows' 4 scale bytes (waves 4 w0 .. 4 w0 + 3, 4 bytes per lane, row = 64 w + L).
-// Rows past the operand re-read its last row (they feed only entries of C not stored).
-__device__ __forceinline__ void mx_stage(const MxOperand &op, int64_t rows, int64_t K,
-                                         int64_t row0, int64_t kt, uint8_t *codes_lds,
-                                         uint8_t *scales_lds, int w0)
+// Start loading step kt into a stage: the codes of A's and B's 256 rows (from m0, n0), 1024
+// slots of 16 bytes per operand (lane L of wave w fills slot 512 k + 64 w + L in round k), and
+// every row's 4 scale bytes (waves 0..3 A's rows 64 w + L, waves 4..7 B's).  No branch: the
+// scale load's operand is chosen by selects on the wave-uniform w.  Rows past an operand
+// re-read its last row (they feed only entries of C that are not stored).
+__device__ __forceinline__ void mx_stage(const MxOperand &A, const MxOperand &B, int64_t M,
+                                         int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                         int64_t kt, uint8_t *stage)
 {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int s = 512 * k + 64 * w + lane;
-        const int i = s >> 2, c = (s & 3) ^ ((i >> 1) & 3);
-        const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
-        const uint8_t *src = op.codes + row * (K >> 1) + kt * MX_ROW + 16 * c;
-        __builtin_amdgcn_global_load_lds(src, MX_LDS(codes_lds + 16 * (512 * k + 64 * w)), 16, 0,
-                                         0);
+    for (int op = 0; op < 2; ++op) {
+        const uint8_t *codes = op ? B.codes : A.codes;
+        const int64_t rows = op ? N : M, row0 = op ? n0 : m0;
+        uint8_t *dst = stage + op * BM * MX_ROW;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int s = 512 * k + 64 * w + lane;
+            const int i = s >> 2, c = (s & 3) ^ ((i >> 1) & 3);
+            const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
+            __builtin_amdgcn_global_load_lds(codes + row * (K >> 1) + kt * MX_ROW + 16 * c,
+                                             MX_LDS(dst + 16 * (512 * k + 64 * w)), 16, 0, 0);
+        }
     }
-    const int ws = w - w0;
-    if (ws >= 0 && ws < 4) {
-        const int i = 64 * ws + lane;
-        const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
-        __builtin_amdgcn_global_load_lds(op.scales + row * (K >> 5) + 4 * kt,
-                                         MX_LDS(scales_lds + 4 * 64 * ws), 4, 0, 0);
-    }
+    const bool on_b = w >= 4;
+    const uint8_t *scales = on_b ? B.scales : A.scales;
+    const int64_t rows = on_b ? N : M, row0 = on_b ? n0 : m0;
+    const int i = 64 * (w & 3) + lane;
+    const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
+    __builtin_amdgcn_global_load_lds(scales + row * (K >> 5) + 4 * kt,
+                                     MX_LDS(stage + MX_CODES + 4 * (on_b ? BM : 0) +
+                                            4 * 64 * (w & 3)),
+                                     4, 0, 0);
 }
 
 __device__ __forceinline__ v8i mx_frag(const uint8_t *lds, int i, int c)
@@ -319,25 +328,88 @@ __device__ __forceinline__ v8i mx_frag(const uint8_t *lds, int i, int c)
     return v8i{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
 }
 
-// Wait for this wave's loads into LDS, then for every wave: the stage just loaded is complete.
-__device__ __forceinline__ void mx_barrier()
+// Stages in flight: while the matrix cores work on one stage, the loads of the next
+// MX_NSTAGE - 1 are outstanding.  Each wave issues exactly MX_LOADS loads per stage (two
+// 16-byte code loads per operand and one scale load), one stage per step, and the vector
+// memory counter retires in issue order, so waiting until at most MX_LOADS loads are
+// outstanding waits for every stage but the one issued last.
+constexpr int MX_NSTAGE = 4;
+constexpr int MX_LOADS = 5;
+
+// Wait for this wave's loads of every stage but the newest, then for every wave: the stage
+// after the current one is complete in LDS.  `all` waits for every load (the prologue).
+__device__ __forceinline__ void mx_barrier(bool all)
 {
-    __asm__ volatile("" ::: "memory");
     // s_waitcnt fields (gfx9): vmcnt bits 3:0 and 15:14, expcnt 6:4 (7 = no wait), lgkmcnt
-    // 11:8: vmcnt(0) lgkmcnt(0)
-    __builtin_amdgcn_s_waitcnt(0x0070);
+    // 11:8 (0: this wave's LDS reads are done too)
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("" ::: "memory");
+    if (all) __builtin_amdgcn_s_waitcnt(0x0070);
+    else __builtin_amdgcn_s_waitcnt(0x0070 | MX_LOADS);
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// One sub-step's operands of a wave: 2 fragments of A, 4 of B (sub-step q of a stage).
+struct MxFrags {
+    v8i a[2], b[4];
+};
+
+__device__ __forceinline__ MxFrags mx_read(const uint8_t *stage, int wm, int wn, int lane, int q)
+{
+    const int half = lane >> 5;
+    MxFrags f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = mx_frag(stage, wm + 32 * i + (lane & 31), 2 * q + half);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        f.b[j] = mx_frag(stage + BM * MX_ROW, wn + 32 * j + (lane & 31), 2 * q + half);
+    return f;
+}
+
+// Each lane's scale bytes of a stage, shifted so that byte 2q is its 32-block's in sub-step q.
+struct MxScales {
+    uint32_t a[2], b[4];
+};
+
+__device__ __forceinline__ MxScales mx_read_scales(const uint8_t *stage, int wm, int wn, int lane)
+{
+    const uint32_t *s = reinterpret_cast<const uint32_t *>(stage + MX_CODES);
+    const int sh = 8 * (lane >> 5);
+    MxScales r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.a[i] = s[wm + 32 * i + (lane & 31)] >> sh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.b[j] = s[BM + wn + 32 * j + (lane & 31)] >> sh;
+    return r;
+}
+
+template <int Q>
+__device__ __forceinline__ void mx_mfma(f32x16 (&acc)[2][4], const MxFrags &f, const MxScales &s)
+{
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                f.a[i], f.b[j], acc[i][j], 4, 4, 2 * Q, (int)s.a[i], 2 * Q, (int)s.b[j]);
 }
 
 // C[M][N] = f * sum_k A[m][k] * B[n][k].  Grid (ceil(N/256), ceil(M/256)), 512 threads.
 // M and N multiples of 32, K a multiple of 128.
+//
+// The fragment reads run one sub-step ahead of the matrix instructions: a step reads its
+// second sub-step's fragments while the first sub-step's instructions run, then (after the
+// barrier that makes the next stage visible) the next step's first fragments and scales while
+// its second sub-step's instructions run.  Every read of a stage is complete before the
+// barrier of the step after it, which is where the loads of a later stage may overwrite it.
 __global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, int64_t M,
                                                     int64_t N, int64_t K, float f,
                                                     float *__restrict__ C)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * MX_STAGE];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, half = lane >> 5;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[MX_NSTAGE * MX_STAGE];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int wm = (w >> 1) * 64, wn = (w & 1) * 128;
     f32x16 acc[2][4];
@@ -346,41 +418,31 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, in
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     const int64_t nk = K / MX_BK;
-    auto stage = [&](int64_t kt) {
-        uint8_t *st = lds + (kt & 1) * MX_STAGE;
-        mx_stage(A, M, K, m0, kt, st, st + MX_CODES, 0);
-        mx_stage(B, N, K, n0, kt, st + BM * MX_ROW, st + MX_CODES + 4 * BM, 4);
+    // stage s goes to buffer s % MX_NSTAGE; past the last step the loads repeat the last
+    // step's data into buffers nobody reads, so every step issues the same loads
+    auto stage = [&](int64_t s) {
+        mx_stage(A, B, M, N, K, m0, n0, s < nk ? s : nk - 1, lds + (s % MX_NSTAGE) * MX_STAGE);
     };
-    if (nk > 0) stage(0);
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        mx_barrier();                    // stage kt & 1 landed; the other one is free
-        if (kt + 1 < nk) stage(kt + 1);
-        const uint8_t *As = lds + (kt & 1) * MX_STAGE, *Bs = As + BM * MX_ROW;
-        const uint32_t *Ss = reinterpret_cast<const uint32_t *>(As + MX_CODES);
-        // each lane's scale bytes, shifted so that byte 2q is its 32-block's in sub-step q
-        uint32_t sa[2], sb[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) sa[i] = Ss[wm + 32 * i + (lane & 31)] >> (8 * half);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sb[j] = Ss[BM + wn + 32 * j + (lane & 31)] >> (8 * half);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            v8i a[2], b[4];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = mx_frag(As, wm + 32 * i + (lane & 31), 2 * q + half);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = mx_frag(Bs, wn + 32 * j + (lane & 31), 2 * q + half);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (q == 0)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            a[i], b[j], acc[i][j], 4, 4, 0, (int)sa[i], 0, (int)sb[j]);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            a[i], b[j], acc[i][j], 4, 4, 2, (int)sa[i], 2, (int)sb[j]);
-                }
+    if (nk > 0) {
+        stage(0);
+        stage(1);
+        stage(2);
+        mx_barrier(true);
+        MxFrags f0 = mx_read(lds, wm, wn, lane, 0);
+        MxScales sc = mx_read_scales(lds, wm, wn, lane);
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const uint8_t *cur = lds + (kt % MX_NSTAGE) * MX_STAGE;
+            const MxFrags f1 = mx_read(cur, wm, wn, lane, 1);
+            mx_mfma<0>(acc, f0, sc);
+            const MxScales sc1 = sc;
+            // stage kt + 1 landed (its loads were issued before the newest, kt + 2's); the
+            // buffer of stage kt - 1 was last read before this barrier
+            mx_barrier(false);
+            stage(kt + MX_NSTAGE - 1);
+            const uint8_t *nxt = lds + ((kt + 1) % MX_NSTAGE) * MX_STAGE;
+            f0 = mx_read(nxt, wm, wn, lane, 0);
+            sc = mx_read_scales(nxt, wm, wn, lane);
+            mx_mfma<1>(acc, f1, sc1);
         }
     }
 #pragma unroll
