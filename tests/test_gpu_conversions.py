@@ -10,7 +10,8 @@ unbiased_nvfp4_gradient_amd/csrc/nvfp4_device.h, the code the kernels include):
 * E2M1 decode (v_cvt_scalef32_pk_f32_fp4): all 256 code bytes at all four byte positions,
   bit for bit (so -0 for code 8);
 * E4M3 values of the 128 codes;
-* scale SR, element SR and Philox4x32-10 on sampled inputs;
+* element SR on every binary32 in [0, 6] with the draw at its rounding threshold, and on
+  sampled inputs; scale SR and Philox4x32-10 on sampled inputs;
 * the MXFP4 block-scale exponent over every non-negative finite binary32.
 
 These roundings are the whole of the contract's element and scale decisions (Telegram digest
@@ -162,6 +163,35 @@ def test_elem_sr_sampled(conv):
     out = torch.empty(n, dtype=torch.uint8, device=DEV)
     assert conv.conv_elem_sr(ad.data_ptr(), wd.data_ptr(), n, out.data_ptr(), _stream()) == 0
     assert np.array_equal(out.cpu().numpy(), oracle.elem_sr_pairs_n(a, w >> 8))
+
+
+def test_elem_sr_every_magnitude_at_its_threshold(conv):
+    """Element SR on every binary32 a in [0, 6], each with the draw just below its rounding
+    threshold (goes up) or at it (stays), alternately: the decision at the exact boundary,
+    for every input.  The threshold ceil(frac * 2^24) only picks the draw; the expected
+    magnitude comes from the oracle."""
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    end = 0x40C00000 + 1                               # bits of 6.0, inclusive
+    chunk = 1 << 26
+    rng = np.random.default_rng(5)
+    print(f"case: element SR, {end} magnitudes", flush=True)
+    out = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    for lo in range(0, end, chunk):
+        n = min(chunk, end - lo)
+        a = _bits(lo, n).view(np.float32)
+        ad = a.astype(np.float64)
+        k = np.minimum(np.searchsorted(grid, ad, side="right") - 1, 6)
+        thr = np.ceil((ad - grid[k]) / (grid[k + 1] - grid[k]) * 2.0**24).astype(np.int64)
+        u = np.clip(thr - 1 + (np.arange(n) & 1), 0, 2**24 - 1).astype(np.uint32)
+        w = (u << np.uint32(8)) | rng.integers(0, 256, n, dtype=np.uint32)
+        ad_t, wd = torch.from_numpy(a).to(DEV), torch.from_numpy(w.view(np.int32)).to(DEV)
+        assert conv.conv_elem_sr(ad_t.data_ptr(), wd.data_ptr(), n, out.data_ptr(),
+                                 _stream()) == 0
+        got = out[:n].cpu().numpy()
+        want = oracle.elem_sr_pairs_n(a, u)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (f"{bad.size} mismatches from a = {a[bad[0]]!r}, u = {u[bad[0]]}: "
+                               f"{got[bad[0]]} != {want[bad[0]]}")
 
 
 def test_philox_sampled(conv):

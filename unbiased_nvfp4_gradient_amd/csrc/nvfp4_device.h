@@ -80,23 +80,26 @@ __device__ __forceinline__ float e2m1_val(uint32_t mag)
     return __uint_as_float(b);
 }
 
-// Stochastic rounding of a magnitude 0 <= a <= 6 onto the E2M1 grid with random word w:
-// lo = the largest grid index whose value vlo <= a, frac = (a - vlo) / step to the next
-// value, and the magnitude is lo + 1 iff the top 24 bits of w, u, satisfy u < frac * 2^24.
-// From 1 up, the grid points are a's binade start and its midpoint: vlo is a with all but
-// the top mantissa bit cleared, lo = (bits(a) >> 22) - 252 (2 at 1, 6 at 4), and the step
-// is half the binade, so 1 / step = 2^(128 - biased exponent).  Below 1 the points are 0,
-// 0.5, 1 (step 0.5).  a = 6 is index 7.  Every operation here is exact.
+// Stochastic rounding of a magnitude 0 <= a <= 6 onto the E2M1 grid with random word w: with
+// lo the largest grid index whose value vlo <= a and frac = (a - vlo) / (step to the next
+// value), the magnitude is lo + 1 iff the top 24 bits of w, u, satisfy u < frac * 2^24.
+// Both forms below count the grid steps a crosses after adding the draw's complement, in
+// integers, so no compare and no select is spent on lo or frac:
+//  - below 2 the grid is uniform (step 1/2): with F = a * 2^25 (exact), lo = floor(F / 2^24)
+//    and frac * 2^24 = F mod 2^24, and u < frac * 2^24 iff u < ceil(F) - lo * 2^24 (u is an
+//    integer), so lo + up = (ceil(F) + 2^24 - 1 - u) >> 24;
+//  - from 1 up the grid points are a's binade start and midpoint (step half the binade): with
+//    m the low 22 bits of a's encoding, frac * 2^24 = 4 m and lo = (bits(a) >> 22) - 252 (2 at
+//    1, 6 at 4, 7 at 6), and u < 4 m iff (w >> 10) < m, so lo + up =
+//    (bits(a) + 2^22 - 1 - (w >> 10) - 252 * 2^22) >> 22 (a = 6 has m = 0 and stays at 7).
+// Every operation is exact; a < 2 takes the first form, a >= 2 the second.
 __device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t w)
 {
     const uint32_t t = __float_as_uint(a);
-    const bool big = a >= 1.0f, half = a >= 0.5f;
-    const uint32_t lo = big ? (t >> 22) - 252u : (uint32_t)half;
-    const float vlo = big ? __uint_as_float(t & 0xFFC00000u) : (half ? 0.5f : 0.0f);
-    const float inv = big ? __uint_as_float(0x7F800000u - (t & 0x7F800000u)) : 2.0f;
-    const float frac = (a - vlo) * inv;
-    const uint32_t up = (float)(w >> 8) < frac * 16777216.0f;
-    return a >= 6.0f ? 7u : lo + up;
+    const uint32_t big = (t + (0x3FFFFFu - (252u << 22)) - (w >> 10)) >> 22;
+    const uint32_t small =
+        ((uint32_t)__builtin_ceilf(a * 33554432.0f) + 0xFFFFFFu - (w >> 8)) >> 24;
+    return a >= 2.0f ? big : small;
 }
 
 // Nearest-even E4M3 of t >= 0, saturating: the hardware conversion is exact below 448.

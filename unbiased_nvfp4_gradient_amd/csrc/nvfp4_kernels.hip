@@ -38,10 +38,11 @@
 // exact zero of either sign into +0, so a code's sign bit is set exactly when r < 0.
 //
 // The global amax must be known before any scale can be rounded, so a quantization is two
-// passes over X: k_amax (rotate, per-workgroup max, one atomic max per workgroup and
-// layout into the workspace) then k_quant (rotate again, quantize, pack, store).  k_quant
-// walks the tiles in the reverse order, so its first tiles are those k_amax touched last,
-// which are the likeliest to still sit in the last-level cache.
+// passes over X: k_amax (rotate, each workgroup's maxima stored in its own workspace slots,
+// or one atomic max per workgroup and layout for the split phase-1 entry point) then k_quant
+// (reduce those slots, rotate again, quantize, pack, store).  k_quant walks the tiles in the
+// reverse order, so its first tiles are those k_amax touched last, which are the likeliest
+// to still sit in the last-level cache.
 //
 // Strip-local scales (the CTA-local variant of the rit.work note on "Format-Aware Fusion for
 // Fast FP4 Pretraining": maxima inside a block of work, row and column corrections applied
