@@ -18,9 +18,10 @@ run through the split entry points (nvfp4_amax, then nvfp4_quantize_amax: the sa
 kernels), with one pair of HIP events on the launch stream bracketing each phase-2 launch;
 achieved = 419,430,408 B / that mean launch time, against MI355X's published 8 TB/s.  The
 kernel is in fact bound by VALU issue at this bandwidth, so two more views are reported
-beside it: the ALU view (the 14 operations per element and layout the method defines --
-sign flip, 7 butterfly stages, block maximum, scaling, E2M1 rounding, grid value, EDEN
-terms -- against the 157.3 TFLOP/s FP32 vector peak counted as 78.64 T lane-operations/s)
+beside it: the ALU view (the 17 operations per element and layout the method defines --
+sign flip, 7 butterfly stages, block maximum, scaling, E2M1 rounding, grid value, and the
+EDEN sums' r*r, den*V, r*q and one addition in each of the two pairwise trees -- against the
+157.3 TFLOP/s FP32 vector peak counted as 78.64 T lane-operations/s)
 and the issue view (VALU instructions per launch from the committed counters, when they were
 taken on the current kernel sources).  `traffic` is the HBM bytes per k_quant launch from the
 committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the
@@ -46,7 +47,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
 VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12     # 78.64: 157.3 TFLOP/s FP32, FMA = 1 op
-QUANT_OPS_PER_ELEM_LAYOUT = 14                   # MS-EDEN phase 2, see the docstring
+QUANT_OPS_PER_ELEM_LAYOUT = 17                   # MS-EDEN phase 2, see the docstring
 ROWS, COLS = 16384, 8192
 METRIC = "MS-EDEN NVFP4 quantize GB/s & % HBM peak, 16384×8192 bf16; MSE vs SR"
 PMC_PROFILE = os.path.join(ROOT, "profiles", "k_quant_eden_16384x8192_pmc.md")
@@ -243,7 +244,7 @@ def main():
             "algorithmic_bytes_per_launch": B,
             "launch_ms_mean": round(quant_ms, 4),
             "alu_view": {"achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2),
-                         "unit": "T lane-ops/s (14 algorithmic operations per element and "
+                         "unit": "T lane-ops/s (17 algorithmic operations per element and "
                                  "layout)",
                          "frac": round(tops / VALU_PEAK_TOPS, 4), "ops_per_launch": ops},
             "issue_view": issue_view(pmc, quant_ms),
@@ -423,18 +424,28 @@ def mx_gemm(nv, workloads, dev, stream, reps=10, warmup=3):
             "frac_of_fp4_dense_peak": round(tflops / 10100.0, 4)}
 
 
+def mx_alg_bytes(rows, cols, layouts=2):
+    """Algorithmic bytes of an MXFP4 quantization: the BF16 read once, and per layout 0.5 B of
+    codes and 1/32 B of E8M0 scales per element (no tensor scale)."""
+    n = rows * cols
+    return 2 * n + layouts * (n // 2 + n // 32)
+
+
 def modes_table(nv, x, out, stream, reps=40):
     """Throughput of every quantizer on the same 16384 x 8192 input, both layouts: one call
-    of its entry point (phase 1 + phase 2), algorithmic GB/s as in the main line, a pair of
-    events around each call.  The modes take turns call by call, so they see the same clock conditions."""
+    of its entry point (NVFP4: phase 1 + phase 2; MXFP4: its one pass), algorithmic GB/s as in
+    the main line (MXFP4 with its own output sizes), a pair of events around each call.  The
+    modes take turns call by call, so they see the same clock conditions."""
     import numpy as np
     import torch
 
     modes = (("rtn", "rtn", False), ("rtn+rht", "rtn", True), ("sr", "sr", False),
              ("sr+rht", "sr", True), ("fp46+rht", "fp46", True), ("eden", "eden", True),
-             ("eden, strip scales", "eden-strips", True))
+             ("eden, strip scales", "eden-strips", True), ("mxfp4 rtn+rht", "mx", True),
+             ("mxfp4 sr+rht", "mx-sr", True))
     dev = x.device
     rows, cols = x.shape
+    out_mx = nv.MXQuantized(nv.empty_mx_layout(rows, cols, dev), nv.empty_mx_layout(cols, rows, dev))
     out_s = nv.Quantized(nv.empty_strip_layout(rows, cols, dev),
                          nv.empty_strip_layout(cols, rows, dev))
     ws_s = torch.empty(nv.strip_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
@@ -446,6 +457,10 @@ def modes_table(nv, x, out, stream, reps=40):
             nv.nvfp4_quantize_strips("eden", x, seed=seed, rht=True, rht_seed=1,
                                      layouts=("row", "col"), out=out_s, workspace=ws_s,
                                      stream=stream)
+            return
+        if mode in ("mx", "mx-sr"):
+            nv.mxfp4_quantize(x, sr=mode == "mx-sr", seed=seed, rht=rht, rht_seed=1,
+                              layouts=("row", "col"), out=out_mx, stream=stream)
             return
         fn = {"rtn": lambda: nv.rtn_quantize(x, rht=rht, rht_seed=1, **kw),
               "sr": lambda: nv.sr_quantize(x, seed=seed, rht=rht, rht_seed=1, **kw),
@@ -466,10 +481,10 @@ def modes_table(nv, x, out, stream, reps=40):
             ev[name].append((e0, e1))
     torch.cuda.synchronize()
     table = {}
-    for name, _, _ in modes:
+    for name, mode, _ in modes:
         ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev[name]]))
-        table[name] = {"ms": round(ms, 4),
-                       "GB/s": round(alg_bytes(ROWS, COLS) / (ms * 1e-3) / 1e9, 1)}
+        nbytes = mx_alg_bytes(ROWS, COLS) if mode.startswith("mx") else alg_bytes(ROWS, COLS)
+        table[name] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
     return table
 
 

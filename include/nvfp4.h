@@ -4,8 +4,10 @@
  * The library implements the hot path of Quartet II, the MS-EDEN unbiased NVFP4 quantizer,
  * with the plain stochastic-rounding (SR) baseline, round-to-nearest (RTN), the forward-pass
  * "4/6" grid choice, a producer that emits both packed layouts in one pass, a dequantizer,
- * a GEMM check consumer, and the strip-local ("CTA-local") scaling variant of each.  Definitions follow the pages summarising "Quartet II: Accurate LLM
- * Pre-Training in NVFP4 by Improved Unbiased Gradient Estimation":
+ * a GEMM check consumer, the strip-local ("CTA-local") scaling variant of each, and a native
+ * FP4 recipe (MXFP4 producer and GEMM on the FP4 matrix cores).  Definitions follow the pages
+ * summarising "Quartet II: Accurate LLM Pre-Training in NVFP4 by Improved Unbiased Gradient
+ * Estimation":
  *   - Telegram digest quant_prune_distill post 640, section "Method": SR; EDEN (random
  *     Hadamard rotation, then multiplication by <x,x> / <Q(Rx), Rx>); stochastic rounding of
  *     the scales to FP8; the 4/6 choice between the (-6,6) and (-4,4) grids; 1x16 groups.
@@ -134,8 +136,11 @@ int sr_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int b
                 const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
                 void *stream);
 
-/* Round-to-nearest NVFP4 (no randomness): tensor scale amax / 2688, block scale and
- * elements rounded to nearest (ties to even), optional rotation as above. */
+/* Round-to-nearest NVFP4 (no randomness; denisavetisyan.com paraphrase, "NVFP4 and
+ * micro-scaling": E2M1 elements under an FP8 scale per 16 and an FP32 tensor scale; Telegram
+ * "Method": round-to-nearest is the biased baseline MS-EDEN corrects): tensor scale
+ * amax / 2688, block scale and elements rounded to nearest (ties to even), optional rotation
+ * as above. */
 int rtn_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
                  int rht, uint64_t rht_seed, const nvfp4_tensor *row_out,
                  const nvfp4_tensor *col_out, void *workspace, size_t workspace_bytes,
@@ -174,7 +179,9 @@ int nvfp4_quantize_amax(int mode, const void *x_bf16, int64_t rows, int64_t cols
                         const nvfp4_tensor *row_out, const nvfp4_tensor *col_out, void *stream);
 
 /* Decode vecs vectors of length n from `in` into out [vecs][n] FP32 (device, 16-byte
- * aligned; codes 8-byte aligned): sign * (E4M3(scale) * g) * magnitude.  With rht != 0 the rotation is undone,
+ * aligned; codes 8-byte aligned): the value the NVFP4 format assigns to a code
+ * (denisavetisyan.com paraphrase, "NVFP4 and micro-scaling": element times block scale times
+ * tensor scale), sign * (E4M3(scale) * g) * magnitude.  With rht != 0 the rotation is undone,
  * x_j = sigma_j * (H q)_j * 2^-7 (H H = 128 I), using the signs of rht_seed, so the output
  * is in the original domain; n must then be a multiple of 128 (else of 16). */
 int dequantize(const nvfp4_tensor *in, int64_t vecs, int64_t n, int group, int block,
