@@ -72,6 +72,13 @@ def test_validation_errors(L):
     assert _eden(L, wsb=8) == nv.ERR_WORKSPACE
     assert _eden(L, wsb=16384 - 1) == nv.ERR_WORKSPACE       # two floats x 2048 workgroups
     assert _eden(L, rows=1 << 32) == nv.ERR_ARG
+    # the stated limits: each dimension below 2^31, their product below 2^40
+    assert _eden(L, rows=1 << 31, col=False) == nv.ERR_ARG
+    assert _eden(L, rows=(1 << 31) - 128, cols=1024, col=False) == nv.ERR_ARG  # > 2^40
+    assert _eden(L, rows=1 << 21, cols=1 << 19, col=False) == nv.ERR_ARG      # = 2^40
+    assert L.dequantize(_layout(), 1 << 31, 128, 128, 16, 0, 0, FAKE, None) == nv.ERR_ARG
+    mx = ctypes.byref(nv._CMx(FAKE, FAKE + 4096))
+    assert L.mxfp4_gemm(mx, mx, 1 << 21, 1 << 19, 128, 0, FAKE, None) == nv.ERR_ARG
     # sr / rtn / fp46 without rotation accept n % 16
     assert L.sr_quantize(FAKE, 256, 200, 128, 16, 1, 0, 1, _layout(), None, FAKE, 256,
                          None) in (nv.ERR_SHAPE,)           # cols % 8 ok, 200 % 16 != 0

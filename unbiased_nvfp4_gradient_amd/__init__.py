@@ -525,9 +525,12 @@ def mxfp4_gemm(a: MXFP4, b: MXFP4, rotated_pair: bool = False,
                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """C = A B^T of two MXFP4 row-layout operands ([M, K] and [N, K]) on the FP4 matrix
     cores, FP32 [M, N]."""
-    if not isinstance(a.codes, torch.Tensor) or not isinstance(b.codes, torch.Tensor) or \
+    a = MXFP4(*a) if isinstance(a, tuple) and len(a) == 2 else a
+    b = MXFP4(*b) if isinstance(b, tuple) and len(b) == 2 else b
+    if not isinstance(a, MXFP4) or not isinstance(b, MXFP4) or \
+            not isinstance(a.codes, torch.Tensor) or not isinstance(b.codes, torch.Tensor) or \
             a.codes.dim() != 2 or b.codes.dim() != 2:
-        raise ValueError("operands must hold 2-D uint8 code tensors")
+        raise ValueError("operands must be MXFP4 (codes, scales) pairs of 2-D uint8 tensors")
     M, K = a.codes.shape[0], a.codes.shape[1] * 2
     N = b.codes.shape[0]
     dev = a.codes.device

@@ -48,8 +48,14 @@ namespace {
 enum { MODE_RTN = 0, MODE_SR = 1, MODE_EDEN = 2, MODE_FP46 = 3 };
 
 constexpr size_t MIN_WORKSPACE_BYTES = 256;   // smallest workspace any quantizer asks for
-constexpr int64_t MAX_DIM = (int64_t)1 << 31; // each dimension
-constexpr int64_t MAX_ELEMS = (int64_t)1 << 40;
+constexpr int64_t MAX_DIM = (int64_t)1 << 31; // each dimension is below this
+constexpr int64_t MAX_ELEMS = (int64_t)1 << 40; // and so is each product of two
+
+// a < MAX_DIM and b < MAX_DIM and a * b < MAX_ELEMS (a, b >= 0)
+bool fits(int64_t a, int64_t b)
+{
+    return a < MAX_DIM && b < MAX_DIM && (a == 0 || b <= (MAX_ELEMS - 1) / a);
+}
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -82,8 +88,7 @@ int check_input(int mode, const void *x, int64_t rows, int64_t cols, int group, 
     if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
     if (mode < MODE_RTN || mode > MODE_FP46) return NVFP4_ERR_ARG;
     if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
-    if (rows > MAX_DIM || cols > MAX_DIM || (rows > 0 && cols > MAX_ELEMS / rows))
-        return NVFP4_ERR_ARG;
+    if (!fits(rows, cols)) return NVFP4_ERR_ARG;
     const bool rotated = rht || mode == MODE_EDEN;
     const int64_t unit = rotated ? 128 : 16;
     if (cols % 8) return NVFP4_ERR_SHAPE;
@@ -121,7 +126,7 @@ int launch_quant(int mode, const void *x, int64_t rows, int64_t cols, uint64_t s
 // padded to 256 bytes.
 size_t strip_workspace_bytes(int64_t rows, int64_t cols)
 {
-    if (rows < 0 || cols < 0 || rows > MAX_DIM || cols > MAX_DIM) return MIN_WORKSPACE_BYTES;
+    if (rows < 0 || cols < 0 || !fits(rows, cols)) return MIN_WORKSPACE_BYTES;
     const size_t b = nvfp4k_strip_workspace(rows, cols);
     return b < MIN_WORKSPACE_BYTES ? MIN_WORKSPACE_BYTES : (b + 255) / 256 * 256;
 }
@@ -170,7 +175,7 @@ int dequantize_common(int local, const nvfp4_tensor *in, int64_t vecs, int64_t n
     if (group != 128 || block != 16) return NVFP4_ERR_GROUP;
     if (rht != 0 && rht != 1) return NVFP4_ERR_ARG;
     if (vecs < 0 || n < 0) return NVFP4_ERR_SHAPE;
-    if (vecs > MAX_DIM || n > MAX_DIM || (vecs > 0 && n > MAX_ELEMS / vecs)) return NVFP4_ERR_ARG;
+    if (!fits(vecs, n)) return NVFP4_ERR_ARG;
     if (n % (rht ? 128 : 16)) return NVFP4_ERR_SHAPE;
     if (!aligned(in->codes, 8) || !aligned(in->scales, 1) || !aligned(in->tensor_scale, 4) ||
         !aligned(out, 16))
@@ -188,9 +193,7 @@ int gemm_common(int local, const nvfp4_tensor *a, const nvfp4_tensor *b, int64_t
     if (!a || !b || !a->tensor_scale || !b->tensor_scale) return NVFP4_ERR_NULL;
     if (rotated_pair != 0 && rotated_pair != 1) return NVFP4_ERR_ARG;
     if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
-    if (M > MAX_DIM || N > MAX_DIM || K > MAX_DIM || (M > 0 && N > MAX_ELEMS / M) ||
-        (M > 0 && K > MAX_ELEMS / M) || (N > 0 && K > MAX_ELEMS / N))
-        return NVFP4_ERR_ARG;
+    if (!fits(M, N) || !fits(M, K) || !fits(N, K)) return NVFP4_ERR_ARG;
     if (M % 32 || N % 32 || K % 64) return NVFP4_ERR_SHAPE;
     if (M > 0 && N > 0 && (!c || (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
         return NVFP4_ERR_NULL;
@@ -362,8 +365,7 @@ int mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int block, in
     if (block != 32) return NVFP4_ERR_GROUP;
     if ((sr != 0 && sr != 1) || (rht != 0 && rht != 1)) return NVFP4_ERR_ARG;
     if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
-    if (rows > MAX_DIM || cols > MAX_DIM || (rows > 0 && cols > MAX_ELEMS / rows))
-        return NVFP4_ERR_ARG;
+    if (!fits(rows, cols)) return NVFP4_ERR_ARG;
     const int64_t unit = rht ? 128 : 32;
     if (cols % 8) return NVFP4_ERR_SHAPE;
     if (row_out && cols % unit) return NVFP4_ERR_SHAPE;
@@ -385,9 +387,7 @@ int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, int64_t M, int64_t 
     if (!a || !b) return NVFP4_ERR_NULL;
     if (rotated_pair != 0 && rotated_pair != 1) return NVFP4_ERR_ARG;
     if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
-    if (M > MAX_DIM || N > MAX_DIM || K > MAX_DIM || (M > 0 && N > MAX_ELEMS / M) ||
-        (M > 0 && K > MAX_ELEMS / M) || (N > 0 && K > MAX_ELEMS / N))
-        return NVFP4_ERR_ARG;
+    if (!fits(M, N) || !fits(M, K) || !fits(N, K)) return NVFP4_ERR_ARG;
     if (M % 32 || N % 32 || K % 128) return NVFP4_ERR_SHAPE;
     if (M > 0 && N > 0 && (!c || (K > 0 && (!a->codes || !a->scales || !b->codes || !b->scales))))
         return NVFP4_ERR_NULL;
