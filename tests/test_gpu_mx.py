@@ -85,10 +85,11 @@ def test_mx_quantize_extremes_and_zeros():
         check_mx(xt, ("row", "col"), sr, rht, what=f"extremes sr={sr} rht={rht}")
 
 
-def test_mx_quantize_config4_full():
-    """16384 x 8192, SR with the rotation, both layouts in one call: every output."""
-    print("case: MXFP4 c4 sr+rht both layouts, every output", flush=True)
-    check_mx(workloads.c4(), ("row", "col"), True, True, seed=1, rht_seed=1, what="c4")
+@pytest.mark.parametrize("sr,rht", [(True, True), (False, True), (True, False)])
+def test_mx_quantize_config4_full(sr, rht):
+    """16384 x 8192, both layouts in one call: every output."""
+    print(f"case: MXFP4 c4 sr={sr} rht={rht} both layouts, every output", flush=True)
+    check_mx(workloads.c4(), ("row", "col"), sr, rht, seed=1, rht_seed=1, what="c4")
 
 
 def _exact(t, rows):
