@@ -126,7 +126,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the MS-EDEN quantizer path runs "
               "on one GPU (a tensor sharded over GPUs would add one all-reduce of two floats "
-              "between the phases; see the design notes)", file=sys.stderr)
+              "between the phases)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -15,9 +15,10 @@
  *     groups, one rotation per tensor, no SR for scales below about 1/32000 of the max.
  *   - rit.work note on "Format-Aware Fusion for Fast FP4 Pretraining": the global NVFP4 max
  *     is a synchronisation point; one producer writes both layouts a GEMM pair needs.
- * The arithmetic is fixed in binary32 (one rounding per operation, no FMA contraction) so
- * that results are reproducible bit for bit; the exact order of every step is written out in
- * the repository's design notes and in the CPU oracle used by the tests.
+ * The arithmetic is fixed in binary32 (one rounding per operation, no FMA contraction) and
+ * in a fixed order (the rotation's butterfly stages by ascending span, every scalar product
+ * and sum of squares as per-term products joined by a balanced pairwise sum in natural
+ * order), so that results are reproducible bit for bit.
  *
  * Conventions shared by every entry point
  *   Pointers.   Every data pointer is a DEVICE pointer allocated by the caller (e.g. a torch

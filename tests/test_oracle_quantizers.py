@@ -188,7 +188,7 @@ def test_rtn_codes_are_nearest(oracle_mod):
 
 
 def test_fp46_choice_against_fp64(oracle_mod):
-    """The emitted block is the lower-error option, judged in fp64, except within a
+    """The emitted block is the lower-error option, decided in fp64, except within a
     relative 1e-5 tie band."""
     x = workloads.c2(shape=(512, 1024))
     xb = _bits(x)
