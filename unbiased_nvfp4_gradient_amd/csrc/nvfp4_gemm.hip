@@ -263,9 +263,10 @@ extern "C" hipError_t nvfp4k_gemm(int local, const uint8_t *a_codes, const uint8
 // instructions, 128 FP32 accumulators per lane); K in steps of 128 (two instructions deep).
 // Each step's codes, 64 bytes per row of A and of B, go straight from memory into one of four
 // LDS stages (global_load_lds_dwordx4, 16 bytes per lane), three steps ahead of the stage that
-// feeds the matrix cores, together with the rows' 4 scale bytes per step; chunk c of row i sits in slot
-// 4 i + (c ^ ((i >> 1) & 3)), so the eight rows a 16-byte LDS read serves at a time hit eight
-// distinct 16-byte bank groups.  The only wait on memory is at the top of each step, for that
+// feeds the matrix cores, together with the rows' 4 scale bytes per step; chunk c of row i sits
+// in slot 4 i + (c ^ ((i >> 2) & 3)).  A 16-byte LDS read serves 16 lanes at a time from 64
+// banks (256 bytes); its lanes read 16 consecutive rows at one chunk, whose slots then cover
+// all 16 residues mod 16, i.e. 16 distinct bank groups (the bank-conflict counter reads 0).  The only wait on memory is at the top of each step, for that
 // step's own loads.
 namespace nvfp4g {
 
@@ -284,47 +285,63 @@ struct MxOperand {
 
 #define MX_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-__device__ __forceinline__ int mx_slot(int i, int c) { return 4 * i + (c ^ ((i >> 1) & 3)); }
+__device__ __forceinline__ int mx_slot(int i, int c) { return 4 * i + (c ^ ((i >> 2) & 3)); }
 
-// Start loading step kt into a stage: the codes of A's and B's 256 rows (from m0, n0), 1024
-// slots of 16 bytes per operand (lane L of wave w fills slot 512 k + 64 w + L in round k), and
-// every row's 4 scale bytes (waves 0..3 A's rows 64 w + L, waves 4..7 B's).  No branch: the
-// scale load's operand is chosen by selects on the wave-uniform w.  Rows past an operand
-// re-read its last row (they feed only entries of C that are not stored).
-__device__ __forceinline__ void mx_stage(const MxOperand &A, const MxOperand &B, int64_t M,
-                                         int64_t N, int64_t K, int64_t m0, int64_t n0,
-                                         int64_t kt, uint8_t *stage)
+// Where one thread's loads of a stage come from and go to.  The codes of A's and B's 256 rows
+// (from m0, n0) are 1024 slots of 16 bytes per operand: lane L of wave w fills slot
+// 512 k + 64 w + L in round k, i.e. chunk c of row i with mx_slot(i, c) that slot.  Every
+// row's 4 scale bytes come in one 4-byte load per lane (waves 0..3 A's rows 64 w + L,
+// waves 4..7 B's).  Rows past an operand re-read its last row (they feed only entries of C
+// that are not stored).  The sources are those of step 0; step kt adds 64 kt bytes to the
+// code sources and 4 kt to the scale source.  The destinations are offsets in a stage, the
+// same for every lane of a wave (the load writes lane L's 16 bytes at offset + 16 L).
+struct MxLoads {
+    const uint8_t *src[4];       // [2 op + k]: codes
+    const uint8_t *ssrc;         // scales
+    uint32_t dst[4], sdst;       // offsets in a stage (wave-uniform)
+};
+
+__device__ __forceinline__ MxLoads mx_loads(const MxOperand &A, const MxOperand &B, int64_t M,
+                                            int64_t N, int64_t K, int64_t m0, int64_t n0)
 {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    MxLoads l;
 #pragma unroll
     for (int op = 0; op < 2; ++op) {
         const uint8_t *codes = op ? B.codes : A.codes;
         const int64_t rows = op ? N : M, row0 = op ? n0 : m0;
-        uint8_t *dst = stage + op * BM * MX_ROW;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int s = 512 * k + 64 * w + lane;
-            const int i = s >> 2, c = (s & 3) ^ ((i >> 1) & 3);
+            const int i = s >> 2, c = (s & 3) ^ ((i >> 2) & 3);
             const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
-            __builtin_amdgcn_global_load_lds(codes + row * (K >> 1) + kt * MX_ROW + 16 * c,
-                                             MX_LDS(dst + 16 * (512 * k + 64 * w)), 16, 0, 0);
+            l.src[2 * op + k] = codes + row * (K >> 1) + 16 * c;
+            l.dst[2 * op + k] = (uint32_t)(op * BM * MX_ROW + 16 * (512 * k + 64 * w));
         }
     }
     const bool on_b = w >= 4;
-    const uint8_t *scales = on_b ? B.scales : A.scales;
     const int64_t rows = on_b ? N : M, row0 = on_b ? n0 : m0;
     const int i = 64 * (w & 3) + lane;
     const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
-    __builtin_amdgcn_global_load_lds(scales + row * (K >> 5) + 4 * kt,
-                                     MX_LDS(stage + MX_CODES + 4 * (on_b ? BM : 0) +
-                                            4 * 64 * (w & 3)),
-                                     4, 0, 0);
+    l.ssrc = (on_b ? B.scales : A.scales) + row * (K >> 5);
+    l.sdst = (uint32_t)(MX_CODES + 4 * (on_b ? BM : 0) + 4 * 64 * (w & 3));
+    return l;
 }
 
-__device__ __forceinline__ v8i mx_frag(const uint8_t *lds, int i, int c)
+// Start loading step kt into a stage: five loads per lane, no branch.
+__device__ __forceinline__ void mx_stage(const MxLoads &l, int64_t kt, uint8_t *stage)
 {
-    const v4i v = *reinterpret_cast<const v4i *>(lds + 16 * mx_slot(i, c));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_global_load_lds(l.src[q] + kt * MX_ROW, MX_LDS(stage + l.dst[q]), 16, 0,
+                                         0);
+    __builtin_amdgcn_global_load_lds(l.ssrc + 4 * kt, MX_LDS(stage + l.sdst), 4, 0, 0);
+}
+
+__device__ __forceinline__ v8i mx_frag(const uint8_t *p)
+{
+    const v4i v = *reinterpret_cast<const v4i *>(p);
     return v8i{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
 }
 
@@ -351,37 +368,70 @@ __device__ __forceinline__ void mx_barrier(bool all)
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// A lane's offsets in a stage of its fragments (sub-step q: A rows wm + 32 i + lane % 32, B
+// rows wn + 32 j + lane % 32, 16-byte chunk 2 q + lane / 32) and of its rows' scale words.
+struct MxOffsets {
+    uint32_t a[2][2], b[4][2];   // [tile][sub-step]
+    uint32_t sa[2], sb[4];
+};
+
+__device__ __forceinline__ MxOffsets mx_offsets(int wm, int wn, int lane)
+{
+    const int half = lane >> 5, r = lane & 31;
+    MxOffsets o;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) o.a[i][q] = 16 * mx_slot(wm + 32 * i + r, 2 * q + half);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o.b[j][q] = BM * MX_ROW + 16 * mx_slot(wn + 32 * j + r, 2 * q + half);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) o.sa[i] = MX_CODES + 4 * (wm + 32 * i + r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.sb[j] = MX_CODES + 4 * (BM + wn + 32 * j + r);
+    return o;
+}
+
 // One sub-step's operands of a wave: 2 fragments of A, 4 of B (sub-step q of a stage).
 struct MxFrags {
     v8i a[2], b[4];
 };
 
-__device__ __forceinline__ MxFrags mx_read(const uint8_t *stage, int wm, int wn, int lane, int q)
+__device__ __forceinline__ MxFrags mx_read(const uint8_t *stage, const MxOffsets &o, int q)
 {
-    const int half = lane >> 5;
     MxFrags f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f.a[i] = mx_frag(stage, wm + 32 * i + (lane & 31), 2 * q + half);
+    for (int i = 0; i < 2; ++i) f.a[i] = mx_frag(stage + o.a[i][q]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        f.b[j] = mx_frag(stage + BM * MX_ROW, wn + 32 * j + (lane & 31), 2 * q + half);
+    for (int j = 0; j < 4; ++j) f.b[j] = mx_frag(stage + o.b[j][q]);
     return f;
 }
 
-// Each lane's scale bytes of a stage, shifted so that byte 2q is its 32-block's in sub-step q.
+// Each lane's scale words of a stage; shifted right by 8 (lane / 32), byte 2q is its
+// 32-block's in sub-step q.
 struct MxScales {
     uint32_t a[2], b[4];
 };
 
-__device__ __forceinline__ MxScales mx_read_scales(const uint8_t *stage, int wm, int wn, int lane)
+__device__ __forceinline__ MxScales mx_read_scales(const uint8_t *stage, const MxOffsets &o)
 {
-    const uint32_t *s = reinterpret_cast<const uint32_t *>(stage + MX_CODES);
-    const int sh = 8 * (lane >> 5);
     MxScales r;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) r.a[i] = s[wm + 32 * i + (lane & 31)] >> sh;
+    for (int i = 0; i < 2; ++i) r.a[i] = *reinterpret_cast<const uint32_t *>(stage + o.sa[i]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.b[j] = s[BM + wn + 32 * j + (lane & 31)] >> sh;
+    for (int j = 0; j < 4; ++j) r.b[j] = *reinterpret_cast<const uint32_t *>(stage + o.sb[j]);
+    return r;
+}
+
+__device__ __forceinline__ MxScales mx_shift(const MxScales &s, int sh)
+{
+    MxScales r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.a[i] = s.a[i] >> sh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.b[j] = s.b[j] >> sh;
     return r;
 }
 
@@ -400,10 +450,13 @@ __device__ __forceinline__ void mx_mfma(f32x16 (&acc)[2][4], const MxFrags &f, c
 // M and N multiples of 32, K a multiple of 128.
 //
 // The fragment reads run one sub-step ahead of the matrix instructions: a step reads its
-// second sub-step's fragments while the first sub-step's instructions run, then (after the
-// barrier that makes the next stage visible) the next step's first fragments and scales while
-// its second sub-step's instructions run.  Every read of a stage is complete before the
-// barrier of the step after it, which is where the loads of a later stage may overwrite it.
+// second sub-step's fragments before its first sub-step's instructions issue, then (after the
+// barrier that makes the next stage visible) the next step's first fragments and scales
+// before its second sub-step's instructions; scheduling barriers keep each group of reads
+// ahead of the instructions that run while they are in flight, and the next step's scale
+// shifts after them.  Every read of a stage is complete before the barrier of the step after
+// it, which is where the loads of a later stage may overwrite it.  The load addresses and the
+// LDS offsets are computed once.
 __global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, int64_t M,
                                                     int64_t N, int64_t K, float f,
                                                     float *__restrict__ C)
@@ -418,31 +471,37 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, in
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     const int64_t nk = K / MX_BK;
+    const MxLoads ld = mx_loads(A, B, M, N, K, m0, n0);
+    const MxOffsets of = mx_offsets(wm, wn, lane);
+    const int sh = 8 * (lane >> 5);
     // stage s goes to buffer s % MX_NSTAGE; past the last step the loads repeat the last
     // step's data into buffers nobody reads, so every step issues the same loads
     auto stage = [&](int64_t s) {
-        mx_stage(A, B, M, N, K, m0, n0, s < nk ? s : nk - 1, lds + (s % MX_NSTAGE) * MX_STAGE);
+        mx_stage(ld, s < nk ? s : nk - 1, lds + (int)(s & (MX_NSTAGE - 1)) * MX_STAGE);
     };
     if (nk > 0) {
         stage(0);
         stage(1);
         stage(2);
         mx_barrier(true);
-        MxFrags f0 = mx_read(lds, wm, wn, lane, 0);
-        MxScales sc = mx_read_scales(lds, wm, wn, lane);
+        MxFrags f0 = mx_read(lds, of, 0);
+        MxScales sc = mx_shift(mx_read_scales(lds, of), sh);
         for (int64_t kt = 0; kt < nk; ++kt) {
-            const uint8_t *cur = lds + (kt % MX_NSTAGE) * MX_STAGE;
-            const MxFrags f1 = mx_read(cur, wm, wn, lane, 1);
+            const uint8_t *cur = lds + (int)(kt & (MX_NSTAGE - 1)) * MX_STAGE;
+            const MxFrags f1 = mx_read(cur, of, 1);
+            __builtin_amdgcn_sched_barrier(0);
             mx_mfma<0>(acc, f0, sc);
-            const MxScales sc1 = sc;
             // stage kt + 1 landed (its loads were issued before the newest, kt + 2's); the
             // buffer of stage kt - 1 was last read before this barrier
             mx_barrier(false);
             stage(kt + MX_NSTAGE - 1);
-            const uint8_t *nxt = lds + ((kt + 1) % MX_NSTAGE) * MX_STAGE;
-            f0 = mx_read(nxt, wm, wn, lane, 0);
-            sc = mx_read_scales(nxt, wm, wn, lane);
-            mx_mfma<1>(acc, f1, sc1);
+            const uint8_t *nxt = lds + (int)((kt + 1) & (MX_NSTAGE - 1)) * MX_STAGE;
+            f0 = mx_read(nxt, of, 0);
+            const MxScales raw = mx_read_scales(nxt, of);
+            __builtin_amdgcn_sched_barrier(0);
+            mx_mfma<1>(acc, f1, sc);
+            __builtin_amdgcn_sched_barrier(0);
+            sc = mx_shift(raw, sh);
         }
     }
 #pragma unroll
