@@ -392,13 +392,14 @@ def gemm_check(nv, workloads, dev, a, stream, reps=10, warmup=3):
         nv.nvfp4_gemm_check(a, b, rotated_pair=True, out=c, stream=stream)
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    all_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms = float(np.median(all_ms))
     M, K = a.codes.shape[0], a.codes.shape[1] * 2
     N = b.codes.shape[0]
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     res = {"kernel": "k_gemm (dequantize into LDS as FP16, v_mfma_f32_32x32x16_f16)", "M": M,
-           "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
-           "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
+           "N": N, "K": K, "ms": round(ms, 4), "min_ms": round(float(min(all_ms)), 4),
+           "tflops": round(tflops, 1), "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
     res["native_fp4"] = mx_gemm(nv, workloads, dev, stream, reps, warmup)
     return res
 
@@ -422,12 +423,18 @@ def mx_gemm(nv, workloads, dev, stream, reps=10, warmup=3):
         nv.mxfp4_gemm(a, b, rotated_pair=True, out=c, stream=stream)
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    all_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms = float(np.median(all_ms))
     M, K = a.codes.shape[0], a.codes.shape[1] * 2
     N = b.codes.shape[0]
-    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    flop = 2.0 * M * N * K
+    tflops = flop / (ms * 1e-3) / 1e12
+    # a sustained FP4 load lowers the part's clock over consecutive launches: the fastest
+    # launch is reported beside the median
     return {"kernel": "k_gemm_mx (MXFP4 operands, v_mfma_scale_f32_32x32x64_f8f6f4)", "M": M,
-            "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "N": N, "K": K, "ms": round(ms, 4), "min_ms": round(float(min(all_ms)), 4),
+            "tflops": round(tflops, 1),
+            "tflops_fastest": round(flop / (min(all_ms) * 1e-3) / 1e12, 1),
             "frac_of_fp4_dense_peak": round(tflops / 10100.0, 4)}
 
 
