@@ -518,6 +518,247 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, in
     }
 }
 
+
+// ------------------------------------------------------------------------------ MXFP4 GEMM, K % 512 == 0
+// The same product with wider K steps, for K a multiple of 512 (every shape the benchmark and
+// the linear layer use).  Each step covers 256 elements of K: 128 code bytes per row of A and
+// B (one 128-byte line per row, where the 128-element steps above fetch half a line per row
+// per step), and each row's scale bytes come 16 at a time, once every two steps.  Measured
+// with the loads alone, a step of the narrow kernel moves its bytes at about half the rate of
+// these; the number of rows a load instruction touches, not its byte count, sets its cost.
+//
+// LDS: two code stages of 64 KiB (256 rows of A then 256 of B, 128 bytes each; chunk c of row
+// i in 16-byte slot 8 i + (c ^ ((i >> 1) & 7)), so the 16 rows one 16-byte read serves at a
+// time cover all 16 bank groups) and two scale stages of 8 KiB (16 bytes per row: the scale
+// bytes of two steps).  A step runs its four sub-steps of 64 elements (8 instructions per
+// wave each); the barrier sits before the last sub-step, so that sub-step's instructions
+// overlap the wait, the next step's loads and its first reads.
+constexpr int MX2_BK = 256;                      // K elements per step
+constexpr int MX2_ROW = MX2_BK / 2;              // code bytes per row and step
+constexpr int MX2_CODES = (BM + BN) * MX2_ROW;   // 64 KiB
+constexpr int MX2_SCALES = (BM + BN) * 16;       // 8 KiB: two steps of scale bytes per row
+
+__device__ __forceinline__ int mx2_slot(int i, int c) { return 8 * i + (c ^ ((i >> 1) & 7)); }
+
+// One thread's loads.  Codes: 4 rounds per operand of 16-byte chunks, lane L of wave w filling
+// slot 512 r + 64 w + L of the operand's half of the stage, i.e. row i = 64 r + i0 (i0 =
+// 8 w + L / 8) at chunk c = (L & 7) ^ ((i0 >> 1) & 7), the same chunk in every round.  Rows past
+// an operand re-read its last row (they feed only entries of C that are not stored); the row
+// is clamped per load, so a thread keeps one pointer per operand.  Scales: one 16-byte load
+// for row t (A's rows for t < 256, then B's).
+struct Mx2Loads {
+    const uint8_t *p[2];         // codes + (row0 + i0) ... : operand base at chunk c
+    int i0, lim[2];              // first row index; last valid row index - row0 per operand
+    const uint8_t *ssrc;         // this thread's scale row
+};
+
+__device__ __forceinline__ Mx2Loads mx2_loads(const MxOperand &A, const MxOperand &B, int64_t M,
+                                              int64_t N, int64_t K, int64_t m0, int64_t n0)
+{
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(t >> 6));
+    Mx2Loads l;
+    l.i0 = 8 * w + (lane >> 3);
+    const int c = (lane & 7) ^ ((l.i0 >> 1) & 7);
+    l.p[0] = A.codes + m0 * (K >> 1) + 16 * c;
+    l.p[1] = B.codes + n0 * (K >> 1) + 16 * c;
+    l.lim[0] = (int)((M - 1 - m0) < 255 ? (M - 1 - m0) : 255);
+    l.lim[1] = (int)((N - 1 - n0) < 255 ? (N - 1 - n0) : 255);
+    const int op = t >> 8, i = t & 255;
+    const int64_t rows = op ? N : M, row0 = op ? n0 : m0;
+    const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
+    l.ssrc = (op ? B.scales : A.scales) + row * (K >> 5);
+    return l;
+}
+
+// A lane's fragment rows: A rows wm + 32 i + lane % 32, B rows wn + 32 j + lane % 32.  Chunk
+// c = 2 q + lane / 32 of row r sits at byte 128 r + 16 (c ^ ((r >> 1) & 7)); rows 32 apart
+// share the xor term, so fragment i of A is at a + 4096 i and the chunk of sub-step q at
+// (a ^ 32 q) + 4096 i, with a = 128 r0 + 16 (lane / 32 ^ ((r0 >> 1) & 7)) for the lane's
+// first row r0 (the chunk bits 5..6 lie below the row bits).  Likewise for B.  The scale
+// words of the lane's rows are at sa + 512 i and sb + 512 j (16 bytes per row).
+struct Mx2Offsets {
+    uint32_t a, b, sa, sb;
+};
+
+__device__ __forceinline__ Mx2Offsets mx2_offsets(int wm, int wn, int lane)
+{
+    const int half = lane >> 5, r = lane & 31;
+    Mx2Offsets o;
+    o.a = (uint32_t)(16 * mx2_slot(wm + r, half));
+    o.b = (uint32_t)(BM * MX2_ROW + 16 * mx2_slot(wn + r, half));
+    o.sa = (uint32_t)(16 * (wm + r));
+    o.sb = (uint32_t)(16 * (BM + wn + r));
+    return o;
+}
+
+__device__ __forceinline__ MxFrags mx2_read(const uint8_t *stage, const Mx2Offsets &o, int q)
+{
+    const uint8_t *pa = stage + (o.a ^ (uint32_t)(32 * q));
+    const uint8_t *pb = stage + (o.b ^ (uint32_t)(32 * q));
+    MxFrags f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = mx_frag(pa + 4096 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = mx_frag(pb + 4096 * j);
+    return f;
+}
+
+// A step's 8 scale bytes per row: word 0 covers sub-steps 0 and 1, word 1 sub-steps 2 and 3.
+struct Mx2Scales {
+    uint2 a[2], b[4];
+};
+
+__device__ __forceinline__ Mx2Scales mx2_read_scales(const uint8_t *sstage, const Mx2Offsets &o,
+                                                     int odd)
+{
+    const uint8_t *pa = sstage + o.sa + 8 * odd, *pb = sstage + o.sb + 8 * odd;
+    Mx2Scales s;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) s.a[i] = *reinterpret_cast<const uint2 *>(pa + 512 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.b[j] = *reinterpret_cast<const uint2 *>(pb + 512 * j);
+    return s;
+}
+
+// The scale words of sub-step q, shifted so that byte 2 (q & 1) is this lane's 32-block's.
+__device__ __forceinline__ MxScales mx2_sub_scales(const Mx2Scales &s, int q, int sh)
+{
+    MxScales r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.a[i] = (q < 2 ? s.a[i].x : s.a[i].y) >> sh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.b[j] = (q < 2 ? s.b[j].x : s.b[j].y) >> sh;
+    return r;
+}
+
+// Wait for all of this wave's loads and LDS reads, then for every wave.
+__device__ __forceinline__ void mx2_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// A step's parity as a type, so that each of the two steps of the loop body is compiled with it.
+template <int V> struct Mx2Parity { static constexpr int value = V; };
+
+// Hide a value from loop-invariant code motion, so that an address is recomputed where it is
+// used (a few instructions per load) instead of being kept in registers across the K loop.
+__device__ __forceinline__ int mx2_opaque(int v)
+{
+    __asm__ volatile("" : "+v"(v));
+    return v;
+}
+
+// C[M][N] = f * sum_k A[m][k] * B[n][k].  Grid (ceil(N/256), ceil(M/256)), 512 threads.
+// M and N multiples of 32, K a multiple of 512.
+//
+// Step kt computes from code stage kt % 2 and scale stage (kt / 2) % 2.  Its barrier (before
+// its last sub-step) finds stage kt + 1 loaded (issued after the previous barrier) and every
+// read of stage kt done, so the loads of stage kt + 2 then go into stage kt's buffer; on even
+// steps the scale bytes of steps kt + 2 and kt + 3 follow into the scale buffer whose steps
+// are over.  The next step's scale words and first fragments are read right after the loads
+// are issued, while this step's last instructions run.  The loop body is two steps (K is a
+// multiple of 512, so the step count is even) and has no branch: loads past the last step
+// re-read the last step's data into buffers nobody reads again, and the reads past it read
+// a buffer whose contents go unused.
+__global__ void __launch_bounds__(512, 1) k_gemm_mx2(MxOperand A, MxOperand B, int64_t M,
+                                                     int64_t N, int64_t K, float f,
+                                                     float *__restrict__ C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * MX2_CODES + 2 * MX2_SCALES];
+    uint8_t *const sbase = lds + 2 * MX2_CODES;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+    const int wm = (w >> 1) * 64, wn = (w & 1) * 128;
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    const int64_t nk = K / MX2_BK;
+    const Mx2Loads ld = mx2_loads(A, B, M, N, K, m0, n0);
+    const Mx2Offsets of = mx2_offsets(wm, wn, lane);
+    const int sh = 8 * (lane >> 5);
+    const int64_t Kh = K >> 1;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    // codes of step min(s, nk - 1) into code buffer s % 2
+    auto load_codes = [&](int64_t s) {
+        uint8_t *st = lds + (int)(s & 1) * MX2_CODES;
+        const int64_t src = (s < nk ? s : nk - 1) * MX2_ROW;
+        const int i0 = mx2_opaque(ld.i0);
+#pragma unroll
+        for (int op = 0; op < 2; ++op) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + 64 * r;
+                const int row = i < ld.lim[op] ? i : ld.lim[op];
+                __builtin_amdgcn_global_load_lds(
+                    ld.p[op] + (int64_t)row * Kh + src,
+                    MX_LDS(st + op * BM * MX2_ROW + 16 * (512 * r + 64 * wu)), 16, 0, 0);
+            }
+        }
+    };
+    // scale bytes of steps 2 ss and 2 ss + 1 (the last pair's past the end) into buffer ss % 2
+    auto load_scales = [&](int64_t ss) {
+        const int64_t src = 16 * (ss < nk / 2 ? ss : nk / 2 - 1);
+        __builtin_amdgcn_global_load_lds(
+            ld.ssrc + src, MX_LDS(sbase + (int)(ss & 1) * MX2_SCALES + 16 * 64 * wu), 16, 0, 0);
+    };
+    // one step; ODD is kt's parity
+    auto step = [&](int64_t kt, auto odd_tag, MxFrags &f0, Mx2Scales &sc) {
+        constexpr int ODD = decltype(odd_tag)::value;
+        const uint8_t *cur = lds + ODD * MX2_CODES;
+        const MxFrags f1 = mx2_read(cur, of, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_mfma<0>(acc, f0, mx2_sub_scales(sc, 0, sh));
+        const MxFrags f2 = mx2_read(cur, of, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_mfma<1>(acc, f1, mx2_sub_scales(sc, 1, sh));
+        const MxFrags f3 = mx2_read(cur, of, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_mfma<0>(acc, f2, mx2_sub_scales(sc, 2, sh));
+        const MxScales s3 = mx2_sub_scales(sc, 3, sh);
+        mx2_barrier();
+        load_codes(kt + 2);
+        if constexpr (!ODD) load_scales(kt / 2 + 1);
+        f0 = mx2_read(lds + (1 - ODD) * MX2_CODES, of, 0);
+        // step kt + 1's scales: the second word pair of this pair's buffer after an even step,
+        // the first of the next pair's after an odd one
+        sc = mx2_read_scales(sbase + (int)(((kt + 1) >> 1) & 1) * MX2_SCALES, of, 1 - ODD);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_mfma<1>(acc, f3, s3);
+    };
+    if (nk > 0) {
+        load_codes(0);
+        load_codes(1);
+        load_scales(0);
+        mx2_barrier();
+        MxFrags f0 = mx2_read(lds, of, 0);
+        Mx2Scales sc = mx2_read_scales(sbase, of, 0);
+        for (int64_t kt = 0; kt < nk; kt += 2) {
+            step(kt, Mx2Parity<0>{}, f0, sc);
+            step(kt + 1, Mx2Parity<1>{}, f0, sc);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + wn + 32 * j + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < M && n < N) C[m * N + n] = acc[i][j][r] * f;
+            }
+        }
+    }
+}
+
 }  // namespace nvfp4g
 
 extern "C" hipError_t nvfp4k_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales,
@@ -529,6 +770,8 @@ extern "C" hipError_t nvfp4k_gemm_mx(const uint8_t *a_codes, const uint8_t *a_sc
     if (M == 0 || N == 0) return hipSuccess;
     const MxOperand A{a_codes, a_scales}, B{b_codes, b_scales};
     const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    k_gemm_mx<<<grid, 512, 0, st>>>(A, B, M, N, K, rotated_pair ? 0.0078125f : 1.0f, c);
+    const float f = rotated_pair ? 0.0078125f : 1.0f;
+    if (K % 512 == 0) k_gemm_mx2<<<grid, 512, 0, st>>>(A, B, M, N, K, f, c);
+    else k_gemm_mx<<<grid, 512, 0, st>>>(A, B, M, N, K, f, c);
     return hipGetLastError();
 }
