@@ -431,7 +431,8 @@ def mx_gemm(nv, workloads, dev, stream, reps=10, warmup=3):
     tflops = flop / (ms * 1e-3) / 1e12
     # a sustained FP4 load lowers the part's clock over consecutive launches: the fastest
     # launch is reported beside the median
-    return {"kernel": "k_gemm_mx (MXFP4 operands, v_mfma_scale_f32_32x32x64_f8f6f4)", "M": M,
+    return {"kernel": "k_gemm_mx2 (MXFP4 operands, K steps of 256 as K % 512 == 0, "
+                      "v_mfma_scale_f32_32x32x64_f8f6f4)", "M": M,
             "N": N, "K": K, "ms": round(ms, 4), "min_ms": round(float(min(all_ms)), 4),
             "tflops": round(tflops, 1),
             "tflops_fastest": round(flop / (min(all_ms) * 1e-3) / 1e12, 1),
