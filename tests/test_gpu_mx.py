@@ -110,8 +110,11 @@ def check_gemm(c, a, b, rows, cols, f):
     return got, ref
 
 
+# K % 512 == 0 takes the 256-wide K step kernel (512, 1024, 1536, 2048), other K the 128-step
+# one; M and N that are not multiples of 256 exercise the clamped rows of partial tiles
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (512, 256, 384), (96, 160, 256),
-                                   (288, 544, 1024)])
+                                   (288, 544, 1024), (256, 256, 512), (64, 96, 1536),
+                                   (544, 288, 2048)])
 def test_mx_gemm_small(M, N, K):
     print(f"case: MXFP4 gemm M={M} N={N} K={K}", flush=True)
     x = workloads.normal((M, K), seed=M + K).to(DEV)
