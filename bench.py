@@ -620,7 +620,8 @@ def training_step(nv, dev, tokens=32768, hidden=2048, ffn=8192, layers=24, reps=
     stream: per layer and projection (q, k, v, o, gate, up, down), 4/6 of the weight (both
     layouts) and of the activation (row layout), MS-EDEN of the grad-output (both layouts),
     GEMM partners sharing a rotation seed; 504 calls.  Synthetic X, dY ~ N(0,1), W ~
-    N(0, 0.02), one buffer per shape.  Median of `reps` timed steps after one warm-up."""
+    N(0, 0.02), one buffer per shape.  Median of `reps` timed steps after one warm-up, issued
+    call by call and replayed from one HIP graph."""
     import numpy as np
     import torch
 
@@ -641,28 +642,46 @@ def training_step(nv, dev, tokens=32768, hidden=2048, ffn=8192, layers=24, reps=
     ws = torch.empty(nv.workspace_bytes(tokens, ffn, 3), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(st):
         for layer in range(layers):
             for p, (o, i) in enumerate(proj):
                 rs = 1000 * layer + 10 * p
                 nv.fp46_quantize(weights[(o, i)], rht=True, rht_seed=rs, layouts=("row", "col"),
-                                 out=outw[(o, i)], workspace=ws, stream=stream)
+                                 out=outw[(o, i)], workspace=ws, stream=st)
                 nv.fp46_quantize(acts[i], rht=True, rht_seed=rs, layouts=("row",),
-                                 out=outx[i], workspace=ws, stream=stream)
+                                 out=outx[i], workspace=ws, stream=st)
                 nv.eden_quantize(grads[o], seed=rs + 3, rht_seed=rs, layouts=("row", "col"),
-                                 out=outd[o], workspace=ws, stream=stream)
+                                 out=outd[o], workspace=ws, stream=st)
 
-    step()
+    def timed(run):
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    step(stream)
     torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    ms = float(np.median(times))
+    ms = timed(lambda: step(stream))
+    # the same 504 calls captured once in a HIP graph and replayed (no entry point allocates,
+    # synchronizes or records a memset, so the whole step captures); the replay must leave
+    # the outputs the eager step left
+    eager = [t.clone() for q in outd.values() for t in (q.row.codes, q.row.scales)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream(dev))
+    for q in outd.values():
+        q.row.codes.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in
+               zip(eager, [t for q in outd.values() for t in (q.row.codes, q.row.scales)]))
+    graph_ms = timed(graph.replay)
+    del graph
     read = written = 0
     for o, i in proj:
         read += 2 * (o * i + tokens * i + tokens * o)
@@ -674,7 +693,10 @@ def training_step(nv, dev, tokens=32768, hidden=2048, ffn=8192, layers=24, reps=
                         f"hidden {hidden}, FFN {ffn}",
             "calls": 3 * len(proj) * layers, "ms": round(ms, 3),
             "algorithmic_GB": round((read + written) / 1e9, 2),
-            "GB/s": round((read + written) / (ms * 1e-3) / 1e9, 1)}
+            "GB/s": round((read + written) / (ms * 1e-3) / 1e9, 1),
+            "hip_graph": {"ms": round(graph_ms, 3),
+                          "GB/s": round((read + written) / (graph_ms * 1e-3) / 1e9, 1),
+                          "replay_matches_eager": same}}
 
 
 def rel_mse(nv, xd, mode, layout):
