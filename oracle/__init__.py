@@ -172,8 +172,9 @@ def scale_sr(c: float, w: int) -> int:
     return int(_load().oracle_scale_sr(c, w))
 
 
-def elem_sr_mag(a: float, u: int) -> int:
-    return int(_load().oracle_elem_sr_mag(a, u))
+def elem_sr_mag(a: float, w: int) -> int:
+    """Element SR magnitude of a in [0, 6] with random word w (the draw is w >> 10)."""
+    return int(_load().oracle_elem_sr_mag(a, w))
 
 
 def _map_u8(fn_name: str, values) -> np.ndarray:
@@ -202,8 +203,8 @@ def scale_sr_n(c: float, words) -> np.ndarray:
     return out
 
 
-def elem_sr_mag_n(a: float, draws) -> np.ndarray:
-    u = np.ascontiguousarray(np.asarray(draws, dtype=np.uint32))
+def elem_sr_mag_n(a: float, words) -> np.ndarray:
+    u = np.ascontiguousarray(np.asarray(words, dtype=np.uint32))
     out = np.zeros(u.shape, dtype=np.uint8)
     _load().oracle_elem_sr_mag_n(a, _ptr(u), _ptr(out), u.size)
     return out
@@ -218,10 +219,10 @@ def scale_sr_pairs_n(c, words) -> np.ndarray:
     return out
 
 
-def elem_sr_pairs_n(a, draws) -> np.ndarray:
-    """Element SR magnitude of each a[i] in [0, 6] with its own 24-bit draw draws[i]."""
+def elem_sr_pairs_n(a, words) -> np.ndarray:
+    """Element SR magnitude of each a[i] in [0, 6] with its own random word words[i]."""
     aa = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
-    u = np.ascontiguousarray(np.asarray(draws, dtype=np.uint32))
+    u = np.ascontiguousarray(np.asarray(words, dtype=np.uint32))
     out = np.zeros(aa.shape, dtype=np.uint8)
     _load().oracle_elem_sr_pairs_n(_ptr(aa), _ptr(u), _ptr(out), aa.size)
     return out
@@ -242,7 +243,7 @@ MARGIN_KINDS = {"e2m1": 0, "e4m3_rne": 1, "e4m3_up": 2, "scale_sr": 3, "elem_sr"
 def margin_n(kind: str, values, aux=None) -> np.ndarray:
     """Margin (ulps from the value to the boundary of the rounding it feeds) of each value:
     "e2m1" nearest of |v|, "e4m3_rne" / "e4m3_up" scale roundings of v >= 0, "scale_sr" of v
-    with random word aux, "elem_sr" of v in [0, 6) with 24-bit draw aux, "ulp" the distance
+    with random word aux, "elem_sr" of v in [0, 6) with random word aux, "ulp" the distance
     between v and the float whose bits are aux."""
     v = np.ascontiguousarray(np.asarray(values, dtype=np.float32))
     a = np.zeros(v.shape, dtype=np.uint32) if aux is None else \

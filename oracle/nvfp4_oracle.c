@@ -187,7 +187,7 @@ static const float E2M1_V[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 /* The two stochastic-rounding steps (defined below, pinned by enumeration of every random
  * word); the quantizers call them for every decision they make. */
 uint8_t oracle_scale_sr(float c, uint32_t w);
-int oracle_elem_sr_mag(float a, uint32_t u);
+int oracle_elem_sr_mag(float a, uint32_t w);
 static const float E2M1_THRESH[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
 
 float oracle_e2m1_value(uint8_t code)
@@ -267,14 +267,15 @@ static uint32_t scale_sr_margin(float c, uint32_t w)
     return sum > 0x100000u ? sum - 0x100000u : 0x100000u - sum;
 }
 
-/* Element SR of a in [0, 6) with 24-bit draw u rounds up exactly when a lies above the
- * point lo + u * 2^-24 * (hi - lo) between its grid neighbours lo < hi: the margin is a's
- * distance from that point (computed in fp64, then rounded to binary32). */
-static uint32_t elem_sr_margin(float a, uint32_t u)
+/* Element SR of a in [0, 6) with word w (draw v = w >> 10) rounds up exactly when a reaches
+ * the point lo + (1 - v * 2^-22) * (hi - lo) between its grid neighbours lo < hi: the margin
+ * is a's distance from that point (exact in fp64, and exact again as a binary32: it needs at
+ * most 24 significant bits). */
+static uint32_t elem_sr_margin(float a, uint32_t w)
 {
     int lo = 0;
     while (E2M1_V[lo + 1] <= a) ++lo;
-    double ab = E2M1_V[lo] + ((double)u / 16777216.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);
+    double ab = E2M1_V[lo] + (1.0 - (double)(w >> 10) / 4194304.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);
     return ulp_dist(a, (float)ab);
 }
 
@@ -542,9 +543,8 @@ static void quantize_rotated_vector(int mode, const float *r, int64_t n, int64_t
                     } else {
                         uint32_t w = rand_word(seed, (uint64_t)(vec * n + e), STREAM_ELEM_SR,
                                                (uint32_t)axis);
-                        uint32_t u = w >> 8;
-                        mag = oracle_elem_sr_mag(a, u);
-                        em = elem_sr_margin(a, u);
+                        mag = oracle_elem_sr_mag(a, w);
+                        em = elem_sr_margin(a, w);
                     }
                     code = (uint8_t)(mag | ((rb[i] < 0.0f) << 3));
                 }
@@ -763,14 +763,19 @@ uint8_t oracle_scale_sr(float c, uint32_t w)
     return oracle_e4m3_rne_sat(f32_of(up_bits));
 }
 
-/* The element-SR step alone: magnitude code of a = min(|y|, 6) with 24-bit draw u. */
-int oracle_elem_sr_mag(float a, uint32_t u)
+/* The element-SR step alone: magnitude code of a = min(|y|, 6) with the element's random
+ * word w.  Its top 22 bits v, read as the fraction v * 2^-22 of a grid step, are added to a's
+ * position between its neighbours lo < hi and the sum is rounded down onto the grid: the
+ * magnitude is hi exactly when frac + v * 2^-22 >= 1, so over the 2^22 draws it moves up
+ * floor(frac * 2^22) times.  frac and the threshold 1 - v * 2^-22 are both exact in binary32. */
+int oracle_elem_sr_mag(float a, uint32_t w)
 {
     if (a >= 6.0f) return 7;
     int lo = 0;
     while (E2M1_V[lo + 1] <= a) ++lo;
     float frac = (a - E2M1_V[lo]) / (E2M1_V[lo + 1] - E2M1_V[lo]);
-    return ((float)u < frac * 16777216.0f) ? lo + 1 : lo;
+    uint32_t v = w >> 10;
+    return frac >= (float)(4194304u - v) / 4194304.0f ? lo + 1 : lo;
 }
 
 void oracle_set_threads(int n)
@@ -816,15 +821,15 @@ void oracle_scale_sr_n(float c, const uint32_t *w, uint8_t *out, int64_t n)
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_scale_sr(c, w[i]);
 }
 
-void oracle_elem_sr_mag_n(float a, const uint32_t *u, uint8_t *out, int64_t n)
+void oracle_elem_sr_mag_n(float a, const uint32_t *w, uint8_t *out, int64_t n)
 {
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)oracle_elem_sr_mag(a, u[i]);
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)oracle_elem_sr_mag(a, w[i]);
 }
 
 /* Margins of single roundings, for the pins: kind 0 = E2M1 nearest of |v|, 1 = E4M3 nearest
  * of v >= 0, 2 = E4M3 round-up of v >= 0, 3 = scale SR of v with word aux[i], 4 = element SR
- * of v in [0, 6) with 24-bit draw aux[i], 5 = ulp distance between v and aux[i] read as a
+ * of v in [0, 6) with word aux[i], 5 = ulp distance between v and aux[i] read as a
  * float. */
 void oracle_margin_n(int kind, const float *v, const uint32_t *aux, uint32_t *out, int64_t n)
 {
@@ -848,10 +853,10 @@ void oracle_scale_sr_pairs_n(const float *c, const uint32_t *w, uint8_t *out, in
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_scale_sr(c[i], w[i]);
 }
 
-void oracle_elem_sr_pairs_n(const float *a, const uint32_t *u, uint8_t *out, int64_t n)
+void oracle_elem_sr_pairs_n(const float *a, const uint32_t *w, uint8_t *out, int64_t n)
 {
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)oracle_elem_sr_mag(a[i], u[i]);
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)oracle_elem_sr_mag(a[i], w[i]);
 }
 
 void oracle_philox_n(const uint64_t *key, const uint32_t *ctr, uint32_t *out, int64_t n)
@@ -917,7 +922,7 @@ int oracle_mx_quantize(int sr, const uint16_t *x, int64_t rows, int64_t cols, in
                 if (sr) {
                     uint32_t w = rand_word(seed, (uint64_t)(vec * n + pos), STREAM_ELEM_SR,
                                            (uint32_t)axis);
-                    mag = oracle_elem_sr_mag(fminf(fabsf(y), 6.0f), w >> 8);
+                    mag = oracle_elem_sr_mag(fminf(fabsf(y), 6.0f), w);
                 } else {
                     mag = oracle_e2m1_rtn_mag(fabsf(y));
                 }

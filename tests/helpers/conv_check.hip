@@ -98,12 +98,19 @@ __global__ void k_scale_sr(const float *c, const uint32_t *w, uint64_t n, uint8_
         out[i] = (uint8_t)e4m3_sr_normal(__float_as_uint(c[i]), w[i]);
 }
 
-// Element SR magnitude of a in [0, 6] with word w (its top 24 bits are the draw).
-__global__ void k_elem_sr(const float *a, const uint32_t *w, uint64_t n, uint8_t *out)
+// Element SR code (sign and magnitude) of y[i] with word w[i], eight at a time through the
+// quantizers' packing routine (so both element positions of the conversion are exercised);
+// out[i] is one code per byte.  n is a multiple of 8.
+__global__ void k_elem_sr(const float *y, const uint32_t *w, uint64_t n, uint8_t *out)
 {
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (uint64_t)gridDim.x * blockDim.x)
-        out[i] = (uint8_t)e2m1_sr_mag(a[i], w[i]);
+    for (uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n / 8;
+         g += (uint64_t)gridDim.x * blockDim.x) {
+        float yy[8];
+        uint32_t ww[8];
+        for (int k = 0; k < 8; ++k) { yy[k] = y[8 * g + k]; ww[k] = w[8 * g + k]; }
+        const uint32_t d = e2m1_sr_pack8(yy, ww);
+        for (int k = 0; k < 8; ++k) out[8 * g + k] = (uint8_t)((d >> (4 * k)) & 15u);
+    }
 }
 
 // MXFP4 scale byte (e + 127) of the floats with bits start + i.
@@ -168,9 +175,10 @@ int conv_scale_sr(const float *c, const uint32_t *w, uint64_t n, uint8_t *out, v
     return status();
 }
 
-int conv_elem_sr(const float *a, const uint32_t *w, uint64_t n, uint8_t *out, void *stream)
+int conv_elem_sr(const float *y, const uint32_t *w, uint64_t n, uint8_t *out, void *stream)
 {
-    k_elem_sr<<<grid_for(n), THREADS, 0, (hipStream_t)stream>>>(a, w, n, out);
+    if (n % 8) return -1;
+    k_elem_sr<<<grid_for(n / 8), THREADS, 0, (hipStream_t)stream>>>(y, w, n, out);
     return status();
 }
 

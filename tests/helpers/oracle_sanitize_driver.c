@@ -41,15 +41,15 @@ int oracle_eden_internals(const uint16_t *x, int64_t rows, int64_t cols, int axi
                           uint64_t rht_seed, float g, int64_t vec, float *r_out, float *q_out,
                           float *S_out, float *c_out);
 uint8_t oracle_scale_sr(float c, uint32_t w);
-int oracle_elem_sr_mag(float a, uint32_t u);
+int oracle_elem_sr_mag(float a, uint32_t w);
 void oracle_margin_n(int kind, const float *v, const uint32_t *aux, uint32_t *out, int64_t n);
 void oracle_e4m3_rne_sat_n(const float *t, uint8_t *out, int64_t n);
 void oracle_e4m3_up_n(const float *t, uint8_t *out, int64_t n);
 void oracle_e2m1_rtn_mag_n(const float *a, uint8_t *out, int64_t n);
 void oracle_scale_sr_n(float c, const uint32_t *w, uint8_t *out, int64_t n);
-void oracle_elem_sr_mag_n(float a, const uint32_t *u, uint8_t *out, int64_t n);
+void oracle_elem_sr_mag_n(float a, const uint32_t *w, uint8_t *out, int64_t n);
 void oracle_scale_sr_pairs_n(const float *c, const uint32_t *w, uint8_t *out, int64_t n);
-void oracle_elem_sr_pairs_n(const float *a, const uint32_t *u, uint8_t *out, int64_t n);
+void oracle_elem_sr_pairs_n(const float *a, const uint32_t *w, uint8_t *out, int64_t n);
 void oracle_philox_n(const uint64_t *key, const uint32_t *ctr, uint32_t *out, int64_t n);
 int oracle_mx_scale_exp(float m);
 int oracle_mx_quantize(int sr, const uint16_t *x, int64_t rows, int64_t cols, int axis,
@@ -190,7 +190,7 @@ static void run_scalars(void)
     for (int i = 0; i < N; ++i) {
         c[i] = 0.015625f + (447.0f - 0.015625f) * (float)(next_u32() % 65536) / 65536.0f;
         a[i] = 6.0f * (float)(next_u32() % 65537) / 65536.0f;
-        u[i] = w[i] >> 8;
+        u[i] = w[i] ^ 0x5A5A5A5Au;
     }
     oracle_scale_sr_pairs_n(c, w, b, N);
     oracle_elem_sr_pairs_n(a, u, b, N);

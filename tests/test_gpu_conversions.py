@@ -149,49 +149,66 @@ def test_scale_sr_sampled(conv):
     assert np.array_equal(out.cpu().numpy(), oracle.scale_sr_pairs_n(c, w))
 
 
+def _elem_sr_codes(y, w):
+    """Oracle codes of signed y with words w: magnitude of min(|y|, 6), sign bit iff y < 0."""
+    mag = oracle.elem_sr_pairs_n(np.minimum(np.abs(y), np.float32(6)), w)
+    return mag | ((y < 0).astype(np.uint8) << 3)
+
+
 def test_elem_sr_sampled(conv):
+    """Signed inputs, both element positions of the conversion, saturation above 6."""
     rng = np.random.default_rng(2)
     n = 1 << 22
-    a = np.concatenate([rng.uniform(0, 6, n - 64).astype(np.float32),
-                        np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6] * 8, dtype=np.float32)])
-    # every grid point and its float neighbours, with draws near the decision point
-    grid_nb = np.concatenate([np.nextafter(a[-64:], np.float32(0)),
-                              np.nextafter(a[-64:], np.float32(7))])
+    a = np.concatenate([rng.uniform(0, 6, n - 80).astype(np.float32),
+                        np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6] * 8, dtype=np.float32),
+                        np.array([6.5, 7, 8, 100, 1e30, 2.0**-130, 1e-9, 5.9999995] * 2,
+                                 dtype=np.float32)])
+    # every grid point and its float neighbours
+    grid_nb = np.concatenate([np.nextafter(a[-80:-16], np.float32(0)),
+                              np.nextafter(a[-80:-16], np.float32(7))])
     a[: grid_nb.size] = np.minimum(grid_nb, np.float32(6))
+    perm = rng.permutation(n)                         # spread the specials over both positions
+    a = a[perm]
+    y = np.where((rng.integers(0, 2, n) == 1) & (a != 0), -a, a).astype(np.float32)
     w = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
-    ad, wd = torch.from_numpy(a).to(DEV), torch.from_numpy(w.view(np.int32)).to(DEV)
+    yd, wd = torch.from_numpy(y).to(DEV), torch.from_numpy(w.view(np.int32)).to(DEV)
     out = torch.empty(n, dtype=torch.uint8, device=DEV)
-    assert conv.conv_elem_sr(ad.data_ptr(), wd.data_ptr(), n, out.data_ptr(), _stream()) == 0
-    assert np.array_equal(out.cpu().numpy(), oracle.elem_sr_pairs_n(a, w >> 8))
+    assert conv.conv_elem_sr(yd.data_ptr(), wd.data_ptr(), n, out.data_ptr(), _stream()) == 0
+    got, want = out.cpu().numpy(), _elem_sr_codes(y, w)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (f"{bad.size} mismatches from y = {y[bad[0]]!r}, w = {w[bad[0]]:#x}, "
+                           f"position {bad[0] % 2}: {got[bad[0]]} != {want[bad[0]]}")
 
 
 def test_elem_sr_every_magnitude_at_its_threshold(conv):
-    """Element SR on every binary32 a in [0, 6], each with the draw just below its rounding
-    threshold (goes up) or at it (stays), alternately: the decision at the exact boundary,
-    for every input.  The threshold ceil(frac * 2^24) only picks the draw; the expected
-    magnitude comes from the oracle."""
+    """Element SR on every binary32 a in [0, 6], each with the draw just below the smallest
+    draw that rounds it up (stays) or at it (goes up), the two alternating in pairs so that
+    both element positions of the conversion see both: the decision at the exact boundary,
+    for every input.  The threshold 2^22 - floor(frac * 2^22) only picks the draw; the
+    expected magnitude comes from the oracle."""
     grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
-    end = 0x40C00000 + 1                               # bits of 6.0, inclusive
+    top = 0x40C00000                                   # bits of 6.0, included
+    end = (top + 1 + 7) // 8 * 8                       # whole groups of 8 (the tail repeats 6.0)
     chunk = 1 << 26
     rng = np.random.default_rng(5)
-    print(f"case: element SR, {end} magnitudes", flush=True)
+    print(f"case: element SR, {top + 1} magnitudes", flush=True)
     out = torch.empty(chunk, dtype=torch.uint8, device=DEV)
     for lo in range(0, end, chunk):
         n = min(chunk, end - lo)
-        a = _bits(lo, n).view(np.float32)
+        a = np.minimum(_bits(lo, n), np.uint32(top)).view(np.float32)
         ad = a.astype(np.float64)
         k = np.minimum(np.searchsorted(grid, ad, side="right") - 1, 6)
-        thr = np.ceil((ad - grid[k]) / (grid[k + 1] - grid[k]) * 2.0**24).astype(np.int64)
-        u = np.clip(thr - 1 + (np.arange(n) & 1), 0, 2**24 - 1).astype(np.uint32)
-        w = (u << np.uint32(8)) | rng.integers(0, 256, n, dtype=np.uint32)
+        first_up = 2**22 - np.floor((ad - grid[k]) / (grid[k + 1] - grid[k]) * 2.0**22)
+        v = np.clip(first_up - 1 + ((np.arange(n) >> 1) & 1), 0, 2**22 - 1).astype(np.uint32)
+        w = (v << np.uint32(10)) | rng.integers(0, 1024, n, dtype=np.uint32)
         ad_t, wd = torch.from_numpy(a).to(DEV), torch.from_numpy(w.view(np.int32)).to(DEV)
         assert conv.conv_elem_sr(ad_t.data_ptr(), wd.data_ptr(), n, out.data_ptr(),
                                  _stream()) == 0
         got = out[:n].cpu().numpy()
-        want = oracle.elem_sr_pairs_n(a, u)
+        want = oracle.elem_sr_pairs_n(a, w)
         bad = np.nonzero(got != want)[0]
-        assert bad.size == 0, (f"{bad.size} mismatches from a = {a[bad[0]]!r}, u = {u[bad[0]]}: "
-                               f"{got[bad[0]]} != {want[bad[0]]}")
+        assert bad.size == 0, (f"{bad.size} mismatches from a = {a[bad[0]]!r}, v = {v[bad[0]]}, "
+                               f"position {bad[0] % 2}: {got[bad[0]]} != {want[bad[0]]}")
 
 
 def test_philox_sampled(conv):

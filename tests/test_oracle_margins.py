@@ -121,13 +121,13 @@ def test_scale_sr_margin():
 
 
 def test_elem_sr_margin():
-    """Element SR of a in [0, 6) with a fixed 24-bit draw u."""
+    """Element SR of a in [0, 6) with a fixed random word (draw v = word >> 10)."""
     rng = np.random.default_rng(4)
     grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
     n = 600
-    u = rng.integers(0, 2**24, n).astype(np.uint32)
+    u = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
     lo = rng.integers(0, 7, n)
-    point = grid[lo] + u / 2**24 * (grid[lo + 1] - grid[lo])     # the boundary, fp64
+    point = grid[lo] + (1 - (u >> 10) / 2**22) * (grid[lo + 1] - grid[lo])   # the boundary
     a = point.astype(np.float32)
     a = np.where(np.arange(n) % 3 == 0, rng.uniform(0, 5.99, n).astype(np.float32), a)
     offs = rng.integers(-30, 31, n)

@@ -34,8 +34,8 @@ MUTATIONS = [
     ("scale SR draws one bit short", "uint32_t up_bits = (bits_of(c) + (w >> 12)) & 0xFFF00000u;",
      "uint32_t up_bits = (bits_of(c) + (w >> 13)) & 0xFFF00000u;",
      [PRIM + "test_scale_sr_enumeration"]),
-    ("element SR compares with <=", "return ((float)u < frac * 16777216.0f) ? lo + 1 : lo;",
-     "return ((float)u <= frac * 16777216.0f) ? lo + 1 : lo;",
+    ("element SR compares with >", "return frac >= (float)(4194304u - v) / 4194304.0f ? lo + 1 : lo;",
+     "return frac > (float)(4194304u - v) / 4194304.0f ? lo + 1 : lo;",
      [PRIM + "test_elem_sr_enumeration"]),
     ("Philox multiplier off by two", "0xD2511F53u", "0xD2511F55u",
      [PRIM + "test_philox_known_answers"]),
@@ -80,8 +80,8 @@ MUTATIONS = [
     ("scale SR margin one bit short", "uint32_t sum = (bits_of(c) & 0xFFFFFu) + (w >> 12);",
      "uint32_t sum = (bits_of(c) & 0xFFFFFu) + (w >> 13);", [MARG + "test_scale_sr_margin"]),
     ("element SR margin from the wrong grid point",
-     "double ab = E2M1_V[lo] + ((double)u / 16777216.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);",
-     "double ab = E2M1_V[lo + 1] - ((double)u / 16777216.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);",
+     "double ab = E2M1_V[lo] + (1.0 - (double)(w >> 10) / 4194304.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);",
+     "double ab = E2M1_V[lo + 1] - (1.0 - (double)(w >> 10) / 4194304.0) * (E2M1_V[lo + 1] - E2M1_V[lo]);",
      [MARG + "test_elem_sr_margin"]),
     ("decoder drops the sign", "o[e] = (code & 8) ? -qv : qv;", "o[e] = qv;",
      [QUANT + "test_dequantize_round_trips_on_grid_inputs"]),

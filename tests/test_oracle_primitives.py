@@ -259,22 +259,28 @@ def test_scale_sr_enumeration(oracle_mod):
 
 
 def test_elem_sr_enumeration(oracle_mod):
-    """Over all 2^24 draws u, #up = ceil(frac * 2^24); the mean lands on a within one
-    2^-24 step of the grid spacing."""
+    """Over all 2^22 draws v (the top 22 bits of the word), the magnitude moves up exactly
+    for the floor(frac * 2^22) largest draws: add-and-round-down stochastic rounding, whose
+    mean lands on a within one 2^-22 step of the grid spacing.  The ten bits below the draw
+    never matter."""
     mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
-    u = np.arange(2 ** 24, dtype=np.uint32)
+    v = np.arange(2 ** 22, dtype=np.uint32)
+    words = v << np.uint32(10)
     rng = np.random.default_rng(4)
+    low = rng.integers(0, 1024, v.size).astype(np.uint32)
     for a in list(rng.uniform(0, 6, 12).astype(np.float32)) + [np.float32(0.0),
                                                               np.float32(1.5),
                                                               np.float32(5.999),
+                                                              np.float32(0.3),
                                                               np.float32(1e-9)]:
         a64 = float(a)
-        got = oracle_mod.elem_sr_mag_n(float(a), u)
+        got = oracle_mod.elem_sr_mag_n(float(a), words)
         lo = int(np.searchsorted(mags, a64, side="right") - 1)
         frac = (a64 - mags[lo]) / (mags[lo + 1] - mags[lo])
-        n_up = int((got == lo + 1).sum())
-        assert set(np.unique(got)).issubset({lo, lo + 1})
-        assert n_up == int(np.ceil(frac * 2 ** 24))
-        mean = mags[lo] + (mags[lo + 1] - mags[lo]) * n_up / 2 ** 24
-        assert abs(mean - a64) <= (mags[lo + 1] - mags[lo]) * 2.0 ** -24
+        n_up = int(np.floor(frac * 2 ** 22))
+        want = np.where(v >= 2 ** 22 - n_up, lo + 1, lo)
+        assert np.array_equal(got, want)
+        assert np.array_equal(oracle_mod.elem_sr_mag_n(float(a), words | low), want)
+        mean = mags[lo] + (mags[lo + 1] - mags[lo]) * n_up / 2 ** 22
+        assert 0 <= a64 - mean < (mags[lo + 1] - mags[lo]) * 2.0 ** -22
     assert oracle_mod.elem_sr_mag(6.0, 0) == 7

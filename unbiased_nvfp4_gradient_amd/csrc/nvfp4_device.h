@@ -80,26 +80,46 @@ __device__ __forceinline__ float e2m1_val(uint32_t mag)
     return __uint_as_float(b);
 }
 
-// Stochastic rounding of a magnitude 0 <= a <= 6 onto the E2M1 grid with random word w: with
-// lo the largest grid index whose value vlo <= a and frac = (a - vlo) / (step to the next
-// value), the magnitude is lo + 1 iff the top 24 bits of w, u, satisfy u < frac * 2^24.
-// Both forms below count the grid steps a crosses after adding the draw's complement, in
-// integers, so no compare and no select is spent on lo or frac:
-//  - below 2 the grid is uniform (step 1/2): with F = a * 2^25 (exact), lo = floor(F / 2^24)
-//    and frac * 2^24 = F mod 2^24, and u < frac * 2^24 iff u < ceil(F) - lo * 2^24 (u is an
-//    integer), so lo + up = (ceil(F) + 2^24 - 1 - u) >> 24;
-//  - from 1 up the grid points are a's binade start and midpoint (step half the binade): with
-//    m the low 22 bits of a's encoding, frac * 2^24 = 4 m and lo = (bits(a) >> 22) - 252 (2 at
-//    1, 6 at 4, 7 at 6), and u < 4 m iff (w >> 10) < m, so lo + up =
-//    (bits(a) + 2^22 - 1 - (w >> 10) - 252 * 2^22) >> 22 (a = 6 has m = 0 and stays at 7).
-// Every operation is exact; a < 2 takes the first form, a >= 2 the second.
-__device__ __forceinline__ uint32_t e2m1_sr_mag(float a, uint32_t w)
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// (m & a) | (~m & b): the bits of a where m is set, of b elsewhere.  m (uniform) passes through an
+// empty asm so that the compiler keeps the select (one v_bfi_b32) rather than splitting a
+// constant mask into separate AND and OR instructions.
+__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b)
 {
-    const uint32_t t = __float_as_uint(a);
-    const uint32_t big = (t + (0x3FFFFFu - (252u << 22)) - (w >> 10)) >> 22;
-    const uint32_t small =
-        ((uint32_t)__builtin_ceilf(a * 33554432.0f) + 0xFFFFFFu - (w >> 8)) >> 24;
-    return a >= 2.0f ? big : small;
+    asm("" : "+s"(m));
+    return (m & a) | (~m & b);
+}
+
+// Stochastic rounding onto the signed E2M1 grid, eight elements into one dword of codes
+// (element k in nibble k).  Element k with random word w[k]: with lo < hi the grid neighbours
+// of a = min(|y|, 6) and frac = (a - lo) / (hi - lo), the top 22 bits v of w[k] are added to
+// the fraction as v * 2^-22 and the sum rounds down, so the magnitude is hi iff
+// frac + v * 2^-22 >= 1; the sign is y's (y is never -0 here: it comes from fma(r, rcp, +0)).
+// gfx950's SR conversion does exactly this per element of its pair, with the draw taken from
+// bits 31..10 of its random operand for the low element and bits 30..9 for the high one, and
+// saturates |y| >= 6 to magnitude 7.  Each element needs its own draw, so every instruction
+// converts the pair (y[2j], y[2j+1]) twice: once with w[2j] (its low nibble kept) and once
+// with w[2j+1] >> 1 (its high nibble kept, which then sees bits 31..10 of w[2j+1]).
+// The instruction writes byte j of its destination and leaves the other three bytes as they
+// were, but the compiler does not carry the builtin's old-value operand into that register
+// (it does for the round-to-nearest form), so only byte j of each result is defined here:
+// the bytes are merged with bit selects.
+__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float *y, const uint32_t *w)
+{
+    uint32_t u[4];
+#define NVFP4_SR_PAIR(j)                                                                       \
+    {                                                                                          \
+        const float2v p = {y[2 * (j)], y[2 * (j) + 1]};                                        \
+        const uint32_t l = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, w[2 * (j)], 1.0f, (j)); \
+        const uint32_t h =                                                                     \
+            __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, w[2 * (j) + 1] >> 1, 1.0f, (j)); \
+        u[j] = bit_select(0x0F0F0F0Fu, l, h);                                                  \
+    }
+    NVFP4_SR_PAIR(0) NVFP4_SR_PAIR(1) NVFP4_SR_PAIR(2) NVFP4_SR_PAIR(3)
+#undef NVFP4_SR_PAIR
+    return bit_select(0x0000FFFFu, bit_select(0x000000FFu, u[0], u[1]),
+                      bit_select(0x00FF0000u, u[2], u[3]));
 }
 
 // Nearest-even E4M3 of t >= 0, saturating: the hardware conversion is exact below 448.
@@ -114,8 +134,6 @@ __device__ __forceinline__ uint32_t e4m3_rne_hw(float t)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, (int)__float_as_uint(c), false) &
            0x7Fu;
 }
-
-typedef float float2v __attribute__((ext_vector_type(2)));
 
 // Codes of y0, y1 (nearest-even E2M1, sign of the input) into byte `sel` of w.
 #define CVT_FP4(w, y0, y1, sel) \

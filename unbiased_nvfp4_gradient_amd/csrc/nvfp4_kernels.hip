@@ -874,19 +874,20 @@ __device__ __forceinline__ void quantize_half(float r[HALF], const float bmax[4]
                     // element index of the block's first element, a multiple of 4
                     const int64_t e0 = vec * n + gi * TILE + HALF * h + 16 * b;
 #pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const uint64_t j = ((uint64_t)e0 >> 2) + qd;
-                        const Word4 w = philox(seed, (uint32_t)j, (uint32_t)(j >> 32),
-                                               STREAM_ELEM_SR, axis);
+                    for (int d = 0; d < 2; ++d) {   // 8 elements, two Philox calls
+                        uint32_t ws[8];
+                        float y[8];
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const int p = 16 * b + 4 * qd + k;
-                            const float y = scaled(rb[4 * qd + k], rcp);
-                            const float a = fminf(fabsf(y), 6.0f);
-                            const uint32_t mag = e2m1_sr_mag(a, w.w[k]);
-                            const uint32_t sgn = __float_as_uint(y) >> 31;   // r < 0
-                            cw[p >> 3] |= (mag | (sgn << 3)) << (4 * (p & 7));
+                        for (int c = 0; c < 2; ++c) {
+                            const uint64_t j = ((uint64_t)e0 >> 2) + 2 * d + c;
+                            const Word4 w = philox(seed, (uint32_t)j, (uint32_t)(j >> 32),
+                                                   STREAM_ELEM_SR, axis);
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) ws[4 * c + k] = w.w[k];
                         }
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) y[k] = scaled(rb[8 * d + k], rcp);
+                        cw[2 * b + d] = e2m1_sr_pack8(y, ws);
                     }
                 }
             }
@@ -976,18 +977,20 @@ __device__ __forceinline__ void quantize_half_mx(const float r[HALF], const floa
                 // element index of the block's first element, a multiple of 4
                 const int64_t e0 = vec * n + gi * TILE + HALF * h + 32 * b;
 #pragma unroll
-                for (int qd = 0; qd < 8; ++qd) {
-                    const uint64_t j = ((uint64_t)e0 >> 2) + qd;
-                    const Word4 w = philox(seed, (uint32_t)j, (uint32_t)(j >> 32),
-                                           STREAM_ELEM_SR, axis);
+                for (int d = 0; d < 4; ++d) {   // 8 elements, two Philox calls
+                    uint32_t ws[8];
+                    float y[8];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int p4 = 4 * qd + k;
-                        const float y = scaled(rb[p4], p);
-                        const uint32_t mag = e2m1_sr_mag(fminf(fabsf(y), 6.0f), w.w[k]);
-                        const uint32_t sgn = __float_as_uint(y) >> 31;   // r < 0
-                        cw[4 * b + (p4 >> 3)] |= (mag | (sgn << 3)) << (4 * (p4 & 7));
+                    for (int c = 0; c < 2; ++c) {
+                        const uint64_t j = ((uint64_t)e0 >> 2) + 2 * d + c;
+                        const Word4 w = philox(seed, (uint32_t)j, (uint32_t)(j >> 32),
+                                               STREAM_ELEM_SR, axis);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) ws[4 * c + k] = w.w[k];
                     }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) y[k] = scaled(rb[8 * d + k], p);
+                    cw[4 * b + d] = e2m1_sr_pack8(y, ws);
                 }
             }
         }
