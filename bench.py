@@ -436,7 +436,55 @@ def mx_gemm(nv, workloads, dev, stream, reps=10, warmup=3):
             "N": N, "K": K, "ms": round(ms, 4), "min_ms": round(float(min(all_ms)), 4),
             "tflops": round(tflops, 1),
             "tflops_fastest": round(flop / (min(all_ms) * 1e-3) / 1e12, 1),
-            "frac_of_fp4_dense_peak": round(tflops / 10100.0, 4)}
+            "frac_of_fp4_dense_peak": round(tflops / 10100.0, 4),
+            "library_reference": mx_gemm_library(a, b, c, flop, stream, reps, warmup)}
+
+
+def mx_gemm_library(a, b, c, flop, stream, reps, warmup):
+    """The same product through torch._scaled_mm on MXFP4 operands (hipBLASLt): the same code
+    and E8M0 scale bytes viewed as float4_e2m1fn_x2 / float8_e8m0fnu, timed the same way
+    right after the library's own kernel, and its result compared with that kernel's
+    (max |difference| over max |C|; the library rounds its output to its out_dtype).
+    Context only: nothing in the library's path calls it."""
+    import numpy as np
+    import torch
+
+    try:
+        a4, b4 = a.codes.view(torch.float4_e2m1fn_x2), b.codes.view(torch.float4_e2m1fn_x2)
+        sa, sb = a.scales.view(torch.float8_e8m0fnu), b.scales.view(torch.float8_e8m0fnu)
+        err = None
+        for dt in (torch.float32, torch.bfloat16):
+            try:
+                with torch.cuda.stream(stream):
+                    ref = torch._scaled_mm(a4, b4.t(), sa, sb, out_dtype=dt)
+                torch.cuda.synchronize()
+                break
+            except Exception as e:          # this out_dtype is not offered: try the next
+                err = e
+        else:
+            raise err
+        # the kernel's C carries the factor 2^-7 of a rotated pair
+        diff = float((c - ref.float() * 2.0 ** -7).abs().max() / c.abs().max())
+        for _ in range(warmup):
+            with torch.cuda.stream(stream):
+                torch._scaled_mm(a4, b4.t(), sa, sb, out_dtype=dt)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            for e0, e1 in ev:
+                e0.record(stream)
+                torch._scaled_mm(a4, b4.t(), sa, sb, out_dtype=dt)
+                e1.record(stream)
+        torch.cuda.synchronize()
+        all_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+        ms = float(np.median(all_ms))
+        return {"call": "torch._scaled_mm (hipBLASLt), MXFP4 operands", "out_dtype": str(dt),
+                "ms": round(ms, 4), "min_ms": round(float(min(all_ms)), 4),
+                "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                "max_abs_diff_over_max_abs_c": diff}
+    except Exception as e:                  # not offered by this torch / hipBLASLt build
+        return {"call": "torch._scaled_mm (hipBLASLt), MXFP4 operands",
+                "error": repr(e)[:300]}
 
 
 def mx_alg_bytes(rows, cols, layouts=2):
