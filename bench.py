@@ -400,53 +400,81 @@ def gemm_check(nv, workloads, dev, a, stream, reps=10, warmup=3):
     res = {"kernel": "k_gemm (dequantize into LDS as FP16, v_mfma_f32_32x32x16_f16)", "M": M,
            "N": N, "K": K, "ms": round(ms, 4), "min_ms": round(float(min(all_ms)), 4),
            "tflops": round(tflops, 1), "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4)}
-    res["native_fp4"] = mx_gemm(nv, workloads, dev, stream, reps, warmup)
+    res["native_fp4"] = mx_gemm(nv, workloads, dev, stream)
     return res
 
 
-def mx_gemm(nv, workloads, dev, stream, reps=10, warmup=3):
+def mx_gemm(nv, workloads, dev, stream, reps=20, warmup=20):
     """The native FP4 consumer on the same shape: the 16384 x 8192 input quantized to MXFP4
     (SR after the rotation) against the 8192 x 8192 weight (RTN after the same rotation),
-    C = A B^T on v_mfma_scale_f32_32x32x64_f8f6f4, against MI355X's 10.1 PFLOP/s dense FP4."""
+    C = A B^T on v_mfma_scale_f32_32x32x64_f8f6f4, against MI355X's 10.1 PFLOP/s dense FP4.
+    The operands are K-tiled (the producer writes each 128-element step of K of all rows in
+    one piece, so the GEMM's loads are contiguous).  Beside it: the same product on row-major
+    operands (the other kernel, equal bit for bit) and through hipBLASLt's own MXFP4 GEMM
+    (torch._scaled_mm on the same code and scale bytes).  The variants take turns launch by
+    launch after `warmup` rounds, so they see the same clock: under a sustained FP4 load the
+    part's clock settles over the first tens of launches."""
     import numpy as np
     import torch
 
-    a = nv.mxfp4_quantize(workloads.c4().to(dev), sr=True, seed=1, rht=True, rht_seed=1).row
-    b = nv.mxfp4_quantize(workloads.c4w().to(dev), rht=True, rht_seed=1).row
-    c = torch.empty((a.codes.shape[0], b.codes.shape[0]), dtype=torch.float32, device=dev)
-    for _ in range(warmup):
-        nv.mxfp4_gemm(a, b, rotated_pair=True, out=c, stream=stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for e0, e1 in ev:
-        e0.record(stream)
-        nv.mxfp4_gemm(a, b, rotated_pair=True, out=c, stream=stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    all_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    ms = float(np.median(all_ms))
-    M, K = a.codes.shape[0], a.codes.shape[1] * 2
-    N = b.codes.shape[0]
+    x, w = workloads.c4().to(dev), workloads.c4w().to(dev)
+
+    def operands(k_tiled):
+        return (nv.mxfp4_quantize(x, sr=True, seed=1, rht=True, rht_seed=1, k_tiled=k_tiled).row,
+                nv.mxfp4_quantize(w, rht=True, rht_seed=1, k_tiled=k_tiled).row)
+
+    M, N, K = x.shape[0], w.shape[0], x.shape[1]
     flop = 2.0 * M * N * K
-    tflops = flop / (ms * 1e-3) / 1e12
-    # a sustained FP4 load lowers the part's clock over consecutive launches: the fastest
-    # launch is reported beside the median
-    return {"kernel": "k_gemm_mx2 (MXFP4 operands, K steps of 256 as K % 512 == 0, "
-                      "v_mfma_scale_f32_32x32x64_f8f6f4)", "M": M,
-            "N": N, "K": K, "ms": round(ms, 4), "min_ms": round(float(min(all_ms)), 4),
-            "tflops": round(tflops, 1),
-            "tflops_fastest": round(flop / (min(all_ms) * 1e-3) / 1e12, 1),
-            "frac_of_fp4_dense_peak": round(tflops / 10100.0, 4),
-            "library_reference": mx_gemm_library(a, b, c, flop, stream, reps, warmup)}
+    (a, b), (ar, br) = operands(True), operands(False)
+    c = torch.empty((M, N), dtype=torch.float32, device=dev)
+    cr = torch.empty((M, N), dtype=torch.float32, device=dev)
+    nv.mxfp4_gemm(a, b, rotated_pair=True, out=c, stream=stream)
+    nv.mxfp4_gemm(ar, br, rotated_pair=True, out=cr, stream=stream)
+    torch.cuda.synchronize()
+    same_bits = bool(torch.equal(c.view(torch.int32), cr.view(torch.int32)))
+    lib = mx_gemm_library(ar, br, cr, stream)
+    variants = {"k_tiled": lambda: nv.mxfp4_gemm(a, b, rotated_pair=True, out=c, stream=stream),
+                "row_major": lambda: nv.mxfp4_gemm(ar, br, rotated_pair=True, out=cr,
+                                                   stream=stream)}
+    if "run" in lib:
+        variants["library"] = lib.pop("run")
+    for _ in range(warmup):
+        for fn in variants.values():
+            fn()
+    ev = {k: [] for k in variants}
+    for _ in range(reps):
+        for k, fn in variants.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev[k].append((e0, e1))
+    torch.cuda.synchronize()
+
+    def summary(k):
+        t = [e0.elapsed_time(e1) for e0, e1 in ev[k]]
+        ms = float(np.median(t))
+        return {"ms": round(ms, 4), "min_ms": round(float(min(t)), 4),
+                "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                "tflops_fastest": round(flop / (min(t) * 1e-3) / 1e12, 1)}
+
+    res = {"kernel": "k_gemm_mx<true> (K-tiled MXFP4 operands, K steps of 128, four LDS "
+                     "stages, v_mfma_scale_f32_32x32x64_f8f6f4)", "M": M, "N": N, "K": K}
+    res.update(summary("k_tiled"))
+    res["frac_of_fp4_dense_peak"] = round(res["tflops"] / 10100.0, 4)
+    res["row_major"] = {"kernel": "k_gemm_mx2 (row-major operands, K steps of 256)",
+                        **summary("row_major"), "same_bits_as_k_tiled": same_bits}
+    if "library" in variants:
+        lib.update(summary("library"))
+    res["library_reference"] = lib
+    return res
 
 
-def mx_gemm_library(a, b, c, flop, stream, reps, warmup):
-    """The same product through torch._scaled_mm on MXFP4 operands (hipBLASLt): the same code
-    and E8M0 scale bytes viewed as float4_e2m1fn_x2 / float8_e8m0fnu, timed the same way
-    right after the library's own kernel, and its result compared with that kernel's
-    (max |difference| over max |C|; the library rounds its output to its out_dtype).
-    Context only: nothing in the library's path calls it."""
-    import numpy as np
+def mx_gemm_library(a, b, c, stream):
+    """hipBLASLt's own MXFP4 GEMM through torch._scaled_mm on the row-major operands' code and
+    E8M0 scale bytes (viewed as float4_e2m1fn_x2 / float8_e8m0fnu), for context: its result is
+    compared with the library's kernel's (max |difference| over max |C|; it rounds its output
+    to its out_dtype), and "run" is the call to time.  Nothing in the library's path calls it."""
     import torch
 
     try:
@@ -465,23 +493,12 @@ def mx_gemm_library(a, b, c, flop, stream, reps, warmup):
             raise err
         # the kernel's C carries the factor 2^-7 of a rotated pair
         diff = float((c - ref.float() * 2.0 ** -7).abs().max() / c.abs().max())
-        for _ in range(warmup):
+
+        def run():
             with torch.cuda.stream(stream):
                 torch._scaled_mm(a4, b4.t(), sa, sb, out_dtype=dt)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        with torch.cuda.stream(stream):
-            for e0, e1 in ev:
-                e0.record(stream)
-                torch._scaled_mm(a4, b4.t(), sa, sb, out_dtype=dt)
-                e1.record(stream)
-        torch.cuda.synchronize()
-        all_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-        ms = float(np.median(all_ms))
         return {"call": "torch._scaled_mm (hipBLASLt), MXFP4 operands", "out_dtype": str(dt),
-                "ms": round(ms, 4), "min_ms": round(float(min(all_ms)), 4),
-                "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
-                "max_abs_diff_over_max_abs_c": diff}
+                "max_abs_diff_over_max_abs_c": diff, "run": run}
     except Exception as e:                  # not offered by this torch / hipBLASLt build
         return {"call": "torch._scaled_mm (hipBLASLt), MXFP4 operands",
                 "error": repr(e)[:300]}
@@ -505,10 +522,13 @@ def modes_table(nv, x, out, stream, reps=40):
     modes = (("rtn", "rtn", False), ("rtn+rht", "rtn", True), ("sr", "sr", False),
              ("sr+rht", "sr", True), ("fp46+rht", "fp46", True), ("eden", "eden", True),
              ("eden, strip scales", "eden-strips", True), ("mxfp4 rtn+rht", "mx", True),
-             ("mxfp4 sr+rht", "mx-sr", True))
+             ("mxfp4 sr+rht", "mx-sr", True), ("mxfp4 rtn+rht, K-tiled", "mx-t", True),
+             ("mxfp4 sr+rht, K-tiled", "mx-sr-t", True))
     dev = x.device
     rows, cols = x.shape
     out_mx = nv.MXQuantized(nv.empty_mx_layout(rows, cols, dev), nv.empty_mx_layout(cols, rows, dev))
+    out_mxt = nv.MXQuantized(nv.empty_mx_layout(rows, cols, dev, k_tiled=True),
+                             nv.empty_mx_layout(cols, rows, dev, k_tiled=True))
     out_s = nv.Quantized(nv.empty_strip_layout(rows, cols, dev),
                          nv.empty_strip_layout(cols, rows, dev))
     ws_s = torch.empty(nv.strip_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
@@ -521,9 +541,10 @@ def modes_table(nv, x, out, stream, reps=40):
                                      layouts=("row", "col"), out=out_s, workspace=ws_s,
                                      stream=stream)
             return
-        if mode in ("mx", "mx-sr"):
-            nv.mxfp4_quantize(x, sr=mode == "mx-sr", seed=seed, rht=rht, rht_seed=1,
-                              layouts=("row", "col"), out=out_mx, stream=stream)
+        if mode.startswith("mx"):
+            nv.mxfp4_quantize(x, sr=mode.startswith("mx-sr"), seed=seed, rht=rht, rht_seed=1,
+                              layouts=("row", "col"),
+                              out=out_mxt if mode.endswith("-t") else out_mx, stream=stream)
             return
         fn = {"rtn": lambda: nv.rtn_quantize(x, rht=rht, rht_seed=1, **kw),
               "sr": lambda: nv.sr_quantize(x, seed=seed, rht=rht, rht_seed=1, **kw),

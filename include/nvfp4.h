@@ -256,24 +256,34 @@ int nvfp4_gemm_check_strips(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_
  * e/4 hi, 3, layout))).  MS-EDEN has no MXFP4 form here: stochastic rounding of its corrected
  * scales onto powers of two would add several percent of variance.  No tensor scale. */
 typedef struct mxfp4_tensor {
-    uint8_t *codes;      /* [vecs][n/2]  packed E2M1 codes, low nibble first; 16-byte aligned */
-    uint8_t *scales;     /* [vecs][n/32] E8M0 bytes, scale = 2^(byte - 127); 4-byte aligned */
+    uint8_t *codes;      /* packed E2M1 codes, low nibble first; 16-byte aligned */
+    uint8_t *scales;     /* E8M0 bytes, scale = 2^(byte - 127); 4-byte aligned */
+    int32_t k_tiled;     /* 0: codes [vecs][n/2], scales [vecs][n/32] (row-major).
+                          * 1: K-tiled, n a multiple of 128: codes [n/128][vecs][64] and
+                          *    scales [n/128][vecs][4], i.e. code byte j of vector v at
+                          *    (j / 64) * vecs * 64 + v * 64 + j % 64 and scale byte s at
+                          *    (s / 4) * vecs * 4 + v * 4 + s % 4.  The same values as the
+                          *    row-major form, stored so that a GEMM's K step of many rows is
+                          *    one contiguous piece. */
 } mxfp4_tensor;
 
 /* MXFP4 quantization of x (as for the NVFP4 quantizers: BF16 row-major, 16-byte aligned,
  * cols % 8 == 0) in one or both layouts, one pass (no tensor-wide maximum is needed).
- * block must be 32; each requested layout's n a multiple of 32 (128 with the rotation).  No
- * workspace; errors as in the conventions above. */
+ * block must be 32; each requested layout's n a multiple of 32 (128 with the rotation or when
+ * that layout is K-tiled; k_tiled must be 0 or 1).  No workspace; errors as in the
+ * conventions above. */
 int mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int block, int sr,
                    uint64_t seed, int rht, uint64_t rht_seed, const mxfp4_tensor *row_out,
                    const mxfp4_tensor *col_out, void *stream);
 
 /* C[m][n] = f * sum_k a(m,k) * b(n,k) on the FP4 matrix cores (v_mfma_scale_f32_32x32x64_
  * f8f6f4), a(m,k) = sign * magnitude * 2^(scale byte - 127) of `a` [M][K] and likewise of `b`
- * [N][K] (row layouts, K contiguous); f = 2^-7 when rotated_pair != 0 (both operands rotated
- * along K with the same rht_seed) else 1.  Products exact, FP32 accumulation (order
- * unspecified).  c is FP32 [M][N] row-major (device, 4-byte aligned).  M and N multiples of
- * 32, K a multiple of 128. */
+ * [N][K] (row layouts: K is each vector's n); f = 2^-7 when rotated_pair != 0 (both operands
+ * rotated along K with the same rht_seed) else 1.  Products exact, FP32 accumulation over K in
+ * ascending 64-element steps (so row-major and K-tiled operands give the same bits).  c is
+ * FP32 [M][N] row-major (device, 4-byte aligned).  M and N multiples of 32, K a multiple of
+ * 128; a and b both row-major or both K-tiled (else NVFP4_ERR_ARG); K-tiled operands take the
+ * faster kernel. */
 int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, int64_t M, int64_t N, int64_t K,
                int rotated_pair, float *c, void *stream);
 

@@ -437,6 +437,22 @@ def mx_quantize(x, axis: int = 0, sr: bool = False, seed: int = 0, rht: bool = F
     return MXQuantized(codes, scales)
 
 
+def mx_k_tile(codes: np.ndarray, scales: np.ndarray):
+    """The K-tiled storage of an MXFP4 layout (the same bytes, rearranged; n a multiple of 128):
+    code byte j of vector v goes to [j // 64][v][j % 64] and scale byte s to [s // 4][v][s % 4],
+    so each 128-element step of K holds every vector's 64 code bytes, then every vector's 4
+    scale bytes, in one piece."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    vecs, half = codes.shape
+    if half % 64 or scales.shape != (vecs, half // 16):
+        raise ValueError("mx_k_tile: n must be a multiple of 128 with n/32 scale bytes per vector")
+    tiles = half // 64
+    tc = np.ascontiguousarray(codes.reshape(vecs, tiles, 64).transpose(1, 0, 2))
+    ts = np.ascontiguousarray(scales.reshape(vecs, tiles, 4).transpose(1, 0, 2))
+    return tc, ts
+
+
 def mx_dequantize(codes: np.ndarray, scales: np.ndarray, rht: bool = False,
                   rht_seed: int = 0) -> np.ndarray:
     lib = _load()

@@ -177,3 +177,23 @@ def test_mxfp4_validation(L):
     assert L.mxfp4_gemm(r, r, 64, 64, 128, 2, FAKE, None) == nv.ERR_ARG
     assert L.mxfp4_gemm(None, r, 64, 64, 128, 0, FAKE, None) == nv.ERR_NULL
     assert L.mxfp4_gemm(r, r, 64, 64, 128, 0, FAKE + 2, None) == nv.ERR_ALIGN
+
+
+def test_mxfp4_k_tiled_validation(L):
+    """The K-tiled flag: 0 or 1; a K-tiled layout needs n % 128 == 0 even without the
+    rotation; the GEMM's operands must agree on it."""
+    r = ctypes.byref(nv._CMx(FAKE, FAKE + 4096, 0))
+    t = ctypes.byref(nv._CMx(FAKE, FAKE + 4096, 1))
+    bad = ctypes.byref(nv._CMx(FAKE, FAKE + 4096, 2))
+
+    def q(rows=256, cols=256, row=t, col=None):
+        return L.mxfp4_quantize(FAKE, rows, cols, 32, 0, 1, 0, 1, row, col, None)
+    assert q(row=bad) == nv.ERR_ARG
+    assert q(cols=160) == nv.ERR_SHAPE                   # K-tiled row layout: cols % 128
+    assert q(rows=96, row=None, col=t) == nv.ERR_SHAPE   # K-tiled column layout: rows % 128
+    if not _has_gpu():                                   # never launch on fake pointers
+        assert q(cols=160, row=r) == nv.ERR_HIP          # row-major only needs cols % 32
+    assert L.mxfp4_gemm(r, t, 64, 64, 128, 0, FAKE, None) == nv.ERR_ARG
+    assert L.mxfp4_gemm(t, r, 64, 64, 128, 0, FAKE, None) == nv.ERR_ARG
+    assert L.mxfp4_gemm(bad, bad, 64, 64, 128, 0, FAKE, None) == nv.ERR_ARG
+    assert L.mxfp4_gemm(t, t, 64, 64, 64, 0, FAKE, None) == nv.ERR_SHAPE     # K % 128

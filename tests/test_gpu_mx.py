@@ -1,7 +1,8 @@
 """The MXFP4 recipe on the GPU: the producer (mxfp4_quantize) against the oracle's MXFP4
-quantizer bit for bit, and the native FP4 matrix-core consumer (mxfp4_gemm) against an fp64
-product of the exact operand values, within the bound of FP32 accumulation
-(|dC| <= 2 K u sum_k |a_k b_k| + 4 u |C|, u = 2^-24)."""
+quantizer bit for bit, in the row-major and the K-tiled layout, and the native FP4 matrix-core
+consumer (mxfp4_gemm) against an fp64 product of the exact operand values, within the bound of
+FP32 accumulation (|dC| <= 2 K u sum_k |a_k b_k| + 4 u |C|, u = 2^-24); K-tiled operands give
+the row-major operands' C bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -17,15 +18,18 @@ U = 2.0 ** -24
 E2M1 = np.array([oracle.e2m1_value(c) for c in range(16)], dtype=np.float64)
 
 
-def _guarded_mx(vecs, n):
+def _guarded_mx(vecs, n, k_tiled=False):
     """An MXFP4 layout whose two tensors sit inside sentinel margins."""
     bufs = []
     views = []
-    for nbytes, shape in ((vecs * (n // 2), (vecs, n // 2)), (vecs * (n // 32), (vecs, n // 32))):
+    shapes = ((n // 128, vecs, 64), (n // 128, vecs, 4)) if k_tiled else \
+        ((vecs, n // 2), (vecs, n // 32))
+    for shape in shapes:
+        nbytes = int(np.prod(shape))
         buf = torch.full((MARGIN + nbytes + MARGIN,), SENTINEL, dtype=torch.uint8, device=DEV)
         bufs.append((buf, nbytes))
         views.append(buf[MARGIN:MARGIN + nbytes].view(shape))
-    return nv.MXFP4(*views), bufs
+    return nv.MXFP4(*views, k_tiled), bufs
 
 
 def _intact(bufs):
@@ -33,11 +37,11 @@ def _intact(bufs):
                for b, n in bufs)
 
 
-def check_mx(x, layouts, sr, rht, seed=5, rht_seed=7, what=""):
+def check_mx(x, layouts, sr, rht, seed=5, rht_seed=7, what="", k_tiled=False):
     xd = x.to(DEV)
     rows, cols = xd.shape
-    row, bufs_r = _guarded_mx(rows, cols) if "row" in layouts else (None, [])
-    col, bufs_c = _guarded_mx(cols, rows) if "col" in layouts else (None, [])
+    row, bufs_r = _guarded_mx(rows, cols, k_tiled) if "row" in layouts else (None, [])
+    col, bufs_c = _guarded_mx(cols, rows, k_tiled) if "col" in layouts else (None, [])
     q = nv.mxfp4_quantize(xd, sr=sr, seed=seed, rht=rht, rht_seed=rht_seed, layouts=layouts,
                           out=nv.MXQuantized(row, col))
     torch.cuda.synchronize()
@@ -47,9 +51,10 @@ def check_mx(x, layouts, sr, rht, seed=5, rht_seed=7, what=""):
         if t is None:
             continue
         ref = oracle.mx_quantize(xb, axis=axis, sr=sr, seed=seed, rht=rht, rht_seed=rht_seed)
+        rc, rs = oracle.mx_k_tile(ref.codes, ref.scales) if k_tiled else (ref.codes, ref.scales)
         codes, scales = t.codes.cpu().numpy(), t.scales.cpu().numpy()
-        cm = int(np.count_nonzero(codes != ref.codes))
-        sm = int(np.count_nonzero(scales != ref.scales))
+        cm = int(np.count_nonzero(codes != rc))
+        sm = int(np.count_nonzero(scales != rs))
         assert cm == 0 and sm == 0, f"{what} axis={axis}: {cm} code bytes, {sm} scales differ"
     return q
 
@@ -92,6 +97,28 @@ def test_mx_quantize_config4_full(sr, rht):
     check_mx(workloads.c4(), ("row", "col"), sr, rht, seed=1, rht_seed=1, what="c4")
 
 
+@pytest.mark.parametrize("shape,sr,rht,layouts", [
+    ((256, 1024), False, False, ("row", "col")),
+    ((256, 1024), True, True, ("row", "col")),
+    ((200, 256), True, True, ("row",)),            # ragged vectors: partial tiles
+    ((384, 640), False, True, ("row", "col")),     # several tiles along both dims
+    ((128, 384), True, False, ("col",)),           # one K tile of 128 vectors' columns
+])
+def test_mx_quantize_k_tiled(shape, sr, rht, layouts):
+    """The K-tiled layout: the oracle's codes and scales rearranged by its definition, every
+    byte, with sentinel margins around both tensors."""
+    print(f"case: MXFP4 K-tiled {shape} sr={sr} rht={rht} {layouts}", flush=True)
+    check_mx(workloads.normal(shape, seed=sum(shape) + 1), layouts, sr, rht, what=f"{shape}",
+             k_tiled=True)
+
+
+def test_mx_quantize_k_tiled_config4_full():
+    """16384 x 8192, both layouts K-tiled (the benchmark GEMM's A takes the row layout)."""
+    print("case: MXFP4 c4 K-tiled sr=True rht=True both layouts, every output", flush=True)
+    check_mx(workloads.c4(), ("row", "col"), True, True, seed=1, rht_seed=1, what="c4 K-tiled",
+             k_tiled=True)
+
+
 def _exact(t, rows):
     codes = oracle.unpack_codes(t.codes[rows].cpu().numpy())
     scale = np.exp2(t.scales[rows].cpu().numpy().astype(np.float64) - 127)
@@ -126,6 +153,43 @@ def test_mx_gemm_small(M, N, K):
     got, _ = check_gemm(c, a, b, np.arange(M), np.arange(N), 2.0 ** -7)
     xw = (x.float() @ w.float().T).cpu().numpy()
     assert np.linalg.norm(got - xw) / np.linalg.norm(xw) < 0.25
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (96, 160, 256), (288, 544, 1024),
+                                   (64, 96, 1536), (544, 288, 2048), (512, 256, 384)])
+def test_mx_gemm_k_tiled_matches_row_major(M, N, K):
+    """K-tiled operands (the same quantization stored K-tiled) give C bit for bit equal to the
+    row-major operands' (both kernels add the 64-element products over K in the same order),
+    so the row-major GEMM's bound check covers them too; checked against the bound as well."""
+    print(f"case: MXFP4 gemm K-tiled M={M} N={N} K={K}", flush=True)
+    x = workloads.normal((M, K), seed=M + K + 2).to(DEV)
+    w = workloads.normal((N, K), seed=N + K + 3, scale=0.02).to(DEV)
+    a = nv.mxfp4_quantize(x, sr=True, seed=3, rht=True, rht_seed=9).row
+    b = nv.mxfp4_quantize(w, rht=True, rht_seed=9).row
+    at = nv.mxfp4_quantize(x, sr=True, seed=3, rht=True, rht_seed=9, k_tiled=True).row
+    bt = nv.mxfp4_quantize(w, rht=True, rht_seed=9, k_tiled=True).row
+    c = nv.mxfp4_gemm(a, b, rotated_pair=True)
+    ct = nv.mxfp4_gemm(at, bt, rotated_pair=True)
+    torch.cuda.synchronize()
+    tc, ts = oracle.mx_k_tile(a.codes.cpu().numpy(), a.scales.cpu().numpy())
+    assert np.array_equal(at.codes.cpu().numpy(), tc) and np.array_equal(at.scales.cpu().numpy(), ts)
+    assert torch.equal(c.view(torch.int32), ct.view(torch.int32))
+    check_gemm(ct, a, b, np.arange(M), np.arange(N), 2.0 ** -7)
+
+
+def test_mx_gemm_k_tiled_config4_full():
+    """The benchmark's shape, 16384 x 8192 x 8192: the K-tiled GEMM equals the row-major one on
+    every entry of C, bit for bit."""
+    print("case: MXFP4 gemm c4 K-tiled against row-major, every entry", flush=True)
+    x, w = workloads.c4().to(DEV), workloads.c4w().to(DEV)
+    c = nv.mxfp4_gemm(nv.mxfp4_quantize(x, sr=True, seed=1, rht=True, rht_seed=1).row,
+                      nv.mxfp4_quantize(w, rht=True, rht_seed=1).row, rotated_pair=True)
+    ct = nv.mxfp4_gemm(nv.mxfp4_quantize(x, sr=True, seed=1, rht=True, rht_seed=1,
+                                         k_tiled=True).row,
+                       nv.mxfp4_quantize(w, rht=True, rht_seed=1, k_tiled=True).row,
+                       rotated_pair=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int32), ct.view(torch.int32))
 
 
 def test_mx_gemm_wide_scales():
@@ -169,3 +233,8 @@ def test_mx_errors():
     c = nv.mxfp4_gemm(r, r)
     torch.cuda.synchronize()
     assert c.shape == (64, 64)
+    t = nv.mxfp4_quantize(workloads.normal((64, 256), seed=2).to(DEV), k_tiled=True).row
+    with pytest.raises(ValueError):
+        nv.mxfp4_gemm(q, t)                                # one row-major, one K-tiled
+    with pytest.raises(ValueError):
+        nv.mxfp4_quantize(x, k_tiled=True)                 # K-tiled needs n % 128 (200)

@@ -168,3 +168,23 @@ def test_sr_draws_are_independent_per_element():
     assert abs(u.mean() - 0.5) < 0.01
     agree = (u[:, 1:] == u[:, :-1]).mean()
     assert abs(agree - 0.5) < 0.01, agree
+
+
+def test_k_tile_places_every_byte_by_its_index():
+    """The K-tiled storage against its definition, one byte at a time: code byte j of vector v
+    at flat offset (j // 64) * vecs * 64 + v * 64 + j % 64, scale byte s at
+    (s // 4) * vecs * 4 + v * 4 + s % 4; and a shape that is not a multiple of 128 is refused."""
+    rng = np.random.default_rng(3)
+    vecs, n = 5, 384
+    codes = rng.integers(0, 256, (vecs, n // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (vecs, n // 32), dtype=np.uint8)
+    tc, ts = oracle.mx_k_tile(codes, scales)
+    assert tc.shape == (n // 128, vecs, 64) and ts.shape == (n // 128, vecs, 4)
+    fc, fs = tc.reshape(-1), ts.reshape(-1)
+    for v in range(vecs):
+        for j in range(n // 2):
+            assert fc[(j // 64) * vecs * 64 + v * 64 + j % 64] == codes[v, j]
+        for k in range(n // 32):
+            assert fs[(k // 4) * vecs * 4 + v * 4 + k % 4] == scales[v, k]
+    with pytest.raises(ValueError):
+        oracle.mx_k_tile(codes[:, :48], scales[:, :6])

@@ -46,12 +46,15 @@ class _CTensor(ctypes.Structure):
 
 
 class _CMx(ctypes.Structure):
-    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("k_tiled", ctypes.c_int32)]
 
 
 class MXFP4(NamedTuple):
-    codes: torch.Tensor         # uint8 [vecs, n/2]
-    scales: torch.Tensor        # uint8 [vecs, n/32], E8M0 bits: 2^(byte - 127)
+    codes: torch.Tensor         # uint8 [vecs, n/2]; K-tiled: [n/128, vecs, 64]
+    scales: torch.Tensor        # uint8 [vecs, n/32], E8M0 bits: 2^(byte - 127); K-tiled:
+                                # [n/128, vecs, 4]
+    k_tiled: bool = False       # the K-tiled layout (same values; the faster GEMM operand)
 
 
 class MXQuantized(NamedTuple):
@@ -473,41 +476,72 @@ def nvfp4_gemm_check(a: NVFP4, b: NVFP4, rotated_pair: bool = False,
     return out
 
 
-def empty_mx_layout(vecs: int, n: int, device) -> MXFP4:
-    """Caller-side allocation of one MXFP4 layout's outputs."""
-    return MXFP4(torch.empty((vecs, n // 2), dtype=torch.uint8, device=device),
-                 torch.empty((vecs, n // 32), dtype=torch.uint8, device=device))
+def _mx_shapes(vecs: int, n: int, k_tiled: bool):
+    if k_tiled:
+        return (n // 128, vecs, 64), (n // 128, vecs, 4)
+    return (vecs, n // 2), (vecs, n // 32)
+
+
+def empty_mx_layout(vecs: int, n: int, device, k_tiled: bool = False) -> MXFP4:
+    """Caller-side allocation of one MXFP4 layout's outputs (K-tiled: n a multiple of 128)."""
+    cs, ss = _mx_shapes(vecs, n, k_tiled)
+    return MXFP4(torch.empty(cs, dtype=torch.uint8, device=device),
+                 torch.empty(ss, dtype=torch.uint8, device=device), bool(k_tiled))
 
 
 def _cmx(t: Optional[MXFP4]):
     if t is None:
         return None
-    return ctypes.byref(_CMx(t.codes.data_ptr(), t.scales.data_ptr()))
+    return ctypes.byref(_CMx(t.codes.data_ptr(), t.scales.data_ptr(), int(bool(t.k_tiled))))
+
+
+def _as_mx(t, name: str) -> MXFP4:
+    if isinstance(t, MXFP4):
+        return t
+    if isinstance(t, tuple) and len(t) in (2, 3):
+        return MXFP4(*t)
+    raise ValueError(f"{name} must be an MXFP4 (codes, scales[, k_tiled]) tuple")
+
+
+def _mx_dims(t: MXFP4, name: str):
+    """(vecs, n) of an MXFP4 layout, from its codes tensor's shape."""
+    want = 3 if t.k_tiled else 2
+    if not isinstance(t.codes, torch.Tensor) or t.codes.dim() != want:
+        raise ValueError(f"{name}.codes must be a {want}-D uint8 tensor")
+    if t.k_tiled:
+        return t.codes.shape[1], t.codes.shape[0] * 128
+    return t.codes.shape[0], t.codes.shape[1] * 2
 
 
 def _check_mx_layout(t, name: str, vecs: int, n: int, device) -> MXFP4:
-    if not isinstance(t, MXFP4):
-        if not (isinstance(t, tuple) and len(t) == 2):
-            raise ValueError(f"{name} must be an MXFP4 (codes, scales) pair")
-        t = MXFP4(*t)
-    _check_buffer(t.codes, f"{name}.codes", torch.uint8, (vecs, n // 2), device)
-    _check_buffer(t.scales, f"{name}.scales", torch.uint8, (vecs, n // 32), device)
+    t = _as_mx(t, name)
+    if t.k_tiled and n % 128:
+        raise ValueError(f"{name}: a K-tiled layout needs n a multiple of 128, not {n}")
+    cs, ss = _mx_shapes(vecs, n, t.k_tiled)
+    _check_buffer(t.codes, f"{name}.codes", torch.uint8, cs, device)
+    _check_buffer(t.scales, f"{name}.scales", torch.uint8, ss, device)
     return t
 
 
 def mxfp4_quantize(x: torch.Tensor, sr: bool = False, seed: int = 0, rht: bool = False,
                    rht_seed: int = 0, layouts=("row",), out: Optional[MXQuantized] = None,
-                   stream=None) -> MXQuantized:
+                   stream=None, k_tiled: bool = False) -> MXQuantized:
     """MXFP4 quantization (E2M1 codes, one E8M0 scale per 32), RTN or SR, optionally after the
-    random-sign Hadamard rotation; the operand format of the native FP4 matrix cores."""
+    random-sign Hadamard rotation; the operand format of the native FP4 matrix cores.  With
+    k_tiled the outputs it allocates take the K-tiled layout (a caller's `out` layouts carry
+    their own flag)."""
     if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous 2-D bfloat16 device tensor")
     rows, cols = x.shape
     want_row, want_col = "row" in layouts, "col" in layouts
     if out is None:
+        for want, n in ((want_row, cols), (want_col, rows)):
+            if want and k_tiled and n % 128:
+                raise ValueError(f"a K-tiled layout needs n a multiple of 128, not {n}")
         with _on(stream, x.device):
-            out = MXQuantized(empty_mx_layout(rows, cols, x.device) if want_row else None,
-                              empty_mx_layout(cols, rows, x.device) if want_col else None)
+            out = MXQuantized(
+                empty_mx_layout(rows, cols, x.device, k_tiled) if want_row else None,
+                empty_mx_layout(cols, rows, x.device, k_tiled) if want_col else None)
     else:
         for name, want, t in (("row", want_row, out.row), ("col", want_col, out.col)):
             if want and t is None:
@@ -524,15 +558,13 @@ def mxfp4_quantize(x: torch.Tensor, sr: bool = False, seed: int = 0, rht: bool =
 def mxfp4_gemm(a: MXFP4, b: MXFP4, rotated_pair: bool = False,
                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """C = A B^T of two MXFP4 row-layout operands ([M, K] and [N, K]) on the FP4 matrix
-    cores, FP32 [M, N]."""
-    a = MXFP4(*a) if isinstance(a, tuple) and len(a) == 2 else a
-    b = MXFP4(*b) if isinstance(b, tuple) and len(b) == 2 else b
-    if not isinstance(a, MXFP4) or not isinstance(b, MXFP4) or \
-            not isinstance(a.codes, torch.Tensor) or not isinstance(b.codes, torch.Tensor) or \
-            a.codes.dim() != 2 or b.codes.dim() != 2:
-        raise ValueError("operands must be MXFP4 (codes, scales) pairs of 2-D uint8 tensors")
-    M, K = a.codes.shape[0], a.codes.shape[1] * 2
-    N = b.codes.shape[0]
+    cores, FP32 [M, N].  Both operands row-major or both K-tiled (the faster kernel); the
+    result is the same bit for bit."""
+    a, b = _as_mx(a, "a"), _as_mx(b, "b")
+    if bool(a.k_tiled) != bool(b.k_tiled):
+        raise ValueError("a and b must both be row-major or both K-tiled")
+    M, K = _mx_dims(a, "a")
+    N, _ = _mx_dims(b, "b")
     dev = a.codes.device
     a = _check_mx_layout(a, "a", M, K, dev)
     b = _check_mx_layout(b, "b", N, K, dev)

@@ -32,13 +32,13 @@ extern "C" hipError_t nvfp4k_gemm(int local, const uint8_t *a_codes, const uint8
                                   int64_t N, int64_t K, int rotated_pair, float *c,
                                   hipStream_t st);
 extern "C" hipError_t nvfp4k_quant_mx(int sr, int rht, int layouts, const void *x, int64_t R,
-                                      int64_t C, uint8_t *codes0, uint8_t *scales0,
-                                      uint8_t *codes1, uint8_t *scales1, uint64_t seed,
-                                      uint64_t rht_seed, hipStream_t st);
+                                      int64_t C, uint8_t *codes0, uint8_t *scales0, int tiled0,
+                                      uint8_t *codes1, uint8_t *scales1, int tiled1,
+                                      uint64_t seed, uint64_t rht_seed, hipStream_t st);
 extern "C" hipError_t nvfp4k_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales,
                                      const uint8_t *b_codes, const uint8_t *b_scales,
-                                     int64_t M, int64_t N, int64_t K, int rotated_pair,
-                                     float *c, hipStream_t st);
+                                     int64_t M, int64_t N, int64_t K, int tiled,
+                                     int rotated_pair, float *c, hipStream_t st);
 extern "C" hipError_t nvfp4k_dequantize(int local, const uint8_t *codes, const uint8_t *scales,
                                         const float *g, int64_t vecs, int64_t n, int rht,
                                         uint64_t rht_seed, float *out, hipStream_t st);
@@ -360,24 +360,25 @@ int mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t cols, int block, in
         if (!t) continue;
         if (!empty && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
         if (!aligned(t->codes, 16) || !aligned(t->scales, 4)) return NVFP4_ERR_ALIGN;
+        if (t->k_tiled != 0 && t->k_tiled != 1) return NVFP4_ERR_ARG;
     }
     if (!x_bf16 && !empty) return NVFP4_ERR_NULL;
     if (block != 32) return NVFP4_ERR_GROUP;
     if ((sr != 0 && sr != 1) || (rht != 0 && rht != 1)) return NVFP4_ERR_ARG;
     if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
     if (!fits(rows, cols)) return NVFP4_ERR_ARG;
-    const int64_t unit = rht ? 128 : 32;
     if (cols % 8) return NVFP4_ERR_SHAPE;
-    if (row_out && cols % unit) return NVFP4_ERR_SHAPE;
-    if (col_out && rows % unit) return NVFP4_ERR_SHAPE;
+    if (row_out && cols % (rht || row_out->k_tiled ? 128 : 32)) return NVFP4_ERR_SHAPE;
+    if (col_out && rows % (rht || col_out->k_tiled ? 128 : 32)) return NVFP4_ERR_SHAPE;
     if (!aligned(x_bf16, 16)) return NVFP4_ERR_ALIGN;
     int rc = check_device();
     if (rc) return rc;
     const int layouts = (row_out ? 1 : 0) | (col_out ? 2 : 0);
     const hipError_t e = nvfp4k_quant_mx(
         sr, rht, layouts, x_bf16, rows, cols, row_out ? row_out->codes : nullptr,
-        row_out ? row_out->scales : nullptr, col_out ? col_out->codes : nullptr,
-        col_out ? col_out->scales : nullptr, seed, rht_seed, static_cast<hipStream_t>(stream));
+        row_out ? row_out->scales : nullptr, row_out ? row_out->k_tiled : 0,
+        col_out ? col_out->codes : nullptr, col_out ? col_out->scales : nullptr,
+        col_out ? col_out->k_tiled : 0, seed, rht_seed, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
@@ -386,6 +387,7 @@ int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, int64_t M, int64_t 
 {
     if (!a || !b) return NVFP4_ERR_NULL;
     if (rotated_pair != 0 && rotated_pair != 1) return NVFP4_ERR_ARG;
+    if ((a->k_tiled != 0 && a->k_tiled != 1) || a->k_tiled != b->k_tiled) return NVFP4_ERR_ARG;
     if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
     if (!fits(M, N) || !fits(M, K) || !fits(N, K)) return NVFP4_ERR_ARG;
     if (M % 32 || N % 32 || K % 128) return NVFP4_ERR_SHAPE;
@@ -397,7 +399,8 @@ int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, int64_t M, int64_t 
     int rc = check_device();
     if (rc) return rc;
     const hipError_t e = nvfp4k_gemm_mx(a->codes, a->scales, b->codes, b->scales, M, N, K,
-                                        rotated_pair, c, static_cast<hipStream_t>(stream));
+                                        a->k_tiled, rotated_pair, c,
+                                        static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

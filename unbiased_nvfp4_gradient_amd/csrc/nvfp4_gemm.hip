@@ -278,9 +278,12 @@ constexpr int MX_ROW = MX_BK / 2;             // code bytes per row and step
 constexpr int MX_CODES = (BM + BN) * MX_ROW;  // code bytes of one A + B stage (32 KiB)
 constexpr int MX_STAGE = MX_CODES + 4 * (BM + BN);   // + 4 scale bytes per row and step
 
+// Row-major operands: codes [rows][K/2], scales [rows][K/32].  K-tiled operands (the layout
+// the MXFP4 producer writes on request): codes [K/128][rows][64], scales [K/128][rows][4], so
+// that one K step of 256 rows is 16 KiB of codes and 1 KiB of scales in one piece.
 struct MxOperand {
-    const uint8_t *codes;    // [rows][K/2]
-    const uint8_t *scales;   // [rows][K/32]
+    const uint8_t *codes;
+    const uint8_t *scales;
 };
 
 #define MX_LDS(p) ((__attribute__((address_space(3))) void *)(p))
@@ -292,15 +295,21 @@ __device__ __forceinline__ int mx_slot(int i, int c) { return 4 * i + (c ^ ((i >
 // 512 k + 64 w + L in round k, i.e. chunk c of row i with mx_slot(i, c) that slot.  Every
 // row's 4 scale bytes come in one 4-byte load per lane (waves 0..3 A's rows 64 w + L,
 // waves 4..7 B's).  Rows past an operand re-read its last row (they feed only entries of C
-// that are not stored).  The sources are those of step 0; step kt adds 64 kt bytes to the
-// code sources and 4 kt to the scale source.  The destinations are offsets in a stage, the
-// same for every lane of a wave (the load writes lane L's 16 bytes at offset + 16 L).
+// that are not stored).  The sources are those of step 0; step kt adds kt times a step to
+// them: 64 bytes of codes and 4 of scales in a row-major operand, a whole K step of the
+// operand's rows (64 or 4 bytes per row) in a K-tiled one.  With K-tiled operands the 64 lanes
+// of a code load read 16 consecutive rows' 64 bytes, 1 KiB in one piece, where a row-major
+// operand spreads them over 16 rows of K/2 bytes each; that difference alone makes the loads
+// markedly cheaper.  The destinations are offsets in a stage, the same for every lane of a
+// wave (the load writes lane L's 16 bytes at offset + 16 L).
 struct MxLoads {
     const uint8_t *src[4];       // [2 op + k]: codes
     const uint8_t *ssrc;         // scales
+    int64_t cstep[2], sstep;     // bytes per K step: codes of A, of B; this thread's scales
     uint32_t dst[4], sdst;       // offsets in a stage (wave-uniform)
 };
 
+template <bool TILED>
 __device__ __forceinline__ MxLoads mx_loads(const MxOperand &A, const MxOperand &B, int64_t M,
                                             int64_t N, int64_t K, int64_t m0, int64_t n0)
 {
@@ -316,15 +325,17 @@ __device__ __forceinline__ MxLoads mx_loads(const MxOperand &A, const MxOperand 
             const int s = 512 * k + 64 * w + lane;
             const int i = s >> 2, c = (s & 3) ^ ((i >> 2) & 3);
             const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
-            l.src[2 * op + k] = codes + row * (K >> 1) + 16 * c;
+            l.src[2 * op + k] = codes + row * (TILED ? MX_ROW : (K >> 1)) + 16 * c;
             l.dst[2 * op + k] = (uint32_t)(op * BM * MX_ROW + 16 * (512 * k + 64 * w));
         }
+        l.cstep[op] = TILED ? rows * MX_ROW : MX_ROW;
     }
     const bool on_b = w >= 4;
     const int64_t rows = on_b ? N : M, row0 = on_b ? n0 : m0;
     const int i = 64 * (w & 3) + lane;
     const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
-    l.ssrc = (on_b ? B.scales : A.scales) + row * (K >> 5);
+    l.ssrc = (on_b ? B.scales : A.scales) + row * (TILED ? 4 : (K >> 5));
+    l.sstep = TILED ? rows * 4 : 4;
     l.sdst = (uint32_t)(MX_CODES + 4 * (on_b ? BM : 0) + 4 * 64 * (w & 3));
     return l;
 }
@@ -334,9 +345,9 @@ __device__ __forceinline__ void mx_stage(const MxLoads &l, int64_t kt, uint8_t *
 {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        __builtin_amdgcn_global_load_lds(l.src[q] + kt * MX_ROW, MX_LDS(stage + l.dst[q]), 16, 0,
-                                         0);
-    __builtin_amdgcn_global_load_lds(l.ssrc + 4 * kt, MX_LDS(stage + l.sdst), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(l.src[q] + kt * l.cstep[q >> 1],
+                                         MX_LDS(stage + l.dst[q]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(l.ssrc + kt * l.sstep, MX_LDS(stage + l.sdst), 4, 0, 0);
 }
 
 __device__ __forceinline__ v8i mx_frag(const uint8_t *p)
@@ -447,7 +458,7 @@ __device__ __forceinline__ void mx_mfma(f32x16 (&acc)[2][4], const MxFrags &f, c
 }
 
 // C[M][N] = f * sum_k A[m][k] * B[n][k].  Grid (ceil(N/256), ceil(M/256)), 512 threads.
-// M and N multiples of 32, K a multiple of 128.
+// M and N multiples of 32, K a multiple of 128; TILED: both operands K-tiled.
 //
 // The fragment reads run one sub-step ahead of the matrix instructions: a step reads its
 // second sub-step's fragments before its first sub-step's instructions issue, then (after the
@@ -457,6 +468,7 @@ __device__ __forceinline__ void mx_mfma(f32x16 (&acc)[2][4], const MxFrags &f, c
 // shifts after them.  Every read of a stage is complete before the barrier of the step after
 // it, which is where the loads of a later stage may overwrite it.  The load addresses and the
 // LDS offsets are computed once.
+template <bool TILED>
 __global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, int64_t M,
                                                     int64_t N, int64_t K, float f,
                                                     float *__restrict__ C)
@@ -471,7 +483,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, in
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     const int64_t nk = K / MX_BK;
-    const MxLoads ld = mx_loads(A, B, M, N, K, m0, n0);
+    const MxLoads ld = mx_loads<TILED>(A, B, M, N, K, m0, n0);
     const MxOffsets of = mx_offsets(wm, wn, lane);
     const int sh = 8 * (lane >> 5);
     // stage s goes to buffer s % MX_NSTAGE; past the last step the loads repeat the last
@@ -763,15 +775,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx2(MxOperand A, MxOperand B, i
 
 extern "C" hipError_t nvfp4k_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales,
                                      const uint8_t *b_codes, const uint8_t *b_scales,
-                                     int64_t M, int64_t N, int64_t K, int rotated_pair,
-                                     float *c, hipStream_t st)
+                                     int64_t M, int64_t N, int64_t K, int tiled,
+                                     int rotated_pair, float *c, hipStream_t st)
 {
     using namespace nvfp4g;
     if (M == 0 || N == 0) return hipSuccess;
     const MxOperand A{a_codes, a_scales}, B{b_codes, b_scales};
     const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     const float f = rotated_pair ? 0.0078125f : 1.0f;
-    if (K % 512 == 0) k_gemm_mx2<<<grid, 512, 0, st>>>(A, B, M, N, K, f, c);
-    else k_gemm_mx<<<grid, 512, 0, st>>>(A, B, M, N, K, f, c);
+    if (tiled) k_gemm_mx<true><<<grid, 512, 0, st>>>(A, B, M, N, K, f, c);
+    else if (K % 512 == 0) k_gemm_mx2<<<grid, 512, 0, st>>>(A, B, M, N, K, f, c);
+    else k_gemm_mx<false><<<grid, 512, 0, st>>>(A, B, M, N, K, f, c);
     return hipGetLastError();
 }

@@ -442,8 +442,9 @@ __device__ __forceinline__ void build_scale_table(ScaleTable &tb, float g, int t
 // ------------------------------------------------------------------------------ arguments
 struct LayoutOut {
     uint8_t *codes;    // [vecs][n/2]
-    uint8_t *scales;   // [vecs][n/16]
+    uint8_t *scales;   // [vecs][n/16] (MXFP4: [vecs][n/32])
     float *g;          // [1], or [ceil(vecs/128)] with strip-local scales
+    int tiled;         // MXFP4 only: codes [n/128][vecs][64], scales [n/128][vecs][4]
 };
 
 struct QuantArgs {
@@ -1045,10 +1046,15 @@ __device__ __forceinline__ void tile_quant(const Tile &tile, const SignTable &st
     const int nb = left >= TILE ? 8 : (int)(left >> 4);
     const int nbl = nb - 4 * ro.h < 0 ? 0 : (nb - 4 * ro.h > 4 ? 4 : nb - 4 * ro.h);
     if constexpr (is_mx(MODE)) {
+        // this group's 64 code bytes and 4 scale bytes: in the vector's row, or (K-tiled, n a
+        // multiple of 128) in the vector's slot of the group's K tile
+        const int64_t vecs = ro.lay == 0 ? a.R : a.C;
+        uint8_t *cg = o.tiled ? o.codes + (start >> 7) * vecs * 64 + vec * 64
+                              : o.codes + vec * (n >> 1) + (start >> 1);
+        uint8_t *sg = o.tiled ? o.scales + (start >> 7) * vecs * 4 + vec * 4
+                              : o.scales + vec * (n >> 5) + (start >> 5);
         quantize_half_mx<MODE == MODE_MX_SR>(r, bm, ro.h, nbl, a.seed, (uint32_t)ro.lay, vec, n,
-                                             start / TILE, o.codes + vec * (n >> 1) + (start >> 1),
-                                             o.scales + vec * (n >> 5) + (start >> 5),
-                                             (n & (TILE - 1)) == 0);
+                                             start / TILE, cg, sg, (n & (TILE - 1)) == 0);
     } else {
         const float4 gs = tb.e[TAB_G];
         quantize_half<MODE>(r, bm, ro.h, nbl, gs.x, tb, gs.y, gs.z, a.seed, (uint32_t)ro.lay, vec,
@@ -1542,14 +1548,14 @@ extern "C" hipError_t nvfp4k_quant(int mode, int rht, int layouts, const void *x
 
 // MXFP4 quantization, one pass (the E8M0 scales need no tensor-wide maximum).
 extern "C" hipError_t nvfp4k_quant_mx(int sr, int rht, int layouts, const void *x, int64_t R,
-                                      int64_t C, uint8_t *codes0, uint8_t *scales0,
-                                      uint8_t *codes1, uint8_t *scales1, uint64_t seed,
-                                      uint64_t rht_seed, hipStream_t st)
+                                      int64_t C, uint8_t *codes0, uint8_t *scales0, int tiled0,
+                                      uint8_t *codes1, uint8_t *scales1, int tiled1,
+                                      uint64_t seed, uint64_t rht_seed, hipStream_t st)
 {
     using namespace nvfp4k;
     QuantArgs a = make_args(x, R, C, nullptr, seed, rht_seed);
-    a.out[0] = {codes0, scales0, nullptr};
-    a.out[1] = {codes1, scales1, nullptr};
+    a.out[0] = {codes0, scales0, nullptr, tiled0};
+    a.out[1] = {codes1, scales1, nullptr, tiled1};
     if (a.tiles == 0) return hipSuccess;
     if (sr) rht ? quant_lay<MODE_MX_SR, true, false>(a, layouts, st)
                 : quant_lay<MODE_MX_SR, false, false>(a, layouts, st);
