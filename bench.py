@@ -616,7 +616,8 @@ def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=7):
     """One Quartet II linear layer's products at the shape of a 1.9B Llama-style model's
     gate projection (32768 tokens, 2048 -> 8192): forward 4/6 + GEMM, backward MS-EDEN of
     dY (both layouts), W and X + two GEMMs.  Reports the whole forward + backward, the
-    three GEMMs alone on already-quantized operands, and the same three products as BF16
+    three GEMMs alone on already-quantized operands, the same with the native FP4 recipe
+    (MXFP4, products on the FP4 matrix cores), and the same three products as BF16
     torch.mm (hipBLASLt) for context."""
     import numpy as np
     import torch
@@ -673,6 +674,24 @@ def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=7):
         torch.mm(dyt, x)
 
     ms_bf16 = timed(bf16)
+
+    # the native FP4 recipe: K-tiled MXFP4 operands (forward RTN, backward SR), products on
+    # the FP4 matrix cores
+    def step_mx():
+        linear.forward_product(x, w, 1, scales="mx")
+        linear.backward_products(dy, x, w, 1, "sr", scales="mx")
+
+    ms_step_mx = timed(step_mx)
+    _, (mx_x, mx_w) = linear.forward_product(x, w, 1, operands=True, scales="mx")
+    _, (mdy_r, mw_c, mdy_c, mx_c) = linear.backward_products(dy, x, w, 1, "sr", operands=True,
+                                                             scales="mx")
+
+    def gemms_mx():
+        nv.mxfp4_gemm(mx_x, mx_w, True, out=outs[0])
+        nv.mxfp4_gemm(mdy_r, mw_c, True, out=outs[1])
+        nv.mxfp4_gemm(mdy_c, mx_c, True, out=outs[2])
+
+    ms_gemm_mx = timed(gemms_mx)
     flops = 3 * 2.0 * t * n_in * n_out
     return {"shape": f"T={t}, in={n_in}, out={n_out} (gate projection)",
             "ms_forward_backward": round(ms_step, 3),
@@ -680,6 +699,10 @@ def linear_layer(nv, dev, t=32768, n_in=2048, n_out=8192, reps=7):
             "ms_three_gemms": round(ms_gemm, 3),
             "ms_quantize": round(ms_step - ms_gemm, 3),
             "gemm_tflops": round(flops / (ms_gemm * 1e-3) / 1e12, 1),
+            "mxfp4_recipe": {"ms_forward_backward": round(ms_step_mx, 3),
+                             "ms_three_gemms": round(ms_gemm_mx, 3),
+                             "ms_quantize": round(ms_step_mx - ms_gemm_mx, 3),
+                             "gemm_tflops": round(flops / (ms_gemm_mx * 1e-3) / 1e12, 1)},
             "bf16_torch_mm_ms": round(ms_bf16, 3),
             "bf16_torch_mm_tflops": round(flops / (ms_bf16 * 1e-3) / 1e12, 1)}
 

@@ -35,3 +35,23 @@ def check_entries(c, a, b, rows, cols, f, strips=False):
     bound = 2 * K * U * mag + 4 * U * np.abs(ref) + 1e-30
     assert np.all(np.abs(got - ref) <= bound), np.max(np.abs(got - ref) / bound)
     return got, ref
+
+
+def mx_exact(codes, scales):
+    """fp64 values of row-major MXFP4 vectors: sign * magnitude * 2^(scale byte - 127)."""
+    c = oracle.unpack_codes(np.asarray(codes))
+    sc = np.exp2(np.asarray(scales).astype(np.float64) - 127)
+    return E2M1[c] * np.repeat(sc, 32, axis=1)
+
+
+def check_mx_entries(c, a_codes, a_scales, b_codes, b_scales, f):
+    """Every entry of C = f * A B^T of two MXFP4 operands (row-major numpy codes and scales)
+    against the exact product, within the bound of FP32 accumulation."""
+    A, B = mx_exact(a_codes, a_scales), mx_exact(b_codes, b_scales)
+    ref = (A @ B.T) * f
+    mag = (np.abs(A) @ np.abs(B).T) * f
+    K = A.shape[1]
+    got = c.cpu().numpy().astype(np.float64)
+    bound = 2 * K * U * mag + 4 * U * np.abs(ref) + 1e-300
+    assert np.all(np.abs(got - ref) <= bound), np.max(np.abs(got - ref) / bound)
+    return got, ref

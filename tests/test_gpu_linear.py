@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from gemm_ref import check_entries
+from gemm_ref import check_entries, check_mx_entries
 from parity import assert_parity
 from unbiased_nvfp4_gradient_amd import linear
 
@@ -187,3 +187,79 @@ def test_fig9_with_strip_scales():
                 expect = single[i] / b / b
                 print(name, b, f"{bias:.3e}/{expect:.3e}", flush=True)
                 assert 0.7 * expect < bias < 1.4 * expect, (name, b, bias, expect)
+
+
+# ----------------------------------------------------------------------------- the MXFP4 recipe
+
+def _mx_operand(q, x_cpu, axis, sr, seed, rht_seed, what):
+    """A K-tiled MXFP4 operand against the oracle's quantization, rearranged by the layout's
+    definition; returns the oracle's row-major codes and scales."""
+    ref = oracle.mx_quantize(workloads.bf16_bits(x_cpu), axis=axis, sr=sr, seed=seed, rht=True,
+                             rht_seed=rht_seed)
+    tc, ts = oracle.mx_k_tile(ref.codes, ref.scales)
+    assert q.k_tiled, what
+    assert np.array_equal(q.codes.cpu().numpy(), tc), what
+    assert np.array_equal(q.scales.cpu().numpy(), ts), what
+    return ref.codes, ref.scales
+
+
+def test_layer_mxfp4_recipe():
+    """scales="mx": every operand K-tiled MXFP4, bit-exact against the oracle (forward RTN,
+    backward SR, the layer's seeds), and every entry of the three products on the FP4 matrix
+    cores against the exact product of its operands within the FP32 bound."""
+    t, n_in, n_out = 256, 384, 128
+    print(f"case: linear layer, MXFP4 recipe, T={t} in={n_in} out={n_out}", flush=True)
+    x, w, dy = layer_inputs(t, n_in, n_out, seed=80)
+    xd, wd, dyd = x.to(DEV), w.to(DEV), dy.to(DEV)
+    s = 3
+    y, (qx, qw) = linear.forward_product(xd, wd, s, operands=True, scales="mx")
+    (dx, dw), (qdy_r, qw_c, qdy_c, qx_c) = linear.backward_products(
+        dyd, xd, wd, s, "sr", operands=True, scales="mx")
+    torch.cuda.synchronize()
+    ax = _mx_operand(qx, x, 0, False, 0, 2 * s, "X rows")
+    aw = _mx_operand(qw, w, 0, False, 0, 2 * s, "W rows")
+    ady_r = _mx_operand(qdy_r, dy, 0, True, 3 * s, 2 * s + 1, "dY rows")
+    ady_c = _mx_operand(qdy_c, dy, 1, True, 3 * s, 2 * s + 1, "dY columns")
+    aw_c = _mx_operand(qw_c, w, 1, True, 3 * s + 1, 2 * s + 1, "W columns")
+    ax_c = _mx_operand(qx_c, x, 1, True, 3 * s + 2, 2 * s + 1, "X columns")
+    f = 2.0 ** -7
+    check_mx_entries(y, *ax, *aw, f)
+    check_mx_entries(dx, *ady_r, *aw_c, f)
+    check_mx_entries(dw, *ady_c, *ax_c, f)
+    xf, wf, dyf = x.double().numpy(), w.double().numpy(), dy.double().numpy()
+    for name, got, ex in (("Y", y, xf @ wf.T), ("dX", dx, dyf @ wf), ("dW", dw, dyf.T @ xf)):
+        rel = np.linalg.norm(got.cpu().double().numpy() - ex) / np.linalg.norm(ex)
+        print(f"{name}: relative error {rel:.4f}", flush=True)
+        assert rel < 0.3, (name, rel)
+    with pytest.raises(ValueError):
+        linear.backward_products(dyd, xd, wd, s, "eden", scales="mx")
+
+
+def test_fig9_mxfp4_recipe():
+    """The MXFP4 recipe's SR backward is unbiased in the layer: the mean of B backward passes
+    tracks mse/B out to B = 256; the mean of round-to-nearest passes (whose rotations change
+    with the seed, but whose rounding is deterministic) has left mse/B by B = 256."""
+    print("case: Fig. 9 method, MXFP4 recipe, 512 x 256 -> 256, B = 1..256", flush=True)
+    t, n_in, n_out = 512, 256, 256
+    x, w, dy = layer_inputs(t, n_in, n_out, seed=90)
+    xd, wd, dyd = x.to(DEV), w.to(DEV), dy.to(DEV)
+    exact = [dyd.double() @ wd.double(), dyd.double().t() @ xd.double()]
+    norms = [float((e * e).sum()) for e in exact]
+    for scheme in ("sr", "rtn"):
+        acc = [torch.zeros_like(e) for e in exact]
+        single = [0.0, 0.0]
+        for b in range(1, 257):
+            grads = linear.backward_products(dyd, xd, wd, b, scheme, scales="mx")
+            for i, g in enumerate(grads):
+                g = g.double()
+                acc[i] += g
+                single[i] += float(((g - exact[i]) ** 2).sum()) / norms[i]
+            if b in (1, 16, 256):
+                for i, name in enumerate(("dX", "dW")):
+                    bias = float(((acc[i] / b - exact[i]) ** 2).sum()) / norms[i]
+                    expect = single[i] / b / b
+                    print(scheme, name, b, f"{bias:.3e}/{expect:.3e}", flush=True)
+                    if scheme == "sr":
+                        assert 0.7 * expect < bias < 1.4 * expect, (name, b, bias, expect)
+                    elif b == 256:
+                        assert bias > 2.0 * expect, (name, b, bias, expect)

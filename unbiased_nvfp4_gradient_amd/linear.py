@@ -27,26 +27,41 @@ vectors of each operand, i.e. per block of 128 rows of the product's first opera
 columns of its second, which the GEMM applies after its sum over K.  Every operand's strips
 run along a dimension that is not contracted, so each product keeps one correction per
 output row block and one per output column block.
+
+scales="mx" runs the layer on the native FP4 recipe instead (the same note's "fast route":
+MXFP4, one power-of-two scale per 32 elements, a Hadamard transform and stochastic rounding):
+every operand is MXFP4 in the K-tiled layout, the forward rounds to nearest, the backward
+uses the scheme "sr" (unbiased) or "rtn", and the three products run on the FP4 matrix
+cores (mxfp4_gemm).  Rotation and rounding seeds are those above.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (eden_quantize, fp46_quantize, nvfp4_gemm_check, nvfp4_gemm_check_strips,
-               nvfp4_quantize_strips, rtn_quantize, sr_quantize)
+from . import (eden_quantize, fp46_quantize, mxfp4_gemm, mxfp4_quantize, nvfp4_gemm_check,
+               nvfp4_gemm_check_strips, nvfp4_quantize_strips, rtn_quantize, sr_quantize)
 
 BACKWARD_SCHEMES = ("eden", "sr", "rtn", "fp46")
-SCALES = ("tensor", "strip")
+MX_BACKWARD_SCHEMES = ("sr", "rtn")
+SCALES = ("tensor", "strip", "mx")
 
 
 def _gemm(scales: str):
     if scales not in SCALES:
         raise ValueError(f"unknown scales {scales!r}; use one of {SCALES}")
+    if scales == "mx":
+        return mxfp4_gemm
     return nvfp4_gemm_check_strips if scales == "strip" else nvfp4_gemm_check
 
 
 def _quantize(scheme: str, x: torch.Tensor, seed: int, rht_seed: int, layouts,
               scales: str = "tensor"):
+    if scales == "mx":
+        if scheme not in MX_BACKWARD_SCHEMES:
+            raise ValueError(f"scheme {scheme!r} has no MXFP4 form; use one of "
+                             f"{MX_BACKWARD_SCHEMES}")
+        return mxfp4_quantize(x, sr=scheme == "sr", seed=seed, rht=True, rht_seed=rht_seed,
+                              layouts=layouts, k_tiled=True)
     if scales == "strip":
         if scheme not in BACKWARD_SCHEMES:
             raise ValueError(f"unknown scheme {scheme!r}; use one of {BACKWARD_SCHEMES}")
@@ -76,12 +91,14 @@ def _check_shapes(x: torch.Tensor, w: torch.Tensor):
 
 def forward_product(x: torch.Tensor, w: torch.Tensor, seed: int, operands: bool = False,
                     scales: str = "tensor"):
-    """Y = Q46(X) Q46(W)^T in FP32, X and W rotated along in with rotation seed 2s.  With
-    operands=True also returns the two quantized operands (X rows, W rows)."""
+    """Y = Q46(X) Q46(W)^T in FP32 (round-to-nearest MXFP4 with scales="mx"), X and W rotated
+    along in with rotation seed 2s.  With operands=True also returns the two quantized
+    operands (X rows, W rows)."""
     gemm = _gemm(scales)
     rs = 2 * seed
-    qx = _quantize("fp46", x, 0, rs, ("row",), scales).row
-    qw = _quantize("fp46", w, 0, rs, ("row",), scales).row
+    fwd = "rtn" if scales == "mx" else "fp46"
+    qx = _quantize(fwd, x, 0, rs, ("row",), scales).row
+    qw = _quantize(fwd, w, 0, rs, ("row",), scales).row
     y = gemm(qx, qw, rotated_pair=True)
     return (y, (qx, qw)) if operands else y
 
@@ -107,6 +124,8 @@ class QuartetLinearFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, w, seed: int, scheme: str = "eden", scales: str = "tensor"):
+        if scales == "mx" and scheme not in MX_BACKWARD_SCHEMES:
+            raise ValueError(f"scheme {scheme!r} has no MXFP4 form")
         _check_shapes(x, w)
         x, w = x.contiguous(), w.contiguous()
         ctx.save_for_backward(x, w)
@@ -132,6 +151,9 @@ class QuartetLinear(torch.nn.Module):
             raise ValueError(f"unknown backward scheme {scheme!r}")
         if scales not in SCALES:
             raise ValueError(f"unknown scales {scales!r}")
+        if scales == "mx" and scheme not in MX_BACKWARD_SCHEMES:
+            raise ValueError(f"scheme {scheme!r} has no MXFP4 form; use one of "
+                             f"{MX_BACKWARD_SCHEMES}")
         self.scales = scales
         self.weight = torch.nn.Parameter(torch.empty(
             (out_features, in_features), dtype=torch.bfloat16, device=device))
