@@ -266,8 +266,11 @@ extern "C" hipError_t nvfp4k_gemm(int local, const uint8_t *a_codes, const uint8
 // feeds the matrix cores, together with the rows' 4 scale bytes per step; chunk c of row i sits
 // in slot 4 i + (c ^ ((i >> 2) & 3)).  A 16-byte LDS read serves 16 lanes at a time from 64
 // banks (256 bytes); its lanes read 16 consecutive rows at one chunk, whose slots then cover
-// all 16 residues mod 16, i.e. 16 distinct bank groups (the bank-conflict counter reads 0).  The only wait on memory is at the top of each step, for that
-// step's own loads.
+// all 16 residues mod 16, i.e. 16 distinct bank groups (the bank-conflict counter reads 0).
+// The only wait on memory is at the top of each step, for that step's own loads.  This
+// kernel serves K-tiled operands (its fastest form: every load reads one contiguous piece)
+// and row-major operands whose K is not a multiple of 512; row-major operands with K a
+// multiple of 512 take k_gemm_mx2 below.
 namespace nvfp4g {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -532,12 +535,13 @@ __global__ void __launch_bounds__(512, 1) k_gemm_mx(MxOperand A, MxOperand B, in
 
 
 // ------------------------------------------------------------------------------ MXFP4 GEMM, K % 512 == 0
-// The same product with wider K steps, for K a multiple of 512 (every shape the benchmark and
-// the linear layer use).  Each step covers 256 elements of K: 128 code bytes per row of A and
-// B (one 128-byte line per row, where the 128-element steps above fetch half a line per row
-// per step), and each row's scale bytes come 16 at a time, once every two steps.  Measured
-// with the loads alone, a step of the narrow kernel moves its bytes at about half the rate of
-// these; the number of rows a load instruction touches, not its byte count, sets its cost.
+// The same product on row-major operands with wider K steps, for K a multiple of 512.  Each
+// step covers 256 elements of K: 128 code bytes per row of A and B (one 128-byte line per row,
+// where the 128-element steps above fetch half a line per row per step), and each row's scale
+// bytes come 16 at a time, once every two steps.  Measured with the loads alone, the narrow
+// kernel's row-major loads move their bytes at about 0.8 of the rate of these: the number of
+// rows a load instruction touches, not its byte count, sets its cost (K-tiled operands, whose
+// loads each touch 8 whole lines, do better still).
 //
 // LDS: two code stages of 64 KiB (256 rows of A then 256 of B, 128 bytes each; chunk c of row
 // i in 16-byte slot 8 i + (c ^ ((i >> 1) & 7)), so the 16 rows one 16-byte read serves at a
