@@ -238,3 +238,50 @@ def test_mx_errors():
         nv.mxfp4_gemm(q, t)                                # one row-major, one K-tiled
     with pytest.raises(ValueError):
         nv.mxfp4_quantize(x, k_tiled=True)                 # K-tiled needs n % 128 (200)
+
+
+def test_mx_graph_capture_and_replay():
+    """The MXFP4 path in a HIP graph: K-tiled SR quantization of both layouts of an input and of
+    a weight, then the FP4 GEMM of the row layouts; each of four replays (outputs cleared and
+    other work run eagerly in between) gives the eager results bit for bit."""
+    print("case: HIP graph capture of mxfp4_quantize (K-tiled) + mxfp4_gemm, 4 replays",
+          flush=True)
+    x = workloads.normal((384, 512), seed=91).to(DEV)
+    w = workloads.normal((256, 512), seed=92, scale=0.02).to(DEV)
+    other = workloads.normal((256, 256), seed=93).to(DEV)
+    qx = nv.MXQuantized(nv.empty_mx_layout(384, 512, DEV, True), nv.empty_mx_layout(512, 384, DEV, True))
+    qw = nv.MXQuantized(nv.empty_mx_layout(256, 512, DEV, True), None)
+    c = torch.empty((384, 256), dtype=torch.float32, device=DEV)
+    rx = nv.mxfp4_quantize(x, sr=True, seed=4, rht=True, rht_seed=5, layouts=("row", "col"),
+                           k_tiled=True)
+    rw = nv.mxfp4_quantize(w, rht=True, rht_seed=5, k_tiled=True)
+    rc = nv.mxfp4_gemm(rx.row, rw.row, rotated_pair=True)
+    torch.cuda.synchronize()
+
+    def work():
+        nv.mxfp4_quantize(x, sr=True, seed=4, rht=True, rht_seed=5, layouts=("row", "col"),
+                          out=qx)
+        nv.mxfp4_quantize(w, rht=True, rht_seed=5, out=qw)
+        nv.mxfp4_gemm(qx.row, qw.row, rotated_pair=True, out=c)
+
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(s):
+        work()                                                # warm-up off the capture
+    torch.cuda.current_stream(DEV).wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        for t in (qx.row.codes, qx.row.scales, qx.col.codes, qx.col.scales, qw.row.codes,
+                  qw.row.scales, c):
+            t.zero_()
+        nv.mxfp4_quantize(other, sr=True, seed=rep, layouts=("row", "col"))   # eager work between
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in ((qx.row.codes, rx.row.codes), (qx.row.scales, rx.row.scales),
+                          (qx.col.codes, rx.col.codes), (qx.col.scales, rx.col.scales),
+                          (qw.row.codes, rw.row.codes), (qw.row.scales, rw.row.scales)):
+            assert torch.equal(got, want), rep
+        assert torch.equal(c.view(torch.int32), rc.view(torch.int32)), rep
