@@ -285,3 +285,29 @@ def test_mx_graph_capture_and_replay():
                           (qw.row.codes, rw.row.codes), (qw.row.scales, rw.row.scales)):
             assert torch.equal(got, want), rep
         assert torch.equal(c.view(torch.int32), rc.view(torch.int32)), rep
+
+
+@pytest.mark.parametrize("k_tiled", [False, True])
+def test_mx_empty_shapes(k_tiled):
+    """Zero vectors or zero length: the producer writes nothing and returns; the GEMM with an
+    empty M or N returns an empty C, and with K = 0 a C of zeros."""
+    print(f"case: MXFP4 empty shapes, k_tiled={k_tiled}", flush=True)
+    q = nv.mxfp4_quantize(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV),
+                          k_tiled=k_tiled).row
+    assert q.codes.numel() == 0 and q.scales.numel() == 0
+    q = nv.mxfp4_quantize(torch.empty((256, 0), dtype=torch.bfloat16, device=DEV),
+                          layouts=("col",), k_tiled=k_tiled).col
+    assert q.codes.numel() == 0 and q.scales.numel() == 0
+    x = workloads.normal((64, 256), seed=5).to(DEV)
+    w = workloads.normal((96, 256), seed=6).to(DEV)
+    a = nv.mxfp4_quantize(x, k_tiled=k_tiled).row
+    b = nv.mxfp4_quantize(w, k_tiled=k_tiled).row
+    empty_a = nv.empty_mx_layout(0, 256, DEV, k_tiled)
+    c = nv.mxfp4_gemm(empty_a, b)
+    assert c.shape == (0, 96)
+    c = nv.mxfp4_gemm(a, nv.empty_mx_layout(0, 256, DEV, k_tiled))
+    assert c.shape == (64, 0)
+    za, zb = nv.empty_mx_layout(64, 0, DEV, k_tiled), nv.empty_mx_layout(96, 0, DEV, k_tiled)
+    c = nv.mxfp4_gemm(za, zb, out=torch.full((64, 96), 7.0, device=DEV))
+    torch.cuda.synchronize()
+    assert c.shape == (64, 96) and bool((c == 0).all())
