@@ -130,7 +130,10 @@ int eden_quantize_noalloc(const void *x_bf16, int64_t rows, int64_t cols, int gr
 
 /* Plain stochastic rounding (itsolotime opening paragraph; Telegram "Method"): tensor scale
  * amax / 2688, block scale rounded UP to E4M3 (no element clips), each element rounded to
- * one of its two E2M1 neighbours with probability given by its distance to them.
+ * one of its two E2M1 neighbours with probability given by its distance to them: the top 22
+ * bits v of element e's Philox word (word e mod 4 of Philox(seed, (e/4 lo, e/4 hi, 3,
+ * layout)), e = vector * n + position) are added to its fraction as v * 2^-22 and the sum is
+ * rounded down, so the probability of rounding up is floor(frac * 2^22) / 2^22.
  * rht != 0 rotates first (random-sign Hadamard, as MS-EDEN), rht == 0 quantizes x as is. */
 int sr_quantize(const void *x_bf16, int64_t rows, int64_t cols, int group, int block,
                 uint64_t seed, int rht, uint64_t rht_seed, const nvfp4_tensor *row_out,
@@ -252,8 +255,9 @@ int nvfp4_gemm_check_strips(const nvfp4_tensor *a, const nvfp4_tensor *b, int64_
  * 6 * 2^e >= max |r| over the block (nothing clips, so SR stays unbiased), clamped to
  * [-127, 127]; elements y = r * 2^-e rounded to the E2M1 grid by round-to-nearest-even
  * (sr == 0; Telegram digest "Method") or stochastically (sr == 1; itsolotime opening
- * paragraph; the draw of element e of a layout is word e mod 4 of Philox(seed, (e/4 lo,
- * e/4 hi, 3, layout))).  MS-EDEN has no MXFP4 form here: stochastic rounding of its corrected
+ * paragraph; the draw of element e of a layout is the top 22 bits of word e mod 4 of
+ * Philox(seed, (e/4 lo, e/4 hi, 3, layout)), added to the fraction and rounded down as for
+ * sr_quantize).  MS-EDEN has no MXFP4 form here: stochastic rounding of its corrected
  * scales onto powers of two would add several percent of variance.  No tensor scale. */
 typedef struct mxfp4_tensor {
     uint8_t *codes;      /* packed E2M1 codes, low nibble first; 16-byte aligned */
